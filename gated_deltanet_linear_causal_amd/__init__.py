@@ -1,0 +1,265 @@
+"""Python binding of libgdn.so, the gfx950 Gated DeltaNet mixer-core library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/gdn.h``.  PyTorch provides
+device memory and the current stream.  If the library has not been built the
+import of any entry point raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
+
+GDN_BF16, GDN_F32 = 0, 1
+GDN_GATE_SILU, GDN_GATE_SIGMOID = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_EUNSUPPORTED",
+          3: "GDN_EWORKSPACE", 4: "GDN_EHIP"}
+CHUNK = 64
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("h_k", ctypes.c_int32), ("h_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("conv_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float), ("l2_eps", ctypes.c_float)]
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("conv_w", ctypes.c_void_p), ("a_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
+
+
+_VP, _I32 = ctypes.c_void_p, ctypes.c_int32
+_SIGNATURES = {
+    "gdn_conv_update": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
+                                       _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "gdn_decode_step": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
+                                       _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "gdn_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Config), _I32, _I32,
+                                                      _I32]),
+    "gdn_prefill_chunked": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
+                                           _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
+                                           _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                           _VP]),
+    "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gdn_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def load_library():
+    """Load libgdn.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m gated_deltanet_linear_causal_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def header_functions():
+    """Names of the functions declared in include/gdn.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+@dataclass(frozen=True)
+class Config:
+    """Geometry and dtypes of one GDN layer (mirrors gdn_config)."""
+    h_k: int
+    h_v: int
+    d_k: int
+    d_v: int
+    conv_k: int = 4
+    act_dtype: torch.dtype = torch.bfloat16
+    out_dtype: torch.dtype = torch.bfloat16
+    gate: str = "silu"
+    norm_eps: float = 1e-6
+    l2_eps: float = 1e-6
+
+    @property
+    def conv_dim(self):
+        return 2 * self.h_k * self.d_k + self.h_v * self.d_v
+
+    @property
+    def value_dim(self):
+        return self.h_v * self.d_v
+
+    def c_struct(self) -> _Config:
+        def code(dt):
+            if dt == torch.bfloat16:
+                return GDN_BF16
+            if dt == torch.float32:
+                return GDN_F32
+            raise ValueError(f"unsupported dtype {dt}")
+        if self.gate not in ("silu", "sigmoid"):
+            raise ValueError(f"unknown gate {self.gate!r}")
+        return _Config(self.h_k, self.h_v, self.d_k, self.d_v, self.conv_k,
+                       code(self.act_dtype), code(self.out_dtype),
+                       GDN_GATE_SIGMOID if self.gate == "sigmoid" else GDN_GATE_SILU,
+                       self.norm_eps, self.l2_eps)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device=True):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _params(cfg: Config, p: dict) -> _Params:
+    _check(p["conv_w"], "conv_w", (cfg.conv_dim, cfg.conv_k), torch.float32)
+    _check(p["a_log"], "a_log", (cfg.h_v,), torch.float32)
+    _check(p["dt_bias"], "dt_bias", (cfg.h_v,), torch.float32)
+    _check(p["norm_w"], "norm_w", (cfg.d_v,), torch.float32)
+    return _Params(p["conv_w"].data_ptr(), p["a_log"].data_ptr(),
+                   p["dt_bias"].data_ptr(), p["norm_w"].data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _raise_on(status: int):
+    if status != 0:
+        raise GdnError(status, load_library().gdn_last_error().decode())
+
+
+class SeqLens:
+    """cu_seqlens held twice: on the host (validation, grid sizes) and on the
+    device (kernels)."""
+
+    def __init__(self, cu, device="cuda"):
+        host = torch.as_tensor(cu, dtype=torch.int32).contiguous().cpu()
+        self.host = host
+        self.dev = host.to(device)
+        self.n_seq = host.numel() - 1
+        self.t_total = int(host[-1]) if host.numel() else 0
+
+
+def conv_update(cfg: Config, params: dict, seqlens: SeqLens, x, conv_state, y=None,
+                stream=None):
+    """silu(causal conv) of packed raw inputs; conv_state updated in place.
+    Returns y [T, conv_dim] fp32."""
+    lib = load_library()
+    T, N = seqlens.t_total, seqlens.n_seq
+    _check(x, "x", (T, cfg.conv_dim), cfg.act_dtype)
+    _check(conv_state, "conv_state", (N, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
+    if y is None:
+        y = torch.empty((T, cfg.conv_dim), dtype=torch.float32, device=x.device)
+    _check(y, "y", (T, cfg.conv_dim), torch.float32)
+    c, p = cfg.c_struct(), _params(cfg, params)
+    _raise_on(lib.gdn_conv_update(ctypes.byref(c), ctypes.byref(p), N, T,
+                                  ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev),
+                                  _ptr(x), _ptr(conv_state), _ptr(y), _stream(stream)))
+    return y
+
+
+def decode_step(cfg: Config, params: dict, qkv, z, a, b, conv_state, state, out=None,
+                stream=None):
+    """One token per sequence; conv_state and state are updated in place.
+    Returns out [B, H_v*d_v] (cfg.out_dtype)."""
+    lib = load_library()
+    B = qkv.shape[0]
+    _check(qkv, "qkv", (B, cfg.conv_dim), cfg.act_dtype)
+    _check(z, "z", (B, cfg.value_dim), cfg.act_dtype)
+    _check(a, "a", (B, cfg.h_v), cfg.act_dtype)
+    _check(b, "b", (B, cfg.h_v), cfg.act_dtype)
+    _check(conv_state, "conv_state", (B, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
+    _check(state, "state", (B, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
+    if out is None:
+        out = torch.empty((B, cfg.value_dim), dtype=cfg.out_dtype, device=qkv.device)
+    _check(out, "out", (B, cfg.value_dim), cfg.out_dtype)
+    c, p = cfg.c_struct(), _params(cfg, params)
+    _raise_on(lib.gdn_decode_step(ctypes.byref(c), ctypes.byref(p), B, _ptr(qkv), _ptr(z),
+                                  _ptr(a), _ptr(b), _ptr(conv_state), _ptr(state), _ptr(out),
+                                  _stream(stream)))
+    return out
+
+
+def prefill_workspace_bytes(cfg: Config, n_seq: int, t_total: int, chunk: int = CHUNK) -> int:
+    c = cfg.c_struct()
+    return int(load_library().gdn_prefill_workspace_bytes(ctypes.byref(c), n_seq, t_total,
+                                                          chunk))
+
+
+def alloc_workspace(cfg: Config, n_seq: int, t_total: int, device="cuda", chunk=CHUNK):
+    nbytes = max(prefill_workspace_bytes(cfg, n_seq, t_total, chunk), 256)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def prefill_chunked(cfg: Config, params: dict, seqlens: SeqLens, qkv, z, a, b,
+                    state_in=None, state_out=None, conv_in=None, conv_out=None, out=None,
+                    workspace=None, chunk: int = CHUNK, stream=None):
+    """Chunked prefill over packed sequences.  Returns (out, state_out, conv_out)."""
+    lib = load_library()
+    T, N = seqlens.t_total, seqlens.n_seq
+    dev = qkv.device
+    _check(qkv, "qkv", (T, cfg.conv_dim), cfg.act_dtype)
+    _check(z, "z", (T, cfg.value_dim), cfg.act_dtype)
+    _check(a, "a", (T, cfg.h_v), cfg.act_dtype)
+    _check(b, "b", (T, cfg.h_v), cfg.act_dtype)
+    sshape = (N, cfg.h_v, cfg.d_k, cfg.d_v)
+    cshape = (N, cfg.conv_k - 1, cfg.conv_dim)
+    if state_in is not None:
+        _check(state_in, "state_in", sshape, torch.float32)
+    if conv_in is not None:
+        _check(conv_in, "conv_in", cshape, torch.float32)
+    if state_out is None:
+        state_out = torch.empty(sshape, dtype=torch.float32, device=dev)
+    if conv_out is None:
+        conv_out = torch.empty(cshape, dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, cfg.value_dim), dtype=cfg.out_dtype, device=dev)
+    _check(state_out, "state_out", sshape, torch.float32)
+    _check(conv_out, "conv_out", cshape, torch.float32)
+    _check(out, "out", (T, cfg.value_dim), cfg.out_dtype)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, N, T, dev, chunk)
+    c, p = cfg.c_struct(), _params(cfg, params)
+    _raise_on(lib.gdn_prefill_chunked(
+        ctypes.byref(c), ctypes.byref(p), chunk, N, T,
+        ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev),
+        _ptr(qkv), _ptr(z), _ptr(a), _ptr(b), _ptr(state_in), _ptr(state_out),
+        _ptr(conv_in), _ptr(conv_out), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, state_out, conv_out
+
+
+__all__ = ["Config", "SeqLens", "GdnError", "load_library", "header_functions",
+           "conv_update", "decode_step", "prefill_workspace_bytes", "alloc_workspace",
+           "prefill_chunked", "LIB_PATH", "CHUNK"]

@@ -1,0 +1,99 @@
+// Device helpers shared by the gfx950 kernels of the GDN library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// bf16 lives in memory as its 16 raw bits.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h)
+{
+    return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (the hardware conversion).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f)
+{
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+template <typename T> __device__ __forceinline__ float load_act(const T *p, size_t i);
+template <> __device__ __forceinline__ float load_act<float>(const float *p, size_t i)
+{
+    return p[i];
+}
+template <> __device__ __forceinline__ float load_act<bf16_t>(const bf16_t *p, size_t i)
+{
+    return bf16_bits_to_f32(p[i]);
+}
+
+// Four consecutive activations starting at a multiple of 4.
+template <typename T> __device__ __forceinline__ float4 load_act4(const T *p, size_t i);
+template <> __device__ __forceinline__ float4 load_act4<float>(const float *p, size_t i)
+{
+    return *reinterpret_cast<const float4 *>(p + i);
+}
+template <> __device__ __forceinline__ float4 load_act4<bf16_t>(const bf16_t *p, size_t i)
+{
+    const uint2 u = *reinterpret_cast<const uint2 *>(p + i);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+// Store four consecutive outputs as fp32 or bf16.
+__device__ __forceinline__ void store_out4(void *out, size_t i, float4 v, bool bf16)
+{
+    if (bf16) {
+        const uint32_t lo = f32_to_bf16(v.x) | (uint32_t(f32_to_bf16(v.y)) << 16);
+        const uint32_t hi = f32_to_bf16(v.z) | (uint32_t(f32_to_bf16(v.w)) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<bf16_t *>(out) + i) = make_uint2(lo, hi);
+    } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(out) + i) = v;
+    }
+}
+
+__device__ __forceinline__ void store_out1(void *out, size_t i, float v, bool bf16)
+{
+    if (bf16)
+        static_cast<bf16_t *>(out)[i] = f32_to_bf16(v);
+    else
+        static_cast<float *>(out)[i] = v;
+}
+
+// Nonlinearities of the mixer ("cortiq-engine 0.6.5 src/qwen4_exp.rs"
+// fn sigmoid / fn silu; softplus with threshold 20 as in "oxinfer 0.0.5
+// src/qwen.rs" DeltaRule::run).  Full-precision expf/log1pf.
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
+__device__ __forceinline__ float softplusf_(float x) { return x > 20.0f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float gatef_(float z, int sigmoid_gate)
+{
+    return sigmoid_gate ? sigmoidf_(z) : siluf_(z);
+}
+
+// Sum over the lanes of an aligned group of W lanes (W a power of two <= 64).
+template <int W> __device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float4 operator+(float4 a, float4 b)
+{
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float4 operator*(float s, float4 a)
+{
+    return make_float4(s * a.x, s * a.y, s * a.z, s * a.w);
+}
+__device__ __forceinline__ float4 fma4(float s, float4 a, float4 c)
+{
+    return make_float4(fmaf(s, a.x, c.x), fmaf(s, a.y, c.y), fmaf(s, a.z, c.z),
+                       fmaf(s, a.w, c.w));
+}
+
+} // namespace gdn

@@ -1,0 +1,42 @@
+// Host-side launch interface between the C ABI (gdn_api.cpp) and the
+// kernels.  Arguments reaching these launchers are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct Dims {
+    int h_k, h_v, d_k, d_v, conv_k;
+    int group;      // h_v / h_k
+    int conv_dim;   // 2*h_k*d_k + h_v*d_v
+    int value_dim;  // h_v*d_v
+    int act_bf16;   // 1: activations are bf16, 0: fp32
+    int out_bf16;   // 1: output is bf16, 0: fp32
+    int gate;       // 0: SiLU, 1: sigmoid
+    float norm_eps, l2_eps;
+};
+
+struct Params {
+    const float *conv_w, *a_log, *dt_bias, *norm_w;
+};
+
+hipError_t launch_conv_update(const Dims &d, const Params &p, int n_seq, int max_len,
+                              const int32_t *cu_dev, const void *x, float *conv_state,
+                              float *y, hipStream_t s);
+
+hipError_t launch_decode(const Dims &d, const Params &p, int batch, const void *qkv,
+                         const void *z, const void *a, const void *b, float *conv_state,
+                         float *state, void *out, hipStream_t s);
+
+// Chunked prefill.  Workspace layout and size are owned by prefill.hip.
+size_t prefill_workspace_bytes(const Dims &d, int n_seq, int t_total);
+hipError_t launch_prefill(const Dims &d, const Params &p, int n_seq, int t_total,
+                          int max_len, const int32_t *cu_dev, const void *qkv,
+                          const void *z, const void *a, const void *b,
+                          const float *state_in, float *state_out, const float *conv_in,
+                          float *conv_out, void *out, void *ws, hipStream_t s);
+
+} // namespace gdn

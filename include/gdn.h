@@ -1,0 +1,164 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet mixer-core library.
+ *
+ * The operation is the mixer core of Gated DeltaNet hybrid language models
+ * ("cherenkov qwen4_exp/cpu.rs", fn deltanet and fn causal_conv; "oxinfer
+ * 0.0.5 src/qwen.rs", DeltaRule::run and gdn_forward):
+ *
+ *   c_t   = silu(causal depthwise conv_K(qkv)_t)       history: last K-1 raw
+ *                                                       inputs, oldest first
+ *   q^,k^ = per key head L2 norm x (sum x^2 + l2_eps)^-1/2, q^ also * d_k^-1/2
+ *   beta  = sigmoid(b),  g = -exp(A_log) softplus(a + dt_bias),  alpha = e^g
+ *   S     <- alpha S;  delta = beta (v - S^T k^);  S <- S + k^ delta^T
+ *   o     = S^T q^                                      (updated state)
+ *   y     = o (mean_{d_v} o^2 + norm_eps)^-1/2 * norm_w * gate(z)
+ *
+ * with value head hv reading key head hv / (H_v / H_k), S a per-(sequence,
+ * value head) fp32 matrix [d_k][d_v], and gate = SiLU or sigmoid.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is device memory owned by the caller; the library
+ *     never allocates or frees memory and keeps no mutable global state.
+ *   - Layouts are dense row-major with the innermost index last:
+ *       qkv   [T][conv_dim], conv_dim = 2*H_k*d_k + H_v*d_v, channels
+ *             ordered q (H_k heads) | k (H_k heads) | v (H_v heads), each
+ *             head's d lanes contiguous;
+ *       z, out [T][H_v*d_v];  a, b [T][H_v];
+ *       state [N][H_v][d_k][d_v] fp32 (key lane major, as on the pages);
+ *       conv state [N][K-1][conv_dim] fp32, slot 0 the oldest raw input;
+ *       params: conv_w [conv_dim][K], a_log [H_v], dt_bias [H_v],
+ *               norm_w [d_v], all fp32.
+ *   - act_dtype selects bf16 or fp32 for qkv, z, a, b; out_dtype selects
+ *     bf16 (round to nearest even) or fp32 for out.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously; no call synchronises the device.
+ *   - Arguments are validated on the host before anything is enqueued: a
+ *     call that returns an error has written nothing.  gdn_last_error()
+ *     then returns a message for the calling thread.
+ *   - Supported: H_v % H_k == 0, d_k and d_v in {32, 64, 128},
+ *     1 <= K <= 4, chunk == 64.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_EINVAL = 1,        /* bad pointer, shape, alias or cu_seqlens */
+    GDN_EUNSUPPORTED = 2,  /* valid but not instantiated (dims, chunk) */
+    GDN_EWORKSPACE = 3,    /* workspace missing or too small */
+    GDN_EHIP = 4           /* the HIP runtime rejected a launch */
+} gdn_status;
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+typedef enum { GDN_GATE_SILU = 0, GDN_GATE_SIGMOID = 1 } gdn_gate;
+
+typedef struct {
+    int32_t h_k, h_v;       /* key heads, value heads */
+    int32_t d_k, d_v;       /* lanes per key / value head */
+    int32_t conv_k;         /* conv kernel width K */
+    int32_t act_dtype;      /* gdn_dtype of qkv, z, a, b */
+    int32_t out_dtype;      /* gdn_dtype of out */
+    int32_t gate;           /* gdn_gate applied to z */
+    float norm_eps;         /* gated RMSNorm epsilon (1e-6 on the pages) */
+    float l2_eps;           /* q/k L2-norm epsilon (1e-6 on the pages) */
+} gdn_config;
+
+typedef struct {
+    const float *conv_w;    /* [conv_dim][K] depthwise conv taps, no bias */
+    const float *a_log;     /* [H_v]  decay magnitude, g = -exp(a_log)... */
+    const float *dt_bias;   /* [H_v]  added to a before softplus */
+    const float *norm_w;    /* [d_v]  gated-norm weight (plain multiplier) */
+} gdn_params;
+
+/*
+ * Causal depthwise conv + SiLU over packed sequences, with history carry
+ * ("cherenkov qwen4_exp/cpu.rs" fn causal_conv; "oxinfer 0.0.5
+ * src/qwen.rs" gdn_forward, conv-state update).
+ *   cu_seqlens_host, cu_seqlens_dev: the same [n_seq+1] offsets (host copy
+ *     for validation and grid sizing, device copy for the kernel);
+ *     cu[0] = 0, non-decreasing, cu[n_seq] = t_total.
+ *   x [t_total][conv_dim] raw inputs (act_dtype);
+ *   conv_state [n_seq][K-1][conv_dim] fp32, read then overwritten in place
+ *     with each sequence's last K-1 raw inputs (a sequence shorter than K-1
+ *     keeps the tail of its old history ahead of its new inputs);
+ *   y [t_total][conv_dim] fp32 receives silu(conv).  y must not overlap x
+ *     or conv_state.
+ */
+gdn_status gdn_conv_update(const gdn_config *cfg, const gdn_params *params,
+                           int32_t n_seq, int32_t t_total,
+                           const int32_t *cu_seqlens_host,
+                           const int32_t *cu_seqlens_dev, const void *x,
+                           float *conv_state, float *y, void *stream);
+
+/*
+ * One decode step: one new token for each of `batch` sequences, one fused
+ * kernel for conv, norms, gates, the delta-rule update and the gated norm
+ * ("cherenkov qwen4_exp/cpu.rs" fn deltanet).
+ *   qkv [batch][conv_dim], z [batch][H_v*d_v], a, b [batch][H_v]
+ *     (act_dtype);
+ *   conv_state [batch][K-1][conv_dim] and state [batch][H_v][d_k][d_v],
+ *     fp32, updated in place;
+ *   out [batch][H_v*d_v] (out_dtype); must not overlap any other argument.
+ *   batch == 0 is a no-op.
+ */
+gdn_status gdn_decode_step(const gdn_config *cfg, const gdn_params *params,
+                           int32_t batch, const void *qkv, const void *z,
+                           const void *a, const void *b, float *conv_state,
+                           float *state, void *out, void *stream);
+
+/*
+ * Bytes of device workspace gdn_prefill_chunked needs for these sizes
+ * (0 if the configuration is invalid or unsupported).
+ */
+size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seq,
+                                   int32_t t_total, int32_t chunk);
+
+/*
+ * Chunked prefill over packed variable-length sequences.  Exactly the
+ * token recurrence above, evaluated chunk by chunk in the UT-transform
+ * form (intra-chunk products on matrix cores, the chain of chunk states
+ * sequential per sequence and head).  Chunks restart at every sequence
+ * start; the last chunk of a sequence may be partial.
+ *   chunk: tokens per chunk (64).
+ *   cu_seqlens_host / _dev: as in gdn_conv_update.
+ *   qkv [t_total][conv_dim], z [t_total][H_v*d_v], a, b [t_total][H_v].
+ *   state_in [n_seq][H_v][d_k][d_v] fp32, or NULL for zeros;
+ *   state_out, same shape: each sequence's final state.  May equal
+ *     state_in (in place) but must not partially overlap it.
+ *   conv_in [n_seq][K-1][conv_dim] fp32, or NULL for zeros; conv_out, same
+ *     shape, the final history.  May equal conv_in.
+ *   out [t_total][H_v*d_v] (out_dtype); must not overlap any other buffer.
+ *   workspace: device memory of at least
+ *     gdn_prefill_workspace_bytes(cfg, n_seq, t_total, chunk) bytes,
+ *     256-byte aligned, owned by the caller, contents undefined on return.
+ *   A sequence of length 0 copies its state and history through.
+ */
+gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params,
+                               int32_t chunk, int32_t n_seq, int32_t t_total,
+                               const int32_t *cu_seqlens_host,
+                               const int32_t *cu_seqlens_dev, const void *qkv,
+                               const void *z, const void *a, const void *b,
+                               const float *state_in, float *state_out,
+                               const float *conv_in, float *conv_out,
+                               void *out, void *workspace, size_t ws_bytes,
+                               void *stream);
+
+/* Static name of a status code. */
+const char *gdn_status_string(gdn_status status);
+
+/* Message describing the last error returned on the calling thread ("" if
+ * none).  The string stays valid until the next call on that thread. */
+const char *gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,155 @@
+"""The C ABI without a GPU: libgdn.so loads, exports every function that
+include/gdn.h declares, and rejects invalid calls during host-side
+validation (nothing is enqueued, no device memory is touched).
+
+The validation cases pass placeholder addresses for device buffers; every
+case is built to fail validation, and the tests that make such calls are
+skipped whenever a GPU is visible so that a validation bug can never turn
+into a launch on bogus pointers.
+"""
+import ctypes
+import subprocess
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_linear_causal_amd as gdn
+
+OK, EINVAL, EUNSUP, EWS = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gdn.load_library()
+
+
+def test_library_exports_every_header_function(lib):
+    names = gdn.header_functions()
+    assert set(names) == {"gdn_conv_update", "gdn_decode_step", "gdn_prefill_workspace_bytes",
+                          "gdn_prefill_chunked", "gdn_status_string", "gdn_last_error"}
+    dyn = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in dyn.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(names) == set(gdn._SIGNATURES)
+
+
+def test_status_strings(lib):
+    for code, name in gdn.STATUS.items():
+        assert lib.gdn_status_string(code).decode() == name
+    assert lib.gdn_status_string(99).decode() == "GDN_UNKNOWN"
+
+
+def _cfg(**kw):
+    base = dict(h_k=2, h_v=4, d_k=64, d_v=64, conv_k=4, act_dtype=0, out_dtype=1, gate=0,
+                norm_eps=1e-6, l2_eps=1e-6)
+    base.update(kw)
+    return gdn._Config(**base)
+
+
+def test_workspace_bytes(lib):
+    c = _cfg()
+    w0 = lib.gdn_prefill_workspace_bytes(ctypes.byref(c), 1, 0, 64)
+    w1 = lib.gdn_prefill_workspace_bytes(ctypes.byref(c), 1, 100, 64)
+    w2 = lib.gdn_prefill_workspace_bytes(ctypes.byref(c), 1, 200, 64)
+    assert w0 == 0 and 0 < w1 < w2
+    assert w1 % 256 == 0
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(c), 1, 100, 32) == 0
+    bad = _cfg(h_v=3)
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(bad), 1, 100, 64) == 0
+    assert lib.gdn_prefill_workspace_bytes(None, 1, 100, 64) == 0
+
+
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="placeholder device pointers are only passed where no GPU exists")
+
+# distinct placeholder device addresses, far apart (never dereferenced)
+_P = [ctypes.c_void_p(0x10000000000 * (i + 1)) for i in range(16)]
+
+
+def _params():
+    return gdn._Params(_P[10].value, _P[11].value, _P[12].value, _P[13].value)
+
+
+def _decode(lib, cfg=None, params=None, batch=2, ptrs=None):
+    p = _P[:7] if ptrs is None else ptrs
+    c = cfg or _cfg()
+    pr = params if params is not None else _params()
+    return lib.gdn_decode_step(ctypes.byref(c), ctypes.byref(pr) if pr is not False else None,
+                               batch, *p, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    (dict(h_v=3), EINVAL), (dict(h_k=0), EINVAL), (dict(d_k=48), EUNSUP),
+    (dict(d_v=256), EUNSUP), (dict(conv_k=5), EUNSUP), (dict(conv_k=0), EINVAL),
+    (dict(act_dtype=7), EINVAL), (dict(gate=2), EINVAL), (dict(norm_eps=-1.0), EINVAL),
+    (dict(l2_eps=float("nan")), EINVAL)])
+def test_decode_rejects_bad_config(lib, kw, code):
+    assert _decode(lib, _cfg(**kw)) == code
+    assert lib.gdn_last_error().decode() != ""
+
+
+@no_gpu
+def test_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, params=False) == EINVAL
+    assert _decode(lib, params=gdn._Params(0, _P[11].value, _P[12].value, _P[13].value)) == EINVAL
+    assert _decode(lib, batch=-1) == EINVAL
+    assert _decode(lib, ptrs=[None] + _P[1:7]) == EINVAL
+    # out aliasing the state
+    assert _decode(lib, ptrs=_P[:5] + [_P[5], _P[5]]) == EINVAL
+    # state overlapping qkv
+    assert _decode(lib, ptrs=_P[:5] + [_P[0], _P[6]]) == EINVAL
+    assert "overlap" in lib.gdn_last_error().decode()
+    # batch 0 is accepted without touching anything
+    assert _decode(lib, batch=0) == OK
+
+
+def _prefill(lib, cu, t_total, cfg=None, chunk=64, ws=(_P[9], 1 << 40), outs=None):
+    c = cfg or _cfg()
+    cu_h = np.asarray(cu, dtype=np.int32)
+    n = len(cu) - 1
+    o = outs or dict(state_in=_P[4], state_out=_P[5], conv_in=_P[6], conv_out=_P[7], out=_P[8])
+    return lib.gdn_prefill_chunked(
+        ctypes.byref(c), ctypes.byref(_params()), chunk, n, t_total,
+        cu_h.ctypes.data_as(ctypes.c_void_p), _P[14], _P[0], _P[1], _P[2], _P[3],
+        o["state_in"], o["state_out"], o["conv_in"], o["conv_out"], o["out"], ws[0],
+        ws[1], None)
+
+
+@no_gpu
+def test_prefill_rejects_bad_cu_seqlens(lib):
+    assert _prefill(lib, [1, 5], 5) == EINVAL          # does not start at 0
+    assert _prefill(lib, [0, 5, 3], 3) == EINVAL       # decreasing
+    assert _prefill(lib, [0, 5, 9], 10) == EINVAL      # does not end at t_total
+    assert "cu_seqlens" in lib.gdn_last_error().decode()
+
+
+@no_gpu
+def test_prefill_rejects_chunk_workspace_and_aliases(lib):
+    assert _prefill(lib, [0, 10], 10, chunk=32) == EUNSUP
+    assert _prefill(lib, [0, 10], 10, ws=(_P[9], 100)) == EWS
+    assert _prefill(lib, [0, 10], 10, ws=(None, 1 << 40)) == EWS
+    assert _prefill(lib, [0, 10], 10, ws=(ctypes.c_void_p(_P[9].value + 8), 1 << 40)) == EINVAL
+    o = dict(state_in=_P[4], state_out=_P[5], conv_in=_P[6], conv_out=_P[7], out=_P[0])
+    assert _prefill(lib, [0, 10], 10, outs=o) == EINVAL   # out overlaps qkv
+    o = dict(state_in=_P[4], state_out=ctypes.c_void_p(_P[4].value + 4), conv_in=_P[6],
+             conv_out=_P[7], out=_P[8])
+    assert _prefill(lib, [0, 10], 10, outs=o) == EINVAL   # partial state overlap
+
+
+def test_last_error_is_thread_local(lib):
+    c = _cfg(h_v=3)
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(c), 1, 10, 64) == 0
+    seen = {}
+
+    def worker():
+        seen["msg"] = lib.gdn_last_error().decode()
+    th = threading.Thread(target=worker)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""

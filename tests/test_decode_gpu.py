@@ -1,0 +1,126 @@
+"""Parity of gdn_decode_step (one fused kernel per step) with the oracle.
+
+The oracle runs the same tokens as packed sequences (one sequence per batch
+row), which its split/resume pin shows equals stepping one token at a time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_parity as P
+import oracle
+from gdn_inputs import Dims, decode_batch, make_case, tiny_recurrent
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_linear_causal_amd as g
+    g.load_library()
+    return g
+
+
+def run_decode(gdn, case, steps, out_dtype=torch.float32, S=None, conv=None):
+    cfg = P.gpu_config(case.dims, case.act_dtype, out_dtype)
+    params = P.dev_params(case)
+    S = (case.S0 if S is None else S).clone().cuda()
+    conv = (case.conv0 if conv is None else conv).clone().cuda()
+    dq = P.to_dev(case.dec["qkv"][:steps], case.act_dtype)
+    dz = P.to_dev(case.dec["z"][:steps], case.act_dtype)
+    da = P.to_dev(case.dec["a"][:steps], case.act_dtype)
+    db = P.to_dev(case.dec["b"][:steps], case.act_dtype)
+    outs = []
+    for s in range(steps):
+        outs.append(gdn.decode_step(cfg, params, dq[s], dz[s], da[s], db[s], conv, S))
+    torch.cuda.synchronize()
+    return torch.stack(outs).float().cpu(), S.cpu(), conv.cpu()
+
+
+def oracle_decode(case, steps, S0=None, conv0=None):
+    cu, qkv, z, a, b = P.decode_as_sequences(case, steps)
+    r = oracle.mixer(P.oracle_shape(case.dims), cu, case.params, qkv, z, a, b,
+                     case.S0 if S0 is None else S0, case.conv0 if conv0 is None else conv0,
+                     nthreads=P.n_threads())
+    B = len(cu) - 1
+    y = r["y"].reshape(B, steps, -1).transpose(1, 0, 2)
+    return y, r["S"], r["conv"]
+
+
+def test_tiny_recurrent_64_steps(gdn):
+    """1 sequence, 64 tokens one at a time, H_k=H_v=2, d=32, K=4, fp32, SiLU."""
+    case = tiny_recurrent()
+    y, S, conv = run_decode(gdn, case, 64)
+    y_ref, S_ref, conv_ref = oracle_decode(case, 64)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
+def test_decode_batch_64x100_steps(gdn):
+    """B=64, H_k=16, H_v=32, d=128, K=4, bf16 inputs, prefilled states, 100
+    consecutive steps; every output and the final states are compared."""
+    case = decode_batch(steps=100)
+    y, S, conv = run_decode(gdn, case, 100)
+    y_ref, S_ref, conv_ref = oracle_decode(case, 100)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
+VARIANTS = [
+    # h_k, h_v, d_k, d_v, K, gate, decay
+    (2, 2, 32, 32, 4, "silu", "weak"),
+    (2, 4, 64, 64, 4, "sigmoid", "weak"),
+    (1, 4, 128, 128, 3, "silu", "weak"),
+    (2, 4, 32, 128, 2, "sigmoid", "strong"),
+    (2, 2, 128, 64, 4, "silu", "weak"),
+    (1, 3, 64, 32, 1, "silu", "weak"),
+    (1, 8, 64, 64, 4, "silu", "weak"),
+]
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("v", VARIANTS, ids=lambda v: "hk%d_hv%d_dk%d_dv%d_K%d_%s_%s" % v)
+def test_decode_variants(gdn, v, act):
+    hk, hv, dk, dv, K, gate, decay = v
+    d = Dims(hk, hv, dk, dv, K, gate)
+    case = make_case(d, [0, 0, 0], act_dtype=act, seed=hk * 100 + hv + dk + K,
+                     decay=decay, s0_std=0.3, conv0_std=1.0, decode_steps=9)
+    y, S, conv = run_decode(gdn, case, 9)
+    y_ref, S_ref, conv_ref = oracle_decode(case, 9)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
+def test_decode_bf16_out_is_rne_of_fp32_out(gdn):
+    case = make_case(Dims(2, 4, 128, 128), [0] * 5, act_dtype="bf16", seed=7,
+                     s0_std=0.02, conv0_std=1.0, decode_steps=3)
+    y32, S32, c32 = run_decode(gdn, case, 3, torch.float32)
+    y16, S16, c16 = run_decode(gdn, case, 3, torch.bfloat16)
+    assert torch.equal(y32.to(torch.bfloat16).float(), y16)
+    assert torch.equal(S32, S16) and torch.equal(c32, c16)
+
+
+def test_decode_deterministic(gdn):
+    case = make_case(Dims(2, 4, 64, 64), [0] * 4, act_dtype="bf16", seed=8,
+                     s0_std=0.02, conv0_std=1.0, decode_steps=5)
+    a = run_decode(gdn, case, 5)
+    b = run_decode(gdn, case, 5)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_decode_batch_zero_is_noop(gdn):
+    d = Dims(2, 4, 64, 64)
+    cfg = P.gpu_config(d, "bf16")
+    case = make_case(d, [0], act_dtype="bf16", seed=9)
+    params = P.dev_params(case)
+    e = torch.empty((0, d.conv_dim), dtype=torch.bfloat16, device="cuda")
+    out = gdn.decode_step(cfg, params, e, torch.empty((0, d.value_dim), dtype=torch.bfloat16, device="cuda"),
+                          torch.empty((0, d.h_v), dtype=torch.bfloat16, device="cuda"),
+                          torch.empty((0, d.h_v), dtype=torch.bfloat16, device="cuda"),
+                          torch.empty((0, 3, d.conv_dim), device="cuda"),
+                          torch.empty((0, d.h_v, 64, 64), device="cuda"))
+    assert out.shape == (0, d.value_dim)

@@ -1,0 +1,192 @@
+"""Parity of gdn_prefill_chunked with the token-by-token oracle.
+
+Small cases compare every output; the full-size workloads compare all
+outputs where the oracle finishes in seconds (T=4096) and otherwise sampled
+key heads, which the oracle computes exactly because heads are independent.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_parity as P
+from gdn_inputs import (Dims, chunked_prefill, long_handoff, make_case,
+                        varlen_prefill)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import gated_deltanet_linear_causal_amd as g
+    g.load_library()
+    return g
+
+
+def run_prefill(gdn, case, out_dtype=torch.float32, state_in=True, conv_in=True,
+                inplace=False):
+    cfg = P.gpu_config(case.dims, case.act_dtype, out_dtype)
+    sl = gdn.SeqLens(case.cu_seqlens)
+    S_in = case.S0.clone().cuda() if state_in else None
+    c_in = case.conv0.clone().cuda() if conv_in else None
+    kw = {}
+    if inplace:
+        kw = {"state_out": S_in, "conv_out": c_in}
+    out, S, conv = gdn.prefill_chunked(cfg, P.dev_params(case), sl,
+                                       P.to_dev(case.qkv, case.act_dtype),
+                                       P.to_dev(case.z, case.act_dtype),
+                                       P.to_dev(case.a, case.act_dtype),
+                                       P.to_dev(case.b, case.act_dtype),
+                                       state_in=S_in, conv_in=c_in, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu(), S.cpu(), conv.cpu()
+
+
+SMALL = [
+    # h_k, h_v, d_k, d_v, K, gate, decay, lengths
+    (2, 4, 64, 64, 4, "silu", "weak", [1, 63, 65, 130]),
+    (2, 4, 64, 64, 4, "sigmoid", "strong", [130, 64, 7]),
+    (1, 2, 128, 128, 4, "silu", "weak", [200]),
+    (2, 2, 32, 32, 4, "silu", "weak", [64, 129, 0, 2]),
+    (1, 2, 128, 32, 3, "sigmoid", "weak", [100, 31]),
+    (2, 2, 32, 128, 2, "silu", "weak", [77]),
+    (1, 3, 64, 64, 1, "silu", "weak", [70, 5]),
+]
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+@pytest.mark.parametrize("v", SMALL, ids=lambda v: "hk%d_hv%d_dk%d_dv%d_K%d_%s_%s_%s" % (
+    *v[:7], "-".join(map(str, v[7]))))
+def test_prefill_small(gdn, v, act):
+    hk, hv, dk, dv, K, gate, decay, lengths = v
+    d = Dims(hk, hv, dk, dv, K, gate)
+    case = make_case(d, lengths, act_dtype=act, seed=sum(lengths) + K, decay=decay,
+                     s0_std=0.3, conv0_std=1.0)
+    y, S, conv = run_prefill(gdn, case)
+    r = P.run_oracle(case)
+    P.assert_y_close(y, r["y"])
+    P.assert_state_close(S, r["S"])
+    np.testing.assert_array_equal(conv.numpy(), r["conv"])
+
+
+def test_prefill_zero_state_pointers_and_empty_sequences(gdn):
+    """NULL state_in / conv_in mean zeros; empty sequences pass their state
+    through unchanged."""
+    d = Dims(2, 4, 64, 64)
+    case = make_case(d, [0, 90, 0, 3], act_dtype="bf16", seed=21)
+    y, S, conv = run_prefill(gdn, case, state_in=False, conv_in=False)
+    r = P.run_oracle(case)  # the case's S0 / conv0 are zeros
+    P.assert_y_close(y, r["y"])
+    P.assert_state_close(S, r["S"])
+    np.testing.assert_array_equal(conv.numpy(), r["conv"])
+    case2 = make_case(d, [0, 5, 0], act_dtype="bf16", seed=22, s0_std=0.5, conv0_std=1.0)
+    y2, S2, c2 = run_prefill(gdn, case2)
+    assert torch.equal(S2[0], case2.S0[0]) and torch.equal(S2[2], case2.S0[2])
+    assert torch.equal(c2[0], case2.conv0[0]) and torch.equal(c2[2], case2.conv0[2])
+
+
+def test_prefill_in_place_states(gdn):
+    d = Dims(2, 4, 64, 64)
+    case = make_case(d, [70, 1, 150], act_dtype="bf16", seed=23, decay="weak",
+                     s0_std=0.3, conv0_std=1.0)
+    y, S, conv = run_prefill(gdn, case, inplace=True)
+    r = P.run_oracle(case)
+    P.assert_y_close(y, r["y"])
+    P.assert_state_close(S, r["S"])
+    np.testing.assert_array_equal(conv.numpy(), r["conv"])
+
+
+def test_prefill_bf16_out_is_rne_of_fp32_out_and_deterministic(gdn):
+    d = Dims(2, 4, 128, 128)
+    case = make_case(d, [300, 45], act_dtype="bf16", seed=24, s0_std=0.02, conv0_std=1.0)
+    y32, S32, c32 = run_prefill(gdn, case, torch.float32)
+    y16, S16, c16 = run_prefill(gdn, case, torch.bfloat16)
+    assert torch.equal(y32.to(torch.bfloat16).float(), y16)
+    assert torch.equal(S32, S16) and torch.equal(c32, c16)
+    y32b, S32b, _ = run_prefill(gdn, case, torch.float32)
+    assert torch.equal(y32, y32b) and torch.equal(S32, S32b)
+
+
+def test_prefill_split_resume_matches_oracle(gdn):
+    """Prefill [0,T1) then [T1,T) from the returned (S, conv) agrees with the
+    oracle over [0,T)."""
+    d = Dims(2, 4, 64, 64)
+    case = make_case(d, [333], act_dtype="bf16", seed=25, decay="weak", s0_std=0.1,
+                     conv0_std=1.0)
+    cfg = P.gpu_config(d, "bf16")
+    params = P.dev_params(case)
+    x = {k: P.to_dev(getattr(case, k), "bf16") for k in ("qkv", "z", "a", "b")}
+    T1 = 100
+    y1, S1, c1 = gdn.prefill_chunked(cfg, params, gdn.SeqLens([0, T1]),
+                                     *(x[k][:T1].contiguous() for k in ("qkv", "z", "a", "b")),
+                                     state_in=case.S0.cuda(), conv_in=case.conv0.cuda())
+    y2, S2, c2 = gdn.prefill_chunked(cfg, params, gdn.SeqLens([0, 333 - T1]),
+                                     *(x[k][T1:].contiguous() for k in ("qkv", "z", "a", "b")),
+                                     state_in=S1, conv_in=c1)
+    torch.cuda.synchronize()
+    r = P.run_oracle(case)
+    P.assert_y_close(torch.cat([y1, y2]).cpu(), r["y"])
+    P.assert_state_close(S2.cpu(), r["S"])
+    np.testing.assert_array_equal(c2.cpu().numpy(), r["conv"])
+
+
+@pytest.mark.slow
+def test_prefill_t4096_all_heads(gdn):
+    """B=1, T=4096, H_k=16, H_v=32, d=128, C=64, bf16 inputs, zero state."""
+    case = chunked_prefill()
+    y, S, conv = run_prefill(gdn, case, state_in=False, conv_in=False)
+    r = P.run_oracle(case)
+    P.assert_y_close(y, r["y"])
+    P.assert_state_close(S, r["S"])
+    np.testing.assert_array_equal(conv.numpy(), r["conv"])
+
+
+@pytest.mark.slow
+def test_prefill_varlen_8_sampled_heads(gdn):
+    """8 sequences of U{512..8192} tokens with random initial states; the
+    oracle runs key heads 0 and 11 (with their value heads) exactly."""
+    case = varlen_prefill()
+    y, S, conv = run_prefill(gdn, case)
+    grp = case.dims.h_v // case.dims.h_k
+    dv = case.dims.d_v
+    for hk in (0, 11):
+        sub = P.subcase(case, hk)
+        r = P.run_oracle(sub)
+        cols = slice(hk * grp * dv, (hk + 1) * grp * dv)
+        P.assert_y_close(y[:, cols], r["y"], f"out[key head {hk}]")
+        P.assert_state_close(S[:, hk * grp:(hk + 1) * grp], r["S"], f"state[key head {hk}]")
+    d = case.dims
+    ref_conv = np.stack([np.concatenate([case.conv0[n].numpy(),
+                                         case.qkv[case.cu_seqlens[n]:case.cu_seqlens[n + 1]].numpy()])[-3:]
+                         for n in range(case.n_seq)])
+    np.testing.assert_array_equal(conv.numpy(), ref_conv)
+
+
+@pytest.mark.slow
+def test_long_handoff_prefill_then_decode_sampled_heads(gdn):
+    """B=1 prefill of T=65536 (sigmoid gate), then 256 decode steps from the
+    returned state; key head 5 and its value heads are checked exactly
+    against the oracle run over all 65536 + 256 tokens."""
+    case = long_handoff()
+    cfg = P.gpu_config(case.dims, "bf16")
+    params = P.dev_params(case)
+    y, S, conv = gdn.prefill_chunked(cfg, params, gdn.SeqLens(case.cu_seqlens),
+                                     *(P.to_dev(getattr(case, k), "bf16") for k in ("qkv", "z", "a", "b")))
+    ys = []
+    for s in range(case.dec["qkv"].shape[0]):
+        ys.append(gdn.decode_step(cfg, params, *(P.to_dev(case.dec[k][s], "bf16") for k in ("qkv", "z", "a", "b")),
+                                  conv, S))
+    torch.cuda.synchronize()
+    hk = 5
+    grp = case.dims.h_v // case.dims.h_k
+    cols = slice(hk * grp * case.dims.d_v, (hk + 1) * grp * case.dims.d_v)
+    sub = P.subcase(case, hk)
+    r = P.run_oracle(sub)
+    P.assert_y_close(y[:, cols].float().cpu(), r["y"], "prefill out")
+    steps = case.dec["qkv"].shape[0]
+    cu, qkv, z, a, b = P.decode_as_sequences(sub, steps)
+    import oracle
+    r2 = oracle.mixer(P.oracle_shape(sub.dims), cu, sub.params, qkv, z, a, b, r["S"], r["conv"],
+                      nthreads=P.n_threads())
+    yd = torch.stack(ys).float().cpu()[:, 0, cols]
+    P.assert_y_close(yd, r2["y"], "decode out")
+    P.assert_state_close(S[:, hk * grp:(hk + 1) * grp].cpu(), r2["S"], "final state")
