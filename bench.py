@@ -1,0 +1,233 @@
+#!/usr/bin/env python
+"""Benchmark of the Gated DeltaNet mixer core on one MI355X (gfx950).
+
+One step = one pass of the whole hot path over one batch of synthetic
+input:
+  * a chunked prefill of one sequence, T = 4096 tokens, H_k = 16, H_v = 32,
+    d_k = d_v = 128, K = 4, C = 64, bf16 activations and output, zero
+    initial state;
+  * one decode step for B = 64 sequences (same heads), bf16 activations and
+    output, fp32 states updated in place (100 distinct per-step input sets
+    cycled, as a serving loop would).
+All inputs are resident in HBM before timing starts.  The two calls of each
+step are bracketed with HIP events on the stream they run on, so the line
+reports prefill tokens/s (``value``) and the decode-step latency separately.
+
+Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build is a
+one-GPU build (the sharding design is written up, not launched).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["gated_deltanet_linear_causal_amd/csrc/decode.hip",
+                  "gated_deltanet_linear_causal_amd/csrc/prefill.hip"]
+
+
+def decode_bytes(d, batch):
+    """Algorithmic HBM bytes of one decode step (per launch): fp32 state and
+    conv history read + written, bf16 inputs read, bf16 output written, and
+    the fp32 parameters read once."""
+    state = batch * d.h_v * d.d_k * d.d_v * 4 * 2
+    conv = batch * (d.conv_k - 1) * d.conv_dim * 4 * 2
+    inp = batch * (d.conv_dim + d.value_dim + 2 * d.h_v) * 2
+    out = batch * d.value_dim * 2
+    params = (d.conv_dim * d.conv_k + 2 * d.h_v + d.d_v) * 4
+    return state + conv + inp + out + params
+
+
+def prefill_flops(d, T, C=64):
+    """Algorithmic flops of the chunked form as computed (per call):
+    per token and key head K K^T and Q K^T rows (4 C d_k); per token and
+    value head K S, Q S and the state update (6 d_k d_v) plus T R and P D
+    (4 C d_v)."""
+    per_tok = d.h_k * 4 * C * d.d_k + d.h_v * (6 * d.d_k * d.d_v + 4 * C * d.d_v)
+    return T * per_tok
+
+
+def prefill_bytes(d, T, n_seq=1):
+    """Algorithmic HBM bytes of one prefill call: bf16 inputs and output,
+    final fp32 state and conv history written (zero initial state)."""
+    io = T * ((d.conv_dim + d.value_dim + 2 * d.h_v) * 2 + d.value_dim * 2)
+    states = n_seq * (d.h_v * d.d_k * d.d_v + (d.conv_k - 1) * d.conv_dim) * 4
+    return io + states
+
+
+def sources_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
+    runs (scaled by a plain-copy calibration), or None if they were taken on
+    other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha") != sources_hash():
+        return None
+    ent = rec.get("kernels", {}).get(kernel)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def cpu_baseline(case, threads):
+    """The oracle, untuned, on the host cores: the full T=4096 prefill over
+    every head (a short warm-up call loads the library first)."""
+    import oracle
+    shape = oracle.Shape(case.dims.h_k, case.dims.h_v, case.dims.d_k, case.dims.d_v,
+                         case.dims.conv_k, case.dims.gate)
+    oracle.mixer(shape, [0, 1], case.params, case.qkv[:1], case.z[:1], case.a[:1],
+                 case.b[:1], case.S0, case.conv0, nthreads=threads)
+    t = time.perf_counter()
+    oracle.mixer(shape, case.cu_seqlens, case.params, case.qkv, case.z, case.a, case.b,
+                 case.S0, case.conv0, nthreads=threads)
+    dt = time.perf_counter() - t
+    T = case.t_total
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"full prefill T={T}, all {case.dims.h_v} value heads, float64 "
+                      f"token-by-token C oracle, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_deltanet_linear_causal_amd as gdn
+    from gdn_inputs import BIG, chunked_prefill, decode_batch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    d = BIG
+    cfg = gdn.Config(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, torch.bfloat16, torch.bfloat16)
+
+    # ---- inputs, resident in HBM ----------------------------------------
+    pf = chunked_prefill()
+    dc = decode_batch(steps=100)
+    bf = torch.bfloat16
+    params = {k: v.to(dev) for k, v in pf.params.items()}
+    dparams = {k: v.to(dev) for k, v in dc.params.items()}
+    seq = gdn.SeqLens(pf.cu_seqlens, dev)
+    x_pf = [getattr(pf, k).to(bf).to(dev).contiguous() for k in ("qkv", "z", "a", "b")]
+    T = pf.t_total
+    out_pf = torch.empty((T, d.value_dim), dtype=bf, device=dev)
+    S_pf = torch.empty((1, d.h_v, d.d_k, d.d_v), dtype=torch.float32, device=dev)
+    c_pf = torch.empty((1, d.conv_k - 1, d.conv_dim), dtype=torch.float32, device=dev)
+    ws = gdn.alloc_workspace(cfg, 1, T, dev)
+    B = dc.dec["qkv"].shape[1]
+    x_dc = [dc.dec[k].to(bf).to(dev).contiguous() for k in ("qkv", "z", "a", "b")]
+    S_dc = dc.S0.to(dev)
+    c_dc = dc.conv0.to(dev)
+    out_dc = torch.empty((B, d.value_dim), dtype=bf, device=dev)
+    n_sets = x_dc[0].shape[0]
+
+    def step(i, evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        gdn.prefill_chunked(cfg, params, seq, *x_pf, state_in=None, state_out=S_pf,
+                            conv_in=None, conv_out=c_pf, out=out_pf, workspace=ws,
+                            stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        j = i % n_sets
+        gdn.decode_step(cfg, dparams, x_dc[0][j], x_dc[1][j], x_dc[2][j], x_dc[3][j], c_dc,
+                        S_dc, out=out_dc, stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pf_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    dc_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ms_step = wall * 1e3 / args.steps
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    dbytes = decode_bytes(d, B)
+    pflops = prefill_flops(d, T)
+    pbytes = prefill_bytes(d, T)
+    dec_gbs = dbytes / (dc_ms * 1e-3) / 1e9
+    pf_tflops = pflops / (pf_ms * 1e-3) / 1e12
+    roof_dec = {"kernel": "gdn::decode_kernel (gdn_decode_step, 1 launch)", "bound": "hbm",
+                "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic("decode_kernel"),
+                "algorithmic_bytes_per_launch": dbytes}
+    roof_pf = {"kernel": "gdn_prefill_chunked (prep + scan + norm + conv_final launches)",
+               "bound": "mfma", "achieved": round(pf_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+               "unit": "TFLOP/s", "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
+               "traffic": load_traffic("prefill_call"),
+               "algorithmic_flops_per_launch": pflops,
+               "hbm_frac": round(pbytes / (pf_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    dominant = roof_pf if pf_ms >= dc_ms else roof_dec
+
+    line = {
+        "metric": "GDN prefill tokens/s (T=4096) + decode step us at B=64; % HBM/MFMA peak",
+        "value": round(T / (pf_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "GDN mixer: prefill B=1 T=4096 + decode step B=64; H_k=16 "
+                               "H_v=32 d_k=d_v=128 K=4 C=64; bf16 activations/output, fp32 "
+                               "state", "global_batch": 64, "seq_len": T,
+                   "parallelism": "single GPU"},
+        "prefill_ms": round(pf_ms, 4),
+        "decode_us_per_step": round(dc_ms * 1e3, 2),
+        "decode_tokens_per_s": round(B / (dc_ms * 1e-3), 1),
+        "roofline": dominant,
+        "rooflines": {"decode": roof_dec, "prefill": roof_pf},
+        "note": "the pages quote no throughput for this path on any hardware",
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        line["cpu_baseline"] = cpu_baseline(pf, threads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
