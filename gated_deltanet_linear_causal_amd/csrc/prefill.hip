@@ -12,23 +12,28 @@
 //     R    = diag(b) (V - diag(e^G) X)
 //     D    = T R
 //     O    = diag(e^G) Y + P D
-//     S'   = e^{G_C} S + (diag(e^{G_C-G}) K)^T D
+//     S'   = e^{G_C} S + K^T (diag(e^{G_C-G}) D)
 // Only differences G_i - G_j with j <= i are exponentiated, so strong
 // decay underflows to zero instead of overflowing.
 //
 // Kernels (one stream, in order):
-//   prep  grid (chunk, key head, seq): conv + SiLU, L2 norms, gates and
-//         their in-chunk prefix sum, K K^T and Q K^T on MFMA, A, the
-//         triangular inverse T in fp32, P.  Writes q^, k^, conv(v), T, P,
-//         G, b to the workspace.  Fully parallel.
-//   scan  grid (seq, value head, 16-column slice of d_v): the chain of
-//         chunk states, sequential over the chunks of one sequence; the
-//         state slice lives in registers.  Writes the pre-norm readout O.
-//   norm  grid (token, value head): gated RMSNorm + output gate -> out;
-//         plus the final conv history.
+//   qknorm  grid (16-token tile, key head, seq): causal conv + SiLU and L2
+//           norm of q and k, a group of lanes per token row; writes q^, k^
+//           split into bf16 hi + lo (ready-made matrix-core operands).
+//   tri     grid (chunk, value head, seq): gates and their in-chunk prefix
+//           sum, K K^T and Q K^T on MFMA, A, the blocked fp32 triangular
+//           inverse T, P; writes T and P rows split into bf16 hi + lo.
+//   scan    grid (seq, value head, 16-column slice of d_v): the chain of
+//           chunk states, sequential over the chunks of one sequence.  The
+//           state slice lives in registers, every matrix operand arrives
+//           pre-split, and the next chunk's inputs are in flight while the
+//           current one is computed.  conv + SiLU of the slice's v channels
+//           happens here.  Writes the pre-norm readout O.
+//   norm    grid (rows of (token, value head)): gated RMSNorm + output gate.
+//   conv_final: each sequence's last K-1 raw inputs become its history.
 //
-// Contractions run on v_mfma_f32_16x16x32_bf16 with each fp32 operand split
-// into bf16 hi + lo and three products (hi.hi + hi.lo + lo.hi, fp32
+// Contractions run on v_mfma_f32_16x16x32_bf16 with every fp32 operand
+// split into bf16 hi + lo and three products (hi.hi + hi.lo + lo.hi, fp32
 // accumulate): plain bf16 operands are far outside the parity tolerance,
 // the split form is within it.
 
@@ -37,15 +42,23 @@
 
 namespace gdn {
 
-constexpr int kC = 64;      // tokens per chunk
-constexpr int kBV = 16;     // d_v columns per scan workgroup
+constexpr int kC = 64;       // tokens per chunk
+constexpr int kBV = 16;      // d_v columns per scan workgroup
+constexpr int kTileTok = 16; // tokens per qknorm workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct Frag {
     bf16x8 hi, lo;
 };
+
+__device__ __forceinline__ void split1(float v, __bf16 &h, __bf16 &l)
+{
+    h = static_cast<__bf16>(v);
+    l = static_cast<__bf16>(v - static_cast<float>(h));
+}
 
 // fp32 -> (hi, lo) bf16 pair with hi + lo = v to ~16 significant bits.
 __device__ __forceinline__ Frag split8(const float (&v)[8])
@@ -53,17 +66,12 @@ __device__ __forceinline__ Frag split8(const float (&v)[8])
     Frag f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const __bf16 h = static_cast<__bf16>(v[e]);
+        __bf16 h, l;
+        split1(v[e], h, l);
         f.hi[e] = h;
-        f.lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(h));
+        f.lo[e] = l;
     }
     return f;
-}
-
-__device__ __forceinline__ Frag split8(float4 a, float4 b)
-{
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    return split8(v);
 }
 
 // D += A B on one 16x16x32 tile, split-bf16 with three MFMAs.
@@ -77,23 +85,70 @@ __device__ __forceinline__ f32x4 mma3(const Frag &A, const Frag &B, f32x4 c)
     return c;
 }
 
-__device__ __forceinline__ Frag lds_frag(const float *row8)
+__device__ __forceinline__ Frag frag_at(const __bf16 *hi, const __bf16 *lo)
 {
-    const float4 a = *reinterpret_cast<const float4 *>(row8);
-    const float4 b = *reinterpret_cast<const float4 *>(row8 + 4);
-    return split8(a, b);
+    Frag f;
+    f.hi = *reinterpret_cast<const bf16x8 *>(hi);
+    f.lo = *reinterpret_cast<const bf16x8 *>(lo);
+    return f;
+}
+
+__device__ __forceinline__ Frag frag_select(bool keep, const Frag &f)
+{
+    Frag z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        z.hi[e] = keep ? f.hi[e] : static_cast<__bf16>(0.0f);
+        z.lo[e] = keep ? f.lo[e] : static_cast<__bf16>(0.0f);
+    }
+    return z;
+}
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+template <typename T> __device__ __forceinline__ f32x4 load_act4v(const T *p, size_t i)
+{
+    const float4 v = load_act4(p, i);
+    return f32x4{v.x, v.y, v.z, v.w};
+}
+
+// Raw activation bits of 4 channels (loaded now, converted when used).
+template <typename T> struct RawAct;
+template <> struct RawAct<bf16_t> {
+    typedef uint2 type;
+    __device__ __forceinline__ static type load(const bf16_t *p, size_t i)
+    {
+        return *reinterpret_cast<const uint2 *>(p + i);
+    }
+    __device__ __forceinline__ static f32x4 to_f32(type u)
+    {
+        return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+    }
+};
+template <> struct RawAct<float> {
+    typedef f32x4 type;
+    __device__ __forceinline__ static type load(const float *p, size_t i)
+    {
+        return *reinterpret_cast<const f32x4 *>(p + i);
+    }
+    __device__ __forceinline__ static f32x4 to_f32(type u) { return u; }
+};
+
+__device__ __forceinline__ uint32_t pack2(__bf16 a, __bf16 b)
+{
+    return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
 // ---------------------------------------------------------------------------
-// Workspace layout (all fp32, each section 256-byte aligned):
-//   qk [T][H_k][2][d_k]   q^ then k^ of each key head
-//   v  [T][H_v*d_v]       conv(v)
-//   tp [T][H_v][2][C]     row of T, then row of P, for the token's chunk
-//   gb [T][H_v][2]        G (in-chunk cumulative log decay), beta
-//   o  [T][H_v*d_v]       pre-norm readout
+// Workspace layout (sections 256-byte aligned):
+//   qk [T][H_k][2: q^,k^][2: hi,lo][d_k] bf16
+//   tp [T][H_v][2: T,P][2: hi,lo][C]    bf16 (row of the token's chunk)
+//   gb [T][H_v][2]                      fp32 (G in-chunk cumulative, beta)
+//   o  [T][H_v*d_v]                     fp32 pre-norm readout
 // ---------------------------------------------------------------------------
 struct WsLayout {
-    size_t qk, v, tp, gb, o, total;
+    size_t qk, tp, gb, o, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -104,11 +159,9 @@ static WsLayout ws_layout(const Dims &d, int t_total)
     const size_t T = (size_t)t_total;
     size_t off = 0;
     w.qk = off;
-    off = align256(off + T * d.h_k * 2 * d.d_k * sizeof(float));
-    w.v = off;
-    off = align256(off + T * d.value_dim * sizeof(float));
+    off = align256(off + T * d.h_k * 4 * d.d_k * 2);
     w.tp = off;
-    off = align256(off + T * d.h_v * 2 * kC * sizeof(float));
+    off = align256(off + T * d.h_v * 4 * kC * 2);
     w.gb = off;
     off = align256(off + T * d.h_v * 2 * sizeof(float));
     w.o = off;
@@ -132,199 +185,263 @@ struct PrefillArgs {
     const float *conv_in;
     float *conv_out;
     void *out;
-    float *ws_qk, *ws_v, *ws_tp, *ws_gb, *ws_o;
+    __bf16 *ws_qk, *ws_tp;
+    float *ws_gb, *ws_o;
     int h_k, h_v, d_v, group, conv_k, conv_dim, value_dim;
     int gate, out_bf16;
     float norm_eps, l2_eps;
 };
 
+// Conv taps of 4 channels starting at ch, right-aligned to 4 taps (zero
+// taps in front when K < 4): w[e][j] multiplies the input 3-j tokens back.
+__device__ __forceinline__ void load_taps4(const PrefillArgs &p, int ch, float (&w)[4][4])
+{
+    const int K = p.conv_k;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int jj = j - (4 - K);
+            w[e][j] = jj >= 0 ? p.conv_w[(size_t)(ch + e) * K + jj] : 0.0f;
+        }
+}
+
+// Raw inputs of 4 channels at sequence position tau (< 0 reaches into the
+// incoming history; zero when there is none).
+template <typename TIn>
+__device__ __forceinline__ f32x4 raw4(const PrefillArgs &p, const TIn *x, int n, int s0, int tau,
+                                      int ch)
+{
+    if (tau >= 0) return load_act4v(x, (size_t)(s0 + tau) * p.conv_dim + ch);
+    const int slot = p.conv_k - 1 + tau;
+    if (p.conv_in && slot >= 0)
+        return ld4(p.conv_in + ((size_t)n * (p.conv_k - 1) + slot) * p.conv_dim + ch);
+    return f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// silu(causal conv) of 4 channels from the 4 taps' raw inputs.
+__device__ __forceinline__ f32x4 conv4(const float (&w)[4][4], const f32x4 (&xr)[4])
+{
+    f32x4 c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = fmaf(w[e][j], xr[j][e], acc);
+        c[e] = siluf_(acc);
+    }
+    return c;
+}
+
 // ---------------------------------------------------------------------------
-// prep: one workgroup per (chunk, key head, sequence), 256 threads.
+// qknorm: one workgroup per (16-token tile, key head, sequence).  Each token
+// row of the key head (q then k, 2*d_k channels) is handled by d_k/2 lanes
+// of 4 channels; each L2 norm is a reduction over d_k/4 lanes.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(256)
-prep_kernel(const PrefillArgs p)
+qknorm_kernel(const PrefillArgs p)
 {
-    constexpr int LDK = DK + 4;   // padded row of q^/k^ in LDS
-    constexpr int LC = kC + 4;    // padded row of the C x C matrices
-    const int c = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
+    constexpr int LPT = DK / 2;                 // lanes per token row
+    constexpr int TPI = 64 / LPT;               // token rows per wave pass
+    constexpr int ITERS = kTileTok / (4 * TPI); // passes per wave
+    const int tile = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
+    const int s0 = p.cu[n], L = p.cu[n + 1] - s0;
+    if (tile * kTileTok >= L) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane / LPT, ll = lane % LPT;
+    const bool isk = ll >= DK / 4;
+    const int c4 = (isk ? ll - DK / 4 : ll) * 4;
+    const int ch = (isk ? p.h_k * DK : 0) + hk * DK + c4;
+    const TIn *x = static_cast<const TIn *>(p.qkv);
+    float w[4][4];
+    load_taps4(p, ch, w);
+    const float extra = isk ? 1.0f : rsqrtf((float)DK);
+
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int tl = tile * kTileTok + (it * 4 + wave) * TPI + sub;
+        const bool valid = tl < L;
+        const int tc = valid ? tl : L - 1;
+        f32x4 xr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xr[j] = raw4(p, x, n, s0, tc - 3 + j, ch);
+        const f32x4 c = conv4(w, xr);
+        float ss = c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3];
+        ss = group_sum<DK / 4>(ss);
+        const float sc = rsqrtf(ss + p.l2_eps) * extra;
+        if (valid) {
+            __bf16 h[4], l[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split1(c[e] * sc, h[e], l[e]);
+            __bf16 *dst = p.ws_qk + ((size_t)(s0 + tl) * p.h_k + hk) * 4 * DK + (isk ? 2 * DK : 0) + c4;
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
+            *reinterpret_cast<uint2 *>(dst + DK) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// tri: one workgroup per (chunk, value head, sequence), 256 threads.
+// ---------------------------------------------------------------------------
+template <typename TIn, int DK>
+__global__ void __launch_bounds__(256)
+tri_kernel(const PrefillArgs p)
+{
+    constexpr int LC = kC + 4;
+    const int c = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
     const int s0 = p.cu[n];
     const int L = p.cu[n + 1] - s0;
     if (c * kC >= L) return;
     const int t0 = s0 + c * kC;
     const int Lc = min(kC, L - c * kC);
+    const int hk = hv / p.group;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int K = p.conv_k, CD = p.conv_dim;
-    const TIn *x = static_cast<const TIn *>(p.qkv);
+    const int col = lane & 15, kq = lane >> 4;
 
-    extern __shared__ float smem[];
-    float *sQ = smem;                 // [C][LDK]   later reused as sA / sT
-    float *sK = sQ + kC * LDK;        // [C][LDK]
-    float *sKK = sK + kC * LDK;       // [C][LC]
-    float *sQKm = sKK + kC * LC;      // [C][LC]
-    float *sG = sQKm + kC * LC;       // [C]
-    float *sB = sG + kC;              // [C]
-    float *sA = sQ;                   // [C][LC], valid once q^/k^ are consumed
+    __shared__ __attribute__((aligned(16))) float sA[kC * LC];
+    __shared__ __attribute__((aligned(16))) float sP[kC * LC];
+    __shared__ __attribute__((aligned(16))) float sT[kC * LC];
+    __shared__ __attribute__((aligned(16))) float sW[4][16 * 17];
+    __shared__ float sG[kC], sB[kC];
 
-    // --- conv + SiLU of the chunk, history from the previous chunk's raw
-    //     inputs or from conv_in ---------------------------------------
-    auto conv_channel = [&](int ch, auto &&emit) {
-        float w[4];
-        for (int j = 0; j < K; ++j) w[j] = p.conv_w[(size_t)ch * K + j];
-        float win[3];
-        for (int j = 0; j < K - 1; ++j) {
-            const int tau = t0 - (K - 1) + j;
-            if (tau >= s0)
-                win[j] = load_act(x, (size_t)tau * CD + ch);
-            else
-                win[j] = p.conv_in ? p.conv_in[((size_t)n * (K - 1) + (K - 1 + tau - s0)) * CD + ch]
-                                   : 0.0f;
-        }
-        for (int t = 0; t < Lc; ++t) {
-            const float cur = load_act(x, (size_t)(t0 + t) * CD + ch);
-            float acc = 0.0f;
-            for (int j = 0; j < K - 1; ++j) acc = fmaf(w[j], win[j], acc);
-            acc = fmaf(w[K - 1], cur, acc);
-            emit(t, siluf_(acc));
-            for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
-            if (K > 1) win[K - 2] = cur;
-        }
-    };
-    for (int l = tid; l < 2 * DK; l += 256) {
-        const bool isq = l < DK;
-        const int ch = isq ? hk * DK + l : p.h_k * DK + hk * DK + (l - DK);
-        float *dst = (isq ? sQ : sK) + (isq ? l : l - DK);
-        conv_channel(ch, [&](int t, float v) { dst[t * LDK] = v; });
-        for (int t = Lc; t < kC; ++t) dst[t * LDK] = 0.0f;
+    for (int i = tid; i < kC * LC / 4; i += 256) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        reinterpret_cast<f32x4 *>(sA)[i] = z;
+        reinterpret_cast<f32x4 *>(sP)[i] = z;
+        reinterpret_cast<f32x4 *>(sT)[i] = z;
     }
-    {
-        const int vbase = 2 * p.h_k * DK + hk * p.group * p.d_v;
-        const int nv = p.group * p.d_v;
-        for (int l = tid; l < nv; l += 256) {
-            float *dst = p.ws_v + (size_t)t0 * p.value_dim + (size_t)hk * nv + l;
-            conv_channel(vbase + l, [&](int t, float v) { dst[(size_t)t * p.value_dim] = v; });
+    // Gates ("cherenkov qwen4_exp/cpu.rs" fn deltanet) and their inclusive
+    // prefix sum over the chunk (wave 0).  Past the chunk end: g = 0, b = 0.
+    if (wave == 0) {
+        float beta = 0.0f, g = 0.0f;
+        if (lane < Lc) {
+            const size_t gi = (size_t)(t0 + lane) * p.h_v + hv;
+            beta = sigmoidf_(load_act(static_cast<const TIn *>(p.b), gi));
+            g = -expf(p.a_log[hv]) *
+                softplusf_(load_act(static_cast<const TIn *>(p.a), gi) + p.dt_bias[hv]);
         }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float u = __shfl_up(g, off, 64);
+            if (lane >= off) g += u;
+        }
+        sG[lane] = g;
+        sB[lane] = beta;
+        if (lane < Lc)
+            *reinterpret_cast<float2 *>(p.ws_gb + ((size_t)(t0 + lane) * p.h_v + hv) * 2) =
+                make_float2(g, beta);
     }
     __syncthreads();
 
-    // --- L2 norms (rows past Lc are zero and stay zero) -----------------
-    for (int r = wave; r < 2 * kC; r += 4) {
-        float *row = (r < kC ? sQ : sK) + (r % kC) * LDK;
-        float ss = 0.0f;
-        for (int i = lane; i < DK; i += 64) ss = fmaf(row[i], row[i], ss);
-        ss = group_sum<64>(ss);
-        const float sc = rsqrtf(ss + p.l2_eps) * (r < kC ? rsqrtf((float)DK) : 1.0f);
-        for (int i = lane; i < DK; i += 64) row[i] *= sc;
-    }
-    __syncthreads();
-
-    // q^, k^ to the workspace for the scan.
-    for (int idx = tid; idx < Lc * 2 * (DK / 4); idx += 256) {
-        const int t = idx / (2 * (DK / 4));
-        const int rem = idx % (2 * (DK / 4));
-        const int which = rem / (DK / 4), q4 = rem % (DK / 4);
-        const float4 v = *reinterpret_cast<const float4 *>((which ? sK : sQ) + t * LDK + 4 * q4);
-        *reinterpret_cast<float4 *>(p.ws_qk + (((size_t)(t0 + t) * p.h_k + hk) * 2 + which) * DK +
-                                    4 * q4) = v;
-    }
-
-    // --- K K^T and Q K^T, lower-triangular 16x16 tiles -------------------
-    // 20 tiles: (which, mt, nt) with nt <= mt; wave w takes every 4th.
+    // K K^T -> A and Q K^T -> P, lower-triangular 16x16 tiles:
+    // 20 tiles (which, mt, nt >= ... nt <= mt); wave w takes every 4th.
+    const __bf16 *qk0 = p.ws_qk + ((size_t)t0 * p.h_k + hk) * 4 * DK;
+    const size_t rs = (size_t)p.h_k * 4 * DK; // bf16 per token row
     for (int tile = wave; tile < 20; tile += 4) {
-        const int which = tile / 10;  // 0: K K^T, 1: Q K^T
+        const int which = tile / 10; // 0: K K^T, 1: Q K^T
         int r = tile % 10, mt = 0;
-        while (r > mt) { r -= mt + 1; ++mt; }
+        while (r > mt) {
+            r -= mt + 1;
+            ++mt;
+        }
         const int nt = r;
-        const float *Arow = (which ? sQ : sK) + (16 * mt + (lane & 15)) * LDK + 8 * (lane >> 4);
-        const float *Brow = sK + (16 * nt + (lane & 15)) * LDK + 8 * (lane >> 4);
+        const int ra = 16 * mt + col, rb = 16 * nt + col;
+        const __bf16 *pA = qk0 + (size_t)(ra < Lc ? ra : 0) * rs + (which == 0 ? 2 * DK : 0) + 8 * kq;
+        const __bf16 *pB = qk0 + (size_t)(rb < Lc ? rb : 0) * rs + 2 * DK + 8 * kq;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s) acc = mma3(lds_frag(Arow + 32 * s), lds_frag(Brow + 32 * s), acc);
-        float *D = (which ? sQKm : sKK) + (16 * mt + 4 * (lane >> 4)) * LC + 16 * nt + (lane & 15);
+        for (int s = 0; s < DK / 32; ++s) {
+            const Frag A = frag_select(ra < Lc, frag_at(pA + 32 * s, pA + DK + 32 * s));
+            const Frag B = frag_select(rb < Lc, frag_at(pB + 32 * s, pB + DK + 32 * s));
+            acc = mma3(A, B, acc);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) D[e * LC] = acc[e];
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * mt + 4 * kq + e, j = 16 * nt + col;
+            const float m = j <= i ? expf(sG[i] - sG[j]) : 0.0f;
+            if (which == 0)
+                sA[i * LC + j] = j < i ? sB[i] * m * acc[e] : 0.0f;
+            else
+                sP[i * LC + j] = m * acc[e];
+        }
     }
     __syncthreads();
 
-    // --- per value head of the group: gates, A, T = (I+A)^-1, P ----------
-    const TIn *pa = static_cast<const TIn *>(p.a);
-    const TIn *pb = static_cast<const TIn *>(p.b);
-    for (int hl = 0; hl < p.group; ++hl) {
-        const int hv = hk * p.group + hl;
-        if (wave == 0) {
-            float beta = 0.0f, g = 0.0f;
-            if (lane < Lc) {
-                const size_t gi = (size_t)(t0 + lane) * p.h_v + hv;
-                beta = sigmoidf_(load_act(pb, gi));
-                g = -expf(p.a_log[hv]) * softplusf_(load_act(pa, gi) + p.dt_bias[hv]);
-            }
-            // inclusive prefix sum over the chunk
+    // T = (I + A)^-1, blocked over 16x16 blocks, fp32.
+    // Diagonal blocks by forward substitution: wave b owns block b; lane
+    // (col j, quarter q) keeps rows 4q..4q+3 of column j.
+    {
+        const int b = wave;
+        float x[4];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float u = __shfl_up(g, off, 64);
-                if (lane >= off) g += u;
-            }
-            sG[lane] = g;
-            sB[lane] = beta;
-            if (lane < Lc) {
-                float *gb = p.ws_gb + ((size_t)(t0 + lane) * p.h_v + hv) * 2;
-                gb[0] = g;
-                gb[1] = beta;
-            }
+        for (int e = 0; e < 4; ++e) x[e] = (4 * kq + e == col) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            const f32x4 a4 = ld4(sA + (16 * b + r) * LC + 16 * b + 4 * kq);
+            float part = a4[0] * x[0] + a4[1] * x[1] + a4[2] * x[2] + a4[3] * x[3];
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if (r > col && kq == r / 4) x[r % 4] = -part;
         }
-        __syncthreads();
-        // A (strict lower) into sA; P (lower incl. diagonal) to the workspace.
-        for (int idx = tid; idx < kC * (kC / 4); idx += 256) {
-            const int i = idx / (kC / 4), j0 = 4 * (idx % (kC / 4));
-            const float Gi = sG[i], bi = sB[i];
-            float av[4], pv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = j0 + e;
-                const float m = j <= i ? expf(Gi - sG[j]) : 0.0f;
-                av[e] = j < i ? bi * m * sKK[i * LC + j] : 0.0f;
-                pv[e] = j <= i ? m * sQKm[i * LC + j] : 0.0f;
-            }
-            *reinterpret_cast<float4 *>(sA + i * LC + j0) = make_float4(av[0], av[1], av[2], av[3]);
-            if (i < Lc)
-                *reinterpret_cast<float4 *>(p.ws_tp + (((size_t)(t0 + i) * p.h_v + hv) * 2 + 1) * kC + j0) =
-                    make_float4(pv[0], pv[1], pv[2], pv[3]);
-        }
-        __syncthreads();
-        // Forward substitution, fp32: thread (column j, quarter q) keeps rows
-        // 16q .. 16q+15 of column j of T in registers.
-        {
-            const int j = tid >> 2, q = tid & 3;
-            float r[16];
+        for (int e = 0; e < 4; ++e) sT[(16 * b + 4 * kq + e) * LC + 16 * b + col] = x[e];
+    }
+    __syncthreads();
+    // Off-diagonal blocks, by distance d from the diagonal:
+    //   T_ij = -T_ii (sum_{m=j}^{i-1} A_im T_mj).
 #pragma unroll
-            for (int s = 0; s < 16; ++s) r[s] = (16 * q + s == j) ? 1.0f : 0.0f;
+    for (int d = 1; d < 4; ++d) {
+        const bool act = wave < 4 - d;
+        const int bi = wave + d, bj = wave;
+        if (act) {
+            float wv[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int m = bj; m < bi; ++m) {
 #pragma unroll
-            for (int i = 1; i < kC; ++i) {
-                const float *Ai = sA + i * LC + 16 * q;
-                float part = 0.0f;
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    float tc[4];
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const float4 av = *reinterpret_cast<const float4 *>(Ai + 4 * s4);
-                    part = fmaf(av.x, r[4 * s4 + 0], part);
-                    part = fmaf(av.y, r[4 * s4 + 1], part);
-                    part = fmaf(av.z, r[4 * s4 + 2], part);
-                    part = fmaf(av.w, r[4 * s4 + 3], part);
+                    for (int kk = 0; kk < 4; ++kk) tc[kk] = sT[(16 * m + 4 * k4 + kk) * LC + 16 * bj + col];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const f32x4 a4 = ld4(sA + (16 * bi + 4 * kq + e) * LC + 16 * m + 4 * k4);
+                        wv[e] = fmaf(a4[0], tc[0], fmaf(a4[1], tc[1], fmaf(a4[2], tc[2], fmaf(a4[3], tc[3], wv[e]))));
+                    }
                 }
-                part += __shfl_xor(part, 1, 64);
-                part += __shfl_xor(part, 2, 64);
-                if (q == i / 16 && i > j) r[i % 16] = -part;
             }
-            __syncthreads(); // every thread is done reading A
 #pragma unroll
-            for (int s = 0; s < 16; ++s) sA[(16 * q + s) * LC + j] = r[s];
+            for (int e = 0; e < 4; ++e) sW[wave][(4 * kq + e) * 17 + col] = wv[e];
         }
         __syncthreads();
-        for (int idx = tid; idx < Lc * (kC / 4); idx += 256) {
-            const int i = idx / (kC / 4), j0 = 4 * (idx % (kC / 4));
-            *reinterpret_cast<float4 *>(p.ws_tp + (((size_t)(t0 + i) * p.h_v + hv) * 2 + 0) * kC + j0) =
-                *reinterpret_cast<const float4 *>(sA + i * LC + j0);
+        if (act) {
+            float tv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                float wk[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) wk[kk] = sW[wave][(4 * k4 + kk) * 17 + col];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const f32x4 t4 = ld4(sT + (16 * bi + 4 * kq + e) * LC + 16 * bi + 4 * k4);
+                    tv[e] = fmaf(t4[0], wk[0], fmaf(t4[1], wk[1], fmaf(t4[2], wk[2], fmaf(t4[3], wk[3], tv[e]))));
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sT[(16 * bi + 4 * kq + e) * LC + 16 * bj + col] = -tv[e];
         }
         __syncthreads();
+    }
+
+    // T and P rows of the chunk's tokens, split into bf16 hi + lo.
+    for (int idx = tid; idx < Lc * 16; idx += 256) {
+        const int i = idx >> 4, which = (idx >> 3) & 1, g = idx & 7;
+        const float *src = (which ? sP : sT) + i * LC + 8 * g;
+        const f32x4 u = ld4(src), v = ld4(src + 4);
+        const float vals[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+        const Frag f = split8(vals);
+        __bf16 *dst = p.ws_tp + ((size_t)(t0 + i) * p.h_v + hv) * 4 * kC + which * 2 * kC + 8 * g;
+        *reinterpret_cast<bf16x8 *>(dst) = f.hi;
+        *reinterpret_cast<bf16x8 *>(dst + kC) = f.lo;
     }
 }
 
@@ -333,15 +450,23 @@ prep_kernel(const PrefillArgs p)
 // threads = 4 waves.  Wave w owns output rows 16w..16w+15 of each chunk and
 // the state rows of M-tiles w, w+4, ... (16 rows each).
 // ---------------------------------------------------------------------------
-template <int DK>
+template <int DK> constexpr size_t scan_smem_bytes()
+{
+    constexpr size_t RK = DK + 8, RT = kC + 8;
+    return 2 * (4 * kC * RK + 2 * DK * RT + 2 * kBV * RK + 6 * kBV * RT) +
+           4 * (kC * kBV + 3 * kC);
+}
+
+template <typename TIn, int DK>
 __global__ void __launch_bounds__(256)
 scan_kernel(const PrefillArgs p, int slices)
 {
-    constexpr int LDK = DK + 4;
-    constexpr int LT = kC + 4;    // padded row of the transposed C-vectors
+    constexpr int RK = DK + 8;    // bf16 row stride: q^/k^ rows, S^T rows
+    constexpr int RT = kC + 8;    // bf16 row stride: transposed chunk vectors
     constexpr int MTS = DK / 16;  // state M-tiles
-    constexpr int MTW = (MTS + 3) / 4; // state M-tiles per wave (max)
-    constexpr int PF = (kC * DK / 4) / 256; // float4 prefetch per thread per matrix
+    constexpr int MTW = (MTS + 3) / 4;
+    constexpr int GPR = DK / 2;   // 16-byte groups per token row (4*DK bf16)
+    constexpr int PF = kC * GPR / 256;
 
     // Map the block index so the slices of one head share an XCD (blocks
     // are dealt round-robin over 8 XCDs): they read the same chunk data.
@@ -366,16 +491,27 @@ scan_kernel(const PrefillArgs p, int slices)
     const int L = p.cu[n + 1] - s0;
     const int nchunks = (L + kC - 1) / kC;
     const int c0 = hv * p.d_v + slice * kBV; // first value column
+    const TIn *x = static_cast<const TIn *>(p.qkv);
 
-    extern __shared__ float smem[];
-    float *sK = smem;              // [C][LDK]
-    float *sQ = sK + kC * LDK;     // [C][LDK]
-    float *sST = sQ + kC * LDK;    // [16][LDK]  state slice, transposed
-    float *sRT = sST + kBV * LDK;  // [16][LT]   R, transposed
-    float *sDT = sRT + kBV * LT;   // [16][LT]   D, transposed
-    float *sV = sDT + kBV * LT;    // [C][16]
-    float *sG = sV + kC * kBV;     // [C]
-    float *sB = sG + kC;           // [C]
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    __bf16 *sQh = reinterpret_cast<__bf16 *>(smem_raw); // [C][RK]
+    __bf16 *sQl = sQh + kC * RK;
+    __bf16 *sKh = sQl + kC * RK;
+    __bf16 *sKl = sKh + kC * RK;
+    __bf16 *sKTh = sKl + kC * RK;  // [DK][RT]  k^ transposed
+    __bf16 *sKTl = sKTh + DK * RT;
+    __bf16 *sSh = sKTl + DK * RT;  // [16][RK]  state slice transposed
+    __bf16 *sSl = sSh + kBV * RK;
+    __bf16 *sRh = sSl + kBV * RK;  // [16][RT]  R transposed
+    __bf16 *sRl = sRh + kBV * RT;
+    __bf16 *sDh = sRl + kBV * RT;  // [16][RT]  D transposed
+    __bf16 *sDl = sDh + kBV * RT;
+    __bf16 *sEh = sDl + kBV * RT;  // [16][RT]  diag(e^{G_C-G}) D transposed
+    __bf16 *sEl = sEh + kBV * RT;
+    float *sV = reinterpret_cast<float *>(sEl + kBV * RT); // [C][16] conv(v)
+    float *sEG = sV + kC * kBV;    // e^{G_t}
+    float *sEGC = sEG + kC;        // e^{G_C - G_t}
+    float *sB = sEGC + kC;         // beta_t
 
     // State slice in registers (D layout): tile mt = wave + 4*u.
     f32x4 S[MTW];
@@ -391,208 +527,259 @@ scan_kernel(const PrefillArgs p, int slices)
             }
             if (mt < MTS)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sST[col * LDK + 16 * mt + 4 * kq + e] = S[u][e];
+                for (int e = 0; e < 4; ++e) {
+                    __bf16 h, l;
+                    split1(S[u][e], h, l);
+                    sSh[col * RK + 16 * mt + 4 * kq + e] = h;
+                    sSl[col * RK + 16 * mt + 4 * kq + e] = l;
+                }
         }
     }
 
-    // Chunk inputs staged through registers one chunk ahead.
-    constexpr int PV = kC * kBV / 256;  // v values per thread per chunk
-    float4 pk[PF], pq[PF];
-    float pv_[PV], pg_ = 0.0f, pb_ = 0.0f;
-    auto fetch = [&](int c) {
-        const int t0 = s0 + c * kC;
-        const int Lc = min(kC, L - c * kC);
-#pragma unroll
-        for (int f = 0; f < PF; ++f) {
-            const int idx = tid + 256 * f;
-            const int t = idx / (DK / 4), i4 = idx % (DK / 4);
-            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-            const float *base = p.ws_qk + (((size_t)(t0 + t) * p.h_k + hk) * 2) * DK + 4 * i4;
-            pq[f] = t < Lc ? *reinterpret_cast<const float4 *>(base) : z;
-            pk[f] = t < Lc ? *reinterpret_cast<const float4 *>(base + DK) : z;
-        }
-#pragma unroll
-        for (int f = 0; f < PV; ++f) {
-            const int idx = tid + 256 * f;
-            const int t = idx / kBV, cc = idx % kBV;
-            pv_[f] = t < Lc ? p.ws_v[(size_t)(t0 + t) * p.value_dim + c0 + cc] : 0.0f;
-        }
-        if (tid < kC) {
-            if (tid < Lc) {
-                const float *gb = p.ws_gb + ((size_t)(t0 + tid) * p.h_v + hv) * 2;
-                pg_ = gb[0];
-                pb_ = gb[1];
-            } else {
-                pg_ = p.ws_gb[((size_t)(t0 + Lc - 1) * p.h_v + hv) * 2]; // g = 0 past the end
-                pb_ = 0.0f;
-            }
-        }
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int f = 0; f < PF; ++f) {
-            const int idx = tid + 256 * f;
-            const int t = idx / (DK / 4), i4 = idx % (DK / 4);
-            *reinterpret_cast<float4 *>(sQ + t * LDK + 4 * i4) = pq[f];
-            *reinterpret_cast<float4 *>(sK + t * LDK + 4 * i4) = pk[f];
-        }
-#pragma unroll
-        for (int f = 0; f < PV; ++f) sV[tid + 256 * f] = pv_[f];
-        if (tid < kC) {
-            sG[tid] = pg_;
-            sB[tid] = pb_;
-        }
-    };
+    // v channels of this thread at staging time: token vt, channels 4*vg..
+    const int vt = tid >> 2, vg = tid & 3;
+    const int vch = 2 * p.h_k * DK + c0 + 4 * vg;
+    float wv[4][4];
+    load_taps4(p, vch, wv);
+
+    // Inputs of the next chunk, in flight in registers while the current
+    // chunk is computed.  The fetch only issues loads (rows past the chunk
+    // end re-read a valid row); every select or conversion that needs the
+    // loaded values happens at staging time, after the compute.
+    typedef typename RawAct<TIn>::type RawT;
+    u32x4 pqk[PF];
+    Frag nT[2], nP[2], cT[2], cP[2];
+    RawT nxr[4];
+    float2 ngb = make_float2(0.f, 0.f);
+    float ngc = 0.0f;
+
+#define GDN_SCAN_FETCH(CH)                                                                     \
+    {                                                                                          \
+        const int ft0 = s0 + (CH) * kC;                                                        \
+        const int fLc = min(kC, L - (CH) * kC);                                                \
+        _Pragma("unroll") for (int f = 0; f < PF; ++f) {                                       \
+            const int idx = tid + 256 * f;                                                     \
+            const int t = idx / GPR, g = idx % GPR;                                            \
+            const int tr = t < fLc ? t : 0;                                                    \
+            pqk[f] = *reinterpret_cast<const u32x4 *>(                                         \
+                p.ws_qk + ((size_t)(ft0 + tr) * p.h_k + hk) * 4 * DK + 8 * g);                 \
+        }                                                                                      \
+        {                                                                                      \
+            const int row = 16 * wave + col;                                                   \
+            const int rr = row < fLc ? row : 0;                                                \
+            const __bf16 *tp = p.ws_tp + ((size_t)(ft0 + rr) * p.h_v + hv) * 4 * kC + 8 * kq;  \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
+                nT[s] = frag_at(tp + 32 * s, tp + kC + 32 * s);                                \
+                nP[s] = frag_at(tp + 2 * kC + 32 * s, tp + 3 * kC + 32 * s);                   \
+            }                                                                                  \
+        }                                                                                      \
+        {                                                                                      \
+            const int tl = (CH) * kC + vt;                                                     \
+            const int tc = tl < L ? tl : L - 1;                                                \
+            /* positions before the sequence start only occur in chunk 0, whose  */            \
+            /* v inputs are read through the history path instead: clamp to 0    */            \
+            _Pragma("unroll") for (int j = 0; j < 4; ++j)                                      \
+                nxr[j] = RawAct<TIn>::load(                                                    \
+                    x, (size_t)(s0 + max(tc - 3 + j, 0)) * p.conv_dim + vch);                  \
+        }                                                                                      \
+        if (tid < kC) {                                                                        \
+            const int tr = tid < fLc ? tid : fLc - 1;                                          \
+            ngb = *reinterpret_cast<const float2 *>(p.ws_gb + ((size_t)(ft0 + tr) * p.h_v + hv) * 2); \
+            ngc = p.ws_gb[((size_t)(ft0 + fLc - 1) * p.h_v + hv) * 2];                         \
+        }                                                                                      \
+    }
+    // Stage chunk CH (its fetch has landed) into LDS.  XR holds the 4 taps'
+    // raw inputs of this thread's v channels.
+#define GDN_SCAN_STAGE(CH, XR)                                                                 \
+    {                                                                                          \
+        const int fLc = min(kC, L - (CH) * kC);                                                \
+        _Pragma("unroll") for (int f = 0; f < PF; ++f) {                                       \
+            const int idx = tid + 256 * f;                                                     \
+            const int t = idx / GPR, g = idx % GPR;                                            \
+            const int which = g / (DK / 4), part = (g / (DK / 8)) & 1, cg = g % (DK / 8);     \
+            const u32x4 zz = {0u, 0u, 0u, 0u};                                                 \
+            const u32x4 v = t < fLc ? pqk[f] : zz;                                             \
+            __bf16 *rowdst = (which ? (part ? sKl : sKh) : (part ? sQl : sQh)) + t * RK + 8 * cg; \
+            *reinterpret_cast<u32x4 *>(rowdst) = v;                                            \
+            if (which) {                                                                       \
+                const bf16x8 v8 = __builtin_bit_cast(bf16x8, v);                               \
+                __bf16 *tdst = (part ? sKTl : sKTh) + (8 * cg) * RT + t;                       \
+                _Pragma("unroll") for (int e = 0; e < 8; ++e) tdst[e * RT] = v8[e];            \
+            }                                                                                  \
+        }                                                                                      \
+        *reinterpret_cast<f32x4 *>(sV + vt * kBV + 4 * vg) = conv4(wv, XR);                    \
+        if (tid < kC) {                                                                        \
+            const float ng = ngb.x; /* g = 0 past the end: G stays at G_{Lc-1} */              \
+            sEG[tid] = expf(ng);                                                               \
+            sEGC[tid] = expf(ngc - ng);                                                        \
+            sB[tid] = tid < fLc ? ngb.y : 0.0f;                                                \
+        }                                                                                      \
+        {                                                                                      \
+            const bool live = 16 * wave + col < fLc;                                           \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
+                cT[s] = frag_select(live, nT[s]);                                              \
+                cP[s] = frag_select(live, nP[s]);                                              \
+            }                                                                                  \
+        }                                                                                      \
+    }
 
     if (nchunks > 0) {
-        fetch(0);
-        stage();
+        GDN_SCAN_FETCH(0)
+        // chunk 0 may reach into the incoming conv history
+        f32x4 x0[4];
+        {
+            const int tc = vt < L ? vt : L - 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x0[j] = raw4(p, x, n, s0, tc - 3 + j, vch);
+        }
+        GDN_SCAN_STAGE(0, x0)
     }
     __syncthreads();
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = s0 + c * kC;
         const int Lc = min(kC, L - c * kC);
-        // T and P rows of this wave's output tile (A operands), issued early.
-        const int row = 16 * wave + col;
-        float Tf[2][8], Pf[2][8];
-        {
-            const float *tp = p.ws_tp + (((size_t)(t0 + row) * p.h_v + hv) * 2) * kC;
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int e4 = 0; e4 < 2; ++e4) {
-                    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-                    const float4 tv = row < Lc ? *reinterpret_cast<const float4 *>(tp + 32 * s + 8 * kq + 4 * e4) : z;
-                    const float4 pv = row < Lc ? *reinterpret_cast<const float4 *>(tp + kC + 32 * s + 8 * kq + 4 * e4) : z;
-                    Tf[s][4 * e4 + 0] = tv.x; Tf[s][4 * e4 + 1] = tv.y;
-                    Tf[s][4 * e4 + 2] = tv.z; Tf[s][4 * e4 + 3] = tv.w;
-                    Pf[s][4 * e4 + 0] = pv.x; Pf[s][4 * e4 + 1] = pv.y;
-                    Pf[s][4 * e4 + 2] = pv.z; Pf[s][4 * e4 + 3] = pv.w;
-                }
-        }
-        if (c + 1 < nchunks) fetch(c + 1);
+        if (c + 1 < nchunks) GDN_SCAN_FETCH(c + 1)
 
         // X = K S and Y = Q S for rows 16w..16w+15.
         f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = X;
         {
-            const float *Ka = sK + (16 * wave + col) * LDK + 8 * kq;
-            const float *Qa = sQ + (16 * wave + col) * LDK + 8 * kq;
-            const float *Bs = sST + col * LDK + 8 * kq;
+            const int ro = (16 * wave + col) * RK + 8 * kq;
 #pragma unroll
             for (int s = 0; s < DK / 32; ++s) {
-                const Frag B = lds_frag(Bs + 32 * s);
-                X = mma3(lds_frag(Ka + 32 * s), B, X);
-                Y = mma3(lds_frag(Qa + 32 * s), B, Y);
+                const Frag B = frag_at(sSh + col * RK + 32 * s + 8 * kq, sSl + col * RK + 32 * s + 8 * kq);
+                X = mma3(frag_at(sKh + ro + 32 * s, sKl + ro + 32 * s), B, X);
+                Y = mma3(frag_at(sQh + ro + 32 * s, sQl + ro + 32 * s), B, Y);
             }
         }
-        const float GC = sG[kC - 1];
-        // R = beta (V - e^G X) -> sRT;  Y' = e^G Y stays in registers.
+        // R = beta (V - e^G X) -> sR (split, transposed);  Y' = e^G Y.
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 16 * wave + 4 * kq + e;
-            const float eg = expf(sG[t]);
-            sRT[col * LT + t] = sB[t] * (sV[t * kBV + col] - eg * X[e]);
+            const float eg = sEG[t];
+            __bf16 h, l;
+            split1(sB[t] * (sV[t * kBV + col] - eg * X[e]), h, l);
+            sRh[col * RT + t] = h;
+            sRl[col * RT + t] = l;
             Y[e] *= eg;
         }
         __syncthreads();
 
-        // D = T R for rows 16w..16w+15.
+        // D = T R for rows 16w..16w+15; also diag(e^{G_C-G}) D.
         f32x4 Dv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-            Dv = mma3(split8(Tf[s]), lds_frag(sRT + col * LT + 32 * s + 8 * kq), Dv);
+            Dv = mma3(cT[s], frag_at(sRh + col * RT + 32 * s + 8 * kq, sRl + col * RT + 32 * s + 8 * kq), Dv);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sDT[col * LT + 16 * wave + 4 * kq + e] = Dv[e];
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * wave + 4 * kq + e;
+            __bf16 h, l;
+            split1(Dv[e], h, l);
+            sDh[col * RT + t] = h;
+            sDl[col * RT + t] = l;
+            split1(Dv[e] * sEGC[t], h, l);
+            sEh[col * RT + t] = h;
+            sEl[col * RT + t] = l;
+        }
         __syncthreads();
 
         // O = Y' + P D
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-            Y = mma3(split8(Pf[s]), lds_frag(sDT + col * LT + 32 * s + 8 * kq), Y);
+            Y = mma3(cP[s], frag_at(sDh + col * RT + 32 * s + 8 * kq, sDl + col * RT + 32 * s + 8 * kq), Y);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 16 * wave + 4 * kq + e;
             if (t < Lc) p.ws_o[(size_t)(t0 + t) * p.value_dim + c0 + col] = Y[e];
         }
 
-        // S' = e^{G_C} S + (diag(e^{G_C - G}) K)^T D
-        const float gam = expf(GC);
+        // S' = e^{G_C} S + K^T diag(e^{G_C-G}) D
+        {
+            const float gam = sEG[kC - 1];
+            Frag Bs[2];
 #pragma unroll
-        for (int u = 0; u < MTW; ++u) {
-            const int mt = wave + 4 * u;
-            if (mt >= MTS) break;
-            f32x4 acc;
+            for (int s = 0; s < 2; ++s)
+                Bs[s] = frag_at(sEh + col * RT + 32 * s + 8 * kq, sEl + col * RT + 32 * s + 8 * kq);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = gam * S[u][e];
+            for (int u = 0; u < MTW; ++u) {
+                const int mt = wave + 4 * u;
+                if (mt < MTS) {
+                    f32x4 acc = gam * S[u];
+                    const int ro = (16 * mt + col) * RT + 8 * kq;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                float av[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int t = 32 * s + 8 * kq + e;
-                    av[e] = expf(GC - sG[t]) * sK[t * LDK + 16 * mt + col];
+                    for (int s = 0; s < 2; ++s)
+                        acc = mma3(frag_at(sKTh + ro + 32 * s, sKTl + ro + 32 * s), Bs[s], acc);
+                    S[u] = acc;
                 }
-                acc = mma3(split8(av), lds_frag(sDT + col * LT + 32 * s + 8 * kq), acc);
             }
-            S[u] = acc;
         }
-        __syncthreads(); // all reads of sK, sQ, sST, sDT for this chunk done
+        __syncthreads(); // every read of this chunk's LDS data is done
+
+        // State slice for the next chunk's products, split and transposed.
 #pragma unroll
         for (int u = 0; u < MTW; ++u) {
             const int mt = wave + 4 * u;
-            if (mt >= MTS) break;
+            if (mt < MTS)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sST[col * LDK + 16 * mt + 4 * kq + e] = S[u][e];
+                for (int e = 0; e < 4; ++e) {
+                    __bf16 h, l;
+                    split1(S[u][e], h, l);
+                    sSh[col * RK + 16 * mt + 4 * kq + e] = h;
+                    sSl[col * RK + 16 * mt + 4 * kq + e] = l;
+                }
         }
-        if (c + 1 < nchunks) stage();
+        if (c + 1 < nchunks) {
+            f32x4 xr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xr[j] = RawAct<TIn>::to_f32(nxr[j]);
+            GDN_SCAN_STAGE(c + 1, xr)
+        }
         __syncthreads();
     }
+#undef GDN_SCAN_FETCH
+#undef GDN_SCAN_STAGE
 
     // Final state slice.
     float *Sout = p.state_out + ((size_t)n * p.h_v + hv) * DK * p.d_v;
 #pragma unroll
     for (int u = 0; u < MTW; ++u) {
         const int mt = wave + 4 * u;
-        if (mt >= MTS) break;
+        if (mt < MTS)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + slice * kBV + col] = S[u][e];
+            for (int e = 0; e < 4; ++e)
+                Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + slice * kBV + col] = S[u][e];
     }
 }
 
 // ---------------------------------------------------------------------------
-// norm: gated RMSNorm of each (token, value head) row; one wave per row.
-// conv_final: each sequence's last K-1 raw inputs become its new history.
+// norm: gated RMSNorm of each (token, value head) row: d_v/4 lanes per row,
+// float4 per lane ("oxinfer 0.0.5 src/qwen.rs" gdn_forward, gated norm).
 // ---------------------------------------------------------------------------
-template <typename TIn>
+template <typename TIn, int DV>
 __global__ void __launch_bounds__(256)
 norm_kernel(const PrefillArgs p, int rows)
 {
-    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (r >= rows) return;
-    const int t = r / p.h_v, hv = r % p.h_v;
-    const int DV = p.d_v;
-    const size_t base = (size_t)t * p.value_dim + (size_t)hv * DV;
-    float o[2], ss = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int j = lane + 64 * u;
-        o[u] = j < DV ? p.ws_o[base + j] : 0.0f;
-        ss = fmaf(o[u], o[u], ss);
-    }
-    ss = group_sum<64>(ss);
+    constexpr int LPR = DV / 4;   // lanes per row
+    constexpr int RPW = 64 / LPR; // rows per wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = (blockIdx.x * 4 + wave) * RPW + lane / LPR;
+    const int c4 = (lane % LPR) * 4;
+    const bool valid = row < rows;
+    const int rr = valid ? row : rows - 1;
+    const int t = rr / p.h_v, hv = rr % p.h_v;
+    const size_t base = (size_t)t * p.value_dim + (size_t)hv * DV + c4;
+    const f32x4 o = ld4(p.ws_o + base);
+    float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+    ss = group_sum<LPR>(ss);
     const float rn = rsqrtf(ss / DV + p.norm_eps);
-    const TIn *z = static_cast<const TIn *>(p.z);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int j = lane + 64 * u;
-        if (j < DV) {
-            const float y = o[u] * rn * p.norm_w[j] * gatef_(load_act(z, base + j), p.gate);
-            store_out1(p.out, base + j, y, p.out_bf16);
-        }
-    }
+    const f32x4 z = load_act4v(static_cast<const TIn *>(p.z), base);
+    const f32x4 w = ld4(p.norm_w + c4);
+    float4 y;
+    y.x = o[0] * rn * w[0] * gatef_(z[0], p.gate);
+    y.y = o[1] * rn * w[1] * gatef_(z[1], p.gate);
+    y.z = o[2] * rn * w[2] * gatef_(z[2], p.gate);
+    y.w = o[3] * rn * w[3] * gatef_(z[3], p.gate);
+    if (valid) store_out4(p.out, base, y, p.out_bf16);
 }
 
 template <typename TIn>
@@ -615,38 +802,46 @@ conv_final_kernel(const PrefillArgs p)
     }
 }
 
+template <typename TIn, int DV>
+static hipError_t launch_norm(const PrefillArgs &a, int rows, hipStream_t s)
+{
+    constexpr int RPB = 4 * (64 / (DV / 4)); // rows per block
+    hipLaunchKernelGGL((norm_kernel<TIn, DV>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a,
+                       rows);
+    return hipGetLastError();
+}
+
 template <typename TIn, int DK>
 static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total, int max_len,
                                    hipStream_t s)
 {
-    const int max_chunks = (max_len + kC - 1) / kC;
-    if (max_chunks > 0) {
-        const size_t sh = sizeof(float) * (2 * kC * (DK + 4) + 2 * kC * (kC + 4) + 2 * kC);
-        hipLaunchKernelGGL((prep_kernel<TIn, DK>), dim3(max_chunks, a.h_k, n_seq), dim3(256), sh,
+    hipError_t e;
+    if (max_len > 0) {
+        hipLaunchKernelGGL((qknorm_kernel<TIn, DK>),
+                           dim3((max_len + kTileTok - 1) / kTileTok, a.h_k, n_seq), dim3(256), 0,
                            s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((tri_kernel<TIn, DK>), dim3((max_len + kC - 1) / kC, a.h_v, n_seq),
+                           dim3(256), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (n_seq > 0) {
         const int slices = a.d_v / kBV;
-        const size_t sh = sizeof(float) * (2 * kC * (DK + 4) + kBV * (DK + 4) +
-                                           2 * kBV * (kC + 4) + kC * kBV + 2 * kC);
-        hipLaunchKernelGGL((scan_kernel<DK>), dim3(n_seq * a.h_v * slices), dim3(256), sh, s, a,
-                           slices);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((scan_kernel<TIn, DK>), dim3(n_seq * a.h_v * slices), dim3(256),
+                           scan_smem_bytes<DK>(), s, a, slices);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int rows = t_total * a.h_v;
     if (rows > 0) {
-        hipLaunchKernelGGL((norm_kernel<TIn>), dim3((rows + 3) / 4), dim3(256), 0, s, a, rows);
-        hipError_t e = hipGetLastError();
+        if (a.d_v == 32) e = launch_norm<TIn, 32>(a, rows, s);
+        else if (a.d_v == 64) e = launch_norm<TIn, 64>(a, rows, s);
+        else e = launch_norm<TIn, 128>(a, rows, s);
         if (e != hipSuccess) return e;
     }
     if (n_seq > 0 && a.conv_k > 1) {
         hipLaunchKernelGGL((conv_final_kernel<TIn>), dim3((a.conv_dim + 255) / 256, n_seq),
                            dim3(256), 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
 }
@@ -654,15 +849,10 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
 template <int DK>
 static void set_smem_limits()
 {
-    const int big = (int)sizeof(float) * (2 * kC * (DK + 4) + 2 * kC * (kC + 4) + 2 * kC);
-    hipFuncSetAttribute(reinterpret_cast<const void *>(prep_kernel<bf16_t, DK>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
-    hipFuncSetAttribute(reinterpret_cast<const void *>(prep_kernel<float, DK>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, big);
-    const int sc = (int)sizeof(float) * (2 * kC * (DK + 4) + kBV * (DK + 4) + 2 * kBV * (kC + 4) +
-                                         kC * kBV + 2 * kC);
-    hipFuncSetAttribute(reinterpret_cast<const void *>(scan_kernel<DK>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, sc);
+    hipFuncSetAttribute(reinterpret_cast<const void *>(scan_kernel<bf16_t, DK>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_smem_bytes<DK>());
+    hipFuncSetAttribute(reinterpret_cast<const void *>(scan_kernel<float, DK>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_smem_bytes<DK>());
 }
 
 hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_total, int max_len,
@@ -688,9 +878,8 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.conv_in = conv_in;
     A.conv_out = conv_out;
     A.out = out;
-    A.ws_qk = reinterpret_cast<float *>(base + w.qk);
-    A.ws_v = reinterpret_cast<float *>(base + w.v);
-    A.ws_tp = reinterpret_cast<float *>(base + w.tp);
+    A.ws_qk = reinterpret_cast<__bf16 *>(base + w.qk);
+    A.ws_tp = reinterpret_cast<__bf16 *>(base + w.tp);
     A.ws_gb = reinterpret_cast<float *>(base + w.gb);
     A.ws_o = reinterpret_cast<float *>(base + w.o);
     A.h_k = d.h_k;
