@@ -17,18 +17,19 @@
 // decay underflows to zero instead of overflowing.
 //
 // Kernels (one stream, in order):
-//   qknorm  grid (16-token tile, key head, seq): causal conv + SiLU and L2
-//           norm of q and k, a group of lanes per token row; writes q^, k^
-//           split into bf16 hi + lo (ready-made matrix-core operands).
+//   qknorm  grid (chunk, key head, seq): causal conv + SiLU and L2 norm of
+//           q and k, a group of lanes per token row; writes q^, k^ rows split
+//           into bf16 hi + lo (ready-made matrix-core operands) and a
+//           transposed, bank-swizzled copy of the chunk's k^.
 //   tri     grid (chunk, value head, seq): gates and their in-chunk prefix
 //           sum, K K^T and Q K^T on MFMA, A, the blocked fp32 triangular
 //           inverse T, P; writes T and P rows split into bf16 hi + lo.
-//   scan    grid (seq, value head, 16-column slice of d_v): the chain of
-//           chunk states, sequential over the chunks of one sequence.  The
-//           state slice lives in registers, every matrix operand arrives
-//           pre-split, and the next chunk's inputs are in flight while the
-//           current one is computed.  conv + SiLU of the slice's v channels
-//           happens here.  Writes the pre-norm readout O.
+//   scan    grid (seq, value head, 16-column slice of d_v), 8 waves: four
+//           consumer waves run the chain of chunk states (state slice in
+//           registers, every matrix operand pre-split); four producer waves
+//           stream the next chunk's operands straight into LDS
+//           (global_load_lds, no register staging), convolve the slice's v
+//           channels and stage the gates.  Writes the pre-norm readout O.
 //   norm    grid (rows of (token, value head)): gated RMSNorm + output gate.
 //   conv_final: each sequence's last K-1 raw inputs become its history.
 //
@@ -44,7 +45,6 @@ namespace gdn {
 
 constexpr int kC = 64;       // tokens per chunk
 constexpr int kBV = 16;      // d_v columns per scan workgroup
-constexpr int kTileTok = 16; // tokens per qknorm workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -141,25 +141,32 @@ __device__ __forceinline__ uint32_t pack2(__bf16 a, __bf16 b)
 }
 
 // ---------------------------------------------------------------------------
-// Workspace layout (sections 256-byte aligned):
-//   qk [T][H_k][2: q^,k^][2: hi,lo][d_k] bf16
-//   tp [T][H_v][2: T,P][2: hi,lo][C]    bf16 (row of the token's chunk)
-//   gb [T][H_v][2]                      fp32 (G in-chunk cumulative, beta)
-//   o  [T][H_v*d_v]                     fp32 pre-norm readout
+// Workspace layout (sections 256-byte aligned; head-major so that a chunk's
+// data of one head is contiguous):
+//   qk [H_k][T][2: q^,k^][2: hi,lo][d_k] bf16
+//   kT [T + C*N slots][H_k*2*d_k] bf16: chunk (n, c) owns the 64 slot rows
+//       from s0 + C*n + C*c, holding per key head [hi,lo][d_k][C] (k^
+//       transposed); the 16-byte groups of a row are permuted by
+//       (group ^ (row & 7)) so that matrix-operand reads spread over banks
+//   tp [H_v][T][2: T,P][2: hi,lo][C]    bf16 (row of the token's chunk)
+//   gb [H_v][T][2]                      fp32 (G in-chunk cumulative, beta)
+//   o  [H_v][T][d_v]                    fp32 pre-norm readout
 // ---------------------------------------------------------------------------
 struct WsLayout {
-    size_t qk, tp, gb, o, total;
+    size_t qk, kt, tp, gb, o, total;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-static WsLayout ws_layout(const Dims &d, int t_total)
+static WsLayout ws_layout(const Dims &d, int n_seq, int t_total)
 {
     WsLayout w;
     const size_t T = (size_t)t_total;
     size_t off = 0;
     w.qk = off;
     off = align256(off + T * d.h_k * 4 * d.d_k * 2);
+    w.kt = off;
+    off = align256(off + (T + (size_t)kC * n_seq) * d.h_k * 2 * d.d_k * 2);
     w.tp = off;
     off = align256(off + T * d.h_v * 4 * kC * 2);
     w.gb = off;
@@ -172,8 +179,7 @@ static WsLayout ws_layout(const Dims &d, int t_total)
 
 size_t prefill_workspace_bytes(const Dims &d, int n_seq, int t_total)
 {
-    (void)n_seq;
-    return ws_layout(d, t_total).total;
+    return t_total > 0 ? ws_layout(d, n_seq, t_total).total : 0;
 }
 
 struct PrefillArgs {
@@ -185,8 +191,9 @@ struct PrefillArgs {
     const float *conv_in;
     float *conv_out;
     void *out;
-    __bf16 *ws_qk, *ws_tp;
+    __bf16 *ws_qk, *ws_kt, *ws_tp;
     float *ws_gb, *ws_o;
+    int t_total;
     int h_k, h_v, d_v, group, conv_k, conv_dim, value_dim;
     int gate, out_bf16;
     float norm_eps, l2_eps;
@@ -234,21 +241,23 @@ __device__ __forceinline__ f32x4 conv4(const float (&w)[4][4], const f32x4 (&xr)
 }
 
 // ---------------------------------------------------------------------------
-// qknorm: one workgroup per (16-token tile, key head, sequence).  Each token
-// row of the key head (q then k, 2*d_k channels) is handled by d_k/2 lanes
-// of 4 channels; each L2 norm is a reduction over d_k/4 lanes.
+// qknorm: one workgroup per (chunk, key head, sequence).  Each token row of
+// the key head (q then k, 2*d_k channels) is handled by d_k/2 lanes of 4
+// channels; each L2 norm is a reduction over d_k/4 lanes.  The k^ rows are
+// also gathered in LDS and written out transposed for the scan.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(256)
 qknorm_kernel(const PrefillArgs p)
 {
-    constexpr int LPT = DK / 2;                 // lanes per token row
-    constexpr int TPI = 64 / LPT;               // token rows per wave pass
-    constexpr int ITERS = kTileTok / (4 * TPI); // passes per wave
-    const int tile = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
+    constexpr int LPT = DK / 2;              // lanes per token row
+    constexpr int TPI = 64 / LPT;            // token rows per wave pass
+    constexpr int PASSES = kC / (4 * TPI);   // passes per wave
+    constexpr int RT = kC + 8;               // LDS row stride of the transpose
+    const int c = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
     const int s0 = p.cu[n], L = p.cu[n + 1] - s0;
-    if (tile * kTileTok >= L) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (c * kC >= L) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = lane / LPT, ll = lane % LPT;
     const bool isk = ll >= DK / 4;
     const int c4 = (isk ? ll - DK / 4 : ll) * 4;
@@ -257,27 +266,47 @@ qknorm_kernel(const PrefillArgs p)
     float w[4][4];
     load_taps4(p, ch, w);
     const float extra = isk ? 1.0f : rsqrtf((float)DK);
+    __shared__ __attribute__((aligned(16))) __bf16 sKt[2][DK][RT];
+    __bf16 *qkrow0 = p.ws_qk + ((size_t)hk * p.t_total + s0) * 4 * DK;
 
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-        const int tl = tile * kTileTok + (it * 4 + wave) * TPI + sub;
+#pragma unroll 4
+    for (int pass = 0; pass < PASSES; ++pass) {
+        const int r = (pass * 4 + wave) * TPI + sub; // row within the chunk
+        const int tl = c * kC + r;                   // position in the sequence
         const bool valid = tl < L;
         const int tc = valid ? tl : L - 1;
         f32x4 xr[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) xr[j] = raw4(p, x, n, s0, tc - 3 + j, ch);
-        const f32x4 c = conv4(w, xr);
-        float ss = c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3];
+        const f32x4 cv = conv4(w, xr);
+        float ss = cv[0] * cv[0] + cv[1] * cv[1] + cv[2] * cv[2] + cv[3] * cv[3];
         ss = group_sum<DK / 4>(ss);
-        const float sc = rsqrtf(ss + p.l2_eps) * extra;
-        if (valid) {
-            __bf16 h[4], l[4];
+        const float sc = valid ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
+        __bf16 h[4], l[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) split1(c[e] * sc, h[e], l[e]);
-            __bf16 *dst = p.ws_qk + ((size_t)(s0 + tl) * p.h_k + hk) * 4 * DK + (isk ? 2 * DK : 0) + c4;
+        for (int e = 0; e < 4; ++e) split1(cv[e] * sc, h[e], l[e]);
+        if (valid) {
+            __bf16 *dst = qkrow0 + (size_t)tl * 4 * DK + (isk ? 2 * DK : 0) + c4;
             *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
             *reinterpret_cast<uint2 *>(dst + DK) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
         }
+        if (isk) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sKt[0][c4 + e][r] = h[e];
+                sKt[1][c4 + e][r] = l[e];
+            }
+        }
+    }
+    __syncthreads();
+    // chunk block of k^ transposed: [hi,lo][d_k][C], 16-byte groups of row i
+    // stored at group (g ^ (i & 7)).
+    __bf16 *kt = p.ws_kt + (size_t)(s0 + kC * n + kC * c) * p.h_k * 2 * DK + (size_t)hk * 2 * DK * kC;
+    for (int idx = tid; idx < 2 * DK * 8; idx += 256) {
+        const int part = idx / (DK * 8), rem = idx % (DK * 8);
+        const int i = rem >> 3, g = rem & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(&sKt[part][i][8 * g]);
+        *reinterpret_cast<u32x4 *>(kt + (size_t)part * DK * kC + (size_t)i * kC + 8 * (g ^ (i & 7))) = v;
     }
 }
 
@@ -329,15 +358,15 @@ tri_kernel(const PrefillArgs p)
         sG[lane] = g;
         sB[lane] = beta;
         if (lane < Lc)
-            *reinterpret_cast<float2 *>(p.ws_gb + ((size_t)(t0 + lane) * p.h_v + hv) * 2) =
+            *reinterpret_cast<float2 *>(p.ws_gb + ((size_t)hv * p.t_total + t0 + lane) * 2) =
                 make_float2(g, beta);
     }
     __syncthreads();
 
     // K K^T -> A and Q K^T -> P, lower-triangular 16x16 tiles:
     // 20 tiles (which, mt, nt >= ... nt <= mt); wave w takes every 4th.
-    const __bf16 *qk0 = p.ws_qk + ((size_t)t0 * p.h_k + hk) * 4 * DK;
-    const size_t rs = (size_t)p.h_k * 4 * DK; // bf16 per token row
+    const __bf16 *qk0 = p.ws_qk + ((size_t)hk * p.t_total + t0) * 4 * DK;
+    constexpr size_t rs = 4 * DK; // bf16 per token row
     for (int tile = wave; tile < 20; tile += 4) {
         const int which = tile / 10; // 0: K K^T, 1: Q K^T
         int r = tile % 10, mt = 0;
@@ -439,34 +468,62 @@ tri_kernel(const PrefillArgs p)
         const f32x4 u = ld4(src), v = ld4(src + 4);
         const float vals[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
         const Frag f = split8(vals);
-        __bf16 *dst = p.ws_tp + ((size_t)(t0 + i) * p.h_v + hv) * 4 * kC + which * 2 * kC + 8 * g;
+        __bf16 *dst = p.ws_tp + ((size_t)hv * p.t_total + t0 + i) * 4 * kC + which * 2 * kC + 8 * g;
         *reinterpret_cast<bf16x8 *>(dst) = f.hi;
         *reinterpret_cast<bf16x8 *>(dst + kC) = f.lo;
     }
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup per (sequence, value head, 16-column slice), 256
-// threads = 4 waves.  Wave w owns output rows 16w..16w+15 of each chunk and
-// the state rows of M-tiles w, w+4, ... (16 rows each).
+// scan: one workgroup per (sequence, value head, 16-column slice), 512
+// threads.  Waves 0-3 (consumers): wave w owns output rows 16w..16w+15 of
+// each chunk and the state rows of M-tiles w, w+4, ...  Waves 4-7
+// (producers): while the consumers compute chunk c they stream chunk c+1's
+// operands into LDS.  Per chunk:
+//   consumers  T/P frags(c+1) ; X,Y | R | D | O, S update, S^T split
+//   producers  k^T(c+1), v/gates regs(c+1) | q^k^ rows(c+1) | sV,b,e^G(c+1)
+//              | e^{G_C-G}(c+1), wait
+// with a workgroup barrier at each '|' and one at the end.  The q^/k^ row
+// buffer is single (refilled once X and Y have read it), the transposed k^
+// buffer is double (read only by the S update at the end of a chunk).
 // ---------------------------------------------------------------------------
-template <int DK> constexpr size_t scan_smem_bytes()
+template <int DK> struct ScanLds {
+    static constexpr int RPI = 128 / DK;     // q^/k^ rows per 1 KB LDS-direct load
+    static constexpr int ROWB = 8 * DK;      // bytes per row: [q^ hi|lo, k^ hi|lo][d_k]
+    static constexpr int GRPB = 1024 + 16;   // bytes per group of RPI rows, padded
+    static constexpr int ROWS_BYTES = (kC / RPI) * GRPB;
+    static constexpr int KT_BYTES = 2 * DK * kC * 2; // one transposed k^ block
+    static constexpr int RK = DK + 8;        // bf16 stride of S^T rows
+    static constexpr int RT = kC + 8;        // bf16 stride of R, D, E rows
+    static constexpr int o_rows = 0;
+    static constexpr int o_kt = o_rows + ROWS_BYTES;   // two buffers
+    static constexpr int o_s = o_kt + 2 * KT_BYTES;    // [hi,lo][16][RK]
+    static constexpr int o_r = o_s + 2 * kBV * RK * 2; // [hi,lo][16][RT]
+    static constexpr int o_d = o_r + 2 * kBV * RT * 2;
+    static constexpr int o_e = o_d + 2 * kBV * RT * 2;
+    static constexpr int o_v = o_e + 2 * kBV * RT * 2; // fp32 [C][16]
+    static constexpr int o_g = o_v + kC * kBV * 4;     // fp32 e^G, e^{G_C-G}, beta
+    static constexpr int total = o_g + 3 * kC * 4;
+};
+template <int DK> constexpr size_t scan_smem_bytes() { return ScanLds<DK>::total; }
+
+// 16 bytes per lane, global -> LDS without register staging: lane l's
+// bytes land at lds_base + 16 l.
+__device__ __forceinline__ void lds_load16(const void *g, void *lds_base)
 {
-    constexpr size_t RK = DK + 8, RT = kC + 8;
-    return 2 * (4 * kC * RK + 2 * DK * RT + 2 * kBV * RK + 6 * kBV * RT) +
-           4 * (kC * kBV + 3 * kC);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)g,
+        (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
 template <typename TIn, int DK>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 scan_kernel(const PrefillArgs p, int slices)
 {
-    constexpr int RK = DK + 8;    // bf16 row stride: q^/k^ rows, S^T rows
-    constexpr int RT = kC + 8;    // bf16 row stride: transposed chunk vectors
-    constexpr int MTS = DK / 16;  // state M-tiles
-    constexpr int MTW = (MTS + 3) / 4;
-    constexpr int GPR = DK / 2;   // 16-byte groups per token row (4*DK bf16)
-    constexpr int PF = kC * GPR / 256;
+    using LY = ScanLds<DK>;
+    constexpr int RPI = LY::RPI, RK = LY::RK, RT = LY::RT;
+    constexpr int MTS = DK / 16;       // state M-tiles
+    constexpr int MTW = (MTS + 3) / 4; // per consumer wave
 
     // Map the block index so the slices of one head share an XCD (blocks
     // are dealt round-robin over 8 XCDs): they read the same chunk data.
@@ -486,6 +543,8 @@ scan_kernel(const PrefillArgs p, int slices)
     const int n = hidx / p.h_v, hv = hidx % p.h_v;
     const int hk = hv / p.group;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool producer = wave >= 4;
+    const int cw = wave & 3; // consumer or producer wave index
     const int col = lane & 15, kq = lane >> 4;
     const int s0 = p.cu[n];
     const int L = p.cu[n + 1] - s0;
@@ -493,33 +552,114 @@ scan_kernel(const PrefillArgs p, int slices)
     const int c0 = hv * p.d_v + slice * kBV; // first value column
     const TIn *x = static_cast<const TIn *>(p.qkv);
 
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    __bf16 *sQh = reinterpret_cast<__bf16 *>(smem_raw); // [C][RK]
-    __bf16 *sQl = sQh + kC * RK;
-    __bf16 *sKh = sQl + kC * RK;
-    __bf16 *sKl = sKh + kC * RK;
-    __bf16 *sKTh = sKl + kC * RK;  // [DK][RT]  k^ transposed
-    __bf16 *sKTl = sKTh + DK * RT;
-    __bf16 *sSh = sKTl + DK * RT;  // [16][RK]  state slice transposed
-    __bf16 *sSl = sSh + kBV * RK;
-    __bf16 *sRh = sSl + kBV * RK;  // [16][RT]  R transposed
-    __bf16 *sRl = sRh + kBV * RT;
-    __bf16 *sDh = sRl + kBV * RT;  // [16][RT]  D transposed
-    __bf16 *sDl = sDh + kBV * RT;
-    __bf16 *sEh = sDl + kBV * RT;  // [16][RT]  diag(e^{G_C-G}) D transposed
-    __bf16 *sEl = sEh + kBV * RT;
-    float *sV = reinterpret_cast<float *>(sEl + kBV * RT); // [C][16] conv(v)
-    float *sEG = sV + kC * kBV;    // e^{G_t}
-    float *sEGC = sEG + kC;        // e^{G_C - G_t}
-    float *sB = sEGC + kC;         // beta_t
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    char *sRows = smem + LY::o_rows;
+    char *sKT = smem + LY::o_kt;
+    __bf16 *sSh = reinterpret_cast<__bf16 *>(smem + LY::o_s), *sSl = sSh + kBV * RK;
+    __bf16 *sRh = reinterpret_cast<__bf16 *>(smem + LY::o_r), *sRl = sRh + kBV * RT;
+    __bf16 *sDh = reinterpret_cast<__bf16 *>(smem + LY::o_d), *sDl = sDh + kBV * RT;
+    __bf16 *sEh = reinterpret_cast<__bf16 *>(smem + LY::o_e), *sEl = sEh + kBV * RT;
+    float *sV = reinterpret_cast<float *>(smem + LY::o_v);
+    float *sEG = reinterpret_cast<float *>(smem + LY::o_g), *sEGC = sEG + kC, *sB = sEGC + kC;
 
-    // State slice in registers (D layout): tile mt = wave + 4*u.
+    const __bf16 *qk_head = p.ws_qk + (size_t)hk * p.t_total * 4 * DK;
+    const __bf16 *kt_seq = p.ws_kt + (size_t)(s0 + kC * n) * p.h_k * 2 * DK + (size_t)hk * 2 * DK * kC;
+    const __bf16 *tp_head = p.ws_tp + (size_t)hv * p.t_total * 4 * kC;
+    const float *gb_head = p.ws_gb + (size_t)hv * p.t_total * 2;
+    float *o_head = p.ws_o + (size_t)hv * p.t_total * p.d_v;
+
+    // ---- producer state: thread (token vt, channels 4 vg) of the v slice
+    typedef typename RawAct<TIn>::type RawT;
+    const int pt = tid - 256;
+    const int vt = (pt & 255) >> 2, vg = pt & 3;
+    const int vch = 2 * p.h_k * DK + c0 + 4 * vg;
+    float wv[4][4];
+    RawT nxr[4];
+    float2 ngb = make_float2(0.f, 0.f);
+    float ngc = 0.0f;
+    if (producer) load_taps4(p, vch, wv);
+
+    // ---- consumer state
     f32x4 S[MTW];
-    {
+    Frag nT[2], nP[2], cT[2], cP[2];
+
+#define GDN_PROD_KT(CH, BUF)                                                                   \
+    {                                                                                          \
+        const char *src = reinterpret_cast<const char *>(kt_seq + (size_t)(CH) * kC * p.h_k * 2 * DK); \
+        for (int k = cw; k < LY::KT_BYTES / 1024; k += 4)                                      \
+            lds_load16(src + k * 1024 + lane * 16, sKT + (BUF) * LY::KT_BYTES + k * 1024);     \
+    }
+#define GDN_PROD_ROWS(CH)                                                                      \
+    {                                                                                          \
+        for (int gi = cw; gi < kC / RPI; gi += 4) {                                            \
+            const int r = gi * RPI + lane / (64 / RPI);                                        \
+            const int tl = (CH) * kC + r;                                                      \
+            const int tc = tl < L ? tl : L - 1; /* rows past the end: any valid row */         \
+            const char *src = reinterpret_cast<const char *>(qk_head + (size_t)(s0 + tc) * 4 * DK) + \
+                              (lane % (64 / RPI)) * 16;                                         \
+            lds_load16(src, sRows + gi * LY::GRPB);                                            \
+        }                                                                                      \
+    }
+#define GDN_PROD_REGS(CH)                                                                      \
+    {                                                                                          \
+        const int fLc = min(kC, L - (CH) * kC);                                                \
+        const int tl = (CH) * kC + vt;                                                         \
+        const int tc = tl < L ? tl : L - 1;                                                    \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+            nxr[j] = RawAct<TIn>::load(x, (size_t)(s0 + max(tc - 3 + j, 0)) * p.conv_dim + vch); \
+        if (pt < kC) {                                                                         \
+            const int tr = pt < fLc ? pt : fLc - 1;                                            \
+            ngb = *reinterpret_cast<const float2 *>(gb_head + (size_t)(s0 + (CH) * kC + tr) * 2); \
+            ngc = gb_head[(size_t)(s0 + (CH) * kC + fLc - 1) * 2];                             \
+        }                                                                                      \
+    }
+#define GDN_PROD_STAGE_V(CH, XR)                                                               \
+    {                                                                                          \
+        const int fLc = min(kC, L - (CH) * kC);                                                \
+        *reinterpret_cast<f32x4 *>(sV + vt * kBV + 4 * vg) = conv4(wv, XR);                    \
+        if (pt < kC) {                                                                         \
+            sEG[pt] = expf(ngb.x); /* g = 0 past the end: G stays at G_{Lc-1} */               \
+            sB[pt] = pt < fLc ? ngb.y : 0.0f;                                                  \
+        }                                                                                      \
+    }
+#define GDN_PROD_STAGE_EGC()                                                                   \
+    {                                                                                          \
+        if (pt < kC) sEGC[pt] = expf(ngc - ngb.x);                                             \
+    }
+#define GDN_CONS_TP(CH, DT, DP)                                                                \
+    {                                                                                          \
+        const int fLc = min(kC, L - (CH) * kC);                                                \
+        const int row = 16 * cw + col;                                                         \
+        const int rr = row < fLc ? row : 0;                                                    \
+        const __bf16 *tp = tp_head + (size_t)(s0 + (CH) * kC + rr) * 4 * kC + 8 * kq;          \
+        _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                        \
+            DT[s] = frag_at(tp + 32 * s, tp + kC + 32 * s);                                    \
+            DP[s] = frag_at(tp + 2 * kC + 32 * s, tp + 3 * kC + 32 * s);                       \
+        }                                                                                      \
+    }
+
+    // ---- prologue: chunk 0 ----------------------------------------------
+    if (producer) {
+        if (nchunks > 0) {
+            GDN_PROD_KT(0, 0)
+            GDN_PROD_ROWS(0)
+            GDN_PROD_REGS(0)
+            // chunk 0 may reach into the incoming conv history
+            f32x4 x0[4];
+            {
+                const int tc = vt < L ? vt : L - 1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x0[j] = raw4(p, x, n, s0, tc - 3 + j, vch);
+            }
+            GDN_PROD_STAGE_V(0, x0)
+            GDN_PROD_STAGE_EGC()
+        }
+        __builtin_amdgcn_s_waitcnt(0); // LDS-direct loads have landed
+    } else {
         const float *Sin = p.state_in ? p.state_in + ((size_t)n * p.h_v + hv) * DK * p.d_v : nullptr;
 #pragma unroll
         for (int u = 0; u < MTW; ++u) {
-            const int mt = wave + 4 * u;
+            const int mt = cw + 4 * u;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * mt + 4 * kq + e;
@@ -534,220 +674,156 @@ scan_kernel(const PrefillArgs p, int slices)
                     sSl[col * RK + 16 * mt + 4 * kq + e] = l;
                 }
         }
-    }
-
-    // v channels of this thread at staging time: token vt, channels 4*vg..
-    const int vt = tid >> 2, vg = tid & 3;
-    const int vch = 2 * p.h_k * DK + c0 + 4 * vg;
-    float wv[4][4];
-    load_taps4(p, vch, wv);
-
-    // Inputs of the next chunk, in flight in registers while the current
-    // chunk is computed.  The fetch only issues loads (rows past the chunk
-    // end re-read a valid row); every select or conversion that needs the
-    // loaded values happens at staging time, after the compute.
-    typedef typename RawAct<TIn>::type RawT;
-    u32x4 pqk[PF];
-    Frag nT[2], nP[2], cT[2], cP[2];
-    RawT nxr[4];
-    float2 ngb = make_float2(0.f, 0.f);
-    float ngc = 0.0f;
-
-#define GDN_SCAN_FETCH(CH)                                                                     \
-    {                                                                                          \
-        const int ft0 = s0 + (CH) * kC;                                                        \
-        const int fLc = min(kC, L - (CH) * kC);                                                \
-        _Pragma("unroll") for (int f = 0; f < PF; ++f) {                                       \
-            const int idx = tid + 256 * f;                                                     \
-            const int t = idx / GPR, g = idx % GPR;                                            \
-            const int tr = t < fLc ? t : 0;                                                    \
-            pqk[f] = *reinterpret_cast<const u32x4 *>(                                         \
-                p.ws_qk + ((size_t)(ft0 + tr) * p.h_k + hk) * 4 * DK + 8 * g);                 \
-        }                                                                                      \
-        {                                                                                      \
-            const int row = 16 * wave + col;                                                   \
-            const int rr = row < fLc ? row : 0;                                                \
-            const __bf16 *tp = p.ws_tp + ((size_t)(ft0 + rr) * p.h_v + hv) * 4 * kC + 8 * kq;  \
-            _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
-                nT[s] = frag_at(tp + 32 * s, tp + kC + 32 * s);                                \
-                nP[s] = frag_at(tp + 2 * kC + 32 * s, tp + 3 * kC + 32 * s);                   \
-            }                                                                                  \
-        }                                                                                      \
-        {                                                                                      \
-            const int tl = (CH) * kC + vt;                                                     \
-            const int tc = tl < L ? tl : L - 1;                                                \
-            /* positions before the sequence start only occur in chunk 0, whose  */            \
-            /* v inputs are read through the history path instead: clamp to 0    */            \
-            _Pragma("unroll") for (int j = 0; j < 4; ++j)                                      \
-                nxr[j] = RawAct<TIn>::load(                                                    \
-                    x, (size_t)(s0 + max(tc - 3 + j, 0)) * p.conv_dim + vch);                  \
-        }                                                                                      \
-        if (tid < kC) {                                                                        \
-            const int tr = tid < fLc ? tid : fLc - 1;                                          \
-            ngb = *reinterpret_cast<const float2 *>(p.ws_gb + ((size_t)(ft0 + tr) * p.h_v + hv) * 2); \
-            ngc = p.ws_gb[((size_t)(ft0 + fLc - 1) * p.h_v + hv) * 2];                         \
-        }                                                                                      \
-    }
-    // Stage chunk CH (its fetch has landed) into LDS.  XR holds the 4 taps'
-    // raw inputs of this thread's v channels.
-#define GDN_SCAN_STAGE(CH, XR)                                                                 \
-    {                                                                                          \
-        const int fLc = min(kC, L - (CH) * kC);                                                \
-        _Pragma("unroll") for (int f = 0; f < PF; ++f) {                                       \
-            const int idx = tid + 256 * f;                                                     \
-            const int t = idx / GPR, g = idx % GPR;                                            \
-            const int which = g / (DK / 4), part = (g / (DK / 8)) & 1, cg = g % (DK / 8);     \
-            const u32x4 zz = {0u, 0u, 0u, 0u};                                                 \
-            const u32x4 v = t < fLc ? pqk[f] : zz;                                             \
-            __bf16 *rowdst = (which ? (part ? sKl : sKh) : (part ? sQl : sQh)) + t * RK + 8 * cg; \
-            *reinterpret_cast<u32x4 *>(rowdst) = v;                                            \
-            if (which) {                                                                       \
-                const bf16x8 v8 = __builtin_bit_cast(bf16x8, v);                               \
-                __bf16 *tdst = (part ? sKTl : sKTh) + (8 * cg) * RT + t;                       \
-                _Pragma("unroll") for (int e = 0; e < 8; ++e) tdst[e * RT] = v8[e];            \
-            }                                                                                  \
-        }                                                                                      \
-        *reinterpret_cast<f32x4 *>(sV + vt * kBV + 4 * vg) = conv4(wv, XR);                    \
-        if (tid < kC) {                                                                        \
-            const float ng = ngb.x; /* g = 0 past the end: G stays at G_{Lc-1} */              \
-            sEG[tid] = expf(ng);                                                               \
-            sEGC[tid] = expf(ngc - ng);                                                        \
-            sB[tid] = tid < fLc ? ngb.y : 0.0f;                                                \
-        }                                                                                      \
-        {                                                                                      \
-            const bool live = 16 * wave + col < fLc;                                           \
-            _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
-                cT[s] = frag_select(live, nT[s]);                                              \
-                cP[s] = frag_select(live, nP[s]);                                              \
-            }                                                                                  \
-        }                                                                                      \
-    }
-
-    if (nchunks > 0) {
-        GDN_SCAN_FETCH(0)
-        // chunk 0 may reach into the incoming conv history
-        f32x4 x0[4];
-        {
-            const int tc = vt < L ? vt : L - 1;
+        if (nchunks > 0) {
+            GDN_CONS_TP(0, nT, nP)
+            const bool live = 16 * cw + col < min(kC, L);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x0[j] = raw4(p, x, n, s0, tc - 3 + j, vch);
+            for (int s = 0; s < 2; ++s) {
+                cT[s] = frag_select(live, nT[s]);
+                cP[s] = frag_select(live, nP[s]);
+            }
         }
-        GDN_SCAN_STAGE(0, x0)
     }
     __syncthreads();
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = s0 + c * kC;
         const int Lc = min(kC, L - c * kC);
-        if (c + 1 < nchunks) GDN_SCAN_FETCH(c + 1)
+        const bool more = c + 1 < nchunks;
+        f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+        float gam = 0.0f;
 
-        // X = K S and Y = Q S for rows 16w..16w+15.
-        f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = X;
-        {
-            const int ro = (16 * wave + col) * RK + 8 * kq;
+        // ---- phase 1: X, Y | producers: k^T(c+1), v/gates loads ---------
+        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+        if (!producer) {
+            if (more) GDN_CONS_TP(c + 1, nT, nP)
+            const int r = 16 * cw + col;
+            const char *rowp = sRows + (r / RPI) * LY::GRPB + (r % RPI) * LY::ROWB + 16 * kq;
 #pragma unroll
             for (int s = 0; s < DK / 32; ++s) {
                 const Frag B = frag_at(sSh + col * RK + 32 * s + 8 * kq, sSl + col * RK + 32 * s + 8 * kq);
-                X = mma3(frag_at(sKh + ro + 32 * s, sKl + ro + 32 * s), B, X);
-                Y = mma3(frag_at(sQh + ro + 32 * s, sQl + ro + 32 * s), B, Y);
+                const __bf16 *rq = reinterpret_cast<const __bf16 *>(rowp) + 32 * s;
+                X = mma3(frag_at(rq + 2 * DK, rq + 3 * DK), B, X);
+                Y = mma3(frag_at(rq, rq + DK), B, Y);
             }
-        }
-        // R = beta (V - e^G X) -> sR (split, transposed);  Y' = e^G Y.
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * wave + 4 * kq + e;
-            const float eg = sEG[t];
-            __bf16 h, l;
-            split1(sB[t] * (sV[t * kBV + col] - eg * X[e]), h, l);
-            sRh[col * RT + t] = h;
-            sRl[col * RT + t] = l;
-            Y[e] *= eg;
+        } else if (more) {
+            GDN_PROD_KT(c + 1, (c + 1) & 1)
+            GDN_PROD_REGS(c + 1)
         }
         __syncthreads();
 
-        // D = T R for rows 16w..16w+15; also diag(e^{G_C-G}) D.
-        f32x4 Dv = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 2: R = beta (V - e^G X) -> sR; Y' = e^G Y | rows(c+1) --
+        if (!producer) {
+            gam = sEG[kC - 1];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            Dv = mma3(cT[s], frag_at(sRh + col * RT + 32 * s + 8 * kq, sRl + col * RT + 32 * s + 8 * kq), Dv);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * wave + 4 * kq + e;
-            __bf16 h, l;
-            split1(Dv[e], h, l);
-            sDh[col * RT + t] = h;
-            sDl[col * RT + t] = l;
-            split1(Dv[e] * sEGC[t], h, l);
-            sEh[col * RT + t] = h;
-            sEl[col * RT + t] = l;
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * cw + 4 * kq + e;
+                const float eg = sEG[t];
+                __bf16 h, l;
+                split1(sB[t] * (sV[t * kBV + col] - eg * X[e]), h, l);
+                sRh[col * RT + t] = h;
+                sRl[col * RT + t] = l;
+                Y[e] *= eg;
+            }
+        } else if (more) {
+            GDN_PROD_ROWS(c + 1)
         }
         __syncthreads();
 
-        // O = Y' + P D
+        // ---- phase 3: D = T R -> sD, sE | sV, beta, e^G (c+1) -------------
+        if (!producer) {
+            f32x4 Dv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            Y = mma3(cP[s], frag_at(sDh + col * RT + 32 * s + 8 * kq, sDl + col * RT + 32 * s + 8 * kq), Y);
+            for (int s = 0; s < 2; ++s)
+                Dv = mma3(cT[s], frag_at(sRh + col * RT + 32 * s + 8 * kq, sRl + col * RT + 32 * s + 8 * kq), Dv);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * wave + 4 * kq + e;
-            if (t < Lc) p.ws_o[(size_t)(t0 + t) * p.value_dim + c0 + col] = Y[e];
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * cw + 4 * kq + e;
+                __bf16 h, l;
+                split1(Dv[e], h, l);
+                sDh[col * RT + t] = h;
+                sDl[col * RT + t] = l;
+                split1(Dv[e] * sEGC[t], h, l);
+                sEh[col * RT + t] = h;
+                sEl[col * RT + t] = l;
+            }
+        } else if (more) {
+            f32x4 xr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xr[j] = RawAct<TIn>::to_f32(nxr[j]);
+            GDN_PROD_STAGE_V(c + 1, xr)
         }
+        __syncthreads();
 
-        // S' = e^{G_C} S + K^T diag(e^{G_C-G}) D
-        {
-            const float gam = sEG[kC - 1];
+        // ---- phase 4: O = Y' + P D; S' = gam S + K^T E | e^{G_C-G} (c+1) --
+        if (!producer) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                Y = mma3(cP[s], frag_at(sDh + col * RT + 32 * s + 8 * kq, sDl + col * RT + 32 * s + 8 * kq), Y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * cw + 4 * kq + e;
+                if (t < Lc) o_head[(size_t)(t0 + t) * p.d_v + slice * kBV + col] = Y[e];
+            }
             Frag Bs[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 Bs[s] = frag_at(sEh + col * RT + 32 * s + 8 * kq, sEl + col * RT + 32 * s + 8 * kq);
+            const char *kt = sKT + (c & 1) * LY::KT_BYTES;
 #pragma unroll
             for (int u = 0; u < MTW; ++u) {
-                const int mt = wave + 4 * u;
+                const int mt = cw + 4 * u;
                 if (mt < MTS) {
+                    const int i = 16 * mt + col;
                     f32x4 acc = gam * S[u];
-                    const int ro = (16 * mt + col) * RT + 8 * kq;
 #pragma unroll
-                    for (int s = 0; s < 2; ++s)
-                        acc = mma3(frag_at(sKTh + ro + 32 * s, sKTl + ro + 32 * s), Bs[s], acc);
+                    for (int s = 0; s < 2; ++s) {
+                        const int g = (4 * s + kq) ^ (i & 7);
+                        const __bf16 *ah = reinterpret_cast<const __bf16 *>(kt + (size_t)i * kC * 2 + g * 16);
+                        acc = mma3(frag_at(ah, ah + DK * kC), Bs[s], acc);
+                    }
                     S[u] = acc;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        __bf16 h, l;
+                        split1(acc[e], h, l);
+                        sSh[col * RK + 16 * mt + 4 * kq + e] = h;
+                        sSl[col * RK + 16 * mt + 4 * kq + e] = l;
+                    }
                 }
             }
-        }
-        __syncthreads(); // every read of this chunk's LDS data is done
-
-        // State slice for the next chunk's products, split and transposed.
+            if (more) {
+                const bool live = 16 * cw + col < min(kC, L - (c + 1) * kC);
 #pragma unroll
-        for (int u = 0; u < MTW; ++u) {
-            const int mt = wave + 4 * u;
-            if (mt < MTS)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    __bf16 h, l;
-                    split1(S[u][e], h, l);
-                    sSh[col * RK + 16 * mt + 4 * kq + e] = h;
-                    sSl[col * RK + 16 * mt + 4 * kq + e] = l;
+                for (int s = 0; s < 2; ++s) {
+                    cT[s] = frag_select(live, nT[s]);
+                    cP[s] = frag_select(live, nP[s]);
                 }
-        }
-        if (c + 1 < nchunks) {
-            f32x4 xr[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xr[j] = RawAct<TIn>::to_f32(nxr[j]);
-            GDN_SCAN_STAGE(c + 1, xr)
+            }
+        } else {
+            if (more) GDN_PROD_STAGE_EGC()
+            __builtin_amdgcn_s_waitcnt(0); // chunk c+1's LDS-direct loads have landed
         }
         __syncthreads();
     }
-#undef GDN_SCAN_FETCH
-#undef GDN_SCAN_STAGE
+#undef GDN_PROD_KT
+#undef GDN_PROD_ROWS
+#undef GDN_PROD_REGS
+#undef GDN_PROD_STAGE_V
+#undef GDN_PROD_STAGE_EGC
+#undef GDN_CONS_TP
 
     // Final state slice.
-    float *Sout = p.state_out + ((size_t)n * p.h_v + hv) * DK * p.d_v;
+    if (!producer) {
+        float *Sout = p.state_out + ((size_t)n * p.h_v + hv) * DK * p.d_v;
 #pragma unroll
-    for (int u = 0; u < MTW; ++u) {
-        const int mt = wave + 4 * u;
-        if (mt < MTS)
+        for (int u = 0; u < MTW; ++u) {
+            const int mt = cw + 4 * u;
+            if (mt < MTS)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + slice * kBV + col] = S[u][e];
+                for (int e = 0; e < 4; ++e)
+                    Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + slice * kBV + col] = S[u][e];
+        }
     }
 }
 
@@ -768,7 +844,7 @@ norm_kernel(const PrefillArgs p, int rows)
     const int rr = valid ? row : rows - 1;
     const int t = rr / p.h_v, hv = rr % p.h_v;
     const size_t base = (size_t)t * p.value_dim + (size_t)hv * DV + c4;
-    const f32x4 o = ld4(p.ws_o + base);
+    const f32x4 o = ld4(p.ws_o + ((size_t)hv * p.t_total + t) * DV + c4);
     float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
     ss = group_sum<LPR>(ss);
     const float rn = rsqrtf(ss / DV + p.norm_eps);
@@ -817,9 +893,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
 {
     hipError_t e;
     if (max_len > 0) {
-        hipLaunchKernelGGL((qknorm_kernel<TIn, DK>),
-                           dim3((max_len + kTileTok - 1) / kTileTok, a.h_k, n_seq), dim3(256), 0,
-                           s, a);
+        hipLaunchKernelGGL((qknorm_kernel<TIn, DK>), dim3((max_len + kC - 1) / kC, a.h_k, n_seq),
+                           dim3(256), 0, s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((tri_kernel<TIn, DK>), dim3((max_len + kC - 1) / kC, a.h_v, n_seq),
                            dim3(256), 0, s, a);
@@ -827,7 +902,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
     }
     if (n_seq > 0) {
         const int slices = a.d_v / kBV;
-        hipLaunchKernelGGL((scan_kernel<TIn, DK>), dim3(n_seq * a.h_v * slices), dim3(256),
+        hipLaunchKernelGGL((scan_kernel<TIn, DK>), dim3(n_seq * a.h_v * slices), dim3(512),
                            scan_smem_bytes<DK>(), s, a, slices);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -861,7 +936,7 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
                           const float *conv_in, float *conv_out, void *out, void *ws,
                           hipStream_t s)
 {
-    const WsLayout w = ws_layout(d, t_total);
+    const WsLayout w = ws_layout(d, n_seq, t_total);
     char *base = static_cast<char *>(ws);
     PrefillArgs A;
     A.qkv = qkv;
@@ -879,6 +954,8 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.conv_out = conv_out;
     A.out = out;
     A.ws_qk = reinterpret_cast<__bf16 *>(base + w.qk);
+    A.ws_kt = reinterpret_cast<__bf16 *>(base + w.kt);
+    A.t_total = t_total;
     A.ws_tp = reinterpret_cast<__bf16 *>(base + w.tp);
     A.ws_gb = reinterpret_cast<float *>(base + w.gb);
     A.ws_o = reinterpret_cast<float *>(base + w.o);
