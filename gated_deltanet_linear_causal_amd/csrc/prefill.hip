@@ -252,7 +252,8 @@ qknorm_kernel(const PrefillArgs p)
 {
     constexpr int LPT = DK / 2;              // lanes per token row
     constexpr int TPI = 64 / LPT;            // token rows per wave pass
-    constexpr int PASSES = kC / (4 * TPI);   // passes per wave
+    constexpr int TPL = kC / (4 * TPI);      // consecutive tokens per lane
+    constexpr int WIN = TPL + 3;             // raw rows a lane reads
     constexpr int RT = kC + 8;               // LDS row stride of the transpose
     const int c = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
     const int s0 = p.cu[n], L = p.cu[n + 1] - s0;
@@ -263,21 +264,37 @@ qknorm_kernel(const PrefillArgs p)
     const int c4 = (isk ? ll - DK / 4 : ll) * 4;
     const int ch = (isk ? p.h_k * DK : 0) + hk * DK + c4;
     const TIn *x = static_cast<const TIn *>(p.qkv);
+    __shared__ __attribute__((aligned(16))) __bf16 sKt[2][DK][RT];
+    __bf16 *qkrow0 = p.ws_qk + ((size_t)hk * p.t_total + s0) * 4 * DK;
+    const int r0 = kC / 4 * wave + TPL * sub; // first chunk row of this lane
+    const int tl0 = c * kC + r0;              // its position in the sequence
+
+    // Every raw input the lane needs, loaded at once (positions clamped into
+    // the sequence; positions before its start are replaced below).
+    typedef typename RawAct<TIn>::type RawT;
+    RawT raw[WIN];
+#pragma unroll
+    for (int j = 0; j < WIN; ++j) {
+        const int tau = min(max(tl0 - 3 + j, 0), L - 1);
+        raw[j] = RawAct<TIn>::load(x, (size_t)(s0 + tau) * p.conv_dim + ch);
+    }
     float w[4][4];
     load_taps4(p, ch, w);
     const float extra = isk ? 1.0f : rsqrtf((float)DK);
-    __shared__ __attribute__((aligned(16))) __bf16 sKt[2][DK][RT];
-    __bf16 *qkrow0 = p.ws_qk + ((size_t)hk * p.t_total + s0) * 4 * DK;
-
-#pragma unroll 4
-    for (int pass = 0; pass < PASSES; ++pass) {
-        const int r = (pass * 4 + wave) * TPI + sub; // row within the chunk
-        const int tl = c * kC + r;                   // position in the sequence
-        const bool valid = tl < L;
-        const int tc = valid ? tl : L - 1;
-        f32x4 xr[4];
+    f32x4 xv[WIN];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xr[j] = raw4(p, x, n, s0, tc - 3 + j, ch);
+    for (int j = 0; j < WIN; ++j) xv[j] = RawAct<TIn>::to_f32(raw[j]);
+    if (tl0 < 3) { // the first rows of a sequence reach into its history
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (tl0 - 3 + j < 0) xv[j] = raw4(p, x, n, s0, tl0 - 3 + j, ch);
+    }
+
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+        const int r = r0 + k, tl = tl0 + k;
+        const bool valid = tl < L;
+        const f32x4 xr[4] = {xv[k], xv[k + 1], xv[k + 2], xv[k + 3]};
         const f32x4 cv = conv4(w, xr);
         float ss = cv[0] * cv[0] + cv[1] * cv[1] + cv[2] * cv[2] + cv[3] * cv[3];
         ss = group_sum<DK / 4>(ss);
@@ -334,6 +351,38 @@ tri_kernel(const PrefillArgs p)
     __shared__ __attribute__((aligned(16))) float sW[4][16 * 17];
     __shared__ float sG[kC], sB[kC];
 
+    // Issue every global load first: the gate inputs (wave 0) and, per
+    // wave w (row block w), the pre-split fragments of Q^ and K^ rows
+    // 16w.. and of K^ rows 16nt.. for the column blocks nt <= w.
+    const TIn *pa = static_cast<const TIn *>(p.a);
+    const TIn *pb = static_cast<const TIn *>(p.b);
+    float a_raw = 0.0f, b_raw = 0.0f;
+    if (wave == 0 && lane < Lc) {
+        const size_t gi = (size_t)(t0 + lane) * p.h_v + hv;
+        a_raw = load_act(pa, gi);
+        b_raw = load_act(pb, gi);
+    }
+    const __bf16 *qk0 = p.ws_qk + ((size_t)hk * p.t_total + t0) * 4 * DK;
+    constexpr int KS = DK / 32;
+    Frag fq[KS], fk[4][KS];
+    {
+        const int ra = 16 * wave + col;
+        const __bf16 *pr = qk0 + (size_t)(ra < Lc ? ra : 0) * 4 * DK + 8 * kq;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            fq[s] = frag_at(pr + 32 * s, pr + DK + 32 * s);
+            fk[3][s] = frag_at(pr + 2 * DK + 32 * s, pr + 3 * DK + 32 * s);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 3; ++nt) {
+            if (nt < wave) {
+                const int rb = 16 * nt + col;
+                const __bf16 *pk = qk0 + (size_t)(rb < Lc ? rb : 0) * 4 * DK + 2 * DK + 8 * kq;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) fk[nt][s] = frag_at(pk + 32 * s, pk + DK + 32 * s);
+            }
+        }
+    }
     for (int i = tid; i < kC * LC / 4; i += 256) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         reinterpret_cast<f32x4 *>(sA)[i] = z;
@@ -345,10 +394,8 @@ tri_kernel(const PrefillArgs p)
     if (wave == 0) {
         float beta = 0.0f, g = 0.0f;
         if (lane < Lc) {
-            const size_t gi = (size_t)(t0 + lane) * p.h_v + hv;
-            beta = sigmoidf_(load_act(static_cast<const TIn *>(p.b), gi));
-            g = -expf(p.a_log[hv]) *
-                softplusf_(load_act(static_cast<const TIn *>(p.a), gi) + p.dt_bias[hv]);
+            beta = sigmoidf_(b_raw);
+            g = -expf(p.a_log[hv]) * softplusf_(a_raw + p.dt_bias[hv]);
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -363,36 +410,29 @@ tri_kernel(const PrefillArgs p)
     }
     __syncthreads();
 
-    // K K^T -> A and Q K^T -> P, lower-triangular 16x16 tiles:
-    // 20 tiles (which, mt, nt >= ... nt <= mt); wave w takes every 4th.
-    const __bf16 *qk0 = p.ws_qk + ((size_t)hk * p.t_total + t0) * 4 * DK;
-    constexpr size_t rs = 4 * DK; // bf16 per token row
-    for (int tile = wave; tile < 20; tile += 4) {
-        const int which = tile / 10; // 0: K K^T, 1: Q K^T
-        int r = tile % 10, mt = 0;
-        while (r > mt) {
-            r -= mt + 1;
-            ++mt;
-        }
-        const int nt = r;
-        const int ra = 16 * mt + col, rb = 16 * nt + col;
-        const __bf16 *pA = qk0 + (size_t)(ra < Lc ? ra : 0) * rs + (which == 0 ? 2 * DK : 0) + 8 * kq;
-        const __bf16 *pB = qk0 + (size_t)(rb < Lc ? rb : 0) * rs + 2 * DK + 8 * kq;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // K K^T -> A and Q K^T -> P for row block mt = w, column blocks nt <= w.
+    {
+        const int mt = wave;
+        const bool arow = 16 * mt + col < Lc;
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-            const Frag A = frag_select(ra < Lc, frag_at(pA + 32 * s, pA + DK + 32 * s));
-            const Frag B = frag_select(rb < Lc, frag_at(pB + 32 * s, pB + DK + 32 * s));
-            acc = mma3(A, B, acc);
-        }
+        for (int nt = 0; nt < 4; ++nt) {
+            if (nt <= mt) {
+                const bool brow = 16 * nt + col < Lc;
+                f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = akk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * mt + 4 * kq + e, j = 16 * nt + col;
-            const float m = j <= i ? expf(sG[i] - sG[j]) : 0.0f;
-            if (which == 0)
-                sA[i * LC + j] = j < i ? sB[i] * m * acc[e] : 0.0f;
-            else
-                sP[i * LC + j] = m * acc[e];
+                for (int s = 0; s < KS; ++s) {
+                    const Frag B = frag_select(brow, nt == mt ? fk[3][s] : fk[nt < 3 ? nt : 0][s]);
+                    akk = mma3(frag_select(arow, fk[3][s]), B, akk);
+                    aqk = mma3(frag_select(arow, fq[s]), B, aqk);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * mt + 4 * kq + e, j = 16 * nt + col;
+                    const float m = j <= i ? expf(sG[i] - sG[j]) : 0.0f;
+                    sA[i * LC + j] = j < i ? sB[i] * m * akk[e] : 0.0f;
+                    sP[i * LC + j] = m * aqk[e];
+                }
+            }
         }
     }
     __syncthreads();
@@ -477,26 +517,22 @@ tri_kernel(const PrefillArgs p)
 // ---------------------------------------------------------------------------
 // scan: one workgroup per (sequence, value head, 16-column slice), 512
 // threads.  Waves 0-3 (consumers): wave w owns output rows 16w..16w+15 of
-// each chunk and the state rows of M-tiles w, w+4, ...  Waves 4-7
-// (producers): while the consumers compute chunk c they stream chunk c+1's
-// operands into LDS.  Per chunk:
-//   consumers  T/P frags(c+1) ; X,Y | R | D | O, S update, S^T split
-//   producers  k^T(c+1), v/gates regs(c+1) | q^k^ rows(c+1) | sV,b,e^G(c+1)
+// each chunk and the state rows of M-tiles w, w+4, ...; it loads the matrix
+// operands that only it uses (its q^/k^ rows, its T and P rows) straight
+// into registers one chunk ahead.  Waves 4-7 (producers): while the
+// consumers compute chunk c they stream chunk c+1's transposed k^ block
+// into LDS (global_load_lds, double buffered), convolve the slice's v
+// channels and stage the gates.  Per chunk:
+//   consumers  operand loads(c+1); X, Y, R | D | O, S update, S^T split
+//   producers  k^T(c+1), v/gates loads(c+1) | sV, b, e^G (c+1)
 //              | e^{G_C-G}(c+1), wait
-// with a workgroup barrier at each '|' and one at the end.  The q^/k^ row
-// buffer is single (refilled once X and Y have read it), the transposed k^
-// buffer is double (read only by the S update at the end of a chunk).
+// with a workgroup barrier at each '|' and one at the end.
 // ---------------------------------------------------------------------------
 template <int DK> struct ScanLds {
-    static constexpr int RPI = 128 / DK;     // q^/k^ rows per 1 KB LDS-direct load
-    static constexpr int ROWB = 8 * DK;      // bytes per row: [q^ hi|lo, k^ hi|lo][d_k]
-    static constexpr int GRPB = 1024 + 16;   // bytes per group of RPI rows, padded
-    static constexpr int ROWS_BYTES = (kC / RPI) * GRPB;
     static constexpr int KT_BYTES = 2 * DK * kC * 2; // one transposed k^ block
     static constexpr int RK = DK + 8;        // bf16 stride of S^T rows
     static constexpr int RT = kC + 8;        // bf16 stride of R, D, E rows
-    static constexpr int o_rows = 0;
-    static constexpr int o_kt = o_rows + ROWS_BYTES;   // two buffers
+    static constexpr int o_kt = 0;           // two buffers
     static constexpr int o_s = o_kt + 2 * KT_BYTES;    // [hi,lo][16][RK]
     static constexpr int o_r = o_s + 2 * kBV * RK * 2; // [hi,lo][16][RT]
     static constexpr int o_d = o_r + 2 * kBV * RT * 2;
@@ -516,12 +552,27 @@ __device__ __forceinline__ void lds_load16(const void *g, void *lds_base)
         (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also
+// waits for every outstanding global-to-LDS load of the calling wave (they
+// write LDS), which would stall the producers' prefetch at every barrier;
+// here each wave only drains its own LDS reads/writes, and the producers
+// drain their global-to-LDS loads explicitly before the barrier that
+// publishes them.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(512)
 scan_kernel(const PrefillArgs p, int slices)
 {
     using LY = ScanLds<DK>;
-    constexpr int RPI = LY::RPI, RK = LY::RK, RT = LY::RT;
+    constexpr int RK = LY::RK, RT = LY::RT;
+    constexpr int KS = DK / 32;        // k-steps over d_k
     constexpr int MTS = DK / 16;       // state M-tiles
     constexpr int MTW = (MTS + 3) / 4; // per consumer wave
 
@@ -542,7 +593,11 @@ scan_kernel(const PrefillArgs p, int slices)
     }
     const int n = hidx / p.h_v, hv = hidx % p.h_v;
     const int hk = hv / p.group;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a scalar: role branches stay wave-uniform, so each
+    // role's waits (e.g. the producers' drain of LDS-direct loads) stay on
+    // that role's path
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool producer = wave >= 4;
     const int cw = wave & 3; // consumer or producer wave index
     const int col = lane & 15, kq = lane >> 4;
@@ -553,7 +608,6 @@ scan_kernel(const PrefillArgs p, int slices)
     const TIn *x = static_cast<const TIn *>(p.qkv);
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char *sRows = smem + LY::o_rows;
     char *sKT = smem + LY::o_kt;
     __bf16 *sSh = reinterpret_cast<__bf16 *>(smem + LY::o_s), *sSl = sSh + kBV * RK;
     __bf16 *sRh = reinterpret_cast<__bf16 *>(smem + LY::o_r), *sRl = sRh + kBV * RT;
@@ -579,26 +633,17 @@ scan_kernel(const PrefillArgs p, int slices)
     float ngc = 0.0f;
     if (producer) load_taps4(p, vch, wv);
 
-    // ---- consumer state
+    // ---- consumer state: state slice and this wave's operand fragments;
+    // each fragment is reloaded with the next chunk's data right after its
+    // last use in the current chunk.
     f32x4 S[MTW];
-    Frag nT[2], nP[2], cT[2], cP[2];
+    Frag cK[KS], cQ[KS], cT[2], cP[2];
 
 #define GDN_PROD_KT(CH, BUF)                                                                   \
     {                                                                                          \
         const char *src = reinterpret_cast<const char *>(kt_seq + (size_t)(CH) * kC * p.h_k * 2 * DK); \
         for (int k = cw; k < LY::KT_BYTES / 1024; k += 4)                                      \
             lds_load16(src + k * 1024 + lane * 16, sKT + (BUF) * LY::KT_BYTES + k * 1024);     \
-    }
-#define GDN_PROD_ROWS(CH)                                                                      \
-    {                                                                                          \
-        for (int gi = cw; gi < kC / RPI; gi += 4) {                                            \
-            const int r = gi * RPI + lane / (64 / RPI);                                        \
-            const int tl = (CH) * kC + r;                                                      \
-            const int tc = tl < L ? tl : L - 1; /* rows past the end: any valid row */         \
-            const char *src = reinterpret_cast<const char *>(qk_head + (size_t)(s0 + tc) * 4 * DK) + \
-                              (lane % (64 / RPI)) * 16;                                         \
-            lds_load16(src, sRows + gi * LY::GRPB);                                            \
-        }                                                                                      \
     }
 #define GDN_PROD_REGS(CH)                                                                      \
     {                                                                                          \
@@ -626,23 +671,33 @@ scan_kernel(const PrefillArgs p, int slices)
     {                                                                                          \
         if (pt < kC) sEGC[pt] = expf(ngc - ngb.x);                                             \
     }
-#define GDN_CONS_TP(CH, DT, DP)                                                                \
+    // Consumer operand loads of chunk CH: row 16w+col of q^, k^ (A of X, Y)
+    // and of T, P (A of D and of O).  Rows past the end read a valid row;
+    // their X, Y rows are never used, and T, P are zeroed at use.
+#define GDN_CONS_ROWOFF(CH) ((size_t)(s0 + (CH) * kC + (16 * cw + col < min(kC, L - (CH) * kC) ? 16 * cw + col : 0)))
+#define GDN_CONS_LOAD_QK(CH)                                                                   \
     {                                                                                          \
-        const int fLc = min(kC, L - (CH) * kC);                                                \
-        const int row = 16 * cw + col;                                                         \
-        const int rr = row < fLc ? row : 0;                                                    \
-        const __bf16 *tp = tp_head + (size_t)(s0 + (CH) * kC + rr) * 4 * kC + 8 * kq;          \
-        _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                        \
-            DT[s] = frag_at(tp + 32 * s, tp + kC + 32 * s);                                    \
-            DP[s] = frag_at(tp + 2 * kC + 32 * s, tp + 3 * kC + 32 * s);                       \
+        const __bf16 *qr = qk_head + GDN_CONS_ROWOFF(CH) * 4 * DK + 8 * kq;                    \
+        _Pragma("unroll") for (int s = 0; s < KS; ++s) {                                       \
+            cQ[s] = frag_at(qr + 32 * s, qr + DK + 32 * s);                                    \
+            cK[s] = frag_at(qr + 2 * DK + 32 * s, qr + 3 * DK + 32 * s);                       \
         }                                                                                      \
+    }
+#define GDN_CONS_LOAD_T(CH)                                                                    \
+    {                                                                                          \
+        const __bf16 *tp = tp_head + GDN_CONS_ROWOFF(CH) * 4 * kC + 8 * kq;                    \
+        _Pragma("unroll") for (int s = 0; s < 2; ++s) cT[s] = frag_at(tp + 32 * s, tp + kC + 32 * s); \
+    }
+#define GDN_CONS_LOAD_P(CH)                                                                    \
+    {                                                                                          \
+        const __bf16 *tp = tp_head + GDN_CONS_ROWOFF(CH) * 4 * kC + 2 * kC + 8 * kq;           \
+        _Pragma("unroll") for (int s = 0; s < 2; ++s) cP[s] = frag_at(tp + 32 * s, tp + kC + 32 * s); \
     }
 
     // ---- prologue: chunk 0 ----------------------------------------------
     if (producer) {
         if (nchunks > 0) {
             GDN_PROD_KT(0, 0)
-            GDN_PROD_ROWS(0)
             GDN_PROD_REGS(0)
             // chunk 0 may reach into the incoming conv history
             f32x4 x0[4];
@@ -654,7 +709,7 @@ scan_kernel(const PrefillArgs p, int slices)
             GDN_PROD_STAGE_V(0, x0)
             GDN_PROD_STAGE_EGC()
         }
-        __builtin_amdgcn_s_waitcnt(0); // LDS-direct loads have landed
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // LDS-direct loads have landed
     } else {
         const float *Sin = p.state_in ? p.state_in + ((size_t)n * p.h_v + hv) * DK * p.d_v : nullptr;
 #pragma unroll
@@ -675,16 +730,12 @@ scan_kernel(const PrefillArgs p, int slices)
                 }
         }
         if (nchunks > 0) {
-            GDN_CONS_TP(0, nT, nP)
-            const bool live = 16 * cw + col < min(kC, L);
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                cT[s] = frag_select(live, nT[s]);
-                cP[s] = frag_select(live, nP[s]);
-            }
+            GDN_CONS_LOAD_QK(0)
+            GDN_CONS_LOAD_T(0)
+            GDN_CONS_LOAD_P(0)
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = s0 + c * kC;
@@ -693,27 +744,17 @@ scan_kernel(const PrefillArgs p, int slices)
         f32x4 Y = {0.f, 0.f, 0.f, 0.f};
         float gam = 0.0f;
 
-        // ---- phase 1: X, Y | producers: k^T(c+1), v/gates loads ---------
-        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 1: X, Y, R = beta (V - e^G X) -> sR | k^T, v/gates (c+1)
+        const bool live = 16 * cw + col < Lc; // this lane's T / P row exists
         if (!producer) {
-            if (more) GDN_CONS_TP(c + 1, nT, nP)
-            const int r = 16 * cw + col;
-            const char *rowp = sRows + (r / RPI) * LY::GRPB + (r % RPI) * LY::ROWB + 16 * kq;
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < DK / 32; ++s) {
+            for (int s = 0; s < KS; ++s) {
                 const Frag B = frag_at(sSh + col * RK + 32 * s + 8 * kq, sSl + col * RK + 32 * s + 8 * kq);
-                const __bf16 *rq = reinterpret_cast<const __bf16 *>(rowp) + 32 * s;
-                X = mma3(frag_at(rq + 2 * DK, rq + 3 * DK), B, X);
-                Y = mma3(frag_at(rq, rq + DK), B, Y);
+                X = mma3(cK[s], B, X);
+                Y = mma3(cQ[s], B, Y);
             }
-        } else if (more) {
-            GDN_PROD_KT(c + 1, (c + 1) & 1)
-            GDN_PROD_REGS(c + 1)
-        }
-        __syncthreads();
-
-        // ---- phase 2: R = beta (V - e^G X) -> sR; Y' = e^G Y | rows(c+1) --
-        if (!producer) {
+            if (more) GDN_CONS_LOAD_QK(c + 1)
             gam = sEG[kC - 1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -726,16 +767,19 @@ scan_kernel(const PrefillArgs p, int slices)
                 Y[e] *= eg;
             }
         } else if (more) {
-            GDN_PROD_ROWS(c + 1)
+            GDN_PROD_KT(c + 1, (c + 1) & 1)
+            GDN_PROD_REGS(c + 1)
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- phase 3: D = T R -> sD, sE | sV, beta, e^G (c+1) -------------
+        // ---- phase 2: D = T R -> sD, sE | sV, beta, e^G (c+1) -------------
         if (!producer) {
             f32x4 Dv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                Dv = mma3(cT[s], frag_at(sRh + col * RT + 32 * s + 8 * kq, sRl + col * RT + 32 * s + 8 * kq), Dv);
+                Dv = mma3(frag_select(live, cT[s]),
+                          frag_at(sRh + col * RT + 32 * s + 8 * kq, sRl + col * RT + 32 * s + 8 * kq), Dv);
+            if (more) GDN_CONS_LOAD_T(c + 1)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * cw + 4 * kq + e;
@@ -753,13 +797,15 @@ scan_kernel(const PrefillArgs p, int slices)
             for (int j = 0; j < 4; ++j) xr[j] = RawAct<TIn>::to_f32(nxr[j]);
             GDN_PROD_STAGE_V(c + 1, xr)
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- phase 4: O = Y' + P D; S' = gam S + K^T E | e^{G_C-G} (c+1) --
+        // ---- phase 3: O = Y' + P D; S' = gam S + K^T E | e^{G_C-G} (c+1) --
         if (!producer) {
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                Y = mma3(cP[s], frag_at(sDh + col * RT + 32 * s + 8 * kq, sDl + col * RT + 32 * s + 8 * kq), Y);
+                Y = mma3(frag_select(live, cP[s]),
+                         frag_at(sDh + col * RT + 32 * s + 8 * kq, sDl + col * RT + 32 * s + 8 * kq), Y);
+            if (more) GDN_CONS_LOAD_P(c + 1)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * cw + 4 * kq + e;
@@ -792,26 +838,20 @@ scan_kernel(const PrefillArgs p, int slices)
                     }
                 }
             }
-            if (more) {
-                const bool live = 16 * cw + col < min(kC, L - (c + 1) * kC);
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    cT[s] = frag_select(live, nT[s]);
-                    cP[s] = frag_select(live, nP[s]);
-                }
-            }
         } else {
             if (more) GDN_PROD_STAGE_EGC()
-            __builtin_amdgcn_s_waitcnt(0); // chunk c+1's LDS-direct loads have landed
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // chunk c+1's LDS-direct loads landed
         }
-        __syncthreads();
+        lds_barrier();
     }
 #undef GDN_PROD_KT
-#undef GDN_PROD_ROWS
 #undef GDN_PROD_REGS
 #undef GDN_PROD_STAGE_V
 #undef GDN_PROD_STAGE_EGC
-#undef GDN_CONS_TP
+#undef GDN_CONS_ROWOFF
+#undef GDN_CONS_LOAD_QK
+#undef GDN_CONS_LOAD_T
+#undef GDN_CONS_LOAD_P
 
     // Final state slice.
     if (!producer) {
@@ -836,26 +876,36 @@ __global__ void __launch_bounds__(256)
 norm_kernel(const PrefillArgs p, int rows)
 {
     constexpr int LPR = DV / 4;   // lanes per row
-    constexpr int RPW = 64 / LPR; // rows per wave
+    constexpr int RPW = 64 / LPR; // rows per wave and slot
+    constexpr int RPT = 4;        // rows per lane (independent loads in flight)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = (blockIdx.x * 4 + wave) * RPW + lane / LPR;
+    const int rbase = (blockIdx.x * 4 + wave) * RPT * RPW + lane / LPR;
     const int c4 = (lane % LPR) * 4;
-    const bool valid = row < rows;
-    const int rr = valid ? row : rows - 1;
-    const int t = rr / p.h_v, hv = rr % p.h_v;
-    const size_t base = (size_t)t * p.value_dim + (size_t)hv * DV + c4;
-    const f32x4 o = ld4(p.ws_o + ((size_t)hv * p.t_total + t) * DV + c4);
-    float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-    ss = group_sum<LPR>(ss);
-    const float rn = rsqrtf(ss / DV + p.norm_eps);
-    const f32x4 z = load_act4v(static_cast<const TIn *>(p.z), base);
+    const TIn *zp = static_cast<const TIn *>(p.z);
+    f32x4 o[RPT], z[RPT];
+    size_t base[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        const int row = rbase + k * RPW;
+        const int rr = row < rows ? row : rows - 1;
+        const int t = rr / p.h_v, hv = rr % p.h_v;
+        base[k] = (size_t)t * p.value_dim + (size_t)hv * DV + c4;
+        o[k] = ld4(p.ws_o + ((size_t)hv * p.t_total + t) * DV + c4);
+        z[k] = load_act4v(zp, base[k]);
+    }
     const f32x4 w = ld4(p.norm_w + c4);
-    float4 y;
-    y.x = o[0] * rn * w[0] * gatef_(z[0], p.gate);
-    y.y = o[1] * rn * w[1] * gatef_(z[1], p.gate);
-    y.z = o[2] * rn * w[2] * gatef_(z[2], p.gate);
-    y.w = o[3] * rn * w[3] * gatef_(z[3], p.gate);
-    if (valid) store_out4(p.out, base, y, p.out_bf16);
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+        float ss = o[k][0] * o[k][0] + o[k][1] * o[k][1] + o[k][2] * o[k][2] + o[k][3] * o[k][3];
+        ss = group_sum<LPR>(ss);
+        const float rn = rsqrtf(ss / DV + p.norm_eps);
+        float4 y;
+        y.x = o[k][0] * rn * w[0] * gatef_(z[k][0], p.gate);
+        y.y = o[k][1] * rn * w[1] * gatef_(z[k][1], p.gate);
+        y.z = o[k][2] * rn * w[2] * gatef_(z[k][2], p.gate);
+        y.w = o[k][3] * rn * w[3] * gatef_(z[k][3], p.gate);
+        if (rbase + k * RPW < rows) store_out4(p.out, base[k], y, p.out_bf16);
+    }
 }
 
 template <typename TIn>
@@ -881,7 +931,7 @@ conv_final_kernel(const PrefillArgs p)
 template <typename TIn, int DV>
 static hipError_t launch_norm(const PrefillArgs &a, int rows, hipStream_t s)
 {
-    constexpr int RPB = 4 * (64 / (DV / 4)); // rows per block
+    constexpr int RPB = 4 * 4 * (64 / (DV / 4)); // rows per block
     hipLaunchKernelGGL((norm_kernel<TIn, DV>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a,
                        rows);
     return hipGetLastError();
