@@ -8,28 +8,27 @@
 // cumulative log-decay and S the state entering the chunk:
 //     A    = strict_lower(diag(b) (e^{G_i-G_j}) o K K^T),  T = (I + A)^-1
 //     P    = lower(e^{G_i-G_j}) o Q K^T
-//     X    = K S,  Y = Q S
-//     R    = diag(b) (V - diag(e^G) X)
-//     D    = T R
-//     O    = diag(e^G) Y + P D
+//     W    = T diag(b e^G) K,      U = T diag(b) V      (no dependence on S)
+//     D    = U - W S               (= T diag(b) (V - diag(e^G) K S))
+//     O    = diag(e^G) Q S + P D
 //     S'   = e^{G_C} S + K^T (diag(e^{G_C-G}) D)
 // Only differences G_i - G_j with j <= i are exponentiated, so strong
 // decay underflows to zero instead of overflowing.
 //
 // Kernels (one stream, in order):
 //   qknorm  grid (chunk, key head, seq): causal conv + SiLU and L2 norm of
-//           q and k, a group of lanes per token row; writes q^, k^ rows split
-//           into bf16 hi + lo (ready-made matrix-core operands) and a
-//           transposed, bank-swizzled copy of the chunk's k^.
+//           q and k; writes q^ and k^T as ready-made matrix-core operands
+//           (split into bf16 hi + lo, one 1 KB fragment per 16x32 tile) and
+//           the chunk's Gram matrices K K^T and Q K^T (fp32, MFMA).
 //   tri     grid (chunk, value head, seq): gates and their in-chunk prefix
-//           sum, K K^T and Q K^T on MFMA, A, the blocked fp32 triangular
-//           inverse T, P; writes T and P rows split into bf16 hi + lo.
-//   scan    grid (seq, value head, 16-column slice of d_v), 8 waves: four
-//           consumer waves run the chain of chunk states (state slice in
-//           registers, every matrix operand pre-split); four producer waves
-//           stream the next chunk's operands straight into LDS
-//           (global_load_lds, no register staging), convolve the slice's v
-//           channels and stage the gates.  Writes the pre-norm readout O.
+//           sum, A and P from the Gram matrices, the blocked fp32
+//           triangular inverse T, the v conv, and W, U on MFMA; writes W
+//           (negated), P as fragments, U in the accumulator layout of the
+//           scan, and the decay factors e^G, e^{G_C-G}.
+//   scan    grid (seq, value head, 16-column slice of d_v), 4 waves: the
+//           chain of chunk states.  Per chunk two phases, D = U - W S and
+//           Q S | S' and O = e^G Q S + P D, with every operand of the next
+//           chunk loaded into registers right after its last use.
 //   norm    grid (rows of (token, value head)): gated RMSNorm + output gate.
 //   conv_final: each sequence's last K-1 raw inputs become its history.
 //
@@ -93,17 +92,6 @@ __device__ __forceinline__ Frag frag_at(const __bf16 *hi, const __bf16 *lo)
     return f;
 }
 
-__device__ __forceinline__ Frag frag_select(bool keep, const Frag &f)
-{
-    Frag z;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        z.hi[e] = keep ? f.hi[e] : static_cast<__bf16>(0.0f);
-        z.lo[e] = keep ? f.lo[e] : static_cast<__bf16>(0.0f);
-    }
-    return z;
-}
-
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 template <typename T> __device__ __forceinline__ f32x4 load_act4v(const T *p, size_t i)
@@ -140,39 +128,78 @@ __device__ __forceinline__ uint32_t pack2(__bf16 a, __bf16 b)
     return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
+// Workgroup barrier that orders LDS traffic only: each wave drains its own
+// LDS reads/writes, then all waves meet.  (No global memory is exchanged
+// between the waves of a workgroup here, so no global fence is needed; the
+// empty asm statements keep the compiler from moving memory accesses
+// across the barrier.)
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
-// Workspace layout (sections 256-byte aligned; head-major so that a chunk's
-// data of one head is contiguous):
-//   qk [H_k][T][2: q^,k^][2: hi,lo][d_k] bf16
-//   kT [T + C*N slots][H_k*2*d_k] bf16: chunk (n, c) owns the 64 slot rows
-//       from s0 + C*n + C*c, holding per key head [hi,lo][d_k][C] (k^
-//       transposed); the 16-byte groups of a row are permuted by
-//       (group ^ (row & 7)) so that matrix-operand reads spread over banks
-//   tp [H_v][T][2: T,P][2: hi,lo][C]    bf16 (row of the token's chunk)
-//   gb [H_v][T][2]                      fp32 (G in-chunk cumulative, beta)
-//   o  [H_v][T][d_v]                    fp32 pre-norm readout
+// Workspace (sections 256-byte aligned).  Chunk c of sequence n lives in
+// chunk slot  cu[n]/C + n + c  (slots never overlap: a sequence of length L
+// starting at s0 spans at most floor((s0+L)/C) - floor(s0/C) + 1 slots), so
+// every chunk owns 64 whole rows, the rows past a sequence's end included.
+//
+// A "fragment" is one 16x32 bf16 operand tile of v_mfma_f32_16x16x32_bf16
+// as the 64 lanes hold it: 1 KB, lane l's 8 values at byte 16 l.  For a
+// matrix M (rows r, contraction index k), fragment (rb, s) holds
+// M[16 rb + l%16][k(s, l/16, e)], stored hi part then lo part.
+//   natural k order:   k = 32 s + 8 q + e
+//   d_k-permuted order: k = 32 s + 4 q + e (e < 4), 32 s + 16 + 4 q + (e-4)
+// The permuted order is the one the scan keeps its state operand in (the
+// state tile of the accumulator layout lands in it with 8-byte writes).
+//
+//   qf   [H_k][slot][rb 4][s d_k/32][hi,lo] fragments of q^ (permuted)
+//   ktf  [H_k][slot][rb d_k/16][s 2][hi,lo] fragments of k^T (natural,
+//        k = token)
+//   gram [H_k][slot][K K^T, Q K^T][64][64] fp32 (tiles on/below the
+//        diagonal written)
+//   wf   [H_v][slot][rb 4][s d_k/32][hi,lo] fragments of -W (permuted)
+//   pf   [H_v][slot][rb 4][s 2][hi,lo] fragments of P (natural)
+//   uf   [H_v][slot][slice d_v/16][rb 4][64 lanes][4] fp32: U in the
+//        accumulator layout (lane l: rows 16 rb + 4 (l/16) + e, column
+//        16 slice + l%16)
+//   gf   [H_v][slot][e^G, e^{G_C-G}][64] fp32
+//   o    [H_v][T][d_v] fp32 pre-norm readout
 // ---------------------------------------------------------------------------
 struct WsLayout {
-    size_t qk, kt, tp, gb, o, total;
+    size_t qf, ktf, gram, wf, pf, uf, gf, o, total;
+    int ns;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+static int chunk_slots(int n_seq, int t_total) { return t_total / kC + n_seq + 1; }
+
 static WsLayout ws_layout(const Dims &d, int n_seq, int t_total)
 {
     WsLayout w;
-    const size_t T = (size_t)t_total;
+    w.ns = chunk_slots(n_seq, t_total);
+    const size_t NS = (size_t)w.ns;
+    const size_t frag_dk = (size_t)kC * d.d_k * 2 * 2; // bytes of a 64 x d_k hi/lo block
     size_t off = 0;
-    w.qk = off;
-    off = align256(off + T * d.h_k * 4 * d.d_k * 2);
-    w.kt = off;
-    off = align256(off + (T + (size_t)kC * n_seq) * d.h_k * 2 * d.d_k * 2);
-    w.tp = off;
-    off = align256(off + T * d.h_v * 4 * kC * 2);
-    w.gb = off;
-    off = align256(off + T * d.h_v * 2 * sizeof(float));
+    w.qf = off;
+    off = align256(off + d.h_k * NS * frag_dk);
+    w.ktf = off;
+    off = align256(off + d.h_k * NS * frag_dk);
+    w.gram = off;
+    off = align256(off + d.h_k * NS * 2 * kC * kC * sizeof(float));
+    w.wf = off;
+    off = align256(off + d.h_v * NS * frag_dk);
+    w.pf = off;
+    off = align256(off + d.h_v * NS * (size_t)kC * kC * 2 * 2);
+    w.uf = off;
+    off = align256(off + d.h_v * NS * (size_t)kC * d.d_v * sizeof(float));
+    w.gf = off;
+    off = align256(off + d.h_v * NS * 2 * kC * sizeof(float));
     w.o = off;
-    off = align256(off + T * d.value_dim * sizeof(float));
+    off = align256(off + (size_t)t_total * d.value_dim * sizeof(float));
     w.total = off;
     return w;
 }
@@ -191,9 +218,9 @@ struct PrefillArgs {
     const float *conv_in;
     float *conv_out;
     void *out;
-    __bf16 *ws_qk, *ws_kt, *ws_tp;
-    float *ws_gb, *ws_o;
-    int t_total;
+    __bf16 *ws_qf, *ws_ktf, *ws_wf, *ws_pf;
+    float *ws_gram, *ws_uf, *ws_gf, *ws_o;
+    int ns, t_total;
     int h_k, h_v, d_v, group, conv_k, conv_dim, value_dim;
     int gate, out_bf16;
     float norm_eps, l2_eps;
@@ -243,9 +270,13 @@ __device__ __forceinline__ f32x4 conv4(const float (&w)[4][4], const f32x4 (&xr)
 // ---------------------------------------------------------------------------
 // qknorm: one workgroup per (chunk, key head, sequence).  Each token row of
 // the key head (q then k, 2*d_k channels) is handled by d_k/2 lanes of 4
-// channels; each L2 norm is a reduction over d_k/4 lanes.  The k^ rows are
-// also gathered in LDS and written out transposed for the scan.
+// channels; each L2 norm is a reduction over d_k/4 lanes.  The normalised
+// rows (split hi/lo, zero past the sequence end) are gathered in LDS, then
+// written out as q^ and k^T fragments, and the Gram tiles on and below the
+// diagonal are formed on MFMA.
 // ---------------------------------------------------------------------------
+template <int DK> constexpr size_t qknorm_smem_bytes() { return 2 * 2 * kC * (DK + 8) * 2; }
+
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(256)
 qknorm_kernel(const PrefillArgs p)
@@ -254,18 +285,21 @@ qknorm_kernel(const PrefillArgs p)
     constexpr int TPI = 64 / LPT;            // token rows per wave pass
     constexpr int TPL = kC / (4 * TPI);      // consecutive tokens per lane
     constexpr int WIN = TPL + 3;             // raw rows a lane reads
-    constexpr int RT = kC + 8;               // LDS row stride of the transpose
+    constexpr int KS = DK / 32, MTS = DK / 16;
+    constexpr int RS = DK + 8;               // LDS row stride (bf16)
     const int c = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
     const int s0 = p.cu[n], L = p.cu[n + 1] - s0;
     if (c * kC >= L) return;
+    const int slot = s0 / kC + n + c;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = lane / LPT, ll = lane % LPT;
     const bool isk = ll >= DK / 4;
     const int c4 = (isk ? ll - DK / 4 : ll) * 4;
     const int ch = (isk ? p.h_k * DK : 0) + hk * DK + c4;
     const TIn *x = static_cast<const TIn *>(p.qkv);
-    __shared__ __attribute__((aligned(16))) __bf16 sKt[2][DK][RT];
-    __bf16 *qkrow0 = p.ws_qk + ((size_t)hk * p.t_total + s0) * 4 * DK;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    // [q,k][hi,lo][row][RS]
+    __bf16 *sQK = reinterpret_cast<__bf16 *>(smem);
     const int r0 = kC / 4 * wave + TPL * sub; // first chunk row of this lane
     const int tl0 = c * kC + r0;              // its position in the sequence
 
@@ -293,48 +327,92 @@ qknorm_kernel(const PrefillArgs p)
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
         const int r = r0 + k, tl = tl0 + k;
-        const bool valid = tl < L;
         const f32x4 xr[4] = {xv[k], xv[k + 1], xv[k + 2], xv[k + 3]};
         const f32x4 cv = conv4(w, xr);
         float ss = cv[0] * cv[0] + cv[1] * cv[1] + cv[2] * cv[2] + cv[3] * cv[3];
         ss = group_sum<DK / 4>(ss);
-        const float sc = valid ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
+        const float sc = tl < L ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
         __bf16 h[4], l[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) split1(cv[e] * sc, h[e], l[e]);
-        if (valid) {
-            __bf16 *dst = qkrow0 + (size_t)tl * 4 * DK + (isk ? 2 * DK : 0) + c4;
-            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
-            *reinterpret_cast<uint2 *>(dst + DK) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
-        }
-        if (isk) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sKt[0][c4 + e][r] = h[e];
-                sKt[1][c4 + e][r] = l[e];
-            }
-        }
+        __bf16 *dst = sQK + ((isk ? 2 : 0) * kC + r) * RS + c4;
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
+        *reinterpret_cast<uint2 *>(dst + kC * RS) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
     }
     __syncthreads();
-    // chunk block of k^ transposed: [hi,lo][d_k][C], 16-byte groups of row i
-    // stored at group (g ^ (i & 7)).
-    __bf16 *kt = p.ws_kt + (size_t)(s0 + kC * n + kC * c) * p.h_k * 2 * DK + (size_t)hk * 2 * DK * kC;
-    for (int idx = tid; idx < 2 * DK * 8; idx += 256) {
-        const int part = idx / (DK * 8), rem = idx % (DK * 8);
-        const int i = rem >> 3, g = rem & 7;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(&sKt[part][i][8 * g]);
-        *reinterpret_cast<u32x4 *>(kt + (size_t)part * DK * kC + (size_t)i * kC + 8 * (g ^ (i & 7))) = v;
+
+    const int col = lane & 15, kq = lane >> 4;
+    auto row = [&](int m, int hl, int r) { return sQK + ((2 * m + hl) * kC + r) * RS; };
+
+    // q^ fragments, d_k-permuted order.
+    __bf16 *qf = p.ws_qf + ((size_t)hk * p.ns + slot) * (2 * kC * DK);
+    for (int f = wave; f < 4 * KS * 2; f += 4) {
+        const int hl = f & 1, s = (f >> 1) % KS, rb = (f >> 1) / KS;
+        const __bf16 *src = row(0, hl, 16 * rb + col) + 32 * s + 4 * kq;
+        const uint2 x0 = *reinterpret_cast<const uint2 *>(src);
+        const uint2 x1 = *reinterpret_cast<const uint2 *>(src + 16);
+        *reinterpret_cast<u32x4 *>(qf + (size_t)f * 512 + lane * 8) = u32x4{x0.x, x0.y, x1.x, x1.y};
+    }
+    // k^T fragments, natural (token) order: lane (i, q) of fragment (rb, s)
+    // gathers k^[32 s + 8 q + e][16 rb + i].
+    __bf16 *ktf = p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK);
+    for (int f = wave; f < MTS * 4; f += 4) {
+        const int hl = f & 1, s = (f >> 1) & 1, rb = f >> 2;
+        const int i = 16 * rb + col, t = 32 * s + 8 * kq;
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = pack2(row(1, hl, t + 2 * e)[i], row(1, hl, t + 2 * e + 1)[i]);
+        *reinterpret_cast<u32x4 *>(ktf + (size_t)f * 512 + lane * 8) = v;
+    }
+    // Gram tiles (mt, nt), nt <= mt, listed row by row; wave w takes tiles
+    // w, w+4, w+8.
+    float *gram = p.ws_gram + ((size_t)hk * p.ns + slot) * (2 * kC * kC);
+    for (int tile = wave; tile < 10; tile += 4) {
+        const int mt = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+        const int nt = tile - mt * (mt + 1) / 2;
+        f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = akk;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int o = 32 * s + 8 * kq;
+            const Frag bk = frag_at(row(1, 0, 16 * nt + col) + o, row(1, 1, 16 * nt + col) + o);
+            const Frag ak = frag_at(row(1, 0, 16 * mt + col) + o, row(1, 1, 16 * mt + col) + o);
+            const Frag aq = frag_at(row(0, 0, 16 * mt + col) + o, row(0, 1, 16 * mt + col) + o);
+            akk = mma3(ak, bk, akk);
+            aqk = mma3(aq, bk, aqk);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * mt + 4 * kq + e, j = 16 * nt + col;
+            gram[i * kC + j] = akk[e];
+            gram[kC * kC + i * kC + j] = aqk[e];
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // tri: one workgroup per (chunk, value head, sequence), 256 threads.
 // ---------------------------------------------------------------------------
-template <typename TIn, int DK>
+template <int DV> struct TriLds {
+    static constexpr int LC = kC + 4;    // fp32 stride of A, P, T rows
+    static constexpr int RV = kC + 8;    // bf16 stride of V^T rows
+    static constexpr int o_t = 0;
+    static constexpr int o_w = o_t + kC * LC * 4;
+    static constexpr int o_g = o_w + 4 * 16 * 17 * 4; // G, beta, beta e^G
+    static constexpr int o_u = o_g + 3 * kC * 4;      // A, P, later V^T
+    static constexpr int ap = 2 * kC * LC * 4, vt = 2 * DV * RV * 2;
+    static constexpr int total = o_u + (ap > vt ? ap : vt);
+};
+
+template <typename TIn, int DK, int DV>
 __global__ void __launch_bounds__(256)
 tri_kernel(const PrefillArgs p)
 {
-    constexpr int LC = kC + 4;
+    using LY = TriLds<DV>;
+    constexpr int LC = LY::LC, RV = LY::RV;
+    constexpr int KS = DK / 32, VS = DV / 16;
+    constexpr int CG = DV / 4;            // v channel groups of 4
+    constexpr int TPG = kC * CG / 256;    // consecutive tokens per thread in the v conv
+    constexpr int VWIN = TPG + 3;
     const int c = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
     const int s0 = p.cu[n];
     const int L = p.cu[n + 1] - s0;
@@ -342,18 +420,19 @@ tri_kernel(const PrefillArgs p)
     const int t0 = s0 + c * kC;
     const int Lc = min(kC, L - c * kC);
     const int hk = hv / p.group;
+    const int slot = s0 / kC + n + c;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, kq = lane >> 4;
 
-    __shared__ __attribute__((aligned(16))) float sA[kC * LC];
-    __shared__ __attribute__((aligned(16))) float sP[kC * LC];
-    __shared__ __attribute__((aligned(16))) float sT[kC * LC];
-    __shared__ __attribute__((aligned(16))) float sW[4][16 * 17];
-    __shared__ float sG[kC], sB[kC];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float *sT = reinterpret_cast<float *>(smem + LY::o_t);
+    float(*sW)[16 * 17] = reinterpret_cast<float(*)[16 * 17]>(smem + LY::o_w);
+    float *sG = reinterpret_cast<float *>(smem + LY::o_g), *sB = sG + kC, *sBE = sB + kC;
+    float *sA = reinterpret_cast<float *>(smem + LY::o_u), *sP = sA + kC * LC;
+    __bf16 *sVh = reinterpret_cast<__bf16 *>(smem + LY::o_u), *sVl = sVh + DV * RV;
 
-    // Issue every global load first: the gate inputs (wave 0) and, per
-    // wave w (row block w), the pre-split fragments of Q^ and K^ rows
-    // 16w.. and of K^ rows 16nt.. for the column blocks nt <= w.
+    // ---- every global load first ---------------------------------------
+    // gates (wave 0)
     const TIn *pa = static_cast<const TIn *>(p.a);
     const TIn *pb = static_cast<const TIn *>(p.b);
     float a_raw = 0.0f, b_raw = 0.0f;
@@ -362,35 +441,52 @@ tri_kernel(const PrefillArgs p)
         a_raw = load_act(pa, gi);
         b_raw = load_act(pb, gi);
     }
-    const __bf16 *qk0 = p.ws_qk + ((size_t)hk * p.t_total + t0) * 4 * DK;
-    constexpr int KS = DK / 32;
-    Frag fq[KS], fk[4][KS];
+    // Gram rows: thread (i, jq) holds row i, columns 16 jq .. 16 jq + 15 of
+    // tiles on or below the diagonal.
+    const int gi_ = tid >> 2, gq = tid & 3;
+    const bool glive = gq <= (gi_ >> 4);
+    f32x4 gkk[4], gqk[4];
     {
-        const int ra = 16 * wave + col;
-        const __bf16 *pr = qk0 + (size_t)(ra < Lc ? ra : 0) * 4 * DK + 8 * kq;
+        const float *g = p.ws_gram + ((size_t)hk * p.ns + slot) * (2 * kC * kC) + gi_ * kC + 16 * gq;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            fq[s] = frag_at(pr + 32 * s, pr + DK + 32 * s);
-            fk[3][s] = frag_at(pr + 2 * DK + 32 * s, pr + 3 * DK + 32 * s);
+        for (int m = 0; m < 4; ++m) {
+            gkk[m] = glive ? ld4(g + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
+            gqk[m] = glive ? ld4(g + kC * kC + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+    }
+    // raw v inputs: thread (channel group cg, token group tg)
+    typedef typename RawAct<TIn>::type RawT;
+    const TIn *x = static_cast<const TIn *>(p.qkv);
+    const int cg = tid % CG, tg = tid / CG;
+    const int vch = 2 * p.h_k * DK + hv * DV + 4 * cg;
+    const int vt0 = c * kC + tg * TPG; // first token (sequence position)
+    RawT vraw[VWIN];
 #pragma unroll
-        for (int nt = 0; nt < 3; ++nt) {
-            if (nt < wave) {
-                const int rb = 16 * nt + col;
-                const __bf16 *pk = qk0 + (size_t)(rb < Lc ? rb : 0) * 4 * DK + 2 * DK + 8 * kq;
+    for (int j = 0; j < VWIN; ++j) {
+        const int tau = min(max(vt0 - 3 + j, 0), L - 1);
+        vraw[j] = RawAct<TIn>::load(x, (size_t)(s0 + tau) * p.conv_dim + vch);
+    }
+    // k^T fragments for the W^T tiles of this wave: column blocks 2 sp and
+    // 2 sp + 1 of d_k (sp = wave), both token steps
+    const int sp = wave;
+    const bool wact = sp < KS;
+    Frag kA[2][2];
+    if (wact) {
+        const __bf16 *kt = p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK) + lane * 8;
 #pragma unroll
-                for (int s = 0; s < KS; ++s) fk[nt][s] = frag_at(pk + 32 * s, pk + DK + 32 * s);
+        for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int f = ((2 * sp + n2) * 2 + s) * 2;
+                kA[n2][s] = frag_at(kt + (size_t)f * 512, kt + (size_t)(f + 1) * 512);
             }
-        }
     }
-    for (int i = tid; i < kC * LC / 4; i += 256) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        reinterpret_cast<f32x4 *>(sA)[i] = z;
-        reinterpret_cast<f32x4 *>(sP)[i] = z;
-        reinterpret_cast<f32x4 *>(sT)[i] = z;
-    }
-    // Gates ("cherenkov qwen4_exp/cpu.rs" fn deltanet) and their inclusive
-    // prefix sum over the chunk (wave 0).  Past the chunk end: g = 0, b = 0.
+    float wv[4][4];
+    load_taps4(p, vch, wv);
+
+    // ---- gates ("cherenkov qwen4_exp/cpu.rs" fn deltanet) and their
+    // inclusive prefix sum over the chunk (wave 0); past the chunk end
+    // g = 0 and b = 0.
     if (wave == 0) {
         float beta = 0.0f, g = 0.0f;
         if (lane < Lc) {
@@ -402,59 +498,76 @@ tri_kernel(const PrefillArgs p)
             const float u = __shfl_up(g, off, 64);
             if (lane >= off) g += u;
         }
+        const float gC = __shfl(g, 63, 64);
+        const float eg = expf(g);
         sG[lane] = g;
         sB[lane] = beta;
-        if (lane < Lc)
-            *reinterpret_cast<float2 *>(p.ws_gb + ((size_t)hv * p.t_total + t0 + lane) * 2) =
-                make_float2(g, beta);
+        sBE[lane] = beta * eg;
+        float *gf = p.ws_gf + ((size_t)hv * p.ns + slot) * (2 * kC);
+        gf[lane] = eg;
+        gf[kC + lane] = expf(gC - g);
     }
     __syncthreads();
 
-    // K K^T -> A and Q K^T -> P for row block mt = w, column blocks nt <= w.
+    // ---- A and P rows from the Gram rows.
     {
-        const int mt = wave;
-        const bool arow = 16 * mt + col < Lc;
+        const int i = gi_;
+        const float Gi = sG[i], bi = sB[i];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            if (nt <= mt) {
-                const bool brow = 16 * nt + col < Lc;
-                f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = akk;
+        for (int m = 0; m < 4; ++m) {
+            f32x4 av, pv;
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const Frag B = frag_select(brow, nt == mt ? fk[3][s] : fk[nt < 3 ? nt : 0][s]);
-                    akk = mma3(frag_select(arow, fk[3][s]), B, akk);
-                    aqk = mma3(frag_select(arow, fq[s]), B, aqk);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * mt + 4 * kq + e, j = 16 * nt + col;
-                    const float m = j <= i ? expf(sG[i] - sG[j]) : 0.0f;
-                    sA[i * LC + j] = j < i ? sB[i] * m * akk[e] : 0.0f;
-                    sP[i * LC + j] = m * aqk[e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * gq + 4 * m + e;
+                const float md = j <= i ? expf(Gi - sG[j]) : 0.0f;
+                av[e] = j < i ? bi * md * gkk[m][e] : 0.0f;
+                pv[e] = md * gqk[m][e];
             }
+            *reinterpret_cast<f32x4 *>(sA + i * LC + 16 * gq + 4 * m) = av;
+            *reinterpret_cast<f32x4 *>(sP + i * LC + 16 * gq + 4 * m) = pv;
         }
     }
     __syncthreads();
 
-    // T = (I + A)^-1, blocked over 16x16 blocks, fp32.
+    // ---- P fragments (natural order): wave w takes (rb, s) = pairs w, w+4.
+    {
+        __bf16 *pf = p.ws_pf + ((size_t)hv * p.ns + slot) * (2 * kC * kC) + lane * 8;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int pr = wave + 4 * k, rb = pr >> 1, s = pr & 1;
+            const float *src = sP + (16 * rb + col) * LC + 32 * s + 8 * kq;
+            const f32x4 u = ld4(src), v = ld4(src + 4);
+            const float vals[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+            const Frag f = split8(vals);
+            *reinterpret_cast<bf16x8 *>(pf + (size_t)(2 * pr) * 512) = f.hi;
+            *reinterpret_cast<bf16x8 *>(pf + (size_t)(2 * pr + 1) * 512) = f.lo;
+        }
+    }
+
+    // ---- T = (I + A)^-1, blocked over 16x16 blocks, fp32.
     // Diagonal blocks by forward substitution: wave b owns block b; lane
     // (col j, quarter q) keeps rows 4q..4q+3 of column j.
     {
         const int b = wave;
-        float x[4];
+        float xs[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = (4 * kq + e == col) ? 1.0f : 0.0f;
+        for (int e = 0; e < 4; ++e) xs[e] = (4 * kq + e == col) ? 1.0f : 0.0f;
 #pragma unroll
         for (int r = 1; r < 16; ++r) {
             const f32x4 a4 = ld4(sA + (16 * b + r) * LC + 16 * b + 4 * kq);
-            float part = a4[0] * x[0] + a4[1] * x[1] + a4[2] * x[2] + a4[3] * x[3];
+            float part = a4[0] * xs[0] + a4[1] * xs[1] + a4[2] * xs[2] + a4[3] * xs[3];
             part += __shfl_xor(part, 16, 64);
             part += __shfl_xor(part, 32, 64);
-            if (r > col && kq == r / 4) x[r % 4] = -part;
+            if (r > col && kq == r / 4) xs[r % 4] = -part;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sT[(16 * b + 4 * kq + e) * LC + 16 * b + col] = x[e];
+        for (int e = 0; e < 4; ++e) sT[(16 * b + 4 * kq + e) * LC + 16 * b + col] = xs[e];
+        // blocks above the diagonal are zero
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+            if (bj > b)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sT[(16 * b + 4 * kq + e) * LC + 16 * bj + col] = 0.0f;
     }
     __syncthreads();
     // Off-diagonal blocks, by distance d from the diagonal:
@@ -464,7 +577,7 @@ tri_kernel(const PrefillArgs p)
         const bool act = wave < 4 - d;
         const int bi = wave + d, bj = wave;
         if (act) {
-            float wv[4] = {0.f, 0.f, 0.f, 0.f};
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
             for (int m = bj; m < bi; ++m) {
 #pragma unroll
                 for (int k4 = 0; k4 < 4; ++k4) {
@@ -474,12 +587,12 @@ tri_kernel(const PrefillArgs p)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const f32x4 a4 = ld4(sA + (16 * bi + 4 * kq + e) * LC + 16 * m + 4 * k4);
-                        wv[e] = fmaf(a4[0], tc[0], fmaf(a4[1], tc[1], fmaf(a4[2], tc[2], fmaf(a4[3], tc[3], wv[e]))));
+                        acc[e] = fmaf(a4[0], tc[0], fmaf(a4[1], tc[1], fmaf(a4[2], tc[2], fmaf(a4[3], tc[3], acc[e]))));
                     }
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sW[wave][(4 * kq + e) * 17 + col] = wv[e];
+            for (int e = 0; e < 4; ++e) sW[wave][(4 * kq + e) * 17 + col] = acc[e];
         }
         __syncthreads();
         if (act) {
@@ -501,80 +614,113 @@ tri_kernel(const PrefillArgs p)
         __syncthreads();
     }
 
-    // T and P rows of the chunk's tokens, split into bf16 hi + lo.
-    for (int idx = tid; idx < Lc * 16; idx += 256) {
-        const int i = idx >> 4, which = (idx >> 3) & 1, g = idx & 7;
-        const float *src = (which ? sP : sT) + i * LC + 8 * g;
-        const f32x4 u = ld4(src), v = ld4(src + 4);
-        const float vals[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
-        const Frag f = split8(vals);
-        __bf16 *dst = p.ws_tp + ((size_t)hv * p.t_total + t0 + i) * 4 * kC + which * 2 * kC + 8 * g;
-        *reinterpret_cast<bf16x8 *>(dst) = f.hi;
-        *reinterpret_cast<bf16x8 *>(dst + kC) = f.lo;
+    // ---- v: silu(causal conv), transposed into LDS (A and P are dead).
+    {
+        f32x4 xv[VWIN];
+#pragma unroll
+        for (int j = 0; j < VWIN; ++j) xv[j] = RawAct<TIn>::to_f32(vraw[j]);
+        if (vt0 < 3) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                if (vt0 - 3 + j < 0) xv[j] = raw4(p, x, n, s0, vt0 - 3 + j, vch);
+        }
+        __bf16 vh[4][TPG], vl[4][TPG];
+#pragma unroll
+        for (int k = 0; k < TPG; ++k) {
+            const f32x4 xr[4] = {xv[k], xv[k + 1], xv[k + 2], xv[k + 3]};
+            const f32x4 cv = conv4(wv, xr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split1(cv[e], vh[e][k], vl[e][k]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            __bf16 *dh = sVh + (4 * cg + e) * RV + tg * TPG;
+            __bf16 *dl = sVl + (4 * cg + e) * RV + tg * TPG;
+#pragma unroll
+            for (int k = 0; k < TPG; k += 2) {
+                *reinterpret_cast<uint32_t *>(dh + k) = pack2(vh[e][k], vh[e][k + 1]);
+                *reinterpret_cast<uint32_t *>(dl + k) = pack2(vl[e][k], vl[e][k + 1]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- W^T = K^T diag(b e^G) T^T (tile (d_k block, row block rb)) and
+    // U = T diag(b) V (tile (rb, d_v block)).  T is lower triangular, so row
+    // blocks 0 and 1 only have the first token step.
+    __bf16 *wf = p.ws_wf + ((size_t)hv * p.ns + slot) * (2 * kC * DK) + lane * 8;
+    float *uf = p.ws_uf + ((size_t)hv * p.ns + slot) * ((size_t)kC * DV) + lane * 4;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int steps = rb < 2 ? 1 : 2;
+        Frag Tw[2], Tu[2]; // rows 16 rb + col, tokens 32 s + 8 kq + e, scaled
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (s < steps) {
+                const int t = 32 * s + 8 * kq;
+                const float *src = sT + (16 * rb + col) * LC + t;
+                const f32x4 u0 = ld4(src), u1 = ld4(src + 4);
+                const f32x4 be0 = ld4(sBE + t), be1 = ld4(sBE + t + 4);
+                const f32x4 b0 = ld4(sB + t), b1 = ld4(sB + t + 4);
+                const float vw[8] = {u0[0] * be0[0], u0[1] * be0[1], u0[2] * be0[2], u0[3] * be0[3],
+                                     u1[0] * be1[0], u1[1] * be1[1], u1[2] * be1[2], u1[3] * be1[3]};
+                const float vu[8] = {u0[0] * b0[0], u0[1] * b0[1], u0[2] * b0[2], u0[3] * b0[3],
+                                     u1[0] * b1[0], u1[1] * b1[1], u1[2] * b1[2], u1[3] * b1[3]};
+                Tw[s] = split8(vw);
+                Tu[s] = split8(vu);
+            }
+        }
+        if (wact) {
+            f32x4 wt[2];
+#pragma unroll
+            for (int n2 = 0; n2 < 2; ++n2) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (s < steps) acc = mma3(kA[n2][s], Tw[s], acc);
+                wt[n2] = acc;
+            }
+            // lane (row 16 rb + col, q) holds W columns 32 sp + 4 q + e and
+            // 32 sp + 16 + 4 q + e: fragment (rb, sp) of -W in permuted order
+            const float vals[8] = {-wt[0][0], -wt[0][1], -wt[0][2], -wt[0][3],
+                                   -wt[1][0], -wt[1][1], -wt[1][2], -wt[1][3]};
+            const Frag f = split8(vals);
+            const int fi = (rb * KS + sp) * 2;
+            *reinterpret_cast<bf16x8 *>(wf + (size_t)fi * 512) = f.hi;
+            *reinterpret_cast<bf16x8 *>(wf + (size_t)(fi + 1) * 512) = f.lo;
+        }
+#pragma unroll
+        for (int nb = wave; nb < VS; nb += 4) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (s < steps) {
+                    const int o = (16 * nb + col) * RV + 32 * s + 8 * kq;
+                    acc = mma3(Tu[s], frag_at(sVh + o, sVl + o), acc);
+                }
+            *reinterpret_cast<f32x4 *>(uf + (size_t)(nb * 4 + rb) * 256) = acc;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup per (sequence, value head, 16-column slice), 512
-// threads.  Waves 0-3 (consumers): wave w owns output rows 16w..16w+15 of
-// each chunk and the state rows of M-tiles w, w+4, ...; it loads the matrix
-// operands that only it uses (its q^/k^ rows, its T and P rows) straight
-// into registers one chunk ahead.  Waves 4-7 (producers): while the
-// consumers compute chunk c they stream chunk c+1's transposed k^ block
-// into LDS (global_load_lds, double buffered), convolve the slice's v
-// channels and stage the gates.  Per chunk:
-//   consumers  operand loads(c+1); X, Y, R | D | O, S update, S^T split
-//   producers  k^T(c+1), v/gates loads(c+1) | sV, b, e^G (c+1)
-//              | e^{G_C-G}(c+1), wait
-// with a workgroup barrier at each '|' and one at the end.
+// scan: one workgroup per (sequence, value head, 16-column slice), 4 waves
+// (one per SIMD).  Wave w owns output rows 16w..16w+15 of each chunk and
+// the state rows of M-tiles w, w+4, ...; all its matrix operands come
+// pre-split from the workspace into registers, each reloaded with the next
+// chunk's data right after its last use.  LDS holds only what the waves
+// exchange: the state slice S^T (d_k-permuted, as B operand), D and
+// e^{G_C-G} D (token order, as B operands).
 // ---------------------------------------------------------------------------
-template <int DK> struct ScanLds {
-    static constexpr int KT_BYTES = 2 * DK * kC * 2; // one transposed k^ block
-    static constexpr int RK = DK + 8;        // bf16 stride of S^T rows
-    static constexpr int RT = kC + 8;        // bf16 stride of R, D, E rows
-    static constexpr int o_kt = 0;           // two buffers
-    static constexpr int o_s = o_kt + 2 * KT_BYTES;    // [hi,lo][16][RK]
-    static constexpr int o_r = o_s + 2 * kBV * RK * 2; // [hi,lo][16][RT]
-    static constexpr int o_d = o_r + 2 * kBV * RT * 2;
-    static constexpr int o_e = o_d + 2 * kBV * RT * 2;
-    static constexpr int o_v = o_e + 2 * kBV * RT * 2; // fp32 [C][16]
-    static constexpr int o_g = o_v + kC * kBV * 4;     // fp32 e^G, e^{G_C-G}, beta
-    static constexpr int total = o_g + 3 * kC * 4;
-};
-template <int DK> constexpr size_t scan_smem_bytes() { return ScanLds<DK>::total; }
-
-// 16 bytes per lane, global -> LDS without register staging: lane l's
-// bytes land at lds_base + 16 l.
-__device__ __forceinline__ void lds_load16(const void *g, void *lds_base)
-{
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void *)g,
-        (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
-
-// Workgroup barrier that orders LDS traffic only.  __syncthreads() also
-// waits for every outstanding global-to-LDS load of the calling wave (they
-// write LDS), which would stall the producers' prefetch at every barrier;
-// here each wave only drains its own LDS reads/writes, and the producers
-// drain their global-to-LDS loads explicitly before the barrier that
-// publishes them.  The empty asm statements keep the compiler from moving
-// memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-template <typename TIn, int DK>
-__global__ void __launch_bounds__(512)
+template <int DK>
+__global__ void __launch_bounds__(256)
 scan_kernel(const PrefillArgs p, int slices)
 {
-    using LY = ScanLds<DK>;
-    constexpr int RK = LY::RK, RT = LY::RT;
+    constexpr int RK = DK + 8;         // bf16 stride of S^T rows
+    constexpr int RT = kC + 8;         // bf16 stride of D, E rows
     constexpr int KS = DK / 32;        // k-steps over d_k
     constexpr int MTS = DK / 16;       // state M-tiles
-    constexpr int MTW = (MTS + 3) / 4; // per consumer wave
+    constexpr int MTW = (MTS + 3) / 4; // per wave
 
     // Map the block index so the slices of one head share an XCD (blocks
     // are dealt round-robin over 8 XCDs): they read the same chunk data.
@@ -594,146 +740,94 @@ scan_kernel(const PrefillArgs p, int slices)
     const int n = hidx / p.h_v, hv = hidx % p.h_v;
     const int hk = hv / p.group;
     const int tid = threadIdx.x, lane = tid & 63;
-    // wave index as a scalar: role branches stay wave-uniform, so each
-    // role's waits (e.g. the producers' drain of LDS-direct loads) stay on
-    // that role's path
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool producer = wave >= 4;
-    const int cw = wave & 3; // consumer or producer wave index
     const int col = lane & 15, kq = lane >> 4;
     const int s0 = p.cu[n];
     const int L = p.cu[n + 1] - s0;
     const int nchunks = (L + kC - 1) / kC;
-    const int c0 = hv * p.d_v + slice * kBV; // first value column
-    const TIn *x = static_cast<const TIn *>(p.qkv);
+    const int slot0 = s0 / kC + n;
 
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    char *sKT = smem + LY::o_kt;
-    __bf16 *sSh = reinterpret_cast<__bf16 *>(smem + LY::o_s), *sSl = sSh + kBV * RK;
-    __bf16 *sRh = reinterpret_cast<__bf16 *>(smem + LY::o_r), *sRl = sRh + kBV * RT;
-    __bf16 *sDh = reinterpret_cast<__bf16 *>(smem + LY::o_d), *sDl = sDh + kBV * RT;
-    __bf16 *sEh = reinterpret_cast<__bf16 *>(smem + LY::o_e), *sEl = sEh + kBV * RT;
-    float *sV = reinterpret_cast<float *>(smem + LY::o_v);
-    float *sEG = reinterpret_cast<float *>(smem + LY::o_g), *sEGC = sEG + kC, *sB = sEGC + kC;
+    __shared__ __attribute__((aligned(16))) __bf16 sS[2][kBV * RK];
+    __shared__ __attribute__((aligned(16))) __bf16 sD[2][kBV * RT];
+    __shared__ __attribute__((aligned(16))) __bf16 sE[2][kBV * RT];
 
-    const __bf16 *qk_head = p.ws_qk + (size_t)hk * p.t_total * 4 * DK;
-    const __bf16 *kt_seq = p.ws_kt + (size_t)(s0 + kC * n) * p.h_k * 2 * DK + (size_t)hk * 2 * DK * kC;
-    const __bf16 *tp_head = p.ws_tp + (size_t)hv * p.t_total * 4 * kC;
-    const float *gb_head = p.ws_gb + (size_t)hv * p.t_total * 2;
+    const __bf16 *qf = p.ws_qf + ((size_t)hk * p.ns + slot0) * (2 * kC * DK) + lane * 8;
+    const __bf16 *ktf = p.ws_ktf + ((size_t)hk * p.ns + slot0) * (2 * kC * DK) + lane * 8;
+    const __bf16 *wf = p.ws_wf + ((size_t)hv * p.ns + slot0) * (2 * kC * DK) + lane * 8;
+    const __bf16 *pf = p.ws_pf + ((size_t)hv * p.ns + slot0) * (2 * kC * kC) + lane * 8;
+    const float *uf = p.ws_uf + ((size_t)hv * p.ns + slot0) * ((size_t)kC * p.d_v) +
+                      (size_t)slice * 4 * 256 + wave * 256 + lane * 4;
+    const float *gf = p.ws_gf + ((size_t)hv * p.ns + slot0) * (2 * kC);
     float *o_head = p.ws_o + (size_t)hv * p.t_total * p.d_v;
 
-    // ---- producer state: thread (token vt, channels 4 vg) of the v slice
-    typedef typename RawAct<TIn>::type RawT;
-    const int pt = tid - 256;
-    const int vt = (pt & 255) >> 2, vg = pt & 3;
-    const int vch = 2 * p.h_k * DK + c0 + 4 * vg;
-    float wv[4][4];
-    RawT nxr[4];
-    float2 ngb = make_float2(0.f, 0.f);
-    float ngc = 0.0f;
-    if (producer) load_taps4(p, vch, wv);
-
-    // ---- consumer state: state slice and this wave's operand fragments;
-    // each fragment is reloaded with the next chunk's data right after its
-    // last use in the current chunk.
     f32x4 S[MTW];
-    Frag cK[KS], cQ[KS], cT[2], cP[2];
+    Frag cW[KS], cQ[KS], cK[MTW][2], cP[2];
+    f32x4 cU, cEG, cEGC;
+    float gam = 0.0f;
 
-#define GDN_PROD_KT(CH, BUF)                                                                   \
+    // Operands of chunk CH used in phase 1 (W, Q rows of this wave, U) and
+    // in phase 2 (k^T rows of this wave's M-tiles, P rows, decays).
+#define GDN_LOAD_PHASE1(CH)                                                                    \
     {                                                                                          \
-        const char *src = reinterpret_cast<const char *>(kt_seq + (size_t)(CH) * kC * p.h_k * 2 * DK); \
-        for (int k = cw; k < LY::KT_BYTES / 1024; k += 4)                                      \
-            lds_load16(src + k * 1024 + lane * 16, sKT + (BUF) * LY::KT_BYTES + k * 1024);     \
-    }
-#define GDN_PROD_REGS(CH)                                                                      \
-    {                                                                                          \
-        const int fLc = min(kC, L - (CH) * kC);                                                \
-        const int tl = (CH) * kC + vt;                                                         \
-        const int tc = tl < L ? tl : L - 1;                                                    \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
-            nxr[j] = RawAct<TIn>::load(x, (size_t)(s0 + max(tc - 3 + j, 0)) * p.conv_dim + vch); \
-        if (pt < kC) {                                                                         \
-            const int tr = pt < fLc ? pt : fLc - 1;                                            \
-            ngb = *reinterpret_cast<const float2 *>(gb_head + (size_t)(s0 + (CH) * kC + tr) * 2); \
-            ngc = gb_head[(size_t)(s0 + (CH) * kC + fLc - 1) * 2];                             \
-        }                                                                                      \
-    }
-#define GDN_PROD_STAGE_V(CH, XR)                                                               \
-    {                                                                                          \
-        const int fLc = min(kC, L - (CH) * kC);                                                \
-        *reinterpret_cast<f32x4 *>(sV + vt * kBV + 4 * vg) = conv4(wv, XR);                    \
-        if (pt < kC) {                                                                         \
-            sEG[pt] = expf(ngb.x); /* g = 0 past the end: G stays at G_{Lc-1} */               \
-            sB[pt] = pt < fLc ? ngb.y : 0.0f;                                                  \
-        }                                                                                      \
-    }
-#define GDN_PROD_STAGE_EGC()                                                                   \
-    {                                                                                          \
-        if (pt < kC) sEGC[pt] = expf(ngc - ngb.x);                                             \
-    }
-    // Consumer operand loads of chunk CH: row 16w+col of q^, k^ (A of X, Y)
-    // and of T, P (A of D and of O).  Rows past the end read a valid row;
-    // their X, Y rows are never used, and T, P are zeroed at use.
-#define GDN_CONS_ROWOFF(CH) ((size_t)(s0 + (CH) * kC + (16 * cw + col < min(kC, L - (CH) * kC) ? 16 * cw + col : 0)))
-#define GDN_CONS_LOAD_QK(CH)                                                                   \
-    {                                                                                          \
-        const __bf16 *qr = qk_head + GDN_CONS_ROWOFF(CH) * 4 * DK + 8 * kq;                    \
+        const size_t off = (size_t)(CH) * (2 * kC * DK);                                       \
         _Pragma("unroll") for (int s = 0; s < KS; ++s) {                                       \
-            cQ[s] = frag_at(qr + 32 * s, qr + DK + 32 * s);                                    \
-            cK[s] = frag_at(qr + 2 * DK + 32 * s, qr + 3 * DK + 32 * s);                       \
+            const int f = (wave * KS + s) * 2;                                                 \
+            cW[s] = frag_at(wf + off + f * 512, wf + off + (f + 1) * 512);                     \
+            cQ[s] = frag_at(qf + off + f * 512, qf + off + (f + 1) * 512);                     \
         }                                                                                      \
+        cU = ld4(uf + (size_t)(CH) * kC * p.d_v);                                              \
     }
-#define GDN_CONS_LOAD_T(CH)                                                                    \
+#define GDN_LOAD_PHASE2(CH)                                                                    \
     {                                                                                          \
-        const __bf16 *tp = tp_head + GDN_CONS_ROWOFF(CH) * 4 * kC + 8 * kq;                    \
-        _Pragma("unroll") for (int s = 0; s < 2; ++s) cT[s] = frag_at(tp + 32 * s, tp + kC + 32 * s); \
-    }
-#define GDN_CONS_LOAD_P(CH)                                                                    \
-    {                                                                                          \
-        const __bf16 *tp = tp_head + GDN_CONS_ROWOFF(CH) * 4 * kC + 2 * kC + 8 * kq;           \
-        _Pragma("unroll") for (int s = 0; s < 2; ++s) cP[s] = frag_at(tp + 32 * s, tp + kC + 32 * s); \
+        const size_t off = (size_t)(CH) * (2 * kC * DK);                                       \
+        _Pragma("unroll") for (int u = 0; u < MTW; ++u) {                                      \
+            const int mt = wave + 4 * u;                                                       \
+            if (mt < MTS)                                                                      \
+                _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                \
+                    const int f = (mt * 2 + s) * 2;                                            \
+                    cK[u][s] = frag_at(ktf + off + f * 512, ktf + off + (f + 1) * 512);        \
+                }                                                                              \
+        }                                                                                      \
+        const size_t offp = (size_t)(CH) * (2 * kC * kC);                                      \
+        _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                        \
+            if (s == 0 || wave >= 2) {                                                         \
+                const int f = (wave * 2 + s) * 2;                                              \
+                cP[s] = frag_at(pf + offp + f * 512, pf + offp + (f + 1) * 512);               \
+            }                                                                                  \
+        }                                                                                      \
+        const float *g = gf + (size_t)(CH) * (2 * kC);                                         \
+        cEG = ld4(g + 16 * wave + 4 * kq);                                                     \
+        cEGC = ld4(g + kC + 16 * wave + 4 * kq);                                               \
+        gam = g[kC - 1];                                                                       \
     }
 
-    // ---- prologue: chunk 0 ----------------------------------------------
-    if (producer) {
-        if (nchunks > 0) {
-            GDN_PROD_KT(0, 0)
-            GDN_PROD_REGS(0)
-            // chunk 0 may reach into the incoming conv history
-            f32x4 x0[4];
-            {
-                const int tc = vt < L ? vt : L - 1;
+    // State tile u into S^T in LDS at its d_k-permuted position.
+    auto put_state = [&](int mt, const f32x4 &v) {
+        __bf16 h[4], l[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x0[j] = raw4(p, x, n, s0, tc - 3 + j, vch);
-            }
-            GDN_PROD_STAGE_V(0, x0)
-            GDN_PROD_STAGE_EGC()
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // LDS-direct loads have landed
-    } else {
+        for (int e = 0; e < 4; ++e) split1(v[e], h[e], l[e]);
+        const int pos = col * RK + 32 * (mt >> 1) + 8 * kq + 4 * (mt & 1);
+        *reinterpret_cast<uint2 *>(&sS[0][pos]) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
+        *reinterpret_cast<uint2 *>(&sS[1][pos]) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
+    };
+
+    // ---- prologue --------------------------------------------------------
+    {
         const float *Sin = p.state_in ? p.state_in + ((size_t)n * p.h_v + hv) * DK * p.d_v : nullptr;
 #pragma unroll
         for (int u = 0; u < MTW; ++u) {
-            const int mt = cw + 4 * u;
+            const int mt = wave + 4 * u;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * mt + 4 * kq + e;
                 S[u][e] = (mt < MTS && Sin) ? Sin[(size_t)i * p.d_v + slice * kBV + col] : 0.0f;
             }
-            if (mt < MTS)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    __bf16 h, l;
-                    split1(S[u][e], h, l);
-                    sSh[col * RK + 16 * mt + 4 * kq + e] = h;
-                    sSl[col * RK + 16 * mt + 4 * kq + e] = l;
-                }
+            if (mt < MTS) put_state(mt, S[u]);
         }
-        if (nchunks > 0) {
-            GDN_CONS_LOAD_QK(0)
-            GDN_CONS_LOAD_T(0)
-            GDN_CONS_LOAD_P(0)
-        }
+    }
+    if (nchunks > 0) {
+        GDN_LOAD_PHASE1(0)
+        GDN_LOAD_PHASE2(0)
     }
     lds_barrier();
 
@@ -741,129 +835,76 @@ scan_kernel(const PrefillArgs p, int slices)
         const int t0 = s0 + c * kC;
         const int Lc = min(kC, L - c * kC);
         const bool more = c + 1 < nchunks;
-        f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-        float gam = 0.0f;
 
-        // ---- phase 1: X, Y, R = beta (V - e^G X) -> sR | k^T, v/gates (c+1)
-        const bool live = 16 * cw + col < Lc; // this lane's T / P row exists
-        if (!producer) {
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 1: D = U - W S and Y = Q S (state slice as B operand)
+        f32x4 Dv = cU, Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const Frag B = frag_at(sSh + col * RK + 32 * s + 8 * kq, sSl + col * RK + 32 * s + 8 * kq);
-                X = mma3(cK[s], B, X);
-                Y = mma3(cQ[s], B, Y);
-            }
-            if (more) GDN_CONS_LOAD_QK(c + 1)
-            gam = sEG[kC - 1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * cw + 4 * kq + e;
-                const float eg = sEG[t];
-                __bf16 h, l;
-                split1(sB[t] * (sV[t * kBV + col] - eg * X[e]), h, l);
-                sRh[col * RT + t] = h;
-                sRl[col * RT + t] = l;
-                Y[e] *= eg;
-            }
-        } else if (more) {
-            GDN_PROD_KT(c + 1, (c + 1) & 1)
-            GDN_PROD_REGS(c + 1)
+        for (int s = 0; s < KS; ++s) {
+            const int o = col * RK + 32 * s + 8 * kq;
+            const Frag B = frag_at(&sS[0][o], &sS[1][o]);
+            Dv = mma3(cW[s], B, Dv);
+            Y = mma3(cQ[s], B, Y);
         }
+        if (more) GDN_LOAD_PHASE1(c + 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * wave + 4 * kq + e;
+            __bf16 h, l;
+            split1(Dv[e], h, l);
+            sD[0][col * RT + t] = h;
+            sD[1][col * RT + t] = l;
+            split1(Dv[e] * cEGC[e], h, l);
+            sE[0][col * RT + t] = h;
+            sE[1][col * RT + t] = l;
+        }
+        Y *= cEG;
         lds_barrier();
 
-        // ---- phase 2: D = T R -> sD, sE | sV, beta, e^G (c+1) -------------
-        if (!producer) {
-            f32x4 Dv = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 2: S' = e^{G_C} S + K^T E; O = e^G Y + P D -----------
+        Frag Be[2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                Dv = mma3(frag_select(live, cT[s]),
-                          frag_at(sRh + col * RT + 32 * s + 8 * kq, sRl + col * RT + 32 * s + 8 * kq), Dv);
-            if (more) GDN_CONS_LOAD_T(c + 1)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * cw + 4 * kq + e;
-                __bf16 h, l;
-                split1(Dv[e], h, l);
-                sDh[col * RT + t] = h;
-                sDl[col * RT + t] = l;
-                split1(Dv[e] * sEGC[t], h, l);
-                sEh[col * RT + t] = h;
-                sEl[col * RT + t] = l;
-            }
-        } else if (more) {
-            f32x4 xr[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xr[j] = RawAct<TIn>::to_f32(nxr[j]);
-            GDN_PROD_STAGE_V(c + 1, xr)
+        for (int s = 0; s < 2; ++s) {
+            const int o = col * RT + 32 * s + 8 * kq;
+            Be[s] = frag_at(&sE[0][o], &sE[1][o]);
         }
-        lds_barrier();
-
-        // ---- phase 3: O = Y' + P D; S' = gam S + K^T E | e^{G_C-G} (c+1) --
-        if (!producer) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                Y = mma3(frag_select(live, cP[s]),
-                         frag_at(sDh + col * RT + 32 * s + 8 * kq, sDl + col * RT + 32 * s + 8 * kq), Y);
-            if (more) GDN_CONS_LOAD_P(c + 1)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * cw + 4 * kq + e;
-                if (t < Lc) o_head[(size_t)(t0 + t) * p.d_v + slice * kBV + col] = Y[e];
-            }
-            Frag Bs[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                Bs[s] = frag_at(sEh + col * RT + 32 * s + 8 * kq, sEl + col * RT + 32 * s + 8 * kq);
-            const char *kt = sKT + (c & 1) * LY::KT_BYTES;
-#pragma unroll
-            for (int u = 0; u < MTW; ++u) {
-                const int mt = cw + 4 * u;
-                if (mt < MTS) {
-                    const int i = 16 * mt + col;
-                    f32x4 acc = gam * S[u];
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const int g = (4 * s + kq) ^ (i & 7);
-                        const __bf16 *ah = reinterpret_cast<const __bf16 *>(kt + (size_t)i * kC * 2 + g * 16);
-                        acc = mma3(frag_at(ah, ah + DK * kC), Bs[s], acc);
-                    }
-                    S[u] = acc;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        __bf16 h, l;
-                        split1(acc[e], h, l);
-                        sSh[col * RK + 16 * mt + 4 * kq + e] = h;
-                        sSl[col * RK + 16 * mt + 4 * kq + e] = l;
-                    }
-                }
-            }
-        } else {
-            if (more) GDN_PROD_STAGE_EGC()
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // chunk c+1's LDS-direct loads landed
-        }
-        lds_barrier();
-    }
-#undef GDN_PROD_KT
-#undef GDN_PROD_REGS
-#undef GDN_PROD_STAGE_V
-#undef GDN_PROD_STAGE_EGC
-#undef GDN_CONS_ROWOFF
-#undef GDN_CONS_LOAD_QK
-#undef GDN_CONS_LOAD_T
-#undef GDN_CONS_LOAD_P
-
-    // Final state slice.
-    if (!producer) {
-        float *Sout = p.state_out + ((size_t)n * p.h_v + hv) * DK * p.d_v;
 #pragma unroll
         for (int u = 0; u < MTW; ++u) {
-            const int mt = cw + 4 * u;
-            if (mt < MTS)
+            const int mt = wave + 4 * u;
+            if (mt < MTS) {
+                f32x4 acc = gam * S[u];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + slice * kBV + col] = S[u][e];
+                for (int s = 0; s < 2; ++s) acc = mma3(cK[u][s], Be[s], acc);
+                S[u] = acc;
+                put_state(mt, acc);
+            }
         }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (s == 0 || wave >= 2) { // P is lower triangular
+                const int o = col * RT + 32 * s + 8 * kq;
+                Y = mma3(cP[s], frag_at(&sD[0][o], &sD[1][o]), Y);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * wave + 4 * kq + e;
+            if (t < Lc) o_head[(size_t)(t0 + t) * p.d_v + slice * kBV + col] = Y[e];
+        }
+        if (more) GDN_LOAD_PHASE2(c + 1)
+        lds_barrier();
+    }
+#undef GDN_LOAD_PHASE1
+#undef GDN_LOAD_PHASE2
+
+    // Final state slice.
+    float *Sout = p.state_out + ((size_t)n * p.h_v + hv) * DK * p.d_v;
+#pragma unroll
+    for (int u = 0; u < MTW; ++u) {
+        const int mt = wave + 4 * u;
+        if (mt < MTS)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + slice * kBV + col] = S[u][e];
     }
 }
 
@@ -937,31 +978,28 @@ static hipError_t launch_norm(const PrefillArgs &a, int rows, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename TIn, int DK>
+template <typename TIn, int DK, int DV>
 static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total, int max_len,
                                    hipStream_t s)
 {
     hipError_t e;
     if (max_len > 0) {
-        hipLaunchKernelGGL((qknorm_kernel<TIn, DK>), dim3((max_len + kC - 1) / kC, a.h_k, n_seq),
-                           dim3(256), 0, s, a);
+        const dim3 grid_k((max_len + kC - 1) / kC, a.h_k, n_seq);
+        hipLaunchKernelGGL((qknorm_kernel<TIn, DK>), grid_k, dim3(256), qknorm_smem_bytes<DK>(), s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((tri_kernel<TIn, DK>), dim3((max_len + kC - 1) / kC, a.h_v, n_seq),
-                           dim3(256), 0, s, a);
+        const dim3 grid_v((max_len + kC - 1) / kC, a.h_v, n_seq);
+        hipLaunchKernelGGL((tri_kernel<TIn, DK, DV>), grid_v, dim3(256), TriLds<DV>::total, s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (n_seq > 0) {
-        const int slices = a.d_v / kBV;
-        hipLaunchKernelGGL((scan_kernel<TIn, DK>), dim3(n_seq * a.h_v * slices), dim3(512),
-                           scan_smem_bytes<DK>(), s, a, slices);
+        const int slices = DV / kBV;
+        hipLaunchKernelGGL((scan_kernel<DK>), dim3(n_seq * a.h_v * slices), dim3(256), 0, s, a,
+                           slices);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int rows = t_total * a.h_v;
     if (rows > 0) {
-        if (a.d_v == 32) e = launch_norm<TIn, 32>(a, rows, s);
-        else if (a.d_v == 64) e = launch_norm<TIn, 64>(a, rows, s);
-        else e = launch_norm<TIn, 128>(a, rows, s);
-        if (e != hipSuccess) return e;
+        if ((e = launch_norm<TIn, DV>(a, rows, s)) != hipSuccess) return e;
     }
     if (n_seq > 0 && a.conv_k > 1) {
         hipLaunchKernelGGL((conv_final_kernel<TIn>), dim3((a.conv_dim + 255) / 256, n_seq),
@@ -971,13 +1009,37 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
     return hipSuccess;
 }
 
-template <int DK>
-static void set_smem_limits()
+// Dynamic LDS above the default 64 KB needs the attribute raised once.
+template <typename TIn, int DK, int DV>
+static hipError_t set_smem_limits()
 {
-    hipFuncSetAttribute(reinterpret_cast<const void *>(scan_kernel<bf16_t, DK>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_smem_bytes<DK>());
-    hipFuncSetAttribute(reinterpret_cast<const void *>(scan_kernel<float, DK>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_smem_bytes<DK>());
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(qknorm_kernel<TIn, DK>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)qknorm_smem_bytes<DK>());
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(tri_kernel<TIn, DK, DV>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)TriLds<DV>::total);
+}
+
+template <typename TIn, int DK, int DV>
+static hipError_t run_prefill(const PrefillArgs &a, int n_seq, int t_total, int max_len,
+                              hipStream_t s)
+{
+    static const hipError_t limits = set_smem_limits<TIn, DK, DV>();
+    if (limits != hipSuccess) return limits;
+    return launch_prefill_t<TIn, DK, DV>(a, n_seq, t_total, max_len, s);
+}
+
+template <typename TIn, int DK>
+static hipError_t dispatch_dv(const PrefillArgs &a, int n_seq, int t_total, int max_len,
+                              hipStream_t s)
+{
+    switch (a.d_v) {
+    case 32: return run_prefill<TIn, DK, 32>(a, n_seq, t_total, max_len, s);
+    case 64: return run_prefill<TIn, DK, 64>(a, n_seq, t_total, max_len, s);
+    case 128: return run_prefill<TIn, DK, 128>(a, n_seq, t_total, max_len, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_total, int max_len,
@@ -1003,12 +1065,16 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.conv_in = conv_in;
     A.conv_out = conv_out;
     A.out = out;
-    A.ws_qk = reinterpret_cast<__bf16 *>(base + w.qk);
-    A.ws_kt = reinterpret_cast<__bf16 *>(base + w.kt);
-    A.t_total = t_total;
-    A.ws_tp = reinterpret_cast<__bf16 *>(base + w.tp);
-    A.ws_gb = reinterpret_cast<float *>(base + w.gb);
+    A.ws_qf = reinterpret_cast<__bf16 *>(base + w.qf);
+    A.ws_ktf = reinterpret_cast<__bf16 *>(base + w.ktf);
+    A.ws_wf = reinterpret_cast<__bf16 *>(base + w.wf);
+    A.ws_pf = reinterpret_cast<__bf16 *>(base + w.pf);
+    A.ws_gram = reinterpret_cast<float *>(base + w.gram);
+    A.ws_uf = reinterpret_cast<float *>(base + w.uf);
+    A.ws_gf = reinterpret_cast<float *>(base + w.gf);
     A.ws_o = reinterpret_cast<float *>(base + w.o);
+    A.ns = w.ns;
+    A.t_total = t_total;
     A.h_k = d.h_k;
     A.h_v = d.h_v;
     A.d_v = d.d_v;
@@ -1021,17 +1087,10 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.norm_eps = d.norm_eps;
     A.l2_eps = d.l2_eps;
 
-    static bool limits_set = false;
-    if (!limits_set) {
-        set_smem_limits<32>();
-        set_smem_limits<64>();
-        set_smem_limits<128>();
-        limits_set = true;
-    }
 #define GDN_PF_CASE(DK_)                                                                      \
     if (d.d_k == DK_)                                                                         \
-        return d.act_bf16 ? launch_prefill_t<bf16_t, DK_>(A, n_seq, t_total, max_len, s)      \
-                          : launch_prefill_t<float, DK_>(A, n_seq, t_total, max_len, s);
+        return d.act_bf16 ? dispatch_dv<bf16_t, DK_>(A, n_seq, t_total, max_len, s)           \
+                          : dispatch_dv<float, DK_>(A, n_seq, t_total, max_len, s);
     GDN_PF_CASE(32)
     GDN_PF_CASE(64)
     GDN_PF_CASE(128)
