@@ -766,7 +766,10 @@ scan_kernel(const PrefillArgs p, int slices)
     float gam = 0.0f;
 
     // Operands of chunk CH used in phase 1 (W, Q rows of this wave, U) and
-    // in phase 2 (k^T rows of this wave's M-tiles, P rows, decays).
+    // in phase 2 (k^T rows of this wave's M-tiles, P rows, decays).  The
+    // loads are unconditional (the last chunk reloads itself) so that the
+    // compiler's load counters stay exact and each wait covers only the
+    // operands it needs, never the prefetch behind them.
 #define GDN_LOAD_PHASE1(CH)                                                                    \
     {                                                                                          \
         const size_t off = (size_t)(CH) * (2 * kC * DK);                                       \
@@ -781,19 +784,16 @@ scan_kernel(const PrefillArgs p, int slices)
     {                                                                                          \
         const size_t off = (size_t)(CH) * (2 * kC * DK);                                       \
         _Pragma("unroll") for (int u = 0; u < MTW; ++u) {                                      \
-            const int mt = wave + 4 * u;                                                       \
-            if (mt < MTS)                                                                      \
-                _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                \
-                    const int f = (mt * 2 + s) * 2;                                            \
-                    cK[u][s] = frag_at(ktf + off + f * 512, ktf + off + (f + 1) * 512);        \
-                }                                                                              \
+            const int mt = min(wave + 4 * u, MTS - 1);                                         \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
+                const int f = (mt * 2 + s) * 2;                                                \
+                cK[u][s] = frag_at(ktf + off + f * 512, ktf + off + (f + 1) * 512);            \
+            }                                                                                  \
         }                                                                                      \
         const size_t offp = (size_t)(CH) * (2 * kC * kC);                                      \
         _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                        \
-            if (s == 0 || wave >= 2) {                                                         \
-                const int f = (wave * 2 + s) * 2;                                              \
-                cP[s] = frag_at(pf + offp + f * 512, pf + offp + (f + 1) * 512);               \
-            }                                                                                  \
+            const int f = (wave * 2 + s) * 2;                                                  \
+            cP[s] = frag_at(pf + offp + f * 512, pf + offp + (f + 1) * 512);                   \
         }                                                                                      \
         const float *g = gf + (size_t)(CH) * (2 * kC);                                         \
         cEG = ld4(g + 16 * wave + 4 * kq);                                                     \
@@ -834,7 +834,7 @@ scan_kernel(const PrefillArgs p, int slices)
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = s0 + c * kC;
         const int Lc = min(kC, L - c * kC);
-        const bool more = c + 1 < nchunks;
+        const int cn = c + 1 < nchunks ? c + 1 : c; // chunk whose operands are prefetched
 
         // ---- phase 1: D = U - W S and Y = Q S (state slice as B operand)
         f32x4 Dv = cU, Y = {0.f, 0.f, 0.f, 0.f};
@@ -845,7 +845,7 @@ scan_kernel(const PrefillArgs p, int slices)
             Dv = mma3(cW[s], B, Dv);
             Y = mma3(cQ[s], B, Y);
         }
-        if (more) GDN_LOAD_PHASE1(c + 1)
+        GDN_LOAD_PHASE1(cn)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 16 * wave + 4 * kq + e;
@@ -890,7 +890,7 @@ scan_kernel(const PrefillArgs p, int slices)
             const int t = 16 * wave + 4 * kq + e;
             if (t < Lc) o_head[(size_t)(t0 + t) * p.d_v + slice * kBV + col] = Y[e];
         }
-        if (more) GDN_LOAD_PHASE2(c + 1)
+        GDN_LOAD_PHASE2(cn)
         lds_barrier();
     }
 #undef GDN_LOAD_PHASE1
