@@ -25,10 +25,10 @@
 //           triangular inverse T, the v conv, and W, U on MFMA; writes W
 //           (negated), P as fragments, U in the accumulator layout of the
 //           scan, and the decay factors e^G, e^{G_C-G}.
-//   scan    grid (seq, value head, 16-column slice of d_v), 4 waves: the
-//           chain of chunk states.  Per chunk two phases, D = U - W S and
-//           Q S | S' and O = e^G Q S + P D, with every operand of the next
-//           chunk loaded into registers right after its last use.
+//   scan    grid (seq, value head, 16-column slice of d_v), 8 waves: four
+//           carry the chain of chunk states (D = U - W S | S'), four trail
+//           them by a chunk and form O = e^G Q S + P D; every operand of the
+//           next chunk is loaded into registers right after its last use.
 //   norm    grid (rows of (token, value head)): gated RMSNorm + output gate.
 //   conv_final: each sequence's last K-1 raw inputs become its history.
 //
@@ -704,23 +704,27 @@ tri_kernel(const PrefillArgs p)
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup per (sequence, value head, 16-column slice), 4 waves
-// (one per SIMD).  Wave w owns output rows 16w..16w+15 of each chunk and
-// the state rows of M-tiles w, w+4, ...; all its matrix operands come
-// pre-split from the workspace into registers, each reloaded with the next
-// chunk's data right after its last use.  LDS holds only what the waves
-// exchange: the state slice S^T (d_k-permuted, as B operand), D and
-// e^{G_C-G} D (token order, as B operands).
+// scan: one workgroup per (sequence, value head, 16-column slice), 8 waves
+// in two roles, one wave of each per SIMD:
+//   chain waves 0-3: wave w carries rows 16w..16w+15 of D = U - W S and the
+//     state rows of M-tiles w, w+4, ... through S' = e^{G_C} S + K^T E;
+//   output waves 4-7: one chunk behind, wave w forms rows 16w.. of
+//     O = e^G (Q S) + P D from the state and D the chain left in LDS.
+// Each role loads only its own operands, pre-split, into registers, each
+// reloaded with the next chunk's data right after its last use; LDS holds
+// what the roles exchange: the state slice S^T (d_k-permuted, B operand,
+// double-buffered by chunk parity), D (double-buffered) and e^{G_C-G} D.
+// Both roles meet at the same two barriers per chunk.
 // ---------------------------------------------------------------------------
 template <int DK>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 scan_kernel(const PrefillArgs p, int slices)
 {
     constexpr int RK = DK + 8;         // bf16 stride of S^T rows
     constexpr int RT = kC + 8;         // bf16 stride of D, E rows
     constexpr int KS = DK / 32;        // k-steps over d_k
     constexpr int MTS = DK / 16;       // state M-tiles
-    constexpr int MTW = (MTS + 3) / 4; // per wave
+    constexpr int MTW = (MTS + 3) / 4; // per chain wave
 
     // Map the block index so the slices of one head share an XCD (blocks
     // are dealt round-robin over 8 XCDs): they read the same chunk data.
@@ -741,170 +745,204 @@ scan_kernel(const PrefillArgs p, int slices)
     const int hk = hv / p.group;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = wave & 3;
     const int col = lane & 15, kq = lane >> 4;
     const int s0 = p.cu[n];
     const int L = p.cu[n + 1] - s0;
     const int nchunks = (L + kC - 1) / kC;
     const int slot0 = s0 / kC + n;
 
-    __shared__ __attribute__((aligned(16))) __bf16 sS[2][kBV * RK];
-    __shared__ __attribute__((aligned(16))) __bf16 sD[2][kBV * RT];
-    __shared__ __attribute__((aligned(16))) __bf16 sE[2][kBV * RT];
+    __shared__ __attribute__((aligned(16))) __bf16 sS[2][2][kBV * RK]; // [parity][hi,lo]
+    __shared__ __attribute__((aligned(16))) __bf16 sD[2][2][kBV * RT]; // [parity][hi,lo]
+    __shared__ __attribute__((aligned(16))) __bf16 sE[2][kBV * RT];    // [hi,lo]
 
-    const __bf16 *qf = p.ws_qf + ((size_t)hk * p.ns + slot0) * (2 * kC * DK) + lane * 8;
-    const __bf16 *ktf = p.ws_ktf + ((size_t)hk * p.ns + slot0) * (2 * kC * DK) + lane * 8;
-    const __bf16 *wf = p.ws_wf + ((size_t)hv * p.ns + slot0) * (2 * kC * DK) + lane * 8;
-    const __bf16 *pf = p.ws_pf + ((size_t)hv * p.ns + slot0) * (2 * kC * kC) + lane * 8;
-    const float *uf = p.ws_uf + ((size_t)hv * p.ns + slot0) * ((size_t)kC * p.d_v) +
-                      (size_t)slice * 4 * 256 + wave * 256 + lane * 4;
-    const float *gf = p.ws_gf + ((size_t)hv * p.ns + slot0) * (2 * kC);
-    float *o_head = p.ws_o + (size_t)hv * p.t_total * p.d_v;
-
-    f32x4 S[MTW];
-    Frag cW[KS], cQ[KS], cK[MTW][2], cP[2];
-    f32x4 cU, cEG, cEGC;
-    float gam = 0.0f;
-
-    // Operands of chunk CH used in phase 1 (W, Q rows of this wave, U) and
-    // in phase 2 (k^T rows of this wave's M-tiles, P rows, decays).  The
-    // loads are unconditional (the last chunk reloads itself) so that the
-    // compiler's load counters stay exact and each wait covers only the
-    // operands it needs, never the prefetch behind them.
-#define GDN_LOAD_PHASE1(CH)                                                                    \
-    {                                                                                          \
-        const size_t off = (size_t)(CH) * (2 * kC * DK);                                       \
-        _Pragma("unroll") for (int s = 0; s < KS; ++s) {                                       \
-            const int f = (wave * KS + s) * 2;                                                 \
-            cW[s] = frag_at(wf + off + f * 512, wf + off + (f + 1) * 512);                     \
-            cQ[s] = frag_at(qf + off + f * 512, qf + off + (f + 1) * 512);                     \
-        }                                                                                      \
-        cU = ld4(uf + (size_t)(CH) * kC * p.d_v);                                              \
-    }
-#define GDN_LOAD_PHASE2(CH)                                                                    \
-    {                                                                                          \
-        const size_t off = (size_t)(CH) * (2 * kC * DK);                                       \
-        _Pragma("unroll") for (int u = 0; u < MTW; ++u) {                                      \
-            const int mt = min(wave + 4 * u, MTS - 1);                                         \
-            _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
-                const int f = (mt * 2 + s) * 2;                                                \
-                cK[u][s] = frag_at(ktf + off + f * 512, ktf + off + (f + 1) * 512);            \
+    if (wave < 4) {
+        // ================= chain waves ===================================
+        const __bf16 *ktf = p.ws_ktf + ((size_t)hk * p.ns + slot0) * (2 * kC * DK) + lane * 8;
+        const __bf16 *wf = p.ws_wf + ((size_t)hv * p.ns + slot0) * (2 * kC * DK) + lane * 8;
+        const float *uf = p.ws_uf + ((size_t)hv * p.ns + slot0) * ((size_t)kC * p.d_v) +
+                          (size_t)slice * 4 * 256 + w * 256 + lane * 4;
+        const float *gf = p.ws_gf + ((size_t)hv * p.ns + slot0) * (2 * kC);
+        f32x4 S[MTW];
+        Frag cW[KS], cK[MTW][2];
+        f32x4 cU, cEGC;
+        float gam = 0.0f;
+        // The loads are unconditional (the last chunk reloads itself) so that
+        // the compiler's load counters stay exact and each wait covers only
+        // the operands it needs, never the prefetch behind them.
+#define GDN_CHAIN_LOAD1(CH)                                                                    \
+        {                                                                                      \
+            const size_t off = (size_t)(CH) * (2 * kC * DK);                                   \
+            _Pragma("unroll") for (int s = 0; s < KS; ++s) {                                   \
+                const int f = (w * KS + s) * 2;                                                \
+                cW[s] = frag_at(wf + off + f * 512, wf + off + (f + 1) * 512);                 \
             }                                                                                  \
-        }                                                                                      \
-        const size_t offp = (size_t)(CH) * (2 * kC * kC);                                      \
-        _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                        \
-            const int f = (wave * 2 + s) * 2;                                                  \
-            cP[s] = frag_at(pf + offp + f * 512, pf + offp + (f + 1) * 512);                   \
-        }                                                                                      \
-        const float *g = gf + (size_t)(CH) * (2 * kC);                                         \
-        cEG = ld4(g + 16 * wave + 4 * kq);                                                     \
-        cEGC = ld4(g + kC + 16 * wave + 4 * kq);                                               \
-        gam = g[kC - 1];                                                                       \
-    }
-
-    // State tile u into S^T in LDS at its d_k-permuted position.
-    auto put_state = [&](int mt, const f32x4 &v) {
-        __bf16 h[4], l[4];
+            cU = ld4(uf + (size_t)(CH) * kC * p.d_v);                                          \
+        }
+#define GDN_CHAIN_LOAD2(CH)                                                                    \
+        {                                                                                      \
+            const size_t off = (size_t)(CH) * (2 * kC * DK);                                   \
+            _Pragma("unroll") for (int u = 0; u < MTW; ++u) {                                  \
+                const int mt = min(w + 4 * u, MTS - 1);                                        \
+                _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                \
+                    const int f = (mt * 2 + s) * 2;                                            \
+                    cK[u][s] = frag_at(ktf + off + f * 512, ktf + off + (f + 1) * 512);        \
+                }                                                                              \
+            }                                                                                  \
+            const float *g = gf + (size_t)(CH) * (2 * kC);                                     \
+            cEGC = ld4(g + kC + 16 * w + 4 * kq);                                              \
+            gam = g[kC - 1];                                                                   \
+        }
+        // State tile mt into S^T (buffer par) at its d_k-permuted position.
+        auto put_state = [&](int par, int mt, const f32x4 &v) {
+            __bf16 h[4], l[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split1(v[e], h[e], l[e]);
-        const int pos = col * RK + 32 * (mt >> 1) + 8 * kq + 4 * (mt & 1);
-        *reinterpret_cast<uint2 *>(&sS[0][pos]) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
-        *reinterpret_cast<uint2 *>(&sS[1][pos]) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
-    };
-
-    // ---- prologue --------------------------------------------------------
-    {
-        const float *Sin = p.state_in ? p.state_in + ((size_t)n * p.h_v + hv) * DK * p.d_v : nullptr;
+            for (int e = 0; e < 4; ++e) split1(v[e], h[e], l[e]);
+            const int pos = col * RK + 32 * (mt >> 1) + 8 * kq + 4 * (mt & 1);
+            *reinterpret_cast<uint2 *>(&sS[par][0][pos]) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
+            *reinterpret_cast<uint2 *>(&sS[par][1][pos]) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
+        };
+        {
+            const float *Sin = p.state_in ? p.state_in + ((size_t)n * p.h_v + hv) * DK * p.d_v : nullptr;
 #pragma unroll
-        for (int u = 0; u < MTW; ++u) {
-            const int mt = wave + 4 * u;
+            for (int u = 0; u < MTW; ++u) {
+                const int mt = w + 4 * u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * mt + 4 * kq + e;
+                    S[u][e] = (mt < MTS && Sin) ? Sin[(size_t)i * p.d_v + slice * kBV + col] : 0.0f;
+                }
+                if (mt < MTS) put_state(0, mt, S[u]);
+            }
+        }
+        GDN_CHAIN_LOAD1(0)
+        GDN_CHAIN_LOAD2(0)
+        lds_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            const int par = c & 1;
+            const int cn = c + 1 < nchunks ? c + 1 : c; // chunk whose operands are prefetched
+            // ---- phase 1: D = U - W S -> sD, e^{G_C-G} D -> sE
+            f32x4 Dv = cU;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int o = col * RK + 32 * s + 8 * kq;
+                Dv = mma3(cW[s], frag_at(&sS[par][0][o], &sS[par][1][o]), Dv);
+            }
+            GDN_CHAIN_LOAD1(cn)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = 16 * mt + 4 * kq + e;
-                S[u][e] = (mt < MTS && Sin) ? Sin[(size_t)i * p.d_v + slice * kBV + col] : 0.0f;
+                const int t = 16 * w + 4 * kq + e;
+                __bf16 h, l;
+                split1(Dv[e], h, l);
+                sD[par][0][col * RT + t] = h;
+                sD[par][1][col * RT + t] = l;
+                split1(Dv[e] * cEGC[e], h, l);
+                sE[0][col * RT + t] = h;
+                sE[1][col * RT + t] = l;
             }
-            if (mt < MTS) put_state(mt, S[u]);
-        }
-    }
-    if (nchunks > 0) {
-        GDN_LOAD_PHASE1(0)
-        GDN_LOAD_PHASE2(0)
-    }
-    lds_barrier();
-
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = s0 + c * kC;
-        const int Lc = min(kC, L - c * kC);
-        const int cn = c + 1 < nchunks ? c + 1 : c; // chunk whose operands are prefetched
-
-        // ---- phase 1: D = U - W S and Y = Q S (state slice as B operand)
-        f32x4 Dv = cU, Y = {0.f, 0.f, 0.f, 0.f};
+            lds_barrier();
+            // ---- phase 2: S' = e^{G_C} S + K^T E -> sS (other parity)
+            Frag Be[2];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int o = col * RK + 32 * s + 8 * kq;
-            const Frag B = frag_at(&sS[0][o], &sS[1][o]);
-            Dv = mma3(cW[s], B, Dv);
-            Y = mma3(cQ[s], B, Y);
-        }
-        GDN_LOAD_PHASE1(cn)
+            for (int s = 0; s < 2; ++s) {
+                const int o = col * RT + 32 * s + 8 * kq;
+                Be[s] = frag_at(&sE[0][o], &sE[1][o]);
+            }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * wave + 4 * kq + e;
-            __bf16 h, l;
-            split1(Dv[e], h, l);
-            sD[0][col * RT + t] = h;
-            sD[1][col * RT + t] = l;
-            split1(Dv[e] * cEGC[e], h, l);
-            sE[0][col * RT + t] = h;
-            sE[1][col * RT + t] = l;
-        }
-        Y *= cEG;
-        lds_barrier();
-
-        // ---- phase 2: S' = e^{G_C} S + K^T E; O = e^G Y + P D -----------
-        Frag Be[2];
+            for (int u = 0; u < MTW; ++u) {
+                const int mt = w + 4 * u;
+                if (mt < MTS) {
+                    f32x4 acc = gam * S[u];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int o = col * RT + 32 * s + 8 * kq;
-            Be[s] = frag_at(&sE[0][o], &sE[1][o]);
+                    for (int s = 0; s < 2; ++s) acc = mma3(cK[u][s], Be[s], acc);
+                    S[u] = acc;
+                    put_state(par ^ 1, mt, acc);
+                }
+            }
+            GDN_CHAIN_LOAD2(cn)
+            lds_barrier();
         }
+#undef GDN_CHAIN_LOAD1
+#undef GDN_CHAIN_LOAD2
+        float *Sout = p.state_out + ((size_t)n * p.h_v + hv) * DK * p.d_v;
 #pragma unroll
         for (int u = 0; u < MTW; ++u) {
-            const int mt = wave + 4 * u;
-            if (mt < MTS) {
-                f32x4 acc = gam * S[u];
+            const int mt = w + 4 * u;
+            if (mt < MTS)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) acc = mma3(cK[u][s], Be[s], acc);
-                S[u] = acc;
-                put_state(mt, acc);
+                for (int e = 0; e < 4; ++e)
+                    Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + slice * kBV + col] = S[u][e];
+        }
+    } else {
+        // ================= output waves (one chunk behind) ==============
+        const __bf16 *qf = p.ws_qf + ((size_t)hk * p.ns + slot0) * (2 * kC * DK) + lane * 8;
+        const __bf16 *pf = p.ws_pf + ((size_t)hv * p.ns + slot0) * (2 * kC * kC) + lane * 8;
+        const float *gf = p.ws_gf + ((size_t)hv * p.ns + slot0) * (2 * kC);
+        float *o_head = p.ws_o + (size_t)hv * p.t_total * p.d_v + slice * kBV + col;
+        Frag cQ[KS], cP[2];
+        f32x4 cEG, Y = {0.f, 0.f, 0.f, 0.f};
+#define GDN_OUT_LOAD1(CH)                                                                      \
+        {                                                                                      \
+            const size_t off = (size_t)(CH) * (2 * kC * DK);                                   \
+            _Pragma("unroll") for (int s = 0; s < KS; ++s) {                                   \
+                const int f = (w * KS + s) * 2;                                                \
+                cQ[s] = frag_at(qf + off + f * 512, qf + off + (f + 1) * 512);                 \
+            }                                                                                  \
+            cEG = ld4(gf + (size_t)(CH) * (2 * kC) + 16 * w + 4 * kq);                         \
+        }
+#define GDN_OUT_LOAD2(CH)                                                                      \
+        {                                                                                      \
+            const size_t off = (size_t)(CH) * (2 * kC * kC);                                   \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
+                const int f = (w * 2 + s) * 2;                                                 \
+                cP[s] = frag_at(pf + off + f * 512, pf + off + (f + 1) * 512);                 \
+            }                                                                                  \
+        }
+        // Y = e^G (Q S) of chunk cc from the state buffer of its parity.
+        auto readout = [&](int cc) {
+            const int par = cc & 1;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int o = col * RK + 32 * s + 8 * kq;
+                acc = mma3(cQ[s], frag_at(&sS[par][0][o], &sS[par][1][o]), acc);
             }
-        }
+            return acc * cEG;
+        };
+        // O = Y + P D of chunk cc, stored for its rows inside the sequence.
+        auto finish = [&](int cc, f32x4 y) {
+            const int par = cc & 1;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if (s == 0 || wave >= 2) { // P is lower triangular
-                const int o = col * RT + 32 * s + 8 * kq;
-                Y = mma3(cP[s], frag_at(&sD[0][o], &sD[1][o]), Y);
+            for (int s = 0; s < 2; ++s) {
+                if (s == 0 || w >= 2) { // P is lower triangular
+                    const int o = col * RT + 32 * s + 8 * kq;
+                    y = mma3(cP[s], frag_at(&sD[par][0][o], &sD[par][1][o]), y);
+                }
             }
-        }
+            const int Lc = min(kC, L - cc * kC);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 16 * wave + 4 * kq + e;
-            if (t < Lc) o_head[(size_t)(t0 + t) * p.d_v + slice * kBV + col] = Y[e];
-        }
-        GDN_LOAD_PHASE2(cn)
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * w + 4 * kq + e;
+                if (t < Lc) o_head[(size_t)(s0 + cc * kC + t) * p.d_v] = y[e];
+            }
+        };
+        GDN_OUT_LOAD1(0)
+        GDN_OUT_LOAD2(0)
         lds_barrier();
-    }
-#undef GDN_LOAD_PHASE1
-#undef GDN_LOAD_PHASE2
-
-    // Final state slice.
-    float *Sout = p.state_out + ((size_t)n * p.h_v + hv) * DK * p.d_v;
-#pragma unroll
-    for (int u = 0; u < MTW; ++u) {
-        const int mt = wave + 4 * u;
-        if (mt < MTS)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + slice * kBV + col] = S[u][e];
+        for (int c = 0; c < nchunks; ++c) {
+            // phase 1: readout of chunk c-1 (its state is still in LDS)
+            if (c > 0) Y = readout(c - 1);
+            GDN_OUT_LOAD1(c)
+            lds_barrier();
+            // phase 2: finish chunk c-1 (its D is still in LDS)
+            if (c > 0) finish(c - 1, Y);
+            GDN_OUT_LOAD2(c)
+            lds_barrier();
+        }
+#undef GDN_OUT_LOAD1
+#undef GDN_OUT_LOAD2
+        // the last chunk: the chain has left its state and D in LDS
+        if (nchunks > 0) finish(nchunks - 1, readout(nchunks - 1));
     }
 }
 
@@ -993,7 +1031,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
     }
     if (n_seq > 0) {
         const int slices = DV / kBV;
-        hipLaunchKernelGGL((scan_kernel<DK>), dim3(n_seq * a.h_v * slices), dim3(256), 0, s, a,
+        hipLaunchKernelGGL((scan_kernel<DK>), dim3(n_seq * a.h_v * slices), dim3(512), 0, s, a,
                            slices);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
