@@ -133,6 +133,9 @@ __device__ __forceinline__ uint32_t pack2(__bf16 a, __bf16 b)
 // between the waves of a workgroup here, so no global fence is needed; the
 // empty asm statements keep the compiler from moving memory accesses
 // across the barrier.)
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xf << 8);
+
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -767,9 +770,11 @@ scan_kernel(const PrefillArgs p, int slices)
         Frag cW[KS], cK[MTW][2];
         f32x4 cU, cEGC;
         float gam = 0.0f;
-        // The loads are unconditional (the last chunk reloads itself) so that
-        // the compiler's load counters stay exact and each wait covers only
-        // the operands it needs, never the prefetch behind them.
+        // Load groups, each issued right after the last use of what it
+        // replaces: W rows and U (phase 1), e^{G_C-G} rows (after E), k^T rows
+        // and e^{G_C} (phase 2).  The loads are unconditional (the last chunk
+        // reloads itself) so that the compiler's load counters stay exact and
+        // each wait covers only its own group, never the prefetch behind it.
 #define GDN_CHAIN_LOAD1(CH)                                                                    \
         {                                                                                      \
             const size_t off = (size_t)(CH) * (2 * kC * DK);                                   \
@@ -779,6 +784,7 @@ scan_kernel(const PrefillArgs p, int slices)
             }                                                                                  \
             cU = ld4(uf + (size_t)(CH) * kC * p.d_v);                                          \
         }
+#define GDN_CHAIN_LOAD1B(CH) cEGC = ld4(gf + (size_t)(CH) * (2 * kC) + kC + 16 * w + 4 * kq);
 #define GDN_CHAIN_LOAD2(CH)                                                                    \
         {                                                                                      \
             const size_t off = (size_t)(CH) * (2 * kC * DK);                                   \
@@ -789,9 +795,7 @@ scan_kernel(const PrefillArgs p, int slices)
                     cK[u][s] = frag_at(ktf + off + f * 512, ktf + off + (f + 1) * 512);        \
                 }                                                                              \
             }                                                                                  \
-            const float *g = gf + (size_t)(CH) * (2 * kC);                                     \
-            cEGC = ld4(g + kC + 16 * w + 4 * kq);                                              \
-            gam = g[kC - 1];                                                                   \
+            gam = gf[(size_t)(CH) * (2 * kC) + kC - 1];                                        \
         }
         // State tile mt into S^T (buffer par) at its d_k-permuted position.
         auto put_state = [&](int par, int mt, const f32x4 &v) {
@@ -816,7 +820,11 @@ scan_kernel(const PrefillArgs p, int slices)
             }
         }
         GDN_CHAIN_LOAD1(0)
+        GDN_CHAIN_LOAD1B(0)
         GDN_CHAIN_LOAD2(0)
+        // Drain the prologue's loads (issued in whatever order the compiler
+        // chose) so that only the loop's own issue order decides its waits.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         lds_barrier();
         for (int c = 0; c < nchunks; ++c) {
             const int par = c & 1;
@@ -840,8 +848,13 @@ scan_kernel(const PrefillArgs p, int slices)
                 sE[0][col * RT + t] = h;
                 sE[1][col * RT + t] = l;
             }
+            GDN_CHAIN_LOAD1B(cn)
             lds_barrier();
             // ---- phase 2: S' = e^{G_C} S + K^T E -> sS (other parity)
+            // (the state is pinned here so that e^{G_C} S, which waits for the
+            // phase-2 loads, is not hoisted into phase 1)
+#pragma unroll
+            for (int u = 0; u < MTW; ++u) asm volatile("" : "+v"(S[u]));
             Frag Be[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -862,6 +875,7 @@ scan_kernel(const PrefillArgs p, int slices)
             GDN_CHAIN_LOAD2(cn)
             lds_barrier();
         }
+#undef GDN_CHAIN_LOAD1B
 #undef GDN_CHAIN_LOAD1
 #undef GDN_CHAIN_LOAD2
         float *Sout = p.state_out + ((size_t)n * p.h_v + hv) * DK * p.d_v;
@@ -928,6 +942,7 @@ scan_kernel(const PrefillArgs p, int slices)
         };
         GDN_OUT_LOAD1(0)
         GDN_OUT_LOAD2(0)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         lds_barrier();
         for (int c = 0; c < nchunks; ++c) {
             // phase 1: readout of chunk c-1 (its state is still in LDS)
