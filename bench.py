@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+CALIB_BYTES = 1 << 30          # the calibration copy reads and writes 1 GiB
 KERNEL_SOURCES = ["gated_deltanet_linear_causal_amd/csrc/decode.hip",
                   "gated_deltanet_linear_causal_amd/csrc/prefill.hip"]
 
@@ -49,11 +50,11 @@ def decode_bytes(d, batch):
 
 
 def prefill_flops(d, T, C=64):
-    """Algorithmic flops of the chunked form as computed (per call):
-    per token and key head K K^T and Q K^T rows (4 C d_k); per token and
-    value head K S, Q S and the state update (6 d_k d_v) plus T R and P D
-    (4 C d_v)."""
-    per_tok = d.h_k * 4 * C * d.d_k + d.h_v * (6 * d.d_k * d.d_v + 4 * C * d.d_v)
+    """Algorithmic flops of the chunked (W/U) form as computed, per call: per
+    token and key head the K K^T and Q K^T rows (4 C d_k); per token and
+    value head W = T diag(b e^G) K (2 C d_k), U = T diag(b) V and P D
+    (2 C d_v each), and W S, Q S and the state update (6 d_k d_v)."""
+    per_tok = d.h_k * 4 * C * d.d_k + d.h_v * (2 * C * (2 * d.d_v + d.d_k) + 6 * d.d_k * d.d_v)
     return T * per_tok
 
 
@@ -73,6 +74,54 @@ def sources_hash():
     return h.hexdigest()[:16]
 
 
+PREFILL_KERNELS = ("qknorm_kernel", "tri_kernel", "scan_kernel", "norm_kernel", "conv_final_kernel")
+
+
+def _counter_rows(directory):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def write_traffic(fetch_dir, write_dir):
+    """Summarise two rocprofv3 --pmc runs of `bench.py --calib-copy` (one
+    with FETCH_SIZE, one with WRITE_SIZE) into per-launch HBM bytes.  Each
+    counter is scaled by what it counts for the calibration copy (the largest
+    non-GDN dispatch, 1 GiB read + 1 GiB written; FETCH_SIZE counts half of
+    the bytes read on gfx950, WRITE_SIZE all of the bytes written)."""
+    out = {"sources_sha": sources_hash(), "kernels": {}, "calibration": {}}
+    per = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        sums, counts, calib = {}, {}, 0.0
+        for r in _counter_rows(directory):
+            if r["Counter_Name"] != counter:
+                continue
+            name, val = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0
+            key = next((k for k in PREFILL_KERNELS + ("decode_kernel",) if k in name), None)
+            if key is None:
+                calib = max(calib, val)
+                continue
+            sums[key] = sums.get(key, 0.0) + val
+            counts[key] = counts.get(key, 0) + 1
+        if not 0.25 * CALIB_BYTES < calib < 4.0 * CALIB_BYTES:
+            raise SystemExit(f"{counter}: calibration copy counted {calib:.3e} B for {CALIB_BYTES} B")
+        scale = CALIB_BYTES / calib
+        out["calibration"][counter] = {"copy_bytes": CALIB_BYTES, "counter_bytes": calib, "scale": scale}
+        per[counter] = {k: sums[k] / counts[k] * scale for k in sums}
+    for k in per["FETCH_SIZE"]:
+        f, w = per["FETCH_SIZE"][k], per["WRITE_SIZE"].get(k, 0.0)
+        out["kernels"][k] = {"fetch_bytes": round(f), "write_bytes": round(w), "bytes_per_launch": round(f + w)}
+    pre = [out["kernels"][k] for k in PREFILL_KERNELS if k in out["kernels"]]
+    out["kernels"]["prefill_call"] = {"bytes_per_launch": sum(e["bytes_per_launch"] for e in pre)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def load_traffic(kernel):
     """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
     runs (scaled by a plain-copy calibration), or None if they were taken on
@@ -88,22 +137,28 @@ def load_traffic(kernel):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
-def cpu_baseline(case, threads):
+def cpu_baseline(case, threads, min_seconds=10.0, max_reps=100):
     """The oracle, untuned, on the host cores: the full T=4096 prefill over
-    every head (a short warm-up call loads the library first)."""
+    every head, repeated until at least min_seconds of wall time (a short
+    warm-up call loads the library first)."""
     import oracle
     shape = oracle.Shape(case.dims.h_k, case.dims.h_v, case.dims.d_k, case.dims.d_v,
                          case.dims.conv_k, case.dims.gate)
     oracle.mixer(shape, [0, 1], case.params, case.qkv[:1], case.z[:1], case.a[:1],
                  case.b[:1], case.S0, case.conv0, nthreads=threads)
+    reps = 0
     t = time.perf_counter()
-    oracle.mixer(shape, case.cu_seqlens, case.params, case.qkv, case.z, case.a, case.b,
-                 case.S0, case.conv0, nthreads=threads)
-    dt = time.perf_counter() - t
+    while True:
+        oracle.mixer(shape, case.cu_seqlens, case.params, case.qkv, case.z, case.a, case.b,
+                     case.S0, case.conv0, nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds or reps >= max_reps:
+            break
     T = case.t_total
-    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"full prefill T={T}, all {case.dims.h_v} value heads, float64 "
-                      f"token-by-token C oracle, {dt:.2f} s wall"}
+    return {"value": reps * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x the full prefill T={T} (all {case.dims.h_v} value heads), "
+                      f"float64 token-by-token C oracle on {threads} threads, {dt:.1f} s wall"}
 
 
 def main():
@@ -114,7 +169,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into "
+                         "profiles/traffic_counters.json and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); "
@@ -181,7 +242,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     if args.calib_copy:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
