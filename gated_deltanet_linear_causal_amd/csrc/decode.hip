@@ -111,6 +111,7 @@ decode_kernel(const DecodeArgs p)
     // one unit ahead (further channels, when a unit has more than NT, are
     // loaded when used).
     float cx = 0.0f, ch0 = 0.0f, ch1 = 0.0f, ch2 = 0.0f;
+    float cw[4] = {0.f, 0.f, 0.f, 0.f};
     auto load_conv = [&](int u) {
         if (tid < nch) {
             const int bs = u / p.h_k, ch = channel(u, tid);
@@ -119,13 +120,16 @@ decode_kernel(const DecodeArgs p)
             if (K > 1) ch0 = hist[0];
             if (K > 2) ch1 = hist[(size_t)CD];
             if (K > 3) ch2 = hist[(size_t)2 * CD];
+            const float *w = p.conv_w + (size_t)ch * K;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < K) cw[j] = w[j];
         }
     };
-    // silu(conv) of one channel from its raw input x and history prev[],
-    // and the history shifted in place.
-    auto conv_one = [&](int u, int l, float x, const float (&prev)[3]) {
+    // silu(conv) of one channel from its raw input x, history prev[] and
+    // taps w[], and the history shifted in place.
+    auto conv_one = [&](int u, int l, float x, const float (&prev)[3], const float (&w)[4]) {
         const int bs = u / p.h_k, ch = channel(u, l);
-        const float *w = p.conv_w + (size_t)ch * K;
         float *hist = p.conv_state + (size_t)bs * (K - 1) * CD + ch;
         float acc = 0.0f;
         for (int j = 0; j < K - 1; ++j) acc = fmaf(w[j], prev[j], acc);
@@ -143,14 +147,15 @@ decode_kernel(const DecodeArgs p)
         // place (each channel has exactly one reader/writer: this thread).
         if (tid < nch) {
             const float prev[3] = {ch0, ch1, ch2};
-            conv_one(u, tid, cx, prev);
+            conv_one(u, tid, cx, prev, cw);
         }
         for (int l = tid + NT; l < nch; l += NT) {
             const int ch = channel(u, l);
             const float *hist = p.conv_state + (size_t)bs * (K - 1) * CD + ch;
-            float prev[3] = {0.f, 0.f, 0.f};
+            float prev[3] = {0.f, 0.f, 0.f}, w[4] = {0.f, 0.f, 0.f, 0.f};
             for (int j = 0; j < K - 1; ++j) prev[j] = hist[(size_t)j * CD];
-            conv_one(u, l, load_act(qkv, (size_t)bs * CD + ch), prev);
+            for (int j = 0; j < K; ++j) w[j] = p.conv_w[(size_t)ch * K + j];
+            conv_one(u, l, load_act(qkv, (size_t)bs * CD + ch), prev, w);
         }
         // Gates, z and norm weights of the first pass.
         const TIn *pa = static_cast<const TIn *>(p.a), *pb = static_cast<const TIn *>(p.b);
