@@ -84,6 +84,33 @@ __device__ __forceinline__ f32x4 mma3(const Frag &A, const Frag &B, f32x4 c)
     return c;
 }
 
+// The same split product on a 16x16x16 tile.  Lane l holds A[l%16][4*(l/16)
+// + e], B[4*(l/16) + e][l%16] and D[4*(l/16) + e][l%16] (e < 4), so an
+// accumulator tile is directly the B operand of the next product.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct Frag4 {
+    s16x4 hi, lo;
+};
+__device__ __forceinline__ Frag4 split4(const f32x4 &v)
+{
+    Frag4 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        __bf16 h, l;
+        split1(v[e], h, l);
+        f.hi[e] = __builtin_bit_cast(short, h);
+        f.lo[e] = __builtin_bit_cast(short, l);
+    }
+    return f;
+}
+__device__ __forceinline__ f32x4 mma3k16(const Frag4 &A, const Frag4 &B, f32x4 c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A.lo, B.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A.hi, B.lo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A.hi, B.hi, c, 0, 0, 0);
+    return c;
+}
+
 __device__ __forceinline__ Frag frag_at(const __bf16 *hi, const __bf16 *lo)
 {
     Frag f;
@@ -396,13 +423,11 @@ qknorm_kernel(const PrefillArgs p)
 // tri: one workgroup per (chunk, value head, sequence), 256 threads.
 // ---------------------------------------------------------------------------
 template <int DV> struct TriLds {
-    static constexpr int LC = kC + 4;    // fp32 stride of A, P, T rows
-    static constexpr int RV = kC + 8;    // bf16 stride of V^T rows
+    static constexpr int LC = kC + 4;    // fp32 stride of A, P, T and V^T rows
     static constexpr int o_t = 0;
-    static constexpr int o_w = o_t + kC * LC * 4;
-    static constexpr int o_g = o_w + 4 * 16 * 17 * 4; // G, beta, beta e^G
+    static constexpr int o_g = o_t + kC * LC * 4;     // G, beta, beta e^G
     static constexpr int o_u = o_g + 3 * kC * 4;      // A, P, later V^T
-    static constexpr int ap = 2 * kC * LC * 4, vt = 2 * DV * RV * 2;
+    static constexpr int ap = 2 * kC * LC * 4, vt = DV * LC * 4;
     static constexpr int total = o_u + (ap > vt ? ap : vt);
 };
 
@@ -411,7 +436,7 @@ __global__ void __launch_bounds__(256)
 tri_kernel(const PrefillArgs p)
 {
     using LY = TriLds<DV>;
-    constexpr int LC = LY::LC, RV = LY::RV;
+    constexpr int LC = LY::LC;
     constexpr int KS = DK / 32, VS = DV / 16;
     constexpr int CG = DV / 4;            // v channel groups of 4
     constexpr int TPG = kC * CG / 256;    // consecutive tokens per thread in the v conv
@@ -429,13 +454,11 @@ tri_kernel(const PrefillArgs p)
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float *sT = reinterpret_cast<float *>(smem + LY::o_t);
-    float(*sW)[16 * 17] = reinterpret_cast<float(*)[16 * 17]>(smem + LY::o_w);
     float *sG = reinterpret_cast<float *>(smem + LY::o_g), *sB = sG + kC, *sBE = sB + kC;
     float *sA = reinterpret_cast<float *>(smem + LY::o_u), *sP = sA + kC * LC;
-    __bf16 *sVh = reinterpret_cast<__bf16 *>(smem + LY::o_u), *sVl = sVh + DV * RV;
+    float *sV = reinterpret_cast<float *>(smem + LY::o_u); // V^T [DV][LC]
 
-    // ---- every global load first ---------------------------------------
-    // gates (wave 0)
+    // ---- loads of the first phases: gates (wave 0) and Gram rows --------
     const TIn *pa = static_cast<const TIn *>(p.a);
     const TIn *pb = static_cast<const TIn *>(p.b);
     float a_raw = 0.0f, b_raw = 0.0f;
@@ -457,36 +480,6 @@ tri_kernel(const PrefillArgs p)
             gqk[m] = glive ? ld4(g + kC * kC + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    // raw v inputs: thread (channel group cg, token group tg)
-    typedef typename RawAct<TIn>::type RawT;
-    const TIn *x = static_cast<const TIn *>(p.qkv);
-    const int cg = tid % CG, tg = tid / CG;
-    const int vch = 2 * p.h_k * DK + hv * DV + 4 * cg;
-    const int vt0 = c * kC + tg * TPG; // first token (sequence position)
-    RawT vraw[VWIN];
-#pragma unroll
-    for (int j = 0; j < VWIN; ++j) {
-        const int tau = min(max(vt0 - 3 + j, 0), L - 1);
-        vraw[j] = RawAct<TIn>::load(x, (size_t)(s0 + tau) * p.conv_dim + vch);
-    }
-    // k^T fragments for the W^T tiles of this wave: column blocks 2 sp and
-    // 2 sp + 1 of d_k (sp = wave), both token steps
-    const int sp = wave;
-    const bool wact = sp < KS;
-    Frag kA[2][2];
-    if (wact) {
-        const __bf16 *kt = p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK) + lane * 8;
-#pragma unroll
-        for (int n2 = 0; n2 < 2; ++n2)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int f = ((2 * sp + n2) * 2 + s) * 2;
-                kA[n2][s] = frag_at(kt + (size_t)f * 512, kt + (size_t)(f + 1) * 512);
-            }
-    }
-    float wv[4][4];
-    load_taps4(p, vch, wv);
-
     // ---- gates ("cherenkov qwen4_exp/cpu.rs" fn deltanet) and their
     // inclusive prefix sum over the chunk (wave 0); past the chunk end
     // g = 0 and b = 0.
@@ -547,6 +540,38 @@ tri_kernel(const PrefillArgs p)
         }
     }
 
+    // ---- loads needed only after the solve, issued now so that the solve
+    // hides their latency: raw v inputs, thread (channel group cg, token
+    // group tg)
+    typedef typename RawAct<TIn>::type RawT;
+    const TIn *x = static_cast<const TIn *>(p.qkv);
+    const int cg = tid % CG, tg = tid / CG;
+    const int vch = 2 * p.h_k * DK + hv * DV + 4 * cg;
+    const int vt0 = c * kC + tg * TPG; // first token (sequence position)
+    RawT vraw[VWIN];
+#pragma unroll
+    for (int j = 0; j < VWIN; ++j) {
+        const int tau = min(max(vt0 - 3 + j, 0), L - 1);
+        vraw[j] = RawAct<TIn>::load(x, (size_t)(s0 + tau) * p.conv_dim + vch);
+    }
+    // k^T fragments for the W^T tiles of this wave: column blocks 2 sp and
+    // 2 sp + 1 of d_k (sp = wave), both token steps
+    const int sp = wave;
+    const bool wact = sp < KS;
+    Frag kA[2][2];
+    if (wact) {
+        const __bf16 *kt = p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK) + lane * 8;
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int f = ((2 * sp + n2) * 2 + s) * 2;
+                kA[n2][s] = frag_at(kt + (size_t)f * 512, kt + (size_t)(f + 1) * 512);
+            }
+    }
+    float wv[4][4];
+    load_taps4(p, vch, wv);
+
     // ---- T = (I + A)^-1, blocked over 16x16 blocks, fp32.
     // Diagonal blocks by forward substitution: wave b owns block b; lane
     // (col j, quarter q) keeps rows 4q..4q+3 of column j.
@@ -573,46 +598,26 @@ tri_kernel(const PrefillArgs p)
                 for (int e = 0; e < 4; ++e) sT[(16 * b + 4 * kq + e) * LC + 16 * bj + col] = 0.0f;
     }
     __syncthreads();
-    // Off-diagonal blocks, by distance d from the diagonal:
-    //   T_ij = -T_ii (sum_{m=j}^{i-1} A_im T_mj).
+    // Off-diagonal blocks, by distance d from the diagonal, on the matrix
+    // cores (split products, fp32 accumulate):
+    //   T_ij = -T_ii (sum_{m=j}^{i-1} A_im T_mj);
+    // the accumulated sum is already the B operand of the product with T_ii.
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
-        const bool act = wave < 4 - d;
-        const int bi = wave + d, bj = wave;
-        if (act) {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (wave < 4 - d) {
+            const int bi = wave + d, bj = wave;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int m = bj; m < bi; ++m) {
+                const Frag4 fa = split4(ld4(sA + (16 * bi + col) * LC + 16 * m + 4 * kq));
+                f32x4 tb;
 #pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) {
-                    float tc[4];
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) tc[kk] = sT[(16 * m + 4 * k4 + kk) * LC + 16 * bj + col];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const f32x4 a4 = ld4(sA + (16 * bi + 4 * kq + e) * LC + 16 * m + 4 * k4);
-                        acc[e] = fmaf(a4[0], tc[0], fmaf(a4[1], tc[1], fmaf(a4[2], tc[2], fmaf(a4[3], tc[3], acc[e]))));
-                    }
-                }
+                for (int e = 0; e < 4; ++e) tb[e] = sT[(16 * m + 4 * kq + e) * LC + 16 * bj + col];
+                acc = mma3k16(fa, split4(tb), acc);
             }
+            const Frag4 ft = split4(ld4(sT + (16 * bi + col) * LC + 16 * bi + 4 * kq));
+            const f32x4 t = mma3k16(ft, split4(acc), f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sW[wave][(4 * kq + e) * 17 + col] = acc[e];
-        }
-        __syncthreads();
-        if (act) {
-            float tv[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                float wk[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) wk[kk] = sW[wave][(4 * k4 + kk) * 17 + col];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const f32x4 t4 = ld4(sT + (16 * bi + 4 * kq + e) * LC + 16 * bi + 4 * k4);
-                    tv[e] = fmaf(t4[0], wk[0], fmaf(t4[1], wk[1], fmaf(t4[2], wk[2], fmaf(t4[3], wk[3], tv[e]))));
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sT[(16 * bi + 4 * kq + e) * LC + 16 * bj + col] = -tv[e];
+            for (int e = 0; e < 4; ++e) sT[(16 * bi + 4 * kq + e) * LC + 16 * bj + col] = -t[e];
         }
         __syncthreads();
     }
@@ -627,23 +632,20 @@ tri_kernel(const PrefillArgs p)
             for (int j = 0; j < 3; ++j)
                 if (vt0 - 3 + j < 0) xv[j] = raw4(p, x, n, s0, vt0 - 3 + j, vch);
         }
-        __bf16 vh[4][TPG], vl[4][TPG];
+        float vt[4][TPG];
 #pragma unroll
         for (int k = 0; k < TPG; ++k) {
             const f32x4 xr[4] = {xv[k], xv[k + 1], xv[k + 2], xv[k + 3]};
             const f32x4 cv = conv4(wv, xr);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) split1(cv[e], vh[e][k], vl[e][k]);
+            for (int e = 0; e < 4; ++e) vt[e][k] = cv[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            __bf16 *dh = sVh + (4 * cg + e) * RV + tg * TPG;
-            __bf16 *dl = sVl + (4 * cg + e) * RV + tg * TPG;
+            float *dst = sV + (4 * cg + e) * LC + tg * TPG;
 #pragma unroll
-            for (int k = 0; k < TPG; k += 2) {
-                *reinterpret_cast<uint32_t *>(dh + k) = pack2(vh[e][k], vh[e][k + 1]);
-                *reinterpret_cast<uint32_t *>(dl + k) = pack2(vl[e][k], vl[e][k + 1]);
-            }
+            for (int k = 0; k < TPG; k += 2)
+                *reinterpret_cast<float2 *>(dst + k) = make_float2(vt[e][k], vt[e][k + 1]);
         }
     }
     __syncthreads();
@@ -698,8 +700,10 @@ tri_kernel(const PrefillArgs p)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 if (s < steps) {
-                    const int o = (16 * nb + col) * RV + 32 * s + 8 * kq;
-                    acc = mma3(Tu[s], frag_at(sVh + o, sVl + o), acc);
+                    const float *src = sV + (16 * nb + col) * LC + 32 * s + 8 * kq;
+                    const f32x4 u0 = ld4(src), u1 = ld4(src + 4);
+                    const float vals[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                    acc = mma3(Tu[s], split8(vals), acc);
                 }
             *reinterpret_cast<f32x4 *>(uf + (size_t)(nb * 4 + rb) * 256) = acc;
         }
