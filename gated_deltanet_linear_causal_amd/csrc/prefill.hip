@@ -283,6 +283,31 @@ __device__ __forceinline__ f32x4 raw4(const PrefillArgs &p, const TIn *x, int n,
     return f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Sum over aligned groups of W lanes (W = 4, 8 or 16, inside one row of 16
+// lanes), every lane of a group ending with the group's sum: DPP moves only
+// (quad permutations, half-row and row mirrors), no LDS traffic.
+template <int CTRL> __device__ __forceinline__ float dppf(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xf, 0xf, false));
+}
+template <int W> __device__ __forceinline__ float row_sum(float v)
+{
+    static_assert(W == 4 || W == 8 || W == 16, "group size");
+    v += dppf<0xb1>(v);                  // quad_perm [1,0,3,2]
+    v += dppf<0x4e>(v);                  // quad_perm [2,3,0,1]
+    if (W >= 8) v += dppf<0x141>(v);     // row_half_mirror
+    if (W >= 16) v += dppf<0x140>(v);    // row_mirror
+    return v;
+}
+
+// silu with the hardware exponential and reciprocal (a few ulp; the
+// parity tolerance is orders of magnitude wider).
+__device__ __forceinline__ float silu_fast(float x)
+{
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
 // silu(causal conv) of 4 channels from the 4 taps' raw inputs.
 __device__ __forceinline__ f32x4 conv4(const float (&w)[4][4], const f32x4 (&xr)[4])
 {
@@ -292,15 +317,15 @@ __device__ __forceinline__ f32x4 conv4(const float (&w)[4][4], const f32x4 (&xr)
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc = fmaf(w[e][j], xr[j][e], acc);
-        c[e] = siluf_(acc);
+        c[e] = silu_fast(acc);
     }
     return c;
 }
 
 // ---------------------------------------------------------------------------
 // qknorm: one workgroup per (chunk, key head, sequence).  Each token row of
-// the key head (q then k, 2*d_k channels) is handled by d_k/2 lanes of 4
-// channels; each L2 norm is a reduction over d_k/4 lanes.  The normalised
+// the key head (q then k, 2*d_k channels) is handled by d_k/4 lanes of 8
+// channels; each L2 norm is a DPP reduction over d_k/8 lanes.  The normalised
 // rows (split hi/lo, zero past the sequence end) are gathered in LDS, then
 // written out as q^ and k^T fragments, and the Gram tiles on and below the
 // diagonal are formed on MFMA.
@@ -311,7 +336,7 @@ template <typename TIn, int DK>
 __global__ void __launch_bounds__(256)
 qknorm_kernel(const PrefillArgs p)
 {
-    constexpr int LPT = DK / 2;              // lanes per token row
+    constexpr int LPT = DK / 4;              // lanes per token row (8 channels each)
     constexpr int TPI = 64 / LPT;            // token rows per wave pass
     constexpr int TPL = kC / (4 * TPI);      // consecutive tokens per lane
     constexpr int WIN = TPL + 3;             // raw rows a lane reads
@@ -323,9 +348,9 @@ qknorm_kernel(const PrefillArgs p)
     const int slot = s0 / kC + n + c;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = lane / LPT, ll = lane % LPT;
-    const bool isk = ll >= DK / 4;
-    const int c4 = (isk ? ll - DK / 4 : ll) * 4;
-    const int ch = (isk ? p.h_k * DK : 0) + hk * DK + c4;
+    const bool isk = ll >= DK / 8;           // q lanes, then k lanes (DK/8 each)
+    const int c8 = (isk ? ll - DK / 8 : ll) * 8;
+    const int ch = (isk ? p.h_k * DK : 0) + hk * DK + c8;
     const TIn *x = static_cast<const TIn *>(p.qkv);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     // [q,k][hi,lo][row][RS]
@@ -333,41 +358,58 @@ qknorm_kernel(const PrefillArgs p)
     const int r0 = kC / 4 * wave + TPL * sub; // first chunk row of this lane
     const int tl0 = c * kC + r0;              // its position in the sequence
 
-    // Every raw input the lane needs, loaded at once (positions clamped into
-    // the sequence; positions before its start are replaced below).
+    // Every raw input the lane needs (8 channels per row), loaded at once
+    // (positions clamped into the sequence; positions before its start are
+    // replaced below).
     typedef typename RawAct<TIn>::type RawT;
-    RawT raw[WIN];
+    RawT raw[WIN][2];
 #pragma unroll
     for (int j = 0; j < WIN; ++j) {
         const int tau = min(max(tl0 - 3 + j, 0), L - 1);
-        raw[j] = RawAct<TIn>::load(x, (size_t)(s0 + tau) * p.conv_dim + ch);
+        const size_t base = (size_t)(s0 + tau) * p.conv_dim + ch;
+        raw[j][0] = RawAct<TIn>::load(x, base);
+        raw[j][1] = RawAct<TIn>::load(x, base + 4);
     }
-    float w[4][4];
-    load_taps4(p, ch, w);
+    float w0[4][4], w1[4][4];
+    load_taps4(p, ch, w0);
+    load_taps4(p, ch + 4, w1);
     const float extra = isk ? 1.0f : rsqrtf((float)DK);
-    f32x4 xv[WIN];
+    f32x4 xv[WIN][2];
 #pragma unroll
-    for (int j = 0; j < WIN; ++j) xv[j] = RawAct<TIn>::to_f32(raw[j]);
+    for (int j = 0; j < WIN; ++j) {
+        xv[j][0] = RawAct<TIn>::to_f32(raw[j][0]);
+        xv[j][1] = RawAct<TIn>::to_f32(raw[j][1]);
+    }
     if (tl0 < 3) { // the first rows of a sequence reach into its history
 #pragma unroll
         for (int j = 0; j < 3; ++j)
-            if (tl0 - 3 + j < 0) xv[j] = raw4(p, x, n, s0, tl0 - 3 + j, ch);
+            if (tl0 - 3 + j < 0) {
+                xv[j][0] = raw4(p, x, n, s0, tl0 - 3 + j, ch);
+                xv[j][1] = raw4(p, x, n, s0, tl0 - 3 + j, ch + 4);
+            }
     }
 
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
         const int r = r0 + k, tl = tl0 + k;
-        const f32x4 xr[4] = {xv[k], xv[k + 1], xv[k + 2], xv[k + 3]};
-        const f32x4 cv = conv4(w, xr);
-        float ss = cv[0] * cv[0] + cv[1] * cv[1] + cv[2] * cv[2] + cv[3] * cv[3];
-        ss = group_sum<DK / 4>(ss);
-        const float sc = tl < L ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
-        __bf16 h[4], l[4];
+        const f32x4 xa[4] = {xv[k][0], xv[k + 1][0], xv[k + 2][0], xv[k + 3][0]};
+        const f32x4 xb[4] = {xv[k][1], xv[k + 1][1], xv[k + 2][1], xv[k + 3][1]};
+        const f32x4 ca = conv4(w0, xa), cb = conv4(w1, xb);
+        float ss = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split1(cv[e] * sc, h[e], l[e]);
-        __bf16 *dst = sQK + ((isk ? 2 : 0) * kC + r) * RS + c4;
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
-        *reinterpret_cast<uint2 *>(dst + kC * RS) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
+        for (int e = 0; e < 4; ++e) ss += ca[e] * ca[e] + cb[e] * cb[e];
+        ss = row_sum<DK / 8>(ss);
+        const float sc = tl < L ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = ca[e] * sc;
+            v[4 + e] = cb[e] * sc;
+        }
+        const Frag f = split8(v);
+        __bf16 *dst = sQK + ((isk ? 2 : 0) * kC + r) * RS + c8;
+        *reinterpret_cast<bf16x8 *>(dst) = f.hi;
+        *reinterpret_cast<bf16x8 *>(dst + kC * RS) = f.lo;
     }
     __syncthreads();
 
