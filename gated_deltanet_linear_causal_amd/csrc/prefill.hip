@@ -44,6 +44,7 @@ namespace gdn {
 
 constexpr int kC = 64;       // tokens per chunk
 constexpr int kBV = 16;      // d_v columns per scan workgroup
+constexpr int kQkChunks = 2; // chunks per qknorm workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -323,7 +324,7 @@ __device__ __forceinline__ f32x4 conv4(const float (&w)[4][4], const f32x4 (&xr)
 }
 
 // ---------------------------------------------------------------------------
-// qknorm: one workgroup per (chunk, key head, sequence).  Each token row of
+// qknorm: one workgroup per (two consecutive chunks, key head, sequence).  Each token row of
 // the key head (q then k, 2*d_k channels) is handled by d_k/4 lanes of 8
 // channels; each L2 norm is a DPP reduction over d_k/8 lanes.  The normalised
 // rows (split hi/lo, zero past the sequence end) are gathered in LDS, then
@@ -342,10 +343,10 @@ qknorm_kernel(const PrefillArgs p)
     constexpr int WIN = TPL + 3;             // raw rows a lane reads
     constexpr int KS = DK / 32, MTS = DK / 16;
     constexpr int RS = DK + 8;               // LDS row stride (bf16)
-    const int c = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
+    const int hk = blockIdx.y, n = blockIdx.z;
     const int s0 = p.cu[n], L = p.cu[n + 1] - s0;
-    if (c * kC >= L) return;
-    const int slot = s0 / kC + n + c;
+    const int cfirst = blockIdx.x * kQkChunks;
+    if (cfirst * kC >= L) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = lane / LPT, ll = lane % LPT;
     const bool isk = ll >= DK / 8;           // q lanes, then k lanes (DK/8 each)
@@ -356,108 +357,125 @@ qknorm_kernel(const PrefillArgs p)
     // [q,k][hi,lo][row][RS]
     __bf16 *sQK = reinterpret_cast<__bf16 *>(smem);
     const int r0 = kC / 4 * wave + TPL * sub; // first chunk row of this lane
-    const int tl0 = c * kC + r0;              // its position in the sequence
+    const int col = lane & 15, kq = lane >> 4;
+    auto row = [&](int m, int hl, int r) { return sQK + ((2 * m + hl) * kC + r) * RS; };
 
-    // Every raw input the lane needs (8 channels per row), loaded at once
-    // (positions clamped into the sequence; positions before its start are
-    // replaced below).
+    // Every raw input the lane needs for a chunk (8 channels per row),
+    // loaded at once (positions clamped into the sequence; positions before
+    // its start are replaced when used).  The raw inputs of all the
+    // workgroup's chunks are put in flight first, so the later chunks' loads
+    // overlap the earlier chunks' work and stores.
     typedef typename RawAct<TIn>::type RawT;
-    RawT raw[WIN][2];
+    auto load_raw = [&](int c, RawT (&raw)[WIN][2]) {
+        const int tl0 = c * kC + r0;
 #pragma unroll
-    for (int j = 0; j < WIN; ++j) {
-        const int tau = min(max(tl0 - 3 + j, 0), L - 1);
-        const size_t base = (size_t)(s0 + tau) * p.conv_dim + ch;
-        raw[j][0] = RawAct<TIn>::load(x, base);
-        raw[j][1] = RawAct<TIn>::load(x, base + 4);
-    }
+        for (int j = 0; j < WIN; ++j) {
+            const int tau = min(max(tl0 - 3 + j, 0), L - 1);
+            const size_t base = (size_t)(s0 + tau) * p.conv_dim + ch;
+            raw[j][0] = RawAct<TIn>::load(x, base);
+            raw[j][1] = RawAct<TIn>::load(x, base + 4);
+        }
+    };
+    RawT rawA[WIN][2], rawB[WIN][2];
+    const bool second = (cfirst + 1) * kC < L;
+    load_raw(cfirst, rawA);
+    if (second) load_raw(cfirst + 1, rawB);
     float w0[4][4], w1[4][4];
     load_taps4(p, ch, w0);
     load_taps4(p, ch + 4, w1);
     const float extra = isk ? 1.0f : rsqrtf((float)DK);
-    f32x4 xv[WIN][2];
+
+    auto process = [&](int c, const RawT (&raw)[WIN][2]) {
+        const int slot = s0 / kC + n + c;
+        const int tl0 = c * kC + r0; // position in the sequence of row r0
+        f32x4 xv[WIN][2];
 #pragma unroll
-    for (int j = 0; j < WIN; ++j) {
-        xv[j][0] = RawAct<TIn>::to_f32(raw[j][0]);
-        xv[j][1] = RawAct<TIn>::to_f32(raw[j][1]);
-    }
-    if (tl0 < 3) { // the first rows of a sequence reach into its history
+        for (int j = 0; j < WIN; ++j) {
+            xv[j][0] = RawAct<TIn>::to_f32(raw[j][0]);
+            xv[j][1] = RawAct<TIn>::to_f32(raw[j][1]);
+        }
+        if (tl0 < 3) { // the first rows of a sequence reach into its history
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
-            if (tl0 - 3 + j < 0) {
-                xv[j][0] = raw4(p, x, n, s0, tl0 - 3 + j, ch);
-                xv[j][1] = raw4(p, x, n, s0, tl0 - 3 + j, ch + 4);
+            for (int j = 0; j < 3; ++j)
+                if (tl0 - 3 + j < 0) {
+                    xv[j][0] = raw4(p, x, n, s0, tl0 - 3 + j, ch);
+                    xv[j][1] = raw4(p, x, n, s0, tl0 - 3 + j, ch + 4);
+                }
+        }
+
+#pragma unroll
+        for (int k = 0; k < TPL; ++k) {
+            const int r = r0 + k, tl = tl0 + k;
+            const f32x4 xa[4] = {xv[k][0], xv[k + 1][0], xv[k + 2][0], xv[k + 3][0]};
+            const f32x4 xb[4] = {xv[k][1], xv[k + 1][1], xv[k + 2][1], xv[k + 3][1]};
+            const f32x4 ca = conv4(w0, xa), cb = conv4(w1, xb);
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += ca[e] * ca[e] + cb[e] * cb[e];
+            ss = row_sum<DK / 8>(ss);
+            const float sc = tl < L ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = ca[e] * sc;
+                v[4 + e] = cb[e] * sc;
             }
-    }
-
-#pragma unroll
-    for (int k = 0; k < TPL; ++k) {
-        const int r = r0 + k, tl = tl0 + k;
-        const f32x4 xa[4] = {xv[k][0], xv[k + 1][0], xv[k + 2][0], xv[k + 3][0]};
-        const f32x4 xb[4] = {xv[k][1], xv[k + 1][1], xv[k + 2][1], xv[k + 3][1]};
-        const f32x4 ca = conv4(w0, xa), cb = conv4(w1, xb);
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ss += ca[e] * ca[e] + cb[e] * cb[e];
-        ss = row_sum<DK / 8>(ss);
-        const float sc = tl < L ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[e] = ca[e] * sc;
-            v[4 + e] = cb[e] * sc;
+            const Frag f = split8(v);
+            __bf16 *dst = sQK + ((isk ? 2 : 0) * kC + r) * RS + c8;
+            *reinterpret_cast<bf16x8 *>(dst) = f.hi;
+            *reinterpret_cast<bf16x8 *>(dst + kC * RS) = f.lo;
         }
-        const Frag f = split8(v);
-        __bf16 *dst = sQK + ((isk ? 2 : 0) * kC + r) * RS + c8;
-        *reinterpret_cast<bf16x8 *>(dst) = f.hi;
-        *reinterpret_cast<bf16x8 *>(dst + kC * RS) = f.lo;
-    }
-    __syncthreads();
+        lds_barrier();
 
-    const int col = lane & 15, kq = lane >> 4;
-    auto row = [&](int m, int hl, int r) { return sQK + ((2 * m + hl) * kC + r) * RS; };
+        // q^ fragments, d_k-permuted order.
+        __bf16 *qf = p.ws_qf + ((size_t)hk * p.ns + slot) * (2 * kC * DK);
+        for (int f = wave; f < 4 * KS * 2; f += 4) {
+            const int hl = f & 1, s = (f >> 1) % KS, rb = (f >> 1) / KS;
+            const __bf16 *src = row(0, hl, 16 * rb + col) + 32 * s + 4 * kq;
+            const uint2 x0 = *reinterpret_cast<const uint2 *>(src);
+            const uint2 x1 = *reinterpret_cast<const uint2 *>(src + 16);
+            *reinterpret_cast<u32x4 *>(qf + (size_t)f * 512 + lane * 8) = u32x4{x0.x, x0.y, x1.x, x1.y};
+        }
+        // k^T fragments, natural (token) order: lane (i, q) of fragment
+        // (rb, s) gathers k^[32 s + 8 q + e][16 rb + i].
+        __bf16 *ktf = p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK);
+        for (int f = wave; f < MTS * 4; f += 4) {
+            const int hl = f & 1, s = (f >> 1) & 1, rb = f >> 2;
+            const int i = 16 * rb + col, t = 32 * s + 8 * kq;
+            u32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = pack2(row(1, hl, t + 2 * e)[i], row(1, hl, t + 2 * e + 1)[i]);
+            *reinterpret_cast<u32x4 *>(ktf + (size_t)f * 512 + lane * 8) = v;
+        }
+        // Gram tiles (mt, nt), nt <= mt, listed row by row; wave w takes
+        // tiles w, w+4, w+8.
+        float *gram = p.ws_gram + ((size_t)hk * p.ns + slot) * (2 * kC * kC);
+        for (int tile = wave; tile < 10; tile += 4) {
+            const int mt = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
+            const int nt = tile - mt * (mt + 1) / 2;
+            f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = akk;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int o = 32 * s + 8 * kq;
+                const Frag bk = frag_at(row(1, 0, 16 * nt + col) + o, row(1, 1, 16 * nt + col) + o);
+                const Frag ak = frag_at(row(1, 0, 16 * mt + col) + o, row(1, 1, 16 * mt + col) + o);
+                const Frag aq = frag_at(row(0, 0, 16 * mt + col) + o, row(0, 1, 16 * mt + col) + o);
+                akk = mma3(ak, bk, akk);
+                aqk = mma3(aq, bk, aqk);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * mt + 4 * kq + e, j = 16 * nt + col;
+                gram[i * kC + j] = akk[e];
+                gram[kC * kC + i * kC + j] = aqk[e];
+            }
+        }
+    };
 
-    // q^ fragments, d_k-permuted order.
-    __bf16 *qf = p.ws_qf + ((size_t)hk * p.ns + slot) * (2 * kC * DK);
-    for (int f = wave; f < 4 * KS * 2; f += 4) {
-        const int hl = f & 1, s = (f >> 1) % KS, rb = (f >> 1) / KS;
-        const __bf16 *src = row(0, hl, 16 * rb + col) + 32 * s + 4 * kq;
-        const uint2 x0 = *reinterpret_cast<const uint2 *>(src);
-        const uint2 x1 = *reinterpret_cast<const uint2 *>(src + 16);
-        *reinterpret_cast<u32x4 *>(qf + (size_t)f * 512 + lane * 8) = u32x4{x0.x, x0.y, x1.x, x1.y};
-    }
-    // k^T fragments, natural (token) order: lane (i, q) of fragment (rb, s)
-    // gathers k^[32 s + 8 q + e][16 rb + i].
-    __bf16 *ktf = p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK);
-    for (int f = wave; f < MTS * 4; f += 4) {
-        const int hl = f & 1, s = (f >> 1) & 1, rb = f >> 2;
-        const int i = 16 * rb + col, t = 32 * s + 8 * kq;
-        u32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = pack2(row(1, hl, t + 2 * e)[i], row(1, hl, t + 2 * e + 1)[i]);
-        *reinterpret_cast<u32x4 *>(ktf + (size_t)f * 512 + lane * 8) = v;
-    }
-    // Gram tiles (mt, nt), nt <= mt, listed row by row; wave w takes tiles
-    // w, w+4, w+8.
-    float *gram = p.ws_gram + ((size_t)hk * p.ns + slot) * (2 * kC * kC);
-    for (int tile = wave; tile < 10; tile += 4) {
-        const int mt = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3;
-        const int nt = tile - mt * (mt + 1) / 2;
-        f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = akk;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int o = 32 * s + 8 * kq;
-            const Frag bk = frag_at(row(1, 0, 16 * nt + col) + o, row(1, 1, 16 * nt + col) + o);
-            const Frag ak = frag_at(row(1, 0, 16 * mt + col) + o, row(1, 1, 16 * mt + col) + o);
-            const Frag aq = frag_at(row(0, 0, 16 * mt + col) + o, row(0, 1, 16 * mt + col) + o);
-            akk = mma3(ak, bk, akk);
-            aqk = mma3(aq, bk, aqk);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * mt + 4 * kq + e, j = 16 * nt + col;
-            gram[i * kC + j] = akk[e];
-            gram[kC * kC + i * kC + j] = aqk[e];
-        }
+    process(cfirst, rawA);
+    if (second) {
+        lds_barrier(); // the first chunk's LDS reads are done
+        process(cfirst + 1, rawB);
     }
 }
 
@@ -1083,7 +1101,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
 {
     hipError_t e;
     if (max_len > 0) {
-        const dim3 grid_k((max_len + kC - 1) / kC, a.h_k, n_seq);
+        const int nch_max = (max_len + kC - 1) / kC;
+        const dim3 grid_k((nch_max + kQkChunks - 1) / kQkChunks, a.h_k, n_seq);
         hipLaunchKernelGGL((qknorm_kernel<TIn, DK>), grid_k, dim3(256), qknorm_smem_bytes<DK>(), s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const dim3 grid_v((max_len + kC - 1) / kC, a.h_v, n_seq);
