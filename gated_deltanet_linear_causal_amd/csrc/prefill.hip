@@ -901,16 +901,19 @@ scan_kernel(const PrefillArgs p, int slices)
                 Dv = mma3(cW[s], frag_at(&sS[par][0][o], &sS[par][1][o]), Dv);
             }
             GDN_CHAIN_LOAD1(cn)
+            {
+                // this lane's 4 consecutive tokens: 8-byte writes
+                __bf16 dh[4], dl[4], eh[4], el[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * w + 4 * kq + e;
-                __bf16 h, l;
-                split1(Dv[e], h, l);
-                sD[par][0][col * RT + t] = h;
-                sD[par][1][col * RT + t] = l;
-                split1(Dv[e] * cEGC[e], h, l);
-                sE[0][col * RT + t] = h;
-                sE[1][col * RT + t] = l;
+                for (int e = 0; e < 4; ++e) {
+                    split1(Dv[e], dh[e], dl[e]);
+                    split1(Dv[e] * cEGC[e], eh[e], el[e]);
+                }
+                const int o = col * RT + 16 * w + 4 * kq;
+                *reinterpret_cast<uint2 *>(&sD[par][0][o]) = make_uint2(pack2(dh[0], dh[1]), pack2(dh[2], dh[3]));
+                *reinterpret_cast<uint2 *>(&sD[par][1][o]) = make_uint2(pack2(dl[0], dl[1]), pack2(dl[2], dl[3]));
+                *reinterpret_cast<uint2 *>(&sE[0][o]) = make_uint2(pack2(eh[0], eh[1]), pack2(eh[2], eh[3]));
+                *reinterpret_cast<uint2 *>(&sE[1][o]) = make_uint2(pack2(el[0], el[1]), pack2(el[2], el[3]));
             }
             GDN_CHAIN_LOAD1B(cn)
             lds_barrier();
