@@ -89,7 +89,10 @@ def _counter_rows(directory):
         return list(csv.DictReader(f))
 
 
-def write_traffic(fetch_dir, write_dir):
+N_XCD, N_CU, SIMD_PER_CU = 8, 256, 4   # MI355X
+
+
+def write_traffic(fetch_dir, write_dir, mfma_dir=None):
     """Summarise two rocprofv3 --pmc runs of `bench.py --calib-copy` (one
     with FETCH_SIZE, one with WRITE_SIZE) into per-launch HBM bytes.  Each
     counter is scaled by what it counts for the calibration copy (the largest
@@ -119,9 +122,45 @@ def write_traffic(fetch_dir, write_dir):
         out["kernels"][k] = {"fetch_bytes": round(f), "write_bytes": round(w), "bytes_per_launch": round(f + w)}
     pre = [out["kernels"][k] for k in PREFILL_KERNELS if k in out["kernels"]]
     out["kernels"]["prefill_call"] = {"bytes_per_launch": sum(e["bytes_per_launch"] for e in pre)}
+    if mfma_dir:
+        # MFMA-busy fraction: SQ_VALU_MFMA_BUSY_CYCLES over every matrix pipe
+        # (CUs x SIMDs) for the kernel's duration (GRBM_GUI_ACTIVE sums the
+        # XCDs).
+        acc = {}
+        for r in _counter_rows(mfma_dir):
+            key = next((k for k in PREFILL_KERNELS + ("decode_kernel",) if k in r["Kernel_Name"]), None)
+            if key is None:
+                continue
+            e = acc.setdefault(key, {})
+            e.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        busy_all = gui_all = 0.0
+        for k, e in acc.items():
+            busy = sum(e.get("SQ_VALU_MFMA_BUSY_CYCLES", [0.0])) / max(1, len(e.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])))
+            gui = sum(e.get("GRBM_GUI_ACTIVE", [0.0])) / max(1, len(e.get("GRBM_GUI_ACTIVE", [0])))
+            pipes = gui / N_XCD * N_CU * SIMD_PER_CU
+            if k in out["kernels"] and pipes > 0:
+                out["kernels"][k]["mfma_busy"] = round(busy / pipes, 4)
+            if k in PREFILL_KERNELS:
+                busy_all += busy
+                gui_all += gui
+        if gui_all > 0:
+            out["kernels"]["prefill_call"]["mfma_busy"] = round(busy_all / (gui_all / N_XCD * N_CU * SIMD_PER_CU), 4)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def load_counter(kernel, field):
+    """A per-kernel field of profiles/traffic_counters.json, or None if the
+    counters were taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha") != sources_hash():
+        return None
+    return rec.get("kernels", {}).get(kernel, {}).get(field)
 
 
 def load_traffic(kernel):
@@ -174,9 +213,11 @@ def main():
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into "
                          "profiles/traffic_counters.json and exit")
+    ap.add_argument("--mfma-dir", help="with --write-traffic: a rocprofv3 run with "
+                    "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(*args.write_traffic, mfma_dir=args.mfma_dir)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -292,6 +333,7 @@ def main():
                "traffic": load_traffic("prefill_call"),
                "algorithmic_flops_per_launch": pflops,
                "duration_us": round(pf_ms * 1e3, 2), "launches_timed": args.steps,
+               "mfma_busy": load_counter("prefill_call", "mfma_busy"),
                "hbm_frac": round(pbytes / (pf_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     # the kernel that takes most of a step's time
     dominant = roof_pf if pf_ms >= dc_ms * n_sets else roof_dec
