@@ -55,6 +55,26 @@ __device__ __forceinline__ void lds_sync()
     asm volatile("" ::: "memory");
 }
 
+// Raw activation values, converted to fp32 only where they are used (a
+// conversion right after the load would wait for it).
+__device__ __forceinline__ float act_to_f32(float v) { return v; }
+__device__ __forceinline__ float act_to_f32(bf16_t v) { return bf16_bits_to_f32(v); }
+template <typename T> struct RawQuad;
+template <> struct RawQuad<float> {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    __device__ __forceinline__ void load(const float *p) { v = *reinterpret_cast<const float4 *>(p); }
+    __device__ __forceinline__ float4 to_f32() const { return v; }
+};
+template <> struct RawQuad<bf16_t> {
+    uint2 v = make_uint2(0u, 0u);
+    __device__ __forceinline__ void load(const bf16_t *p) { v = *reinterpret_cast<const uint2 *>(p); }
+    __device__ __forceinline__ float4 to_f32() const
+    {
+        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    }
+};
+
 template <typename TIn, int DK, int DV, int NSLOT>
 __global__ void __launch_bounds__(2 * DV * NSLOT)
 decode_kernel(const DecodeArgs p)
@@ -112,6 +132,22 @@ decode_kernel(const DecodeArgs p)
     // loaded when used).
     float cx = 0.0f, ch0 = 0.0f, ch1 = 0.0f, ch2 = 0.0f;
     float cw[4] = {0.f, 0.f, 0.f, 0.f};
+    const float4 w4 = *reinterpret_cast<const float4 *>(p.norm_w + 4 * c4); // same for every head
+    // The first pass's gate inputs and z of a unit, also loaded one unit
+    // ahead and kept as raw values until used.
+    const TIn *pa = static_cast<const TIn *>(p.a), *pb = static_cast<const TIn *>(p.b);
+    const TIn *pz = static_cast<const TIn *>(p.z);
+    TIn nb = TIn(0), na = TIn(0);
+    float nalog = 0.0f, ndtb = 0.0f;
+    RawQuad<TIn> nz;
+    auto load_gates = [&](int u) {
+        const int bs = u / p.h_k, hv = (u % p.h_k) * group + slot;
+        nb = pb[(size_t)bs * p.h_v + hv];
+        na = pa[(size_t)bs * p.h_v + hv];
+        nalog = p.a_log[hv];
+        ndtb = p.dt_bias[hv];
+        if (rg == 0) nz.load(pz + (size_t)bs * p.value_dim + (size_t)hv * DV + 4 * c4);
+    };
     auto load_conv = [&](int u) {
         if (tid < nch) {
             const int bs = u / p.h_k, ch = channel(u, tid);
@@ -157,23 +193,20 @@ decode_kernel(const DecodeArgs p)
             for (int j = 0; j < K; ++j) w[j] = p.conv_w[(size_t)ch * K + j];
             conv_one(u, l, load_act(qkv, (size_t)bs * CD + ch), prev, w);
         }
-        // Gates, z and norm weights of the first pass.
-        const TIn *pa = static_cast<const TIn *>(p.a), *pb = static_cast<const TIn *>(p.b);
-        float g_b = 0.0f, g_a = 0.0f, g_alog = 0.0f, g_dtb = 0.0f;
-        float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f), w4 = z4;
+        // Gates and z of the first pass (prefetched), of later passes loaded
+        // when used.
+        float g_b = act_to_f32(nb), g_a = act_to_f32(na), g_alog = nalog, g_dtb = ndtb;
+        float4 z4 = nz.to_f32();
         auto load_pass = [&](int hv) {
             g_b = load_act(pb, (size_t)bs * p.h_v + hv);
             g_a = load_act(pa, (size_t)bs * p.h_v + hv);
             g_alog = p.a_log[hv];
             g_dtb = p.dt_bias[hv];
-            if (rg == 0) {
-                z4 = load_act4(static_cast<const TIn *>(p.z), (size_t)bs * p.value_dim + (size_t)hv * DV + 4 * c4);
-                w4 = *reinterpret_cast<const float4 *>(p.norm_w + 4 * c4);
-            }
+            if (rg == 0) z4 = load_act4(pz, (size_t)bs * p.value_dim + (size_t)hv * DV + 4 * c4);
         };
-        load_pass(hk * group + slot);
         asm volatile("" ::: "memory");
         if (u + G < p.units) {
+            load_gates(u + G);
             load_conv(u + G);
             load_state(s_next, u + G, slot);
         }
@@ -271,6 +304,7 @@ decode_kernel(const DecodeArgs p)
     f32x4 sa[RPT], sb[RPT];
     int u = blockIdx.x;
     if (u < p.units) {
+        load_gates(u);
         load_conv(u);
         load_state(sa, u, slot);
     }
