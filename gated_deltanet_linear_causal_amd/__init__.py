@@ -20,6 +20,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 
 GDN_BF16, GDN_F32 = 0, 1
 GDN_GATE_SILU, GDN_GATE_SIGMOID = 0, 1
+GDN_HEADS_GROUPED, GDN_HEADS_TILED = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_EUNSUPPORTED",
           3: "GDN_EWORKSPACE", 4: "GDN_EHIP"}
 CHUNK = 64
@@ -36,12 +37,14 @@ class _Config(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("conv_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
-                ("norm_eps", ctypes.c_float), ("l2_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("l2_eps", ctypes.c_float),
+                ("head_map", ctypes.c_int32)]
 
 
 class _Params(ctypes.Structure):
     _fields_ = [("conv_w", ctypes.c_void_p), ("a_log", ctypes.c_void_p),
-                ("dt_bias", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
+                ("dt_bias", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("decay_coef", ctypes.c_void_p)]
 
 
 _VP, _I32 = ctypes.c_void_p, ctypes.c_int32
@@ -50,6 +53,10 @@ _SIGNATURES = {
                                        _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
     "gdn_decode_step": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
                                        _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "gdn_decode_multi": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
+                                        _I32, _I32] + [_VP] * 12),
+    "gdn_rewind": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
+                                  _I32, _I32] + [_VP] * 9),
     "gdn_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Config), _I32, _I32,
                                                       _I32]),
     "gdn_prefill_chunked": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
@@ -99,6 +106,7 @@ class Config:
     gate: str = "silu"
     norm_eps: float = 1e-6
     l2_eps: float = 1e-6
+    head_map: str = "grouped"   # "grouped" (hv // group) or "tiled" (hv % h_k)
 
     @property
     def conv_dim(self):
@@ -117,10 +125,13 @@ class Config:
             raise ValueError(f"unsupported dtype {dt}")
         if self.gate not in ("silu", "sigmoid"):
             raise ValueError(f"unknown gate {self.gate!r}")
+        if self.head_map not in ("grouped", "tiled"):
+            raise ValueError(f"unknown head_map {self.head_map!r}")
         return _Config(self.h_k, self.h_v, self.d_k, self.d_v, self.conv_k,
                        code(self.act_dtype), code(self.out_dtype),
                        GDN_GATE_SIGMOID if self.gate == "sigmoid" else GDN_GATE_SILU,
-                       self.norm_eps, self.l2_eps)
+                       self.norm_eps, self.l2_eps,
+                       GDN_HEADS_TILED if self.head_map == "tiled" else GDN_HEADS_GROUPED)
 
 
 def _ptr(t):
@@ -141,12 +152,21 @@ def _check(t, name, shape, dtype, device=True):
 
 
 def _params(cfg: Config, p: dict) -> _Params:
+    """params: conv_w, dt_bias, norm_w and exactly one of a_log (g = -exp(a_log)
+    softplus(...)) or decay_coef (g = decay_coef softplus(...))."""
     _check(p["conv_w"], "conv_w", (cfg.conv_dim, cfg.conv_k), torch.float32)
-    _check(p["a_log"], "a_log", (cfg.h_v,), torch.float32)
+    a_log, coef = p.get("a_log"), p.get("decay_coef")
+    if (a_log is None) == (coef is None):
+        raise ValueError("give exactly one of a_log and decay_coef")
+    if a_log is not None:
+        _check(a_log, "a_log", (cfg.h_v,), torch.float32)
+    else:
+        _check(coef, "decay_coef", (cfg.h_v,), torch.float32)
     _check(p["dt_bias"], "dt_bias", (cfg.h_v,), torch.float32)
     _check(p["norm_w"], "norm_w", (cfg.d_v,), torch.float32)
-    return _Params(p["conv_w"].data_ptr(), p["a_log"].data_ptr(),
-                   p["dt_bias"].data_ptr(), p["norm_w"].data_ptr())
+    return _Params(p["conv_w"].data_ptr(), None if a_log is None else a_log.data_ptr(),
+                   p["dt_bias"].data_ptr(), p["norm_w"].data_ptr(),
+                   None if coef is None else coef.data_ptr())
 
 
 def _stream(stream):
@@ -211,6 +231,90 @@ def decode_step(cfg: Config, params: dict, qkv, z, a, b, conv_state, state, out=
     return out
 
 
+MAX_NEW_TOKENS = 8
+
+
+def _check_counts(n, B, device):
+    if n is None:
+        return None
+    if not isinstance(n, torch.Tensor):
+        n = torch.as_tensor(n, dtype=torch.int32)
+    n = n.to(device=device, dtype=torch.int32).contiguous()
+    if tuple(n.shape) != (B,):
+        raise ValueError(f"token counts have shape {tuple(n.shape)}, expected ({B},)")
+    return n
+
+
+def decode_multi(cfg: Config, params: dict, qkv, z, a, b, conv_state, state, out=None,
+                 n_tok=None, conv_out=None, state_out=None, ckpt=None, want_out=True,
+                 stream=None):
+    """t_new tokens per sequence in one call.  qkv [B, t_new, conv_dim],
+    z [B, t_new, value_dim], a, b [B, t_new, H_v].  The states are updated in
+    place unless conv_out / state_out are given.  n_tok: optional [B] counts
+    (first n_tok[i] tokens of sequence i).  ckpt: optional
+    [B, t_new, H_v, d_k, d_v] fp32 per-token states.  Returns out
+    [B, t_new, value_dim] (None when want_out is False)."""
+    lib = load_library()
+    B, T = qkv.shape[0], qkv.shape[1]
+    dev = qkv.device
+    _check(qkv, "qkv", (B, T, cfg.conv_dim), cfg.act_dtype)
+    _check(a, "a", (B, T, cfg.h_v), cfg.act_dtype)
+    _check(b, "b", (B, T, cfg.h_v), cfg.act_dtype)
+    sshape = (B, cfg.h_v, cfg.d_k, cfg.d_v)
+    cshape = (B, cfg.conv_k - 1, cfg.conv_dim)
+    _check(conv_state, "conv_state", cshape, torch.float32)
+    _check(state, "state", sshape, torch.float32)
+    conv_out = conv_state if conv_out is None else conv_out
+    state_out = state if state_out is None else state_out
+    _check(conv_out, "conv_out", cshape, torch.float32)
+    _check(state_out, "state_out", sshape, torch.float32)
+    if ckpt is not None:
+        _check(ckpt, "ckpt", (B, T, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
+    if want_out:
+        _check(z, "z", (B, T, cfg.value_dim), cfg.act_dtype)
+        if out is None:
+            out = torch.empty((B, T, cfg.value_dim), dtype=cfg.out_dtype, device=dev)
+        _check(out, "out", (B, T, cfg.value_dim), cfg.out_dtype)
+    else:
+        out = None
+    n = _check_counts(n_tok, B, dev)
+    c, p = cfg.c_struct(), _params(cfg, params)
+    _raise_on(lib.gdn_decode_multi(ctypes.byref(c), ctypes.byref(p), B, T, _ptr(n), _ptr(qkv),
+                                   _ptr(z) if want_out else None, _ptr(a), _ptr(b),
+                                   _ptr(conv_state), _ptr(conv_out), _ptr(state),
+                                   _ptr(state_out), _ptr(ckpt), _ptr(out), _stream(stream)))
+    return out
+
+
+def rewind(cfg: Config, params: dict, qkv_rec, a_rec, b_rec, state0, conv0, keep=None,
+           state=None, conv_state=None, stream=None):
+    """Rebuild each sequence's state from the saved state0 / conv0 by
+    replaying its first keep[i] recorded tokens (all when keep is None).
+    Returns (state, conv_state)."""
+    lib = load_library()
+    B, T = qkv_rec.shape[0], qkv_rec.shape[1]
+    dev = qkv_rec.device
+    _check(qkv_rec, "qkv_rec", (B, T, cfg.conv_dim), cfg.act_dtype)
+    _check(a_rec, "a_rec", (B, T, cfg.h_v), cfg.act_dtype)
+    _check(b_rec, "b_rec", (B, T, cfg.h_v), cfg.act_dtype)
+    sshape = (B, cfg.h_v, cfg.d_k, cfg.d_v)
+    cshape = (B, cfg.conv_k - 1, cfg.conv_dim)
+    _check(state0, "state0", sshape, torch.float32)
+    _check(conv0, "conv0", cshape, torch.float32)
+    if state is None:
+        state = torch.empty(sshape, dtype=torch.float32, device=dev)
+    if conv_state is None:
+        conv_state = torch.empty(cshape, dtype=torch.float32, device=dev)
+    _check(state, "state", sshape, torch.float32)
+    _check(conv_state, "conv_state", cshape, torch.float32)
+    n = _check_counts(keep, B, dev)
+    c, p = cfg.c_struct(), _params(cfg, params)
+    _raise_on(lib.gdn_rewind(ctypes.byref(c), ctypes.byref(p), B, T, _ptr(n), _ptr(qkv_rec),
+                             _ptr(a_rec), _ptr(b_rec), _ptr(state0), _ptr(conv0), _ptr(state),
+                             _ptr(conv_state), _stream(stream)))
+    return state, conv_state
+
+
 def prefill_workspace_bytes(cfg: Config, n_seq: int, t_total: int, chunk: int = CHUNK) -> int:
     c = cfg.c_struct()
     return int(load_library().gdn_prefill_workspace_bytes(ctypes.byref(c), n_seq, t_total,
@@ -261,5 +365,5 @@ def prefill_chunked(cfg: Config, params: dict, seqlens: SeqLens, qkv, z, a, b,
 
 
 __all__ = ["Config", "SeqLens", "GdnError", "load_library", "header_functions",
-           "conv_update", "decode_step", "prefill_workspace_bytes", "alloc_workspace",
-           "prefill_chunked", "LIB_PATH", "CHUNK"]
+           "conv_update", "decode_step", "decode_multi", "rewind", "prefill_workspace_bytes",
+           "alloc_workspace", "prefill_chunked", "LIB_PATH", "CHUNK", "MAX_NEW_TOKENS"]

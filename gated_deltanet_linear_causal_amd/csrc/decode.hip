@@ -37,10 +37,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 struct DecodeArgs {
     const void *qkv, *z, *a, *b;
     const float *conv_w, *a_log, *dt_bias, *norm_w;
+    const float *decay_coef; // when not NULL, the log-decay coefficient itself (a_log NULL)
     float *conv_state, *state;
     void *out;
     int h_k, h_v, group, conv_k, conv_dim, value_dim;
-    int gate, out_bf16;
+    int gate, out_bf16, tiled;
     float norm_eps, l2_eps;
     int units; // batch * h_k
 };
@@ -103,9 +104,11 @@ decode_kernel(const DecodeArgs p)
     f32x4 *red = reinterpret_cast<f32x4 *>(sv + group * DV); // [NSLOT][RG][C4][2]
     float *scal = reinterpret_cast<float *>(red + NSLOT * RG * C4 * 2); // [4]
 
+    // Value head of member hl of unit u's group.
+    auto vhead = [&](int u, int hl) { return value_head_of(u % p.h_k, hl, p.h_k, group, p.tiled); };
     auto state_ptr = [&](int u, int hl) {
-        const int bs = u / p.h_k, hk = u % p.h_k;
-        return p.state + ((size_t)bs * p.h_v + hk * group + hl) * DK * DV;
+        const int bs = u / p.h_k;
+        return p.state + ((size_t)bs * p.h_v + vhead(u, hl)) * DK * DV;
     };
     auto load_state = [&](f32x4 (&s)[RPT], int u, int hl) {
         const float *Sp = state_ptr(u, hl);
@@ -125,7 +128,8 @@ decode_kernel(const DecodeArgs p)
         const int hk = u % p.h_k;
         if (l < DK) return hk * DK + l;
         if (l < 2 * DK) return p.h_k * DK + hk * DK + (l - DK);
-        return 2 * p.h_k * DK + hk * group * DV + (l - 2 * DK);
+        const int lv = l - 2 * DK;
+        return 2 * p.h_k * DK + vhead(u, lv / DV) * DV + lv % DV;
     };
     // Raw input and history of this thread's first channel of a unit, loaded
     // one unit ahead (further channels, when a unit has more than NT, are
@@ -134,17 +138,20 @@ decode_kernel(const DecodeArgs p)
     float cw[4] = {0.f, 0.f, 0.f, 0.f};
     const float4 w4 = *reinterpret_cast<const float4 *>(p.norm_w + 4 * c4); // same for every head
     // The first pass's gate inputs and z of a unit, also loaded one unit
-    // ahead and kept as raw values until used.
+    // ahead and kept as raw values until used (the decay coefficient as
+    // stored: A_log, or the coefficient itself).
+    const float *coef_src = p.decay_coef ? p.decay_coef : p.a_log;
+    auto coef_of = [&](float raw) { return p.decay_coef ? raw : -expf(raw); };
     const TIn *pa = static_cast<const TIn *>(p.a), *pb = static_cast<const TIn *>(p.b);
     const TIn *pz = static_cast<const TIn *>(p.z);
     TIn nb = TIn(0), na = TIn(0);
     float nalog = 0.0f, ndtb = 0.0f;
     RawQuad<TIn> nz;
     auto load_gates = [&](int u) {
-        const int bs = u / p.h_k, hv = (u % p.h_k) * group + slot;
+        const int bs = u / p.h_k, hv = vhead(u, slot);
         nb = pb[(size_t)bs * p.h_v + hv];
         na = pa[(size_t)bs * p.h_v + hv];
-        nalog = p.a_log[hv];
+        nalog = coef_src[hv];
         ndtb = p.dt_bias[hv];
         if (rg == 0) nz.load(pz + (size_t)bs * p.value_dim + (size_t)hv * DV + 4 * c4);
     };
@@ -176,7 +183,7 @@ decode_kernel(const DecodeArgs p)
     };
 
     auto run_unit = [&](int u, f32x4 (&s)[RPT], f32x4 (&s_next)[RPT]) {
-        const int bs = u / p.h_k, hk = u % p.h_k;
+        const int bs = u / p.h_k;
         lds_sync(); // the previous unit's LDS reads are done
 
         // Causal conv + SiLU of this unit's channels, history update in
@@ -200,7 +207,7 @@ decode_kernel(const DecodeArgs p)
         auto load_pass = [&](int hv) {
             g_b = load_act(pb, (size_t)bs * p.h_v + hv);
             g_a = load_act(pa, (size_t)bs * p.h_v + hv);
-            g_alog = p.a_log[hv];
+            g_alog = coef_src[hv];
             g_dtb = p.dt_bias[hv];
             if (rg == 0) z4 = load_act4(pz, (size_t)bs * p.value_dim + (size_t)hv * DV + 4 * c4);
         };
@@ -238,7 +245,7 @@ decode_kernel(const DecodeArgs p)
         const int npass = group / NSLOT;
         for (int pass = 0; pass < npass; ++pass) {
             const int hl = pass * NSLOT + slot; // value head within the group
-            const int hv = hk * group + hl;
+            const int hv = vhead(u, hl);
             float *Sp = state_ptr(u, hl);
             if (pass > 0) {
                 load_state(s, u, hl);
@@ -246,7 +253,7 @@ decode_kernel(const DecodeArgs p)
             }
             // Gates ("cherenkov qwen4_exp/cpu.rs" fn deltanet).
             const float beta = sigmoidf_(g_b);
-            const float g = -expf(g_alog) * softplusf_(g_a + g_dtb);
+            const float g = coef_of(g_alog) * softplusf_(g_a + g_dtb);
             const float alpha = expf(g);
 
             f32x4 mk = {0.f, 0.f, 0.f, 0.f}, mq = mk;
@@ -371,6 +378,7 @@ hipError_t launch_decode(const Dims &d, const Params &p, int batch, const void *
     args.b = b;
     args.conv_w = p.conv_w;
     args.a_log = p.a_log;
+    args.decay_coef = p.decay_coef;
     args.dt_bias = p.dt_bias;
     args.norm_w = p.norm_w;
     args.conv_state = conv_state;
@@ -383,6 +391,7 @@ hipError_t launch_decode(const Dims &d, const Params &p, int batch, const void *
     args.conv_dim = d.conv_dim;
     args.value_dim = d.value_dim;
     args.gate = d.gate;
+    args.tiled = d.tiled;
     args.out_bf16 = d.out_bf16;
     args.norm_eps = d.norm_eps;
     args.l2_eps = d.l2_eps;

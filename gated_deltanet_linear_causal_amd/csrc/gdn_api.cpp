@@ -49,6 +49,8 @@ gdn_status check_config(const gdn_config *cfg, gdn::Dims &d)
         return fail(GDN_EINVAL, "out_dtype %d is not a gdn_dtype", cfg->out_dtype);
     if (cfg->gate != GDN_GATE_SILU && cfg->gate != GDN_GATE_SIGMOID)
         return fail(GDN_EINVAL, "gate %d is not a gdn_gate", cfg->gate);
+    if (cfg->head_map != GDN_HEADS_GROUPED && cfg->head_map != GDN_HEADS_TILED)
+        return fail(GDN_EINVAL, "head_map %d is not a gdn_head_map", cfg->head_map);
     if (!(cfg->norm_eps >= 0.0f) || !std::isfinite(cfg->norm_eps) || !(cfg->l2_eps >= 0.0f) ||
         !std::isfinite(cfg->l2_eps))
         return fail(GDN_EINVAL, "norm_eps and l2_eps must be finite and >= 0");
@@ -71,6 +73,7 @@ gdn_status check_config(const gdn_config *cfg, gdn::Dims &d)
     d.act_bf16 = cfg->act_dtype == GDN_BF16;
     d.out_bf16 = cfg->out_dtype == GDN_BF16;
     d.gate = cfg->gate;
+    d.tiled = cfg->head_map == GDN_HEADS_TILED;
     d.norm_eps = cfg->norm_eps;
     d.l2_eps = cfg->l2_eps;
     return GDN_OK;
@@ -79,10 +82,13 @@ gdn_status check_config(const gdn_config *cfg, gdn::Dims &d)
 gdn_status check_params(const gdn_params *p, gdn::Params &out)
 {
     if (!p) return fail(GDN_EINVAL, "params is NULL");
-    if (!p->conv_w || !p->a_log || !p->dt_bias || !p->norm_w)
-        return fail(GDN_EINVAL, "every parameter pointer must be non-NULL");
+    if (!p->conv_w || !p->dt_bias || !p->norm_w)
+        return fail(GDN_EINVAL, "conv_w, dt_bias and norm_w must be non-NULL");
+    if ((p->a_log == nullptr) == (p->decay_coef == nullptr))
+        return fail(GDN_EINVAL, "exactly one of a_log and decay_coef must be given");
     out.conv_w = p->conv_w;
     out.a_log = p->a_log;
+    out.decay_coef = p->decay_coef;
     out.dt_bias = p->dt_bias;
     out.norm_w = p->norm_w;
     return GDN_OK;
@@ -190,6 +196,119 @@ gdn_status gdn_decode_step(const gdn_config *cfg, const gdn_params *params, int3
                                          static_cast<hipStream_t>(stream)),
                       "gdn_decode_step launch");
 }
+
+} // extern "C"
+
+namespace {
+
+// Shared checks of the multi-token entry points; fills the ranges used for
+// the overlap tests.
+gdn_status check_multi(const gdn::Dims &d, int32_t batch, int32_t t_new, const void *qkv,
+                       const void *a, const void *b, const float *conv_in,
+                       const float *conv_out, const float *state_in, const float *state_out)
+{
+    if (batch < 0) return fail(GDN_EINVAL, "batch must be >= 0 (got %d)", batch);
+    if (batch > 65535) return fail(GDN_EUNSUPPORTED, "batch must be <= 65535 (got %d)", batch);
+    if (t_new < 1 || t_new > gdn::kDecodeMultiMaxTokens)
+        return fail(GDN_EUNSUPPORTED, "tokens per sequence must be in [1, %d] (got %d)",
+                    gdn::kDecodeMultiMaxTokens, t_new);
+    if (gdn::decode_multi_lds_bytes(d, t_new) > gdn::kDecodeMultiMaxLds)
+        return fail(GDN_EUNSUPPORTED,
+                    "%d tokens of %d conv channels per key head exceed the on-chip buffer",
+                    t_new, 2 * d.d_k + d.group * d.d_v);
+    if (batch == 0) return GDN_OK;
+    if (!qkv || !a || !b || !state_in || !state_out ||
+        (d.conv_k > 1 && (!conv_in || !conv_out)))
+        return fail(GDN_EINVAL,
+                    "qkv, a, b, the states (and the conv histories when K > 1) are required");
+    return GDN_OK;
+}
+
+gdn_status launch_multi_checked(const gdn::Dims &d, const gdn::Params &p, int32_t batch,
+                                int32_t t_new, const int32_t *n_tok, const void *qkv,
+                                const void *z, const void *a, const void *b,
+                                const float *conv_in, float *conv_out, const float *state_in,
+                                float *state_out, float *ckpt, void *out, void *stream,
+                                const char *what)
+{
+    const size_t esz = d.act_bf16 ? 2 : 4, osz = d.out_bf16 ? 2 : 4;
+    const size_t tok = (size_t)batch * t_new;
+    const size_t sbytes = (size_t)batch * d.h_v * d.d_k * d.d_v * 4;
+    const size_t cbytes = (size_t)batch * (d.conv_k - 1) * d.conv_dim * 4;
+    const Range ins[] = {{qkv, tok * d.conv_dim * esz},
+                         {z, tok * d.value_dim * esz},
+                         {a, tok * d.h_v * esz},
+                         {b, tok * d.h_v * esz},
+                         {n_tok, (size_t)batch * 4}};
+    const Range rsi{state_in, sbytes}, rso{state_out, sbytes};
+    const Range rci{conv_in, cbytes}, rco{conv_out, cbytes};
+    const Range rck{ckpt, tok * d.h_v * d.d_k * d.d_v * 4};
+    const Range ro{out, tok * d.value_dim * osz};
+    const Range outs[] = {rso, rco, rck, ro};
+    for (const Range &o : outs)
+        for (const Range &r : ins)
+            if (overlap(o, r)) return fail(GDN_EINVAL, "outputs and states must not overlap the inputs");
+    if (overlap(rso, rco) || overlap(rso, rck) || overlap(rso, ro) || overlap(rco, rck) ||
+        overlap(rco, ro) || overlap(rck, ro) || overlap(rck, rsi) || overlap(rck, rci) ||
+        overlap(ro, rsi) || overlap(ro, rci) || overlap(rso, rci) || overlap(rco, rsi))
+        return fail(GDN_EINVAL, "out, checkpoints, state_out and conv_out must be disjoint buffers");
+    if (overlap(rsi, rso) && state_in != state_out)
+        return fail(GDN_EINVAL, "state_out may equal state_in but must not partially overlap it");
+    if (overlap(rci, rco) && conv_in != conv_out)
+        return fail(GDN_EINVAL, "conv_out may equal conv_in but must not partially overlap it");
+    return hip_status(gdn::launch_decode_multi(d, p, batch, t_new, n_tok, qkv, z, a, b, conv_in,
+                                               conv_out, state_in, state_out, ckpt, out,
+                                               static_cast<hipStream_t>(stream)),
+                      what);
+}
+
+} // namespace
+
+extern "C" {
+
+gdn_status gdn_decode_multi(const gdn_config *cfg, const gdn_params *params, int32_t batch,
+                            int32_t t_new, const int32_t *n_tok_dev, const void *qkv,
+                            const void *z, const void *a, const void *b, const float *conv_in,
+                            float *conv_out, const float *state_in, float *state_out,
+                            float *state_ckpt, void *out, void *stream)
+{
+    gdn::Dims d;
+    gdn::Params p;
+    gdn_status st;
+    if ((st = check_config(cfg, d)) != GDN_OK) return st;
+    if ((st = check_params(params, p)) != GDN_OK) return st;
+    if ((st = check_multi(d, batch, t_new, qkv, a, b, conv_in, conv_out, state_in, state_out)) !=
+        GDN_OK)
+        return st;
+    if (batch == 0) return ok();
+    if (out && !z) return fail(GDN_EINVAL, "z is required when out is given");
+    return launch_multi_checked(d, p, batch, t_new, n_tok_dev, qkv, out ? z : nullptr, a, b,
+                                conv_in, conv_out, state_in, state_out, state_ckpt, out, stream,
+                                "gdn_decode_multi launch");
+}
+
+gdn_status gdn_rewind(const gdn_config *cfg, const gdn_params *params, int32_t batch,
+                      int32_t t_rec, const int32_t *keep_dev, const void *qkv_rec,
+                      const void *a_rec, const void *b_rec, const float *state0,
+                      const float *conv0, float *state, float *conv_state, void *stream)
+{
+    gdn::Dims d;
+    gdn::Params p;
+    gdn_status st;
+    if ((st = check_config(cfg, d)) != GDN_OK) return st;
+    if ((st = check_params(params, p)) != GDN_OK) return st;
+    if ((st = check_multi(d, batch, t_rec, qkv_rec, a_rec, b_rec, conv0, conv_state, state0,
+                          state)) != GDN_OK)
+        return st;
+    if (batch == 0) return ok();
+    return launch_multi_checked(d, p, batch, t_rec, keep_dev, qkv_rec, nullptr, a_rec, b_rec,
+                                conv0, conv_state, state0, state, nullptr, nullptr, stream,
+                                "gdn_rewind launch");
+}
+
+} // extern "C"
+
+extern "C" {
 
 size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seq, int32_t t_total,
                                    int32_t chunk)

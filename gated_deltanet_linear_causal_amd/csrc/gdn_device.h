@@ -74,6 +74,28 @@ __device__ __forceinline__ float gatef_(float z, int sigmoid_gate)
     return sigmoid_gate ? sigmoidf_(z) : siluf_(z);
 }
 
+// Key head read by value head hv: contiguous groups of H_v/H_k value heads
+// per key head, or the tiled order hv mod H_k of GGUF conversions ("oxinfer
+// 0.0.5 src/qwen.rs", DeltaRule::run).
+__device__ __forceinline__ int key_head_of(int hv, int h_k, int group, int tiled)
+{
+    return tiled ? hv % h_k : hv / group;
+}
+
+// Value head of the hl-th member (0 <= hl < H_v/H_k) of key head hk's group.
+__device__ __forceinline__ int value_head_of(int hk, int hl, int h_k, int group, int tiled)
+{
+    return tiled ? hl * h_k + hk : hk * group + hl;
+}
+
+// Coefficient of softplus in the log-decay g of value head hv: -exp(A_log),
+// or the coefficient itself when a layer stores it directly (GGUF ssm_a;
+// "oxinfer 0.0.5 src/qwen.rs", weight loading).
+__device__ __forceinline__ float decay_coef_of(const float *a_log, const float *decay_coef, int hv)
+{
+    return decay_coef ? decay_coef[hv] : -expf(a_log[hv]);
+}
+
 // Sum over the lanes of an aligned group of W lanes (W a power of two <= 64).
 template <int W> __device__ __forceinline__ float group_sum(float v)
 {

@@ -16,11 +16,13 @@ struct Dims {
     int act_bf16;   // 1: activations are bf16, 0: fp32
     int out_bf16;   // 1: output is bf16, 0: fp32
     int gate;       // 0: SiLU, 1: sigmoid
+    int tiled;      // 0: key head hv / group, 1: key head hv % h_k
     float norm_eps, l2_eps;
 };
 
 struct Params {
     const float *conv_w, *a_log, *dt_bias, *norm_w;
+    const float *decay_coef; // replaces -exp(a_log) when not NULL (a_log is then NULL)
 };
 
 hipError_t launch_conv_update(const Dims &d, const Params &p, int n_seq, int max_len,
@@ -30,6 +32,17 @@ hipError_t launch_conv_update(const Dims &d, const Params &p, int n_seq, int max
 hipError_t launch_decode(const Dims &d, const Params &p, int batch, const void *qkv,
                          const void *z, const void *a, const void *b, float *conv_state,
                          float *state, void *out, hipStream_t s);
+
+// Several new tokens per sequence (at most kDecodeMultiMaxTokens), and the
+// replay of recorded tokens from a saved state (out == NULL).
+constexpr int kDecodeMultiMaxTokens = 8;
+constexpr size_t kDecodeMultiMaxLds = 65536;
+size_t decode_multi_lds_bytes(const Dims &d, int t_new);
+hipError_t launch_decode_multi(const Dims &d, const Params &p, int batch, int t_new,
+                               const int32_t *n_tok, const void *qkv, const void *z,
+                               const void *a, const void *b, const float *conv_in,
+                               float *conv_out, const float *state_in, float *state_out,
+                               float *ckpt, void *out, hipStream_t s);
 
 // Chunked prefill.  Workspace layout and size are owned by prefill.hip.
 size_t prefill_workspace_bytes(const Dims &d, int n_seq, int t_total);

@@ -243,6 +243,7 @@ size_t prefill_workspace_bytes(const Dims &d, int n_seq, int t_total)
 struct PrefillArgs {
     const void *qkv, *z, *a, *b;
     const float *conv_w, *a_log, *dt_bias, *norm_w;
+    const float *decay_coef; // when not NULL, the log-decay coefficient itself (a_log NULL)
     const int32_t *cu;
     const float *state_in;
     float *state_out;
@@ -253,7 +254,7 @@ struct PrefillArgs {
     float *ws_gram, *ws_uf, *ws_gf, *ws_o;
     int ns, t_total;
     int h_k, h_v, d_v, group, conv_k, conv_dim, value_dim;
-    int gate, out_bf16;
+    int gate, out_bf16, tiled;
     float norm_eps, l2_eps;
 };
 
@@ -507,7 +508,7 @@ tri_kernel(const PrefillArgs p)
     if (c * kC >= L) return;
     const int t0 = s0 + c * kC;
     const int Lc = min(kC, L - c * kC);
-    const int hk = hv / p.group;
+    const int hk = key_head_of(hv, p.h_k, p.group, p.tiled);
     const int slot = s0 / kC + n + c;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, kq = lane >> 4;
@@ -547,7 +548,7 @@ tri_kernel(const PrefillArgs p)
         float beta = 0.0f, g = 0.0f;
         if (lane < Lc) {
             beta = sigmoidf_(b_raw);
-            g = -expf(p.a_log[hv]) * softplusf_(a_raw + p.dt_bias[hv]);
+            g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplusf_(a_raw + p.dt_bias[hv]);
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -809,7 +810,7 @@ scan_kernel(const PrefillArgs p, int slices)
         }
     }
     const int n = hidx / p.h_v, hv = hidx % p.h_v;
-    const int hk = hv / p.group;
+    const int hk = key_head_of(hv, p.h_k, p.group, p.tiled);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int w = wave & 3;
@@ -1178,6 +1179,7 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.b = b;
     A.conv_w = pr.conv_w;
     A.a_log = pr.a_log;
+    A.decay_coef = pr.decay_coef;
     A.dt_bias = pr.dt_bias;
     A.norm_w = pr.norm_w;
     A.cu = cu_dev;
@@ -1204,6 +1206,7 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.conv_dim = d.conv_dim;
     A.value_dim = d.value_dim;
     A.gate = d.gate;
+    A.tiled = d.tiled;
     A.out_bf16 = d.out_bf16;
     A.norm_eps = d.norm_eps;
     A.l2_eps = d.l2_eps;

@@ -33,6 +33,7 @@ class Dims:
     d_v: int
     conv_k: int = 4
     gate: str = "silu"
+    head_map: str = "grouped"      # key head of value head hv: hv // group or hv % h_k
 
     @property
     def conv_dim(self) -> int:
@@ -98,6 +99,14 @@ def make_params(gen, dims: Dims, decay: str = "strong") -> dict:
     norm_w = 1.0 + _normal(gen, (dims.d_v,), 0.1)
     return {"conv_w": conv_w, "a_log": a_log, "dt_bias": dt_bias,
             "norm_w": norm_w}
+
+
+def with_decay_coef(params: dict) -> dict:
+    """The same parameters with the decay given as the coefficient
+    -exp(A_log) itself (rounded once to float32) instead of A_log."""
+    out = {k: v for k, v in params.items() if k != "a_log"}
+    out["decay_coef"] = (-torch.exp(params["a_log"].double())).float()
+    return out
 
 
 def make_case(dims: Dims, lengths, act_dtype="bf16", seed=0, decay="strong",

@@ -13,8 +13,9 @@
  *   o     = S^T q^                                      (updated state)
  *   y     = o (mean_{d_v} o^2 + norm_eps)^-1/2 * norm_w * gate(z)
  *
- * with value head hv reading key head hv / (H_v / H_k), S a per-(sequence,
- * value head) fp32 matrix [d_k][d_v], and gate = SiLU or sigmoid.
+ * with value head hv reading key head hv / (H_v / H_k) (or hv mod H_k, see
+ * gdn_head_map), S a per-(sequence, value head) fp32 matrix [d_k][d_v], and
+ * gate = SiLU or sigmoid.
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is device memory owned by the caller; the library
@@ -26,8 +27,8 @@
  *       z, out [T][H_v*d_v];  a, b [T][H_v];
  *       state [N][H_v][d_k][d_v] fp32 (key lane major, as on the pages);
  *       conv state [N][K-1][conv_dim] fp32, slot 0 the oldest raw input;
- *       params: conv_w [conv_dim][K], a_log [H_v], dt_bias [H_v],
- *               norm_w [d_v], all fp32.
+ *       params: conv_w [conv_dim][K], a_log or decay_coef [H_v],
+ *               dt_bias [H_v], norm_w [d_v], all fp32.
  *   - act_dtype selects bf16 or fp32 for qkv, z, a, b; out_dtype selects
  *     bf16 (round to nearest even) or fp32 for out.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
@@ -59,6 +60,12 @@ typedef enum {
 typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
 typedef enum { GDN_GATE_SILU = 0, GDN_GATE_SIGMOID = 1 } gdn_gate;
 
+/* Which key head value head hv reads ("oxinfer 0.0.5 src/qwen.rs",
+ * DeltaRule::run): GROUPED is the contiguous grouping hv / (H_v / H_k) of
+ * the original checkpoints, TILED the order hv mod H_k that GGUF
+ * conversions use.  The two agree when H_v == H_k. */
+typedef enum { GDN_HEADS_GROUPED = 0, GDN_HEADS_TILED = 1 } gdn_head_map;
+
 typedef struct {
     int32_t h_k, h_v;       /* key heads, value heads */
     int32_t d_k, d_v;       /* lanes per key / value head */
@@ -68,13 +75,20 @@ typedef struct {
     int32_t gate;           /* gdn_gate applied to z */
     float norm_eps;         /* gated RMSNorm epsilon (1e-6 on the pages) */
     float l2_eps;           /* q/k L2-norm epsilon (1e-6 on the pages) */
+    int32_t head_map;       /* gdn_head_map */
 } gdn_config;
 
+/* Exactly one of a_log and decay_coef is given, the other is NULL: the
+ * log-decay is g = -exp(a_log[hv]) * softplus(a + dt_bias[hv]), or
+ * g = decay_coef[hv] * softplus(a + dt_bias[hv]) for layers that store the
+ * coefficient -exp(A_log) itself (GGUF ssm_a; "oxinfer 0.0.5 src/qwen.rs",
+ * weight loading). */
 typedef struct {
     const float *conv_w;    /* [conv_dim][K] depthwise conv taps, no bias */
     const float *a_log;     /* [H_v]  decay magnitude, g = -exp(a_log)... */
     const float *dt_bias;   /* [H_v]  added to a before softplus */
     const float *norm_w;    /* [d_v]  gated-norm weight (plain multiplier) */
+    const float *decay_coef;/* [H_v]  or the coefficient itself, g = decay_coef... */
 } gdn_params;
 
 /*
@@ -112,6 +126,66 @@ gdn_status gdn_decode_step(const gdn_config *cfg, const gdn_params *params,
                            int32_t batch, const void *qkv, const void *z,
                            const void *a, const void *b, float *conv_state,
                            float *state, void *out, void *stream);
+
+/*
+ * Several new tokens per sequence in one call (speculative verification of
+ * drafted tokens): the single-token step above applied t_new times in
+ * order, with the state read from and written to HBM once per call
+ * ("oxinfer 0.0.5 src/qwen.rs", DeltaRule::run over t tokens and the
+ * recording forward used for speculative verification).
+ *   t_new: tokens per sequence, 1 <= t_new <= 8 (GDN_EUNSUPPORTED beyond,
+ *     or when t_new tokens of one key head's conv channels do not fit the
+ *     on-chip buffer: t_new * (2*d_k + (H_v/H_k)*d_v) * 4 bytes plus
+ *     reduction space must stay within 64 KiB).
+ *   n_tok_dev: NULL (every sequence runs t_new tokens) or a device
+ *     [batch] int32 array: sequence i runs its first n_tok_dev[i] tokens
+ *     (values are clamped to [0, t_new]); later tokens are not read and
+ *     their rows of out and state_ckpt are not written.
+ *   qkv [batch][t_new][conv_dim], z [batch][t_new][H_v*d_v],
+ *     a, b [batch][t_new][H_v] (act_dtype).  z may be NULL when out is.
+ *   conv_in / conv_out [batch][K-1][conv_dim] fp32: history before and
+ *     after the tokens; may be the same buffer (in place).
+ *   state_in / state_out [batch][H_v][d_k][d_v] fp32: may be the same
+ *     buffer (in place) but must not partially overlap.
+ *   state_ckpt: NULL or [batch][t_new][H_v][d_k][d_v] fp32, the state after
+ *     each token (for callers that keep per-token states instead of
+ *     replaying; 2 MiB per token and sequence at H_v = 32, d = 128).
+ *   out: NULL (no outputs) or [batch][t_new][H_v*d_v] (out_dtype).
+ *   batch == 0 is a no-op.
+ */
+gdn_status gdn_decode_multi(const gdn_config *cfg, const gdn_params *params,
+                            int32_t batch, int32_t t_new,
+                            const int32_t *n_tok_dev, const void *qkv,
+                            const void *z, const void *a, const void *b,
+                            const float *conv_in, float *conv_out,
+                            const float *state_in, float *state_out,
+                            float *state_ckpt, void *out, void *stream);
+
+/*
+ * Rewind after speculative verification: a recurrent state cannot be
+ * truncated, so the state of each sequence is rebuilt from the state saved
+ * before the verified span by replaying the delta rule over the first
+ * keep_dev[i] recorded tokens ("oxinfer 0.0.5 src/qwen.rs",
+ * QwenSession::rewind and GdnRecord).  The replay is gdn_decode_multi with
+ * no outputs, so keeping every recorded token reproduces the state the
+ * verification reached bit for bit.
+ *   t_rec: recorded tokens per sequence (1 <= t_rec <= 8, as t_new above).
+ *   keep_dev: NULL (keep all t_rec) or device [batch] int32, clamped to
+ *     [0, t_rec].
+ *   qkv_rec [batch][t_rec][conv_dim], a_rec, b_rec [batch][t_rec][H_v]: the
+ *     recorded raw inputs (act_dtype).
+ *   state0 [batch][H_v][d_k][d_v], conv0 [batch][K-1][conv_dim] fp32: the
+ *     saved state and history before the span (read only).
+ *   state, conv_state: receive the rewound state and history (the last K-1
+ *     raw inputs up to the last kept token, reaching into conv0 when fewer
+ *     than K-1 tokens are kept).  May equal state0 / conv0.
+ */
+gdn_status gdn_rewind(const gdn_config *cfg, const gdn_params *params,
+                      int32_t batch, int32_t t_rec, const int32_t *keep_dev,
+                      const void *qkv_rec, const void *a_rec,
+                      const void *b_rec, const float *state0,
+                      const float *conv0, float *state, float *conv_state,
+                      void *stream);
 
 /*
  * Bytes of device workspace gdn_prefill_chunked needs for these sizes

@@ -41,7 +41,8 @@ class _Cfg(ctypes.Structure):
     _fields_ = [("h_k", ctypes.c_int32), ("h_v", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("conv_k", ctypes.c_int32), ("gate", ctypes.c_int32),
-                ("norm_eps", ctypes.c_double), ("l2_eps", ctypes.c_double)]
+                ("norm_eps", ctypes.c_double), ("l2_eps", ctypes.c_double),
+                ("head_map", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -55,6 +56,7 @@ class Shape:
     gate: str = "silu"          # "silu" or "sigmoid"
     norm_eps: float = 1e-6
     l2_eps: float = 1e-6
+    head_map: str = "grouped"   # "grouped": hv // (H_v/H_k); "tiled": hv % H_k
 
     @property
     def conv_dim(self) -> int:
@@ -67,9 +69,12 @@ class Shape:
     def c_struct(self) -> _Cfg:
         if self.gate not in ("silu", "sigmoid"):
             raise ValueError(f"unknown gate {self.gate!r}")
+        if self.head_map not in ("grouped", "tiled"):
+            raise ValueError(f"unknown head_map {self.head_map!r}")
         return _Cfg(self.h_k, self.h_v, self.d_k, self.d_v, self.conv_k,
                     1 if self.gate == "sigmoid" else 0,
-                    self.norm_eps, self.l2_eps)
+                    self.norm_eps, self.l2_eps,
+                    1 if self.head_map == "tiled" else 0)
 
 
 _lib = None
@@ -92,7 +97,7 @@ def _load():
                                     dp, dp, dp, dp]
         lib.oracle_mixer.restype = ctypes.c_int
         lib.oracle_mixer.argtypes = ([ctypes.POINTER(_Cfg), ctypes.c_int32, ip]
-                                     + [dp] * 12
+                                     + [dp] * 13
                                      + [ctypes.c_int32] * 3)
         _lib = lib
     return _lib
@@ -154,8 +159,9 @@ def mixer(shape: Shape, cu_seqlens, params, qkv, z, a, b, S0, conv0,
           heads=None, nthreads=1, want_pre=False):
     """Run the full mixer core on packed sequences.
 
-    params: dict with conv_w [conv_dim, K], a_log [H_v], dt_bias [H_v],
-    norm_w [d_v].  S0: [N, H_v, d_k, d_v]; conv0: [N, K-1, conv_dim].
+    params: dict with conv_w [conv_dim, K], dt_bias [H_v], norm_w [d_v] and
+    exactly one of a_log [H_v] (coefficient -exp(a_log)) or decay_coef [H_v]
+    (the coefficient itself).  S0: [N, H_v, d_k, d_v]; conv0: [N, K-1, conv_dim].
     heads: optional (begin, end) range of value heads to run (others leave
     their y / S entries untouched: y is zero there, S equals S0).
     Returns dict(y, S, conv, o_pre?) as float64 arrays.
@@ -174,11 +180,16 @@ def mixer(shape: Shape, cu_seqlens, params, qkv, z, a, b, S0, conv0,
     o_pre = np.zeros((T, shape.value_dim)) if want_pre else None
     h0, h1 = (0, shape.h_v) if heads is None else heads
     cfg = shape.c_struct()
+    a_log, coef = params.get("a_log"), params.get("decay_coef")
+    if (a_log is None) == (coef is None):
+        raise ValueError("give exactly one of a_log and decay_coef")
+    a_log = None if a_log is None else _f64(a_log)
+    coef = None if coef is None else _f64(coef)
     rc = lib.oracle_mixer(
         ctypes.byref(cfg), n, _iptr(cu),
-        _ptr(_f64(params["conv_w"])), _ptr(_f64(params["a_log"])),
+        _ptr(_f64(params["conv_w"])), _ptr(a_log),
         _ptr(_f64(params["dt_bias"])), _ptr(_f64(params["norm_w"])),
-        _ptr(qkv), _ptr(z), _ptr(a), _ptr(b), _ptr(S), _ptr(st), _ptr(y),
+        _ptr(coef), _ptr(qkv), _ptr(z), _ptr(a), _ptr(b), _ptr(S), _ptr(st), _ptr(y),
         _ptr(o_pre), h0, h1, int(nthreads))
     if rc != 0:
         raise ValueError("oracle_mixer rejected its arguments")

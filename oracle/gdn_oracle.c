@@ -24,7 +24,10 @@
  *   - The gated-norm weight is a plain multiplier of shape [d_v], shared by
  *     all value heads ([qwen.rs] Gdn struct, "plain weight (gated norm)").
  *   - Value head hv reads key head hv / (H_v / H_k) (contiguous groups,
- *     [cpu.rs] deltanet).
+ *     [cpu.rs] deltanet), or hv mod H_k when the layer uses the tiled order
+ *     ([qwen.rs] DeltaRule::run, `tiled`).
+ *   - The decay coefficient is -exp(A_log), or a given coefficient for
+ *     layers that store it directly ([qwen.rs] weight loading, GGUF ssm_a).
  *   - The conv history holds the last K-1 raw inputs, oldest first, laid out
  *     [K-1][conv_dim] per sequence ([qwen.rs] GdnState).
  *   - A sequence of length 0 passes its state and conv history through.
@@ -39,6 +42,7 @@ typedef struct {
     int32_t h_k, h_v, d_k, d_v, conv_k;
     int32_t gate; /* 0: SiLU output gate, 1: sigmoid output gate */
     double norm_eps, l2_eps;
+    int32_t head_map; /* 0: key head hv / (H_v/H_k), 1: key head hv mod H_k */
 } oracle_cfg;
 
 /* [exp.rs] fn sigmoid, fn silu; [qwen.rs] DeltaRule::run (softplus). */
@@ -154,6 +158,7 @@ typedef struct {
     int32_t n_seq;
     const int32_t *cu;
     const double *conv_w, *a_log, *dt_bias, *norm_w;
+    const double *decay_coef; /* [H_v] or NULL: then -exp(a_log) */
     const double *qkv, *z, *a, *b;
     const double *conv_in; /* [N][K-1][conv_dim], read only */
     double *S;             /* [N][H_v][dk][dv] in/out */
@@ -175,7 +180,7 @@ static void mixer_task(mixer_job *J, int n, int hv)
     const int HK = cfg->h_k, HV = cfg->h_v, DK = cfg->d_k, DV = cfg->d_v;
     const int K = cfg->conv_k;
     const int CD = 2 * HK * DK + HV * DV, VD = HV * DV;
-    const int hk = hv / (HV / HK);
+    const int hk = cfg->head_map ? hv % HK : hv / (HV / HK);
     const int km1 = K > 1 ? K - 1 : 1;
     /* channel index of each lane: q of hk, k of hk, v of hv */
     const int nch = 2 * DK + DV;
@@ -199,7 +204,7 @@ static void mixer_task(mixer_job *J, int n, int hv)
             win[(size_t)l * km1 + j] = st[(size_t)j * CD + chan[l]];
 
     const double qscale = 1.0 / sqrt((double)DK);
-    const double coef = -exp(J->a_log[hv]);
+    const double coef = J->decay_coef ? J->decay_coef[hv] : -exp(J->a_log[hv]);
 
     for (int t = J->cu[n]; t < J->cu[n + 1]; ++t) {
         const double *xt = J->qkv + (size_t)t * CD;
@@ -274,7 +279,8 @@ static void *mixer_worker(void *arg)
  * The full mixer core over packed sequences.
  *   qkv [T][conv_dim] raw fused projection (channels q | k | v, head-major),
  *   z [T][H_v*d_v], a, b [T][H_v]; conv_w [conv_dim][K]; a_log, dt_bias
- *   [H_v]; norm_w [d_v]; cu [N+1].
+ *   [H_v]; norm_w [d_v]; cu [N+1].  decay_coef [H_v], when not NULL,
+ *   replaces -exp(a_log) (a_log must then be NULL).
  *   S [N][H_v][d_k][d_v] in/out; conv_state [N][K-1][conv_dim] in/out;
  *   y [T][H_v*d_v] out; o_pre (optional) receives the pre-norm readout.
  * Only value heads [hv_begin, hv_end) run the recurrence (their S, y and
@@ -286,14 +292,16 @@ static void *mixer_worker(void *arg)
 int oracle_mixer(const oracle_cfg *cfg, int32_t n_seq, const int32_t *cu,
                  const double *conv_w, const double *a_log,
                  const double *dt_bias, const double *norm_w,
-                 const double *qkv, const double *z, const double *a,
+                 const double *decay_coef, const double *qkv, const double *z, const double *a,
                  const double *b, double *S, double *conv_state, double *y,
                  double *o_pre, int32_t hv_begin, int32_t hv_end,
                  int32_t nthreads)
 {
     if (cfg->h_k <= 0 || cfg->h_v <= 0 || cfg->h_v % cfg->h_k != 0 ||
         cfg->d_k <= 0 || cfg->d_v <= 0 || cfg->conv_k < 1 || n_seq < 0 ||
-        hv_begin < 0 || hv_end > cfg->h_v || hv_begin > hv_end)
+        hv_begin < 0 || hv_end > cfg->h_v || hv_begin > hv_end ||
+        (cfg->head_map != 0 && cfg->head_map != 1) ||
+        (a_log == NULL) == (decay_coef == NULL))
         return -1;
     for (int n = 0; n < n_seq; ++n)
         if (cu[n + 1] < cu[n]) return -1;
@@ -314,6 +322,7 @@ int oracle_mixer(const oracle_cfg *cfg, int32_t n_seq, const int32_t *cu,
     J.a_log = a_log;
     J.dt_bias = dt_bias;
     J.norm_w = norm_w;
+    J.decay_coef = decay_coef;
     J.qkv = qkv;
     J.z = z;
     J.a = a;

@@ -26,14 +26,14 @@ def n_threads() -> int:
 
 
 def oracle_shape(d: Dims) -> oracle.Shape:
-    return oracle.Shape(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, d.gate)
+    return oracle.Shape(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, d.gate, head_map=d.head_map)
 
 
 def gpu_config(d: Dims, act_dtype: str, out_dtype=torch.float32):
     import gated_deltanet_linear_causal_amd as gdn
     return gdn.Config(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k,
                       torch.bfloat16 if act_dtype == "bf16" else torch.float32,
-                      out_dtype, d.gate)
+                      out_dtype, d.gate, head_map=d.head_map)
 
 
 def to_dev(t: torch.Tensor, act_dtype: str | None = None, device="cuda"):
@@ -54,6 +54,7 @@ def subcase(case: Case, hk: int) -> Case:
     full layer.  Sequences and heads are independent, so running the
     oracle on it gives exactly the full layer's results for those heads."""
     d = case.dims
+    assert d.head_map == "grouped" and "a_log" in case.params
     grp = d.h_v // d.h_k
     HK, DK, DV = d.h_k, d.d_k, d.d_v
     qc = list(range(hk * DK, (hk + 1) * DK))

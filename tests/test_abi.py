@@ -27,7 +27,8 @@ def lib():
 
 def test_library_exports_every_header_function(lib):
     names = gdn.header_functions()
-    assert set(names) == {"gdn_conv_update", "gdn_decode_step", "gdn_prefill_workspace_bytes",
+    assert set(names) == {"gdn_conv_update", "gdn_decode_step", "gdn_decode_multi",
+                          "gdn_rewind", "gdn_prefill_workspace_bytes",
                           "gdn_prefill_chunked", "gdn_status_string", "gdn_last_error"}
     dyn = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -46,7 +47,7 @@ def test_status_strings(lib):
 
 def _cfg(**kw):
     base = dict(h_k=2, h_v=4, d_k=64, d_v=64, conv_k=4, act_dtype=0, out_dtype=1, gate=0,
-                norm_eps=1e-6, l2_eps=1e-6)
+                norm_eps=1e-6, l2_eps=1e-6, head_map=0)
     base.update(kw)
     return gdn._Config(**base)
 
@@ -72,7 +73,7 @@ _P = [ctypes.c_void_p(0x10000000000 * (i + 1)) for i in range(16)]
 
 
 def _params():
-    return gdn._Params(_P[10].value, _P[11].value, _P[12].value, _P[13].value)
+    return gdn._Params(_P[10].value, _P[11].value, _P[12].value, _P[13].value, None)
 
 
 def _decode(lib, cfg=None, params=None, batch=2, ptrs=None):
@@ -88,7 +89,7 @@ def _decode(lib, cfg=None, params=None, batch=2, ptrs=None):
     (dict(h_v=3), EINVAL), (dict(h_k=0), EINVAL), (dict(d_k=48), EUNSUP),
     (dict(d_v=256), EUNSUP), (dict(conv_k=5), EUNSUP), (dict(conv_k=0), EINVAL),
     (dict(act_dtype=7), EINVAL), (dict(gate=2), EINVAL), (dict(norm_eps=-1.0), EINVAL),
-    (dict(l2_eps=float("nan")), EINVAL)])
+    (dict(l2_eps=float("nan")), EINVAL), (dict(head_map=2), EINVAL)])
 def test_decode_rejects_bad_config(lib, kw, code):
     assert _decode(lib, _cfg(**kw)) == code
     assert lib.gdn_last_error().decode() != ""
@@ -97,7 +98,14 @@ def test_decode_rejects_bad_config(lib, kw, code):
 @no_gpu
 def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, params=False) == EINVAL
-    assert _decode(lib, params=gdn._Params(0, _P[11].value, _P[12].value, _P[13].value)) == EINVAL
+    assert _decode(lib, params=gdn._Params(0, _P[11].value, _P[12].value, _P[13].value,
+                                           None)) == EINVAL
+    # exactly one of a_log and decay_coef
+    assert _decode(lib, params=gdn._Params(_P[10].value, _P[11].value, _P[12].value,
+                                           _P[13].value, _P[15].value)) == EINVAL
+    assert "a_log" in lib.gdn_last_error().decode()
+    assert _decode(lib, params=gdn._Params(_P[10].value, None, _P[12].value,
+                                           _P[13].value, None)) == EINVAL
     assert _decode(lib, batch=-1) == EINVAL
     assert _decode(lib, ptrs=[None] + _P[1:7]) == EINVAL
     # out aliasing the state
@@ -107,6 +115,47 @@ def test_decode_rejects_bad_arguments(lib):
     assert "overlap" in lib.gdn_last_error().decode()
     # batch 0 is accepted without touching anything
     assert _decode(lib, batch=0) == OK
+
+
+def _multi(lib, cfg=None, batch=2, t_new=4, ptrs=None):
+    # n_tok, qkv, z, a, b, conv_in, conv_out, state_in, state_out, ckpt, out
+    p = [None] + _P[:4] + [_P[4], _P[5], _P[6], _P[7], None, _P[8]] if ptrs is None else ptrs
+    c = cfg or _cfg()
+    return lib.gdn_decode_multi(ctypes.byref(c), ctypes.byref(_params()), batch, t_new, *p, None)
+
+
+def _rewind(lib, cfg=None, batch=2, t_rec=4, ptrs=None):
+    # keep, qkv, a, b, state0, conv0, state, conv_state
+    p = [None, _P[0], _P[2], _P[3], _P[6], _P[4], _P[7], _P[5]] if ptrs is None else ptrs
+    c = cfg or _cfg()
+    return lib.gdn_rewind(ctypes.byref(c), ctypes.byref(_params()), batch, t_rec, *p, None)
+
+
+@no_gpu
+def test_decode_multi_and_rewind_reject_bad_arguments(lib):
+    assert _multi(lib, t_new=0) == EUNSUP
+    assert _multi(lib, t_new=9) == EUNSUP
+    assert "tokens per sequence" in lib.gdn_last_error().decode()
+    # 8 tokens of a wide group do not fit the on-chip buffer
+    assert _multi(lib, cfg=_cfg(h_k=1, h_v=16, d_k=128, d_v=128), t_new=8) == EUNSUP
+    assert _multi(lib, batch=-1) == EINVAL
+    assert _multi(lib, batch=0) == OK
+    base = [None] + _P[:4] + [_P[4], _P[5], _P[6], _P[7], None, _P[8]]
+    # qkv missing
+    assert _multi(lib, ptrs=base[:1] + [None] + base[2:]) == EINVAL
+    # z missing while out is requested
+    assert _multi(lib, ptrs=base[:2] + [None] + base[3:]) == EINVAL
+    # out aliasing state_out
+    assert _multi(lib, ptrs=base[:10] + [_P[7]]) == EINVAL
+    # checkpoints overlapping the input state
+    assert _multi(lib, ptrs=base[:9] + [_P[6]] + base[10:]) == EINVAL
+    # state_out partially overlapping state_in
+    assert _multi(lib, ptrs=base[:8] + [ctypes.c_void_p(_P[6].value + 4)] + base[9:]) == EINVAL
+    assert _rewind(lib, t_rec=9) == EUNSUP
+    assert _rewind(lib, ptrs=[None, _P[0], _P[2], _P[3], None, _P[4], _P[7], _P[5]]) == EINVAL
+    # the rewound state must not overlap the recorded inputs
+    assert _rewind(lib, ptrs=[None, _P[0], _P[2], _P[3], _P[6], _P[4], _P[0], _P[5]]) == EINVAL
+    assert _rewind(lib, batch=0) == OK
 
 
 def _prefill(lib, cu, t_total, cfg=None, chunk=64, ws=(_P[9], 1 << 40), outs=None):

@@ -9,7 +9,7 @@ import torch
 
 import gdn_parity as P
 import oracle
-from gdn_inputs import Dims, decode_batch, make_case, tiny_recurrent
+from gdn_inputs import Dims, decode_batch, make_case, tiny_recurrent, with_decay_coef
 
 pytestmark = pytest.mark.gpu
 
@@ -89,6 +89,33 @@ def test_decode_variants(gdn, v, act):
                      decay=decay, s0_std=0.3, conv0_std=1.0, decode_steps=9)
     y, S, conv = run_decode(gdn, case, 9)
     y_ref, S_ref, conv_ref = oracle_decode(case, 9)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
+LAYOUTS = [
+    # h_k, h_v, d, head_map, decay form
+    (2, 6, 64, "tiled", "decay_coef"),
+    (4, 8, 128, "tiled", "a_log"),
+    (2, 6, 32, "grouped", "decay_coef"),
+    (3, 3, 64, "tiled", "a_log"),
+]
+
+
+@pytest.mark.parametrize("v", LAYOUTS, ids=lambda v: "hk%d_hv%d_d%d_%s_%s" % v)
+def test_decode_head_map_and_decay_coef(gdn, v):
+    """Tiled key-head order (hv % H_k) and the decay coefficient given
+    directly ("oxinfer 0.0.5 src/qwen.rs", DeltaRule::run and weight
+    loading)."""
+    hk, hv, dd, head_map, form = v
+    d = Dims(hk, hv, dd, dd, 4, "silu", head_map)
+    case = make_case(d, [0, 0, 0], act_dtype="bf16", seed=300 + hk + hv + dd,
+                     decay="weak", s0_std=0.3, conv0_std=1.0, decode_steps=7)
+    if form == "decay_coef":
+        case.params = with_decay_coef(case.params)
+    y, S, conv = run_decode(gdn, case, 7)
+    y_ref, S_ref, conv_ref = oracle_decode(case, 7)
     P.assert_y_close(y, y_ref)
     P.assert_state_close(S, S_ref)
     np.testing.assert_array_equal(conv.numpy(), conv_ref)

@@ -305,14 +305,27 @@ def test_mixer_gated_norm_is_torch_rms_norm(gate):
                                rtol=1e-12, atol=1e-14)
 
 
-def test_mixer_matches_independent_formulation():
+@pytest.mark.parametrize("head_map,decay_form", [("grouped", "a_log"), ("tiled", "a_log"),
+                                                  ("grouped", "decay_coef"),
+                                                  ("tiled", "decay_coef")])
+def test_mixer_matches_independent_formulation(head_map, decay_form):
     """Whole mixer vs. a second formulation: scipy FIR conv, torch SiLU /
     sigmoid / softplus / rms_norm, explicit L2 scaling, transition-matrix
-    recurrence; several tokens, grouped heads, non-zero states."""
-    d = Dims(2, 4, 6, 5, conv_k=4)
+    recurrence; several tokens, grouped heads, non-zero states.  Both key-head
+    orders ("oxinfer 0.0.5 src/qwen.rs", DeltaRule::run: contiguous groups
+    hv // (H_v/H_k), or tiled hv % H_k) and both forms of the decay
+    coefficient (-exp(A_log), or the coefficient given directly as GGUF's
+    ssm_a stores it).  H_v/H_k = 3 and H_k = 2, so that neither order can
+    pass for the other or for hv % group."""
+    d = Dims(2, 6, 6, 5, conv_k=4)
     L = 10
     c = _case(d, [L], seed=14, s0_std=0.3, conv0_std=1.0, decay="weak")
-    out = _run(c, want_pre=True)
+    if decay_form == "decay_coef":
+        c.params["decay_coef"] = -torch.exp(c.params.pop("a_log").double()).float()
+    out = oracle.mixer(oracle.Shape(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, d.gate,
+                                    head_map=head_map),
+                       c.cu_seqlens, c.params, c.qkv, c.z, c.a, c.b, c.S0, c.conv0,
+                       want_pre=True)
     HK, HV, DK, DV, K = d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k
     x = np.asarray(c.qkv, np.float64)
     full = np.concatenate([np.asarray(c.conv0[0], np.float64), x])
@@ -321,10 +334,13 @@ def test_mixer_matches_independent_formulation():
                   for ch in range(d.conv_dim)], axis=1)
     act = F.silu(_t(h)).numpy()
     sp = F.softplus(_t(c.a) + _t(c.params["dt_bias"]), threshold=20).numpy()
-    g = -np.exp(np.asarray(c.params["a_log"], np.float64)) * sp
+    if decay_form == "decay_coef":
+        g = np.asarray(c.params["decay_coef"], np.float64) * sp
+    else:
+        g = -np.exp(np.asarray(c.params["a_log"], np.float64)) * sp
     beta = torch.sigmoid(_t(c.b)).numpy()
     for hv in range(HV):
-        hk = hv // (HV // HK)
+        hk = hv % HK if head_map == "tiled" else hv // (HV // HK)
         q = act[:, hk * DK:(hk + 1) * DK]
         k = act[:, HK * DK + hk * DK:HK * DK + (hk + 1) * DK]
         v = act[:, 2 * HK * DK + hv * DV:2 * HK * DK + (hv + 1) * DV]
@@ -417,3 +433,14 @@ def test_mixer_head_subset_and_threads_bit_exact():
     np.testing.assert_array_equal(sub["S"][:, 1:3], full["S"][:, 1:3])
     np.testing.assert_array_equal(sub["S"][:, 0], c.S0[:, 0].numpy())
     np.testing.assert_array_equal(sub["conv"], full["conv"])
+
+
+def test_mixer_rejects_both_or_neither_decay_form():
+    d = Dims(1, 1, 4, 4, conv_k=2)
+    c = _case(d, [3], seed=18)
+    both = dict(c.params, decay_coef=-torch.exp(c.params["a_log"]))
+    with pytest.raises(ValueError):
+        _run(c.__class__(**{**c.__dict__, "params": both}))
+    neither = {k: v for k, v in c.params.items() if k != "a_log"}
+    with pytest.raises(ValueError):
+        _run(c.__class__(**{**c.__dict__, "params": neither}))

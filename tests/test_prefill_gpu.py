@@ -10,7 +10,7 @@ import torch
 
 import gdn_parity as P
 from gdn_inputs import (Dims, chunked_prefill, long_handoff, make_case,
-                        varlen_prefill)
+                        varlen_prefill, with_decay_coef)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,32 @@ def test_prefill_small(gdn, v, act):
     d = Dims(hk, hv, dk, dv, K, gate)
     case = make_case(d, lengths, act_dtype=act, seed=sum(lengths) + K, decay=decay,
                      s0_std=0.3, conv0_std=1.0)
+    y, S, conv = run_prefill(gdn, case)
+    r = P.run_oracle(case)
+    P.assert_y_close(y, r["y"])
+    P.assert_state_close(S, r["S"])
+    np.testing.assert_array_equal(conv.numpy(), r["conv"])
+
+
+LAYOUTS = [
+    # h_k, h_v, d, head_map, decay form
+    (2, 6, 64, "tiled", "decay_coef"),
+    (2, 4, 128, "tiled", "a_log"),
+    (2, 6, 32, "grouped", "decay_coef"),
+]
+
+
+@pytest.mark.parametrize("v", LAYOUTS, ids=lambda v: "hk%d_hv%d_d%d_%s_%s" % v)
+def test_prefill_head_map_and_decay_coef(gdn, v):
+    """Tiled key-head order (hv % H_k) and the decay coefficient given
+    directly ("oxinfer 0.0.5 src/qwen.rs", DeltaRule::run and weight
+    loading), over ragged chunks."""
+    hk, hv, dd, head_map, form = v
+    d = Dims(hk, hv, dd, dd, 4, "silu", head_map)
+    case = make_case(d, [1, 63, 65, 130], act_dtype="bf16", seed=400 + hk + hv + dd,
+                     decay="weak", s0_std=0.3, conv0_std=1.0)
+    if form == "decay_coef":
+        case.params = with_decay_coef(case.params)
     y, S, conv = run_prefill(gdn, case)
     r = P.run_oracle(case)
     P.assert_y_close(y, r["y"])
