@@ -51,6 +51,18 @@ def decode_bytes(d, batch):
     return state + conv + inp + out + params
 
 
+def decode_multi_bytes(d, batch, t_new):
+    """Algorithmic HBM bytes of one multi-token decode call: the state and
+    conv history cross HBM once (read + write) whatever t_new is; inputs and
+    outputs scale with the tokens."""
+    state = batch * d.h_v * d.d_k * d.d_v * 4 * 2
+    conv = batch * (d.conv_k - 1) * d.conv_dim * 4 * 2
+    inp = batch * t_new * (d.conv_dim + d.value_dim + 2 * d.h_v) * 2
+    out = batch * t_new * d.value_dim * 2
+    params = (d.conv_dim * d.conv_k + 2 * d.h_v + d.d_v) * 4
+    return state + conv + inp + out + params
+
+
 def prefill_flops(d, T, C=64):
     """Algorithmic flops of the chunked (W/U) form as computed, per call: per
     token and key head the K K^T and Q K^T rows (4 C d_k); per token and
@@ -304,6 +316,23 @@ def main():
     dc_cold_ms = ev_c[0].elapsed_time(ev_c[1]) / cold_steps
     del S_rot, c_rot
 
+    # Multi-token decode (speculative verification of t_new drafted tokens per
+    # sequence, gdn_decode_multi), same batch, states updated in place.
+    multi = {}
+    for t_new in (2, 4, 8):
+        xm = [x_dc[k][:t_new].transpose(0, 1).contiguous() for k in range(4)]
+        out_m = torch.empty((B, t_new, d.value_dim), dtype=bf, device=dev)
+        calls = 50
+        for _ in range(3):
+            gdn.decode_multi(cfg, dparams, *xm, c_dc, S_dc, out=out_m, stream=stream)
+        ev_m = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev_m[0].record(stream)
+        for _ in range(calls):
+            gdn.decode_multi(cfg, dparams, *xm, c_dc, S_dc, out=out_m, stream=stream)
+        ev_m[1].record(stream)
+        torch.cuda.synchronize()
+        multi[t_new] = (ev_m[0].elapsed_time(ev_m[1]) / calls, calls)
+
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -335,6 +364,16 @@ def main():
                "duration_us": round(pf_ms * 1e3, 2), "launches_timed": args.steps,
                "mfma_busy": load_counter("prefill_call", "mfma_busy"),
                "hbm_frac": round(pbytes / (pf_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    roof_multi = {}
+    for t_new, (ms, calls) in multi.items():
+        mb = decode_multi_bytes(d, B, t_new)
+        gbs = mb / (ms * 1e-3) / 1e9
+        roof_multi[f"decode_multi_t{t_new}"] = {
+            "kernel": f"gdn::decode_multi_kernel (gdn_decode_multi, {t_new} tokens/sequence)",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": mb, "duration_us": round(ms * 1e3, 2),
+            "launches_timed": calls, "tokens_per_s": round(B * t_new / (ms * 1e-3), 1)}
     # the kernel that takes most of a step's time
     dominant = roof_pf if pf_ms >= dc_ms * n_sets else roof_dec
 
@@ -355,7 +394,8 @@ def main():
         "decode_cold_us_per_step": round(dc_cold_ms * 1e3, 2),
         "decode_tokens_per_s": round(B / (dc_ms * 1e-3), 1),
         "roofline": dominant,
-        "rooflines": {"decode": roof_dec, "decode_cold": roof_dec_cold, "prefill": roof_pf},
+        "rooflines": {"decode": roof_dec, "decode_cold": roof_dec_cold, "prefill": roof_pf,
+                      **roof_multi},
         "note": "the pages quote no throughput for this path on any hardware",
     }
     if not args.no_cpu_baseline:

@@ -11,20 +11,23 @@
 //
 // A workgroup owns one (sequence, key head): the q/k channels of the key
 // head and the v channels of its value heads.  It
-//   1. runs the causal conv + SiLU of every owned channel over the n new
-//      tokens (one thread per channel, the K-1 history in registers) into
-//      LDS and writes the new history (last K-1 raw inputs);
-//   2. forms the q/k L2 scales of every token;
-//   3. per value head: loads the [d_k][d_v] fp32 state into registers once,
-//      steps it through the n tokens (per token one LDS reduction for
-//      S^T k^ and S^T q^, then the rank-one update and the gated RMSNorm),
-//      and stores it once.
+//   1. issues every global load at once (first value head's state, gate
+//      inputs, z, conv inputs), runs the causal conv + SiLU of every owned
+//      channel over the n new tokens (one thread per channel, the history in
+//      registers) into LDS, writes the new history (last K-1 raw inputs),
+//      and forms the gates and the q/k L2 scales of every token;
+//   2. per value head: keeps the [d_k][d_v] fp32 state in registers and
+//      steps it through the n tokens; each wave owns 32 whole columns, so
+//      S^T k^ and S^T q^ reduce over rows inside the wave (lane shuffles)
+//      and the token loop has no barrier; the pre-norm readout of every
+//      token goes to LDS;
+//   3. applies the gated RMSNorm to all (token, head) rows in parallel.
 // The state, the dominant traffic, therefore crosses HBM once per call
 // however many tokens the call carries.
 //
-// Thread layout per value head (as in the single-token kernel): 2*d_v
-// threads = (d_v/4 column quads) x (8 row groups); thread (c4, rg) holds rows
-// rg, rg+8, ... of columns 4*c4 .. 4*c4+3.
+// Thread layout per value head: 2*d_v threads = d_v/32 waves; wave w owns
+// columns 32w .. 32w+31; lane l holds column quad 8w + (l mod 8) of rows
+// l/8, l/8 + 8, ... (d_k/8 rows of 4 columns).
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -68,19 +71,16 @@ decode_multi_kernel(const MultiArgs p)
     constexpr int TPH = 2 * DV;     // threads per value head
     constexpr int NT = TPH * NSLOT; // threads per workgroup
     constexpr int NW = NT / 64;     // waves
-    constexpr int C4 = DV / 4;      // column quads
-    constexpr int RG = TPH / C4;    // row groups (8)
-    constexpr int RPT = DK / RG;    // state rows per thread
-    constexpr int RPW = 64 / C4;    // row groups per wave (summed by lane shuffles)
-    constexpr int NPART = RG / RPW; // partial sums per column quad left for LDS
-    static_assert(RG == 8 && DK % RG == 0 && NT % 64 == 0 && RPW >= 1, "layout");
+    constexpr int C4 = DV / 4;      // column quads per head
+    constexpr int RPT = DK / 8;     // state rows per thread
+    static_assert(DV % 32 == 0 && DK % 8 == 0, "layout");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int slot = __builtin_amdgcn_readfirstlane(tid / TPH); // TPH is a multiple of 64
-    const int lt = tid % TPH;
-    const int c4 = lt % C4;
-    const int rg = lt / C4;
+    const int wv = (tid % TPH) >> 6;                              // wave within the head
+    const int c4 = wv * 8 + (lane & 7);                           // column quad
+    const int rg = lane >> 3;                                     // row group 0..7
     const int group = p.group, K = p.conv_k, CD = p.conv_dim, T = p.t_new;
     const int u = blockIdx.x, bs = u / p.h_k, hk = u % p.h_k;
     const int nch = 2 * DK + group * DV;
@@ -89,15 +89,48 @@ decode_multi_kernel(const MultiArgs p)
     n = __builtin_amdgcn_readfirstlane(n);
 
     extern __shared__ __attribute__((aligned(16))) float smem[];
-    float *cb = smem;                                      // [T][nch]
-    float *scal = cb + (size_t)T * nch;                    // [T][4]
+    float *cb = smem;                                      // [T][nch] silu(conv)
+    float *scal = cb + (size_t)T * nch;                    // [T][4] q/k scales, q^.k^
     float *sgate = scal + 4 * T;                           // [T][group][2] beta, alpha
-    f32x4 *red = reinterpret_cast<f32x4 *>(sgate + 2 * ((T * group + 1) & ~1)); // [2][NSLOT][NPART][C4][2]
+    float *sz = sgate + 2 * ((T * group + 1) & ~1);        // [T][group][DV] z
+    float *so = sz + (size_t)T * group * DV;               // [T][group][DV] pre-norm readout
 
-    // ---- 1. causal conv + SiLU of the owned channels, new history --------
-    // The window holds the last three raw inputs, oldest first, and the taps
-    // are right-aligned to four (zero taps in front when K < 4), so one code
-    // path serves every K <= 4.
+    // ---- 1. loads, conv, gates, L2 scales ---------------------------------
+    // State rows are addressed as a uniform head base plus a 32-bit lane
+    // offset, so that no 64-bit per-lane row addresses stay live.
+    const int toff = rg * DV + 4 * c4;
+    auto head_base = [&](int hv) { return ((size_t)bs * p.h_v + hv) * DK * DV; };
+    f32x4 s[RPT];
+    {
+        const float *Sin = p.state_in + head_base(value_head_of(hk, slot, p.h_k, group, p.tiled));
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+            s[r] = *reinterpret_cast<const f32x4 *>(Sin + toff + r * 8 * DV);
+    }
+    const TIn *pa = static_cast<const TIn *>(p.a), *pb = static_cast<const TIn *>(p.b);
+    const TIn *pz = static_cast<const TIn *>(p.z);
+    const int ngate = n * group;                   // (token, value head) pairs
+    const int nzq = p.out ? ngate * C4 : 0;        // z quads
+    auto gate_index = [&](int i) {
+        const int hv = value_head_of(hk, i % group, p.h_k, group, p.tiled);
+        return ((size_t)bs * T + i / group) * p.h_v + hv;
+    };
+    auto out_index = [&](int q) { // quad q of the [n][group][DV] rows
+        const int pair = q / C4, t = pair / group;
+        const int hv = value_head_of(hk, pair % group, p.h_k, group, p.tiled);
+        return ((size_t)bs * T + t) * p.value_dim + (size_t)hv * DV + 4 * (q % C4);
+    };
+    TIn ga0 = TIn(0), gb0 = TIn(0);
+    if (tid < ngate) {
+        ga0 = pa[gate_index(tid)];
+        gb0 = pb[gate_index(tid)];
+    }
+    RawQuad<TIn> zq0;
+    if (tid < nzq) zq0.load(pz + out_index(tid));
+
+    // Causal conv + SiLU of the owned channels.  The window holds the last
+    // three raw inputs, oldest first, and the taps are right-aligned to four
+    // (zero taps in front when K < 4), so one code path serves every K <= 4.
     const TIn *qkv = static_cast<const TIn *>(p.qkv);
     for (int l = tid; l < nch; l += NT) {
         int ch;
@@ -140,23 +173,22 @@ decode_multi_kernel(const MultiArgs p)
         float *hout = p.conv_out + (size_t)bs * (K - 1) * CD + ch;
         for (int j = 0; j < K - 1; ++j) hout[(size_t)j * CD] = pick3(win, 3 - (K - 1) + j);
     }
-    lds_sync_m();
-
-    // ---- 2. L2 scales of q and k and q^.k^ per token (a wave per token),
-    // and the gates of every (token, value head) ("cherenkov
-    // qwen4_exp/cpu.rs" fn deltanet) ------------------------------------
-    {
-        const TIn *pa = static_cast<const TIn *>(p.a), *pb = static_cast<const TIn *>(p.b);
-        for (int i = tid; i < n * group; i += NT) {
-            const int t = i / group, hl = i % group;
-            const int hv = value_head_of(hk, hl, p.h_k, group, p.tiled);
-            const size_t gi = ((size_t)bs * T + t) * p.h_v + hv;
-            const float g = decay_coef_of(p.a_log, p.decay_coef, hv) *
-                            softplusf_(load_act(pa, gi) + p.dt_bias[hv]);
-            sgate[2 * i + 0] = sigmoidf_(load_act(pb, gi));
-            sgate[2 * i + 1] = expf(g);
-        }
+    // Gates of every (token, value head) ("cherenkov qwen4_exp/cpu.rs"
+    // fn deltanet) and z, into LDS.
+    for (int i = tid; i < ngate; i += NT) {
+        const int hv = value_head_of(hk, i % group, p.h_k, group, p.tiled);
+        const float ar = i == tid ? act_to_f32(ga0) : load_act(pa, gate_index(i));
+        const float br = i == tid ? act_to_f32(gb0) : load_act(pb, gate_index(i));
+        const float g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplusf_(ar + p.dt_bias[hv]);
+        sgate[2 * i + 0] = sigmoidf_(br);
+        sgate[2 * i + 1] = expf(g);
     }
+    for (int q = tid; q < nzq; q += NT) {
+        const float4 z4 = q == tid ? zq0.to_f32() : load_act4(pz, out_index(q));
+        *reinterpret_cast<float4 *>(sz + 4 * (size_t)q) = z4;
+    }
+    lds_sync_m();
+    // L2 scales of q and k and q^.k^ per token (a wave per token).
     for (int t = wave; t < n; t += NW) {
         const float *ct = cb + (size_t)t * nch;
         float ssq = 0.f, ssk = 0.f, dqk = 0.f;
@@ -179,70 +211,50 @@ decode_multi_kernel(const MultiArgs p)
     }
     lds_sync_m();
 
-    // ---- 3. the delta rule over the tokens, per value head ---------------
-    const TIn *pz = static_cast<const TIn *>(p.z);
-    const float4 w4 = *reinterpret_cast<const float4 *>(p.norm_w + 4 * c4);
+    // ---- 2. the delta rule over the tokens, per value head ----------------
+    //   m = S_old^T k^,  r = S_old^T q^,  delta = beta (v - alpha m),
+    //   o = alpha r + (q^.k^) delta  (= S_new^T q^),  S_new = alpha S_old + k^ delta^T
     const int npass = group / NSLOT;
     for (int pass = 0; pass < npass; ++pass) {
         const int hl = pass * NSLOT + slot;
         const int hv = value_head_of(hk, hl, p.h_k, group, p.tiled);
-        // Uniform head base plus a 32-bit lane offset, so that row addresses
-        // are not kept as 64-bit per-lane pairs.
-        const size_t head = ((size_t)bs * p.h_v + hv) * DK * DV;
-        const int toff = rg * DV + 4 * c4;
-        const float *Sin = p.state_in + head;
-        f32x4 s[RPT];
+        const size_t head = head_base(hv);
+        if (pass > 0) {
+            const float *Sin = p.state_in + head;
 #pragma unroll
-        for (int r = 0; r < RPT; ++r)
-            s[r] = *reinterpret_cast<const f32x4 *>(Sin + toff + r * RG * DV);
+            for (int r = 0; r < RPT; ++r)
+                s[r] = *reinterpret_cast<const f32x4 *>(Sin + toff + r * 8 * DV);
+        }
 #pragma unroll 1
         for (int t = 0; t < n; ++t) {
             const float *ct = cb + (size_t)t * nch;
             const float qs = scal[4 * t + 0], ks = scal[4 * t + 1], qk = scal[4 * t + 2];
-            float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            const size_t obase = ((size_t)bs * T + t) * p.value_dim + (size_t)hv * DV + 4 * c4;
-            if (p.out) z4 = load_act4(pz, obase); // (uniform branch: the load stays in flight)
             const float beta = sgate[2 * (t * group + hl) + 0];
             const float alpha = sgate[2 * (t * group + hl) + 1];
-
             float kk[RPT]; // k^ of this thread's rows, for S^T k^ and the update
             f32x4 mk = {0.f, 0.f, 0.f, 0.f}, mq = mk;
 #pragma unroll
             for (int r = 0; r < RPT; ++r) {
-                const int i = rg + RG * r;
+                const int i = rg + 8 * r;
                 kk[r] = ct[DK + i] * ks;
                 mk += kk[r] * s[r];
                 mq += (ct[i] * qs) * s[r];
             }
-            // Sum over the row groups: those of one wave by lane shuffles,
-            // the waves' partials through LDS (double-buffered by token
-            // parity, so one barrier per token).
+            // sum over the 8 row groups of the wave (lanes l, l^8, l^16, ...)
 #pragma unroll
-            for (int off = C4; off < 64; off <<= 1) {
+            for (int off = 8; off < 64; off <<= 1) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     mk[e] += __shfl_xor(mk[e], off, 64);
                     mq[e] += __shfl_xor(mq[e], off, 64);
                 }
             }
-            f32x4 *rd = red + ((size_t)(t & 1) * NSLOT + slot) * NPART * C4 * 2;
-            if (rg % RPW == 0) {
-                rd[((rg / RPW) * C4 + c4) * 2 + 0] = mk;
-                rd[((rg / RPW) * C4 + c4) * 2 + 1] = mq;
-            }
-            lds_sync_m();
-            f32x4 MK = rd[c4 * 2 + 0], MQ = rd[c4 * 2 + 1];
-#pragma unroll
-            for (int g2 = 1; g2 < NPART; ++g2) {
-                MK += rd[(g2 * C4 + c4) * 2 + 0];
-                MQ += rd[(g2 * C4 + c4) * 2 + 1];
-            }
             const f32x4 v4 = *reinterpret_cast<const f32x4 *>(ct + 2 * DK + hl * DV + 4 * c4);
             f32x4 delta, o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                delta[e] = beta * (v4[e] - alpha * MK[e]);
-                o[e] = fmaf(alpha, MQ[e], qk * delta[e]); // = S_new^T q^
+                delta[e] = beta * (v4[e] - alpha * mk[e]);
+                o[e] = fmaf(alpha, mq[e], qk * delta[e]);
             }
             // (one row at a time: the scheduler would otherwise form all
             // the k delta^T products first and double the live registers)
@@ -256,42 +268,53 @@ decode_multi_kernel(const MultiArgs p)
                 float *cp = p.ckpt + (((size_t)bs * T + t) * p.h_v + hv) * DK * DV;
 #pragma unroll
                 for (int r = 0; r < RPT; ++r)
-                    *reinterpret_cast<f32x4 *>(cp + toff + r * RG * DV) = s[r];
+                    *reinterpret_cast<f32x4 *>(cp + toff + r * 8 * DV) = s[r];
             }
-            if (p.out) {
-                // Gated RMSNorm over the d_v lanes of this head.
-                float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-                ss = group_sum<C4>(ss);
-                if (rg == 0) {
-                    const float rn = rsqrtf(ss / DV + p.norm_eps);
-                    float4 y;
-                    y.x = o[0] * rn * w4.x * gatef_(z4.x, p.gate);
-                    y.y = o[1] * rn * w4.y * gatef_(z4.y, p.gate);
-                    y.z = o[2] * rn * w4.z * gatef_(z4.z, p.gate);
-                    y.w = o[3] * rn * w4.w * gatef_(z4.w, p.gate);
-                    store_out4(p.out, obase, y, p.out_bf16);
-                }
-            }
+            if (rg == 0)
+                *reinterpret_cast<f32x4 *>(so + ((size_t)t * group + hl) * DV + 4 * c4) = o;
         }
         float *Sout = p.state_out + head;
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
-            *reinterpret_cast<f32x4 *>(Sout + toff + r * RG * DV) = s[r];
-        if (pass + 1 < npass) lds_sync_m(); // the reduction buffers are reused
+            *reinterpret_cast<f32x4 *>(Sout + toff + r * 8 * DV) = s[r];
+    }
+
+    // ---- 3. gated RMSNorm of every (token, value head) row ----------------
+    if (!p.out) return;
+    lds_sync_m();
+    const int nq = ngate * C4;
+    const int rounds = (nq + NT - 1) / NT; // uniform trip count for the lane sums
+    for (int k = 0; k < rounds; ++k) {
+        const int q = tid + k * NT;
+        const bool live = q < nq; // whole C4-lane groups are live or not
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        if (live) o = *reinterpret_cast<const f32x4 *>(so + 4 * (size_t)q);
+        float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+        ss = group_sum<C4>(ss);
+        if (live) {
+            const int cq = q % C4;
+            const float4 w4 = *reinterpret_cast<const float4 *>(p.norm_w + 4 * cq);
+            const float4 z4 = *reinterpret_cast<const float4 *>(sz + 4 * (size_t)q);
+            const float rn = rsqrtf(ss / DV + p.norm_eps);
+            float4 y;
+            y.x = o[0] * rn * w4.x * gatef_(z4.x, p.gate);
+            y.y = o[1] * rn * w4.y * gatef_(z4.y, p.gate);
+            y.z = o[2] * rn * w4.z * gatef_(z4.z, p.gate);
+            y.w = o[3] * rn * w4.w * gatef_(z4.w, p.gate);
+            store_out4(p.out, out_index(q), y, p.out_bf16);
+        }
     }
 }
 
 // LDS of one workgroup: [T][nch] conv outputs, [T][4] q/k scales,
-// [T][group][2] gates (padded to 16 bytes) and [2][NSLOT][NPART][d_v/4][2]
-// f32x4 reduction partials.
+// [T][group][2] gates (padded to 16 bytes), and [T][group][d_v] z and
+// pre-norm readouts.
 size_t decode_multi_lds_bytes(const Dims &d, int t_new)
 {
     const int nch = 2 * d.d_k + d.group * d.d_v;
-    const int nslot = d.group % 2 == 0 ? 2 : 1;
-    const int c4 = d.d_v / 4, npart = 8 / (64 / c4 < 8 ? 64 / c4 : 8);
     const size_t gates = 2 * (((size_t)t_new * d.group + 1) & ~(size_t)1);
-    return sizeof(float) * ((size_t)t_new * nch + 4 * (size_t)t_new + gates) +
-           sizeof(f32x4) * 2 * nslot * npart * c4 * 2;
+    const size_t rows = (size_t)t_new * d.group * d.d_v;
+    return sizeof(float) * ((size_t)t_new * nch + 4 * (size_t)t_new + gates + 2 * rows);
 }
 
 template <typename TIn, int DK, int DV, int NSLOT>

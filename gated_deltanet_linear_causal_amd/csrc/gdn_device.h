@@ -43,6 +43,26 @@ template <> __device__ __forceinline__ float4 load_act4<bf16_t>(const bf16_t *p,
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
+// Raw activation values, converted to fp32 only where they are used (a
+// conversion right after the load would wait for it).
+__device__ __forceinline__ float act_to_f32(float v) { return v; }
+__device__ __forceinline__ float act_to_f32(bf16_t v) { return bf16_bits_to_f32(v); }
+template <typename T> struct RawQuad;
+template <> struct RawQuad<float> {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    __device__ __forceinline__ void load(const float *p) { v = *reinterpret_cast<const float4 *>(p); }
+    __device__ __forceinline__ float4 to_f32() const { return v; }
+};
+template <> struct RawQuad<bf16_t> {
+    uint2 v = make_uint2(0u, 0u);
+    __device__ __forceinline__ void load(const bf16_t *p) { v = *reinterpret_cast<const uint2 *>(p); }
+    __device__ __forceinline__ float4 to_f32() const
+    {
+        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    }
+};
+
 // Store four consecutive outputs as fp32 or bf16.
 __device__ __forceinline__ void store_out4(void *out, size_t i, float4 v, bool bf16)
 {
