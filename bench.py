@@ -36,7 +36,9 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CALIB_BYTES = 1 << 30          # the calibration copy reads and writes 1 GiB
 KERNEL_SOURCES = ["gated_deltanet_linear_causal_amd/csrc/decode.hip",
+                  "gated_deltanet_linear_causal_amd/csrc/decode_multi.hip",
                   "gated_deltanet_linear_causal_amd/csrc/prefill.hip"]
+DECODE_KERNELS = ("decode_multi_kernel", "decode_kernel")
 
 
 def decode_bytes(d, batch):
@@ -118,7 +120,7 @@ def write_traffic(fetch_dir, write_dir, mfma_dir=None):
             if r["Counter_Name"] != counter:
                 continue
             name, val = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0
-            key = next((k for k in PREFILL_KERNELS + ("decode_kernel",) if k in name), None)
+            key = next((k for k in PREFILL_KERNELS + DECODE_KERNELS if k in name), None)
             if key is None:
                 calib = max(calib, val)
                 continue
@@ -140,7 +142,7 @@ def write_traffic(fetch_dir, write_dir, mfma_dir=None):
         # XCDs).
         acc = {}
         for r in _counter_rows(mfma_dir):
-            key = next((k for k in PREFILL_KERNELS + ("decode_kernel",) if k in r["Kernel_Name"]), None)
+            key = next((k for k in PREFILL_KERNELS + DECODE_KERNELS if k in r["Kernel_Name"]), None)
             if key is None:
                 continue
             e = acc.setdefault(key, {})
@@ -220,6 +222,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-multi", action="store_true",
+                    help="skip the multi-token decode legs (profiling runs: every "
+                         "decode_multi_kernel launch is then a gdn_decode_step)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -319,7 +324,7 @@ def main():
     # Multi-token decode (speculative verification of t_new drafted tokens per
     # sequence, gdn_decode_multi), same batch, states updated in place.
     multi = {}
-    for t_new in (2, 4, 8):
+    for t_new in (() if args.no_multi else (1, 2, 4, 8)):
         xm = [x_dc[k][:t_new].transpose(0, 1).contiguous() for k in range(4)]
         out_m = torch.empty((B, t_new, d.value_dim), dtype=bf, device=dev)
         calls = 50
@@ -345,10 +350,11 @@ def main():
     dec_gbs = dbytes / (dc_ms * 1e-3) / 1e9
     dec_cold_gbs = dbytes / (dc_cold_ms * 1e-3) / 1e9
     pf_tflops = pflops / (pf_ms * 1e-3) / 1e12
-    roof_dec = {"kernel": "gdn::decode_kernel (gdn_decode_step, 1 launch)", "bound": "hbm",
+    roof_dec = {"kernel": "gdn::decode_multi_kernel (gdn_decode_step: 1 token per sequence, "
+                          "1 launch)", "bound": "hbm",
                 "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                "traffic": load_traffic("decode_kernel"),
+                "traffic": load_traffic("decode_multi_kernel"),
                 "algorithmic_bytes_per_launch": dbytes,
                 "duration_us": round(dc_ms * 1e3, 2),
                 "launches_timed": args.steps * n_sets}

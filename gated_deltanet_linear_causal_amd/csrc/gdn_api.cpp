@@ -192,6 +192,14 @@ gdn_status gdn_decode_step(const gdn_config *cfg, const gdn_params *params, int3
             return fail(GDN_EINVAL, "outputs and states must not overlap the inputs");
     if (overlap(ro, rs) || overlap(ro, rc) || overlap(rs, rc))
         return fail(GDN_EINVAL, "out, state and conv_state must not overlap each other");
+    // One token is the multi-token kernel with t_new = 1 whenever its
+    // per-key-head buffer fits; very wide groups use the persistent
+    // single-token kernel, which needs no per-token buffer.
+    if (gdn::decode_multi_lds_bytes(d, 1) <= gdn::kDecodeMultiMaxLds)
+        return hip_status(gdn::launch_decode_multi(d, p, batch, 1, nullptr, qkv, z, a, b,
+                                                   conv_state, conv_state, state, state, nullptr,
+                                                   out, static_cast<hipStream_t>(stream)),
+                          "gdn_decode_step launch");
     return hip_status(gdn::launch_decode(d, p, batch, qkv, z, a, b, conv_state, state, out,
                                          static_cast<hipStream_t>(stream)),
                       "gdn_decode_step launch");
