@@ -34,6 +34,12 @@ class Dims:
     conv_k: int = 4
     gate: str = "silu"
     head_map: str = "grouped"      # key head of value head hv: hv // group or hv % h_k
+    decay: str = "head"            # one decay per value head, or per key channel ("channel")
+
+    @property
+    def gate_width(self) -> int:
+        """Values of `a` and dt_bias per value head."""
+        return self.d_k if self.decay == "channel" else 1
 
     @property
     def conv_dim(self) -> int:
@@ -54,7 +60,7 @@ class Case:
     conv0: torch.Tensor            # [N, K-1, conv_dim] fp32
     qkv: torch.Tensor              # [T, conv_dim]
     z: torch.Tensor                # [T, value_dim]
-    a: torch.Tensor                # [T, H_v]
+    a: torch.Tensor                # [T, H_v] ([T, H_v * d_k] with per-channel decay)
     b: torch.Tensor                # [T, H_v]
     # decode continuation: [steps, N, ...] per-step single-token inputs
     dec: dict = field(default_factory=dict)
@@ -95,7 +101,7 @@ def make_params(gen, dims: Dims, decay: str = "strong") -> dict:
         a_log = torch.log(_uniform(gen, (dims.h_v,), 0.001, 0.01))
     else:
         raise ValueError(decay)
-    dt_bias = _normal(gen, (dims.h_v,), 1.0)
+    dt_bias = _normal(gen, (dims.h_v * dims.gate_width,), 1.0)
     norm_w = 1.0 + _normal(gen, (dims.d_v,), 0.1)
     return {"conv_w": conv_w, "a_log": a_log, "dt_bias": dt_bias,
             "norm_w": norm_w}
@@ -126,14 +132,14 @@ def make_case(dims: Dims, lengths, act_dtype="bf16", seed=0, decay="strong",
     conv0 = _normal(gen, (n, dims.conv_k - 1, dims.conv_dim), conv0_std)
     qkv = _act(gen, (T, dims.conv_dim), act_dtype)
     z = _act(gen, (T, dims.value_dim), act_dtype)
-    a = _act(gen, (T, dims.h_v), act_dtype)
+    a = _act(gen, (T, dims.h_v * dims.gate_width), act_dtype)
     b = _act(gen, (T, dims.h_v), act_dtype)
     dec = {}
     if decode_steps:
         dec = {
             "qkv": _act(gen, (decode_steps, n, dims.conv_dim), act_dtype),
             "z": _act(gen, (decode_steps, n, dims.value_dim), act_dtype),
-            "a": _act(gen, (decode_steps, n, dims.h_v), act_dtype),
+            "a": _act(gen, (decode_steps, n, dims.h_v * dims.gate_width), act_dtype),
             "b": _act(gen, (decode_steps, n, dims.h_v), act_dtype),
         }
     return Case(dims, act_dtype, cu, params, S0, conv0, qkv, z, a, b, dec,

@@ -42,7 +42,7 @@ class _Cfg(ctypes.Structure):
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("conv_k", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("norm_eps", ctypes.c_double), ("l2_eps", ctypes.c_double),
-                ("head_map", ctypes.c_int32)]
+                ("head_map", ctypes.c_int32), ("decay_mode", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -57,6 +57,12 @@ class Shape:
     norm_eps: float = 1e-6
     l2_eps: float = 1e-6
     head_map: str = "grouped"   # "grouped": hv // (H_v/H_k); "tiled": hv % H_k
+    decay: str = "head"         # "head": one decay per value head; "channel": per key channel (KDA)
+
+    @property
+    def gate_width(self) -> int:
+        """Values of `a` and dt_bias per value head."""
+        return self.d_k if self.decay == "channel" else 1
 
     @property
     def conv_dim(self) -> int:
@@ -71,10 +77,13 @@ class Shape:
             raise ValueError(f"unknown gate {self.gate!r}")
         if self.head_map not in ("grouped", "tiled"):
             raise ValueError(f"unknown head_map {self.head_map!r}")
+        if self.decay not in ("head", "channel"):
+            raise ValueError(f"unknown decay {self.decay!r}")
         return _Cfg(self.h_k, self.h_v, self.d_k, self.d_v, self.conv_k,
                     1 if self.gate == "sigmoid" else 0,
                     self.norm_eps, self.l2_eps,
-                    1 if self.head_map == "tiled" else 0)
+                    1 if self.head_map == "tiled" else 0,
+                    1 if self.decay == "channel" else 0)
 
 
 _lib = None
@@ -172,7 +181,7 @@ def mixer(shape: Shape, cu_seqlens, params, qkv, z, a, b, S0, conv0,
     T = int(cu[-1])
     qkv = _f64(qkv, (T, shape.conv_dim))
     z = _f64(z, (T, shape.value_dim))
-    a = _f64(a, (T, shape.h_v))
+    a = _f64(a, (T, shape.h_v * shape.gate_width))
     b = _f64(b, (T, shape.h_v))
     S = _f64(S0).reshape(n, shape.h_v, shape.d_k, shape.d_v).copy()
     st = _f64(conv0).reshape(n, shape.conv_k - 1, shape.conv_dim).copy()
@@ -188,7 +197,8 @@ def mixer(shape: Shape, cu_seqlens, params, qkv, z, a, b, S0, conv0,
     rc = lib.oracle_mixer(
         ctypes.byref(cfg), n, _iptr(cu),
         _ptr(_f64(params["conv_w"])), _ptr(a_log),
-        _ptr(_f64(params["dt_bias"])), _ptr(_f64(params["norm_w"])),
+        _ptr(_f64(params["dt_bias"], (shape.h_v * shape.gate_width,))),
+        _ptr(_f64(params["norm_w"])),
         _ptr(coef), _ptr(qkv), _ptr(z), _ptr(a), _ptr(b), _ptr(S), _ptr(st), _ptr(y),
         _ptr(o_pre), h0, h1, int(nthreads))
     if rc != 0:

@@ -28,6 +28,13 @@
  *     ([qwen.rs] DeltaRule::run, `tiled`).
  *   - The decay coefficient is -exp(A_log), or a given coefficient for
  *     layers that store it directly ([qwen.rs] weight loading, GGUF ssm_a).
+ *   - Kimi Delta Attention ("cortiq-engine 0.8.76 pipeline.rs",
+ *     AttnKind::Kda: a per-channel decayed delta rule) is read as the same
+ *     rule with the scalar decay replaced by one decay per key channel:
+ *     g[i] = coef * softplus(a[i] + dt_bias[i]) for the d_k channels of the
+ *     value head, S <- diag(e^g) S, everything else unchanged.  Its
+ *     separate q/k/v short convs are the per-channel depthwise conv already
+ *     here, and its sigmoid output gate is the sigmoid gate option.
  *   - The conv history holds the last K-1 raw inputs, oldest first, laid out
  *     [K-1][conv_dim] per sequence ([qwen.rs] GdnState).
  *   - A sequence of length 0 passes its state and conv history through.
@@ -43,6 +50,7 @@ typedef struct {
     int32_t gate; /* 0: SiLU output gate, 1: sigmoid output gate */
     double norm_eps, l2_eps;
     int32_t head_map; /* 0: key head hv / (H_v/H_k), 1: key head hv mod H_k */
+    int32_t decay_mode; /* 0: one decay per value head, 1: one per key channel */
 } oracle_cfg;
 
 /* [exp.rs] fn sigmoid, fn silu; [qwen.rs] DeltaRule::run (softplus). */
@@ -53,20 +61,21 @@ static double o_softplus(double x) { return x > 20.0 ? x : log1p(exp(x)); }
 /*
  * One token of the gated delta rule on one value head ([cpu.rs] deltanet,
  * [qwen.rs] DeltaRule::run):
- *   S <- alpha S;  m = S^T k;  delta = beta (v - m);  S <- S + k delta^T;
+ *   S <- diag(alpha) S;  m = S^T k;  delta = beta (v - m);  S <- S + k delta^T;
  *   o = S^T q  (read out from the updated state).
- * q and k arrive already normalised (q also scaled).  S is [dk][dv].
+ * alpha [dk] holds the decay of each key row: all equal to e^g for the
+ * scalar-decay rule, one per channel for the per-channel rule.  q and k
+ * arrive already normalised (q also scaled).  S is [dk][dv].
  */
 static void delta_step(int dk, int dv, const double *q, const double *k,
-                       const double *v, double g, double beta, double *S,
-                       double *m, double *delta, double *o)
+                       const double *v, const double *alpha, double beta,
+                       double *S, double *m, double *delta, double *o)
 {
-    const double alpha = exp(g);
     for (int j = 0; j < dv; ++j) m[j] = 0.0;
     for (int i = 0; i < dk; ++i) {
         double *row = S + (size_t)i * dv;
         for (int j = 0; j < dv; ++j) {
-            row[j] *= alpha;
+            row[j] *= alpha[i];
             m[j] += row[j] * k[i];
         }
     }
@@ -94,14 +103,18 @@ void oracle_delta_core(int32_t L, int32_t dk, int32_t dv, const double *q,
     double *m = malloc(sizeof(double) * dv);
     double *delta = malloc(sizeof(double) * dv);
     double *ot = malloc(sizeof(double) * dv);
+    double *alpha = malloc(sizeof(double) * dk);
     for (int t = 0; t < L; ++t) {
+        const double a = exp(g[t]);
+        for (int i = 0; i < dk; ++i) alpha[i] = a;
         delta_step(dk, dv, q + (size_t)t * dk, k + (size_t)t * dk,
-                   v + (size_t)t * dv, g[t], beta[t], S, m, delta, ot);
+                   v + (size_t)t * dv, alpha, beta[t], S, m, delta, ot);
         if (o) memcpy(o + (size_t)t * dv, ot, sizeof(double) * dv);
     }
     free(m);
     free(delta);
     free(ot);
+    free(alpha);
 }
 
 /*
@@ -196,6 +209,7 @@ static void mixer_task(mixer_job *J, int n, int hv)
     double *m = malloc(sizeof(double) * DV);
     double *delta = malloc(sizeof(double) * DV);
     double *o = malloc(sizeof(double) * DV);
+    double *alpha = malloc(sizeof(double) * DK);
     double *S = J->S + ((size_t)n * HV + hv) * DK * DV;
     const double *st = J->conv_in + (size_t)n * (K - 1) * CD;
 
@@ -229,12 +243,24 @@ static void mixer_task(mixer_job *J, int n, int hv)
             cq[i] = cq[i] * qinv * qscale;
             ck[i] = ck[i] * kinv;
         }
-        /* Gates: beta = sigmoid(b); g = -exp(A_log) softplus(a + dt_bias). */
+        /* Gates: beta = sigmoid(b); g = -exp(A_log) softplus(a + dt_bias),
+         * per value head, or per key channel of it (a and dt_bias then hold
+         * d_k values per value head). */
         const double beta = o_sigmoid(J->b[(size_t)t * HV + hv]);
-        const double g =
-            coef * o_softplus(J->a[(size_t)t * HV + hv] + J->dt_bias[hv]);
+        if (cfg->decay_mode) {
+            for (int i = 0; i < DK; ++i) {
+                const size_t c = (size_t)hv * DK + i;
+                alpha[i] = exp(coef * o_softplus(J->a[(size_t)t * HV * DK + c] +
+                                                 J->dt_bias[c]));
+            }
+        } else {
+            const double g =
+                coef * o_softplus(J->a[(size_t)t * HV + hv] + J->dt_bias[hv]);
+            const double ag = exp(g);
+            for (int i = 0; i < DK; ++i) alpha[i] = ag;
+        }
 
-        delta_step(DK, DV, cq, ck, cv, g, beta, S, m, delta, o);
+        delta_step(DK, DV, cq, ck, cv, alpha, beta, S, m, delta, o);
 
         if (J->o_pre)
             memcpy(J->o_pre + (size_t)t * VD + (size_t)hv * DV, o,
@@ -250,6 +276,7 @@ static void mixer_task(mixer_job *J, int n, int hv)
             yt[j] = o[j] * r * J->norm_w[j] * gz;
         }
     }
+    free(alpha);
     free(chan);
     free(win);
     free(cq);
@@ -279,7 +306,8 @@ static void *mixer_worker(void *arg)
  * The full mixer core over packed sequences.
  *   qkv [T][conv_dim] raw fused projection (channels q | k | v, head-major),
  *   z [T][H_v*d_v], a, b [T][H_v]; conv_w [conv_dim][K]; a_log, dt_bias
- *   [H_v]; norm_w [d_v]; cu [N+1].  decay_coef [H_v], when not NULL,
+ *   [H_v]; norm_w [d_v]; cu [N+1].  With the per-channel decay, a is
+ *   [T][H_v*d_k] and dt_bias [H_v*d_k].  decay_coef [H_v], when not NULL,
  *   replaces -exp(a_log) (a_log must then be NULL).
  *   S [N][H_v][d_k][d_v] in/out; conv_state [N][K-1][conv_dim] in/out;
  *   y [T][H_v*d_v] out; o_pre (optional) receives the pre-norm readout.
@@ -301,6 +329,7 @@ int oracle_mixer(const oracle_cfg *cfg, int32_t n_seq, const int32_t *cu,
         cfg->d_k <= 0 || cfg->d_v <= 0 || cfg->conv_k < 1 || n_seq < 0 ||
         hv_begin < 0 || hv_end > cfg->h_v || hv_begin > hv_end ||
         (cfg->head_map != 0 && cfg->head_map != 1) ||
+        (cfg->decay_mode != 0 && cfg->decay_mode != 1) ||
         (a_log == NULL) == (decay_coef == NULL))
         return -1;
     for (int n = 0; n < n_seq; ++n)

@@ -26,7 +26,8 @@ def n_threads() -> int:
 
 
 def oracle_shape(d: Dims) -> oracle.Shape:
-    return oracle.Shape(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, d.gate, head_map=d.head_map)
+    return oracle.Shape(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, d.gate, head_map=d.head_map,
+                        decay=d.decay)
 
 
 def gpu_config(d: Dims, act_dtype: str, out_dtype=torch.float32):
@@ -54,7 +55,7 @@ def subcase(case: Case, hk: int) -> Case:
     full layer.  Sequences and heads are independent, so running the
     oracle on it gives exactly the full layer's results for those heads."""
     d = case.dims
-    assert d.head_map == "grouped" and "a_log" in case.params
+    assert d.head_map == "grouped" and d.decay == "head" and "a_log" in case.params
     grp = d.h_v // d.h_k
     HK, DK, DV = d.h_k, d.d_k, d.d_v
     qc = list(range(hk * DK, (hk + 1) * DK))

@@ -444,3 +444,90 @@ def test_mixer_rejects_both_or_neither_decay_form():
     neither = {k: v for k, v in c.params.items() if k != "a_log"}
     with pytest.raises(ValueError):
         _run(c.__class__(**{**c.__dict__, "params": neither}))
+
+
+# --------------------------------------------------------------------------
+# per-channel decay (Kimi Delta Attention; "cortiq-engine 0.8.76
+# pipeline.rs", AttnKind::Kda)
+# --------------------------------------------------------------------------
+
+def _kda_shape(d, **kw):
+    return oracle.Shape(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, d.gate, decay="channel", **kw)
+
+
+def test_kda_equal_channels_is_the_scalar_rule():
+    """Per-channel gate inputs that are equal across the channels of a head
+    give the scalar-decay rule bit for bit."""
+    d = Dims(2, 4, 8, 6, conv_k=4)
+    c = _case(d, [9, 3], seed=31, s0_std=0.3, conv0_std=1.0, decay="weak")
+    ref = _run(c)
+    a_ch = np.repeat(np.asarray(c.a, np.float64), d.d_k, axis=1)
+    params = dict(c.params, dt_bias=np.repeat(np.asarray(c.params["dt_bias"], np.float64), d.d_k))
+    out = oracle.mixer(_kda_shape(d), c.cu_seqlens, params, c.qkv, c.z, a_ch, c.b, c.S0, c.conv0)
+    np.testing.assert_array_equal(out["y"], ref["y"])
+    np.testing.assert_array_equal(out["S"], ref["S"])
+
+
+def test_kda_beta_zero_decays_each_key_row():
+    """b = -inf makes beta = 0, so S_L = diag(exp(sum_t g_t)) S_0 with
+    g_t[i] = -exp(A_log) softplus(a_t[i] + dt_bias[i]) from torch."""
+    d = Dims(1, 2, 4, 3, conv_k=2, decay="channel")
+    L = 5
+    c = _case(d, [L], seed=32, s0_std=1.0, conv0_std=1.0, decay="weak")
+    c.b[:] = -float("inf")
+    c.a[:] = torch.linspace(-3.0, 25.0, L * 8).reshape(L, 8)
+    out = oracle.mixer(_kda_shape(d), c.cu_seqlens, c.params, c.qkv, c.z, c.a, c.b, c.S0,
+                       c.conv0)
+    sp = F.softplus(_t(c.a) + _t(c.params["dt_bias"]), threshold=20)   # [L, H_v*d_k]
+    g = -torch.exp(_t(c.params["a_log"])).repeat_interleave(d.d_k) * sp
+    decay = torch.exp(g.sum(0)).view(d.h_v, d.d_k).numpy()
+    np.testing.assert_allclose(out["S"][0], decay[:, :, None] * c.S0[0].numpy(), rtol=1e-13)
+
+
+def _brute_force_channel_core(q, k, v, g, beta, S0):
+    """Transition-matrix form with a diagonal decay:
+    S_t = (I - b_t k k^T) diag(exp(g_t)) S_{t-1} + b_t k v^T, o_t = S_t^T q_t."""
+    S = S0.copy()
+    dk = S.shape[0]
+    out = []
+    for t in range(len(beta)):
+        kk = k[t][:, None]
+        Tm = (np.eye(dk) - beta[t] * (kk @ kk.T)) @ np.diag(np.exp(g[t]))
+        S = Tm @ S + beta[t] * (kk @ v[t][None, :])
+        out.append(S.T @ q[t])
+    return np.array(out), S
+
+
+@pytest.mark.parametrize("head_map", ["grouped", "tiled"])
+def test_kda_matches_independent_formulation(head_map):
+    """Per-channel decay vs a second formulation: scipy FIR conv, torch
+    nonlinearities, explicit L2 scaling and diagonal-decay transition
+    matrices."""
+    d = Dims(2, 4, 6, 5, conv_k=4, decay="channel", head_map=head_map)
+    L = 9
+    c = _case(d, [L], seed=33, s0_std=0.3, conv0_std=1.0, decay="weak")
+    out = oracle.mixer(_kda_shape(d, head_map=head_map), c.cu_seqlens, c.params, c.qkv, c.z,
+                       c.a, c.b, c.S0, c.conv0, want_pre=True)
+    HK, HV, DK, DV, K = d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k
+    x = np.asarray(c.qkv, np.float64)
+    full = np.concatenate([np.asarray(c.conv0[0], np.float64), x])
+    w = np.asarray(c.params["conv_w"], np.float64)
+    h = np.stack([lfilter(w[ch, ::-1], [1.0], full[:, ch])[K - 1:]
+                  for ch in range(d.conv_dim)], axis=1)
+    act = F.silu(_t(h)).numpy()
+    sp = F.softplus(_t(c.a) + _t(c.params["dt_bias"]), threshold=20).numpy()
+    coef = -np.exp(np.asarray(c.params["a_log"], np.float64))
+    beta = torch.sigmoid(_t(c.b)).numpy()
+    for hv in range(HV):
+        hk = hv % HK if head_map == "tiled" else hv // (HV // HK)
+        q = act[:, hk * DK:(hk + 1) * DK]
+        k = act[:, HK * DK + hk * DK:HK * DK + (hk + 1) * DK]
+        v = act[:, 2 * HK * DK + hv * DV:2 * HK * DK + (hv + 1) * DV]
+        qn = q / np.sqrt((q * q).sum(1, keepdims=True) + 1e-6) / np.sqrt(DK)
+        kn = k / np.sqrt((k * k).sum(1, keepdims=True) + 1e-6)
+        g = coef[hv] * sp[:, hv * DK:(hv + 1) * DK]
+        o_ref, S_ref = _brute_force_channel_core(qn, kn, v, g, beta[:, hv],
+                                                 np.asarray(c.S0[0, hv], np.float64))
+        np.testing.assert_allclose(out["o_pre"][:, hv * DV:(hv + 1) * DV], o_ref,
+                                   rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(out["S"][0, hv], S_ref, rtol=1e-11, atol=1e-13)
