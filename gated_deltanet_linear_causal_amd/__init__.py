@@ -21,6 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 GDN_BF16, GDN_F32 = 0, 1
 GDN_GATE_SILU, GDN_GATE_SIGMOID = 0, 1
 GDN_HEADS_GROUPED, GDN_HEADS_TILED = 0, 1
+GDN_DECAY_HEAD, GDN_DECAY_CHANNEL = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_EUNSUPPORTED",
           3: "GDN_EWORKSPACE", 4: "GDN_EHIP"}
 CHUNK = 64
@@ -38,7 +39,7 @@ class _Config(ctypes.Structure):
                 ("conv_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("norm_eps", ctypes.c_float), ("l2_eps", ctypes.c_float),
-                ("head_map", ctypes.c_int32)]
+                ("head_map", ctypes.c_int32), ("decay_mode", ctypes.c_int32)]
 
 
 class _Params(ctypes.Structure):
@@ -107,6 +108,12 @@ class Config:
     norm_eps: float = 1e-6
     l2_eps: float = 1e-6
     head_map: str = "grouped"   # "grouped" (hv // group) or "tiled" (hv % h_k)
+    decay: str = "head"         # "head" (one decay per value head) or "channel" (per key channel)
+
+    @property
+    def gate_width(self):
+        """Values of a and dt_bias per value head."""
+        return self.d_k if self.decay == "channel" else 1
 
     @property
     def conv_dim(self):
@@ -127,11 +134,14 @@ class Config:
             raise ValueError(f"unknown gate {self.gate!r}")
         if self.head_map not in ("grouped", "tiled"):
             raise ValueError(f"unknown head_map {self.head_map!r}")
+        if self.decay not in ("head", "channel"):
+            raise ValueError(f"unknown decay {self.decay!r}")
         return _Config(self.h_k, self.h_v, self.d_k, self.d_v, self.conv_k,
                        code(self.act_dtype), code(self.out_dtype),
                        GDN_GATE_SIGMOID if self.gate == "sigmoid" else GDN_GATE_SILU,
                        self.norm_eps, self.l2_eps,
-                       GDN_HEADS_TILED if self.head_map == "tiled" else GDN_HEADS_GROUPED)
+                       GDN_HEADS_TILED if self.head_map == "tiled" else GDN_HEADS_GROUPED,
+                       GDN_DECAY_CHANNEL if self.decay == "channel" else GDN_DECAY_HEAD)
 
 
 def _ptr(t):
@@ -162,7 +172,7 @@ def _params(cfg: Config, p: dict) -> _Params:
         _check(a_log, "a_log", (cfg.h_v,), torch.float32)
     else:
         _check(coef, "decay_coef", (cfg.h_v,), torch.float32)
-    _check(p["dt_bias"], "dt_bias", (cfg.h_v,), torch.float32)
+    _check(p["dt_bias"], "dt_bias", (cfg.h_v * cfg.gate_width,), torch.float32)
     _check(p["norm_w"], "norm_w", (cfg.d_v,), torch.float32)
     return _Params(p["conv_w"].data_ptr(), None if a_log is None else a_log.data_ptr(),
                    p["dt_bias"].data_ptr(), p["norm_w"].data_ptr(),
@@ -217,7 +227,7 @@ def decode_step(cfg: Config, params: dict, qkv, z, a, b, conv_state, state, out=
     B = qkv.shape[0]
     _check(qkv, "qkv", (B, cfg.conv_dim), cfg.act_dtype)
     _check(z, "z", (B, cfg.value_dim), cfg.act_dtype)
-    _check(a, "a", (B, cfg.h_v), cfg.act_dtype)
+    _check(a, "a", (B, cfg.h_v * cfg.gate_width), cfg.act_dtype)
     _check(b, "b", (B, cfg.h_v), cfg.act_dtype)
     _check(conv_state, "conv_state", (B, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
     _check(state, "state", (B, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
@@ -258,7 +268,7 @@ def decode_multi(cfg: Config, params: dict, qkv, z, a, b, conv_state, state, out
     B, T = qkv.shape[0], qkv.shape[1]
     dev = qkv.device
     _check(qkv, "qkv", (B, T, cfg.conv_dim), cfg.act_dtype)
-    _check(a, "a", (B, T, cfg.h_v), cfg.act_dtype)
+    _check(a, "a", (B, T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
     _check(b, "b", (B, T, cfg.h_v), cfg.act_dtype)
     sshape = (B, cfg.h_v, cfg.d_k, cfg.d_v)
     cshape = (B, cfg.conv_k - 1, cfg.conv_dim)
@@ -295,7 +305,7 @@ def rewind(cfg: Config, params: dict, qkv_rec, a_rec, b_rec, state0, conv0, keep
     B, T = qkv_rec.shape[0], qkv_rec.shape[1]
     dev = qkv_rec.device
     _check(qkv_rec, "qkv_rec", (B, T, cfg.conv_dim), cfg.act_dtype)
-    _check(a_rec, "a_rec", (B, T, cfg.h_v), cfg.act_dtype)
+    _check(a_rec, "a_rec", (B, T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
     _check(b_rec, "b_rec", (B, T, cfg.h_v), cfg.act_dtype)
     sshape = (B, cfg.h_v, cfg.d_k, cfg.d_v)
     cshape = (B, cfg.conv_k - 1, cfg.conv_dim)
@@ -335,7 +345,7 @@ def prefill_chunked(cfg: Config, params: dict, seqlens: SeqLens, qkv, z, a, b,
     dev = qkv.device
     _check(qkv, "qkv", (T, cfg.conv_dim), cfg.act_dtype)
     _check(z, "z", (T, cfg.value_dim), cfg.act_dtype)
-    _check(a, "a", (T, cfg.h_v), cfg.act_dtype)
+    _check(a, "a", (T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
     _check(b, "b", (T, cfg.h_v), cfg.act_dtype)
     sshape = (N, cfg.h_v, cfg.d_k, cfg.d_v)
     cshape = (N, cfg.conv_k - 1, cfg.conv_dim)

@@ -51,6 +51,8 @@ struct MultiArgs {
     int gate, out_bf16, tiled;
     float norm_eps, l2_eps;
 };
+// (with one decay per key channel, a is [batch][t_new][H_v*d_k] and dt_bias
+// [H_v*d_k])
 
 __device__ __forceinline__ void lds_sync_m()
 {
@@ -64,7 +66,7 @@ __device__ __forceinline__ float pick3(const float (&w)[3], int i)
     return i == 0 ? w[0] : (i == 1 ? w[1] : w[2]);
 }
 
-template <typename TIn, int DK, int DV, int NSLOT>
+template <typename TIn, int DK, int DV, int NSLOT, bool CH>
 __global__ void __launch_bounds__(2 * DV * NSLOT)
 decode_multi_kernel(const MultiArgs p)
 {
@@ -94,6 +96,7 @@ decode_multi_kernel(const MultiArgs p)
     float *sgate = scal + 4 * T;                           // [T][group][2] beta, alpha
     float *sz = sgate + 2 * ((T * group + 1) & ~1);        // [T][group][DV] z
     float *so = sz + (size_t)T * group * DV;               // [T][group][DV] pre-norm readout
+    float *salpha = so + (size_t)T * group * DV;           // [T][group][DK] decays (per channel)
 
     // ---- 1. loads, conv, gates, L2 scales ---------------------------------
     // State rows are addressed as a uniform head base plus a 32-bit lane
@@ -111,6 +114,7 @@ decode_multi_kernel(const MultiArgs p)
     const TIn *pz = static_cast<const TIn *>(p.z);
     const int ngate = n * group;                   // (token, value head) pairs
     const int nzq = p.out ? ngate * C4 : 0;        // z quads
+    const int nalpha = CH ? ngate * DK : 0;        // per-channel decays
     auto gate_index = [&](int i) {
         const int hv = value_head_of(hk, i % group, p.h_k, group, p.tiled);
         return ((size_t)bs * T + i / group) * p.h_v + hv;
@@ -122,8 +126,17 @@ decode_multi_kernel(const MultiArgs p)
     };
     TIn ga0 = TIn(0), gb0 = TIn(0);
     if (tid < ngate) {
-        ga0 = pa[gate_index(tid)];
+        if (!CH) ga0 = pa[gate_index(tid)];
         gb0 = pb[gate_index(tid)];
+    }
+    // per-channel decay inputs: element e = (pair, channel) of a [.][H_v*d_k]
+    auto alpha_index = [&](int e) { return gate_index(e / DK) * DK + e % DK; };
+    constexpr int kAlphaPre = 4; // elements per thread loaded up front
+    TIn gac[kAlphaPre];
+#pragma unroll
+    for (int k = 0; k < kAlphaPre; ++k) {
+        const int e = tid + k * NT;
+        gac[k] = (CH && e < nalpha) ? pa[alpha_index(e)] : TIn(0);
     }
     RawQuad<TIn> zq0;
     if (tid < nzq) zq0.load(pz + out_index(tid));
@@ -177,11 +190,29 @@ decode_multi_kernel(const MultiArgs p)
     // fn deltanet) and z, into LDS.
     for (int i = tid; i < ngate; i += NT) {
         const int hv = value_head_of(hk, i % group, p.h_k, group, p.tiled);
-        const float ar = i == tid ? act_to_f32(ga0) : load_act(pa, gate_index(i));
         const float br = i == tid ? act_to_f32(gb0) : load_act(pb, gate_index(i));
-        const float g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplusf_(ar + p.dt_bias[hv]);
         sgate[2 * i + 0] = sigmoidf_(br);
-        sgate[2 * i + 1] = expf(g);
+        if (!CH) {
+            const float ar = i == tid ? act_to_f32(ga0) : load_act(pa, gate_index(i));
+            const float g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplusf_(ar + p.dt_bias[hv]);
+            sgate[2 * i + 1] = expf(g);
+        }
+    }
+    if (CH) {
+        // one decay per (token, value head, key channel): Kimi Delta
+        // Attention ("cortiq-engine 0.8.76 pipeline.rs", AttnKind::Kda)
+        for (int e = tid; e < nalpha; e += NT) {
+            const int k = (e - tid) / NT;
+            const int hv = value_head_of(hk, (e / DK) % group, p.h_k, group, p.tiled);
+            float ar = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kAlphaPre; ++j)
+                if (j == k) ar = act_to_f32(gac[j]);
+            if (k >= kAlphaPre) ar = load_act(pa, alpha_index(e));
+            const float g = decay_coef_of(p.a_log, p.decay_coef, hv) *
+                            softplusf_(ar + p.dt_bias[(size_t)hv * DK + e % DK]);
+            salpha[e] = expf(g);
+        }
     }
     for (int q = tid; q < nzq; q += NT) {
         const float4 z4 = q == tid ? zq0.to_f32() : load_act4(pz, out_index(q));
@@ -230,7 +261,14 @@ decode_multi_kernel(const MultiArgs p)
             const float *ct = cb + (size_t)t * nch;
             const float qs = scal[4 * t + 0], ks = scal[4 * t + 1], qk = scal[4 * t + 2];
             const float beta = sgate[2 * (t * group + hl) + 0];
-            const float alpha = sgate[2 * (t * group + hl) + 1];
+            // scalar decay: folded into the sums below; per-channel decay:
+            // applied to the state rows first
+            const float alpha = CH ? 1.0f : sgate[2 * (t * group + hl) + 1];
+            if (CH) {
+                const float *al = salpha + ((size_t)t * group + hl) * DK;
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) s[r] = al[rg + 8 * r] * s[r];
+            }
             float kk[RPT]; // k^ of this thread's rows, for S^T k^ and the update
             f32x4 mk = {0.f, 0.f, 0.f, 0.f}, mq = mk;
 #pragma unroll
@@ -253,8 +291,13 @@ decode_multi_kernel(const MultiArgs p)
             f32x4 delta, o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                delta[e] = beta * (v4[e] - alpha * mk[e]);
-                o[e] = fmaf(alpha, mq[e], qk * delta[e]);
+                if (CH) {
+                    delta[e] = beta * (v4[e] - mk[e]);
+                    o[e] = mq[e] + qk * delta[e];
+                } else {
+                    delta[e] = beta * (v4[e] - alpha * mk[e]);
+                    o[e] = fmaf(alpha, mq[e], qk * delta[e]);
+                }
             }
             // (one row at a time: the scheduler would otherwise form all
             // the k delta^T products first and double the live registers)
@@ -307,42 +350,49 @@ decode_multi_kernel(const MultiArgs p)
 }
 
 // LDS of one workgroup: [T][nch] conv outputs, [T][4] q/k scales,
-// [T][group][2] gates (padded to 16 bytes), and [T][group][d_v] z and
-// pre-norm readouts.
+// [T][group][2] gates (padded to 16 bytes), [T][group][d_v] z and
+// pre-norm readouts, and with per-channel decay [T][group][d_k] decays.
 size_t decode_multi_lds_bytes(const Dims &d, int t_new)
 {
     const int nch = 2 * d.d_k + d.group * d.d_v;
     const size_t gates = 2 * (((size_t)t_new * d.group + 1) & ~(size_t)1);
     const size_t rows = (size_t)t_new * d.group * d.d_v;
-    return sizeof(float) * ((size_t)t_new * nch + 4 * (size_t)t_new + gates + 2 * rows);
+    const size_t alphas = d.chan_decay ? (size_t)t_new * d.group * d.d_k : 0;
+    return sizeof(float) * ((size_t)t_new * nch + 4 * (size_t)t_new + gates + 2 * rows + alphas);
 }
 
 template <typename TIn, int DK, int DV, int NSLOT>
-static hipError_t launch_multi_t(const MultiArgs &a, int batch, hipStream_t s)
+static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int batch, hipStream_t s)
 {
     constexpr int NT = 2 * DV * NSLOT;
     Dims d;
     d.d_k = DK;
     d.d_v = DV;
     d.group = a.group;
+    d.chan_decay = ch;
     const size_t shmem = decode_multi_lds_bytes(d, a.t_new); // <= 64 KiB, checked by the caller
-    hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT>), dim3(batch * a.h_k), dim3(NT),
-                       shmem, s, a);
+    if (ch)
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true>), dim3(batch * a.h_k),
+                           dim3(NT), shmem, s, a);
+    else
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false>), dim3(batch * a.h_k),
+                           dim3(NT), shmem, s, a);
     return hipGetLastError();
 }
 
 template <typename TIn, int DK, int DV>
-static hipError_t launch_multi_slots(const MultiArgs &a, int batch, hipStream_t s)
+static hipError_t launch_multi_slots(const MultiArgs &a, bool ch, int batch, hipStream_t s)
 {
-    if (a.group % 2 == 0) return launch_multi_t<TIn, DK, DV, 2>(a, batch, s);
-    return launch_multi_t<TIn, DK, DV, 1>(a, batch, s);
+    if (a.group % 2 == 0) return launch_multi_t<TIn, DK, DV, 2>(a, ch, batch, s);
+    return launch_multi_t<TIn, DK, DV, 1>(a, ch, batch, s);
 }
 
 template <typename TIn>
-static hipError_t launch_multi_dims(const MultiArgs &a, int dk, int dv, int batch, hipStream_t s)
+static hipError_t launch_multi_dims(const MultiArgs &a, bool ch, int dk, int dv, int batch,
+                                    hipStream_t s)
 {
 #define GDN_MULTI_CASE(K_, V_)                                                                \
-    if (dk == K_ && dv == V_) return launch_multi_slots<TIn, K_, V_>(a, batch, s);
+    if (dk == K_ && dv == V_) return launch_multi_slots<TIn, K_, V_>(a, ch, batch, s);
     GDN_MULTI_CASE(32, 32) GDN_MULTI_CASE(32, 64) GDN_MULTI_CASE(32, 128)
     GDN_MULTI_CASE(64, 32) GDN_MULTI_CASE(64, 64) GDN_MULTI_CASE(64, 128)
     GDN_MULTI_CASE(128, 32) GDN_MULTI_CASE(128, 64) GDN_MULTI_CASE(128, 128)
@@ -387,8 +437,8 @@ hipError_t launch_decode_multi(const Dims &d, const Params &p, int batch, int t_
     args.tiled = d.tiled;
     args.norm_eps = d.norm_eps;
     args.l2_eps = d.l2_eps;
-    if (d.act_bf16) return launch_multi_dims<bf16_t>(args, d.d_k, d.d_v, batch, s);
-    return launch_multi_dims<float>(args, d.d_k, d.d_v, batch, s);
+    if (d.act_bf16) return launch_multi_dims<bf16_t>(args, d.chan_decay, d.d_k, d.d_v, batch, s);
+    return launch_multi_dims<float>(args, d.chan_decay, d.d_k, d.d_v, batch, s);
 }
 
 } // namespace gdn

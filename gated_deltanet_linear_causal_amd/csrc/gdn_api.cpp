@@ -51,6 +51,8 @@ gdn_status check_config(const gdn_config *cfg, gdn::Dims &d)
         return fail(GDN_EINVAL, "gate %d is not a gdn_gate", cfg->gate);
     if (cfg->head_map != GDN_HEADS_GROUPED && cfg->head_map != GDN_HEADS_TILED)
         return fail(GDN_EINVAL, "head_map %d is not a gdn_head_map", cfg->head_map);
+    if (cfg->decay_mode != GDN_DECAY_HEAD && cfg->decay_mode != GDN_DECAY_CHANNEL)
+        return fail(GDN_EINVAL, "decay_mode %d is not a gdn_decay_mode", cfg->decay_mode);
     if (!(cfg->norm_eps >= 0.0f) || !std::isfinite(cfg->norm_eps) || !(cfg->l2_eps >= 0.0f) ||
         !std::isfinite(cfg->l2_eps))
         return fail(GDN_EINVAL, "norm_eps and l2_eps must be finite and >= 0");
@@ -74,6 +76,7 @@ gdn_status check_config(const gdn_config *cfg, gdn::Dims &d)
     d.out_bf16 = cfg->out_dtype == GDN_BF16;
     d.gate = cfg->gate;
     d.tiled = cfg->head_map == GDN_HEADS_TILED;
+    d.chan_decay = cfg->decay_mode == GDN_DECAY_CHANNEL;
     d.norm_eps = cfg->norm_eps;
     d.l2_eps = cfg->l2_eps;
     return GDN_OK;
@@ -185,7 +188,7 @@ gdn_status gdn_decode_step(const gdn_config *cfg, const gdn_params *params, int3
     const Range ro{out, (size_t)batch * d.value_dim * osz};
     const Range ins[] = {{qkv, (size_t)batch * d.conv_dim * esz},
                          {z, (size_t)batch * d.value_dim * esz},
-                         {a, (size_t)batch * d.h_v * esz},
+                         {a, (size_t)batch * d.h_v * (d.chan_decay ? d.d_k : 1) * esz},
                          {b, (size_t)batch * d.h_v * esz}};
     for (const Range &r : ins)
         if (overlap(ro, r) || overlap(rs, r) || overlap(rc, r))
@@ -194,8 +197,14 @@ gdn_status gdn_decode_step(const gdn_config *cfg, const gdn_params *params, int3
         return fail(GDN_EINVAL, "out, state and conv_state must not overlap each other");
     // One token is the multi-token kernel with t_new = 1 whenever its
     // per-key-head buffer fits; very wide groups use the persistent
-    // single-token kernel, which needs no per-token buffer.
-    if (gdn::decode_multi_lds_bytes(d, 1) <= gdn::kDecodeMultiMaxLds)
+    // single-token kernel, which needs no per-token buffer (and has no
+    // per-channel decay).
+    const bool fits = gdn::decode_multi_lds_bytes(d, 1) <= gdn::kDecodeMultiMaxLds;
+    if (!fits && d.chan_decay)
+        return fail(GDN_EUNSUPPORTED,
+                    "per-channel decay needs %d conv channels per key head to fit the on-chip "
+                    "buffer", 2 * d.d_k + d.group * d.d_v);
+    if (fits)
         return hip_status(gdn::launch_decode_multi(d, p, batch, 1, nullptr, qkv, z, a, b,
                                                    conv_state, conv_state, state, state, nullptr,
                                                    out, static_cast<hipStream_t>(stream)),
@@ -245,7 +254,7 @@ gdn_status launch_multi_checked(const gdn::Dims &d, const gdn::Params &p, int32_
     const size_t cbytes = (size_t)batch * (d.conv_k - 1) * d.conv_dim * 4;
     const Range ins[] = {{qkv, tok * d.conv_dim * esz},
                          {z, tok * d.value_dim * esz},
-                         {a, tok * d.h_v * esz},
+                         {a, tok * d.h_v * (d.chan_decay ? d.d_k : 1) * esz},
                          {b, tok * d.h_v * esz},
                          {n_tok, (size_t)batch * 4}};
     const Range rsi{state_in, sbytes}, rso{state_out, sbytes};
@@ -322,9 +331,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seq, int32_t
                                    int32_t chunk)
 {
     gdn::Dims d;
-    const char *saved = nullptr;
-    (void)saved;
-    if (check_config(cfg, d) != GDN_OK || n_seq < 0 || t_total < 0 || chunk != 64) return 0;
+    if (check_config(cfg, d) != GDN_OK || n_seq < 0 || t_total < 0 || chunk != 64 || d.chan_decay)
+        return 0;
     return gdn::prefill_workspace_bytes(d, n_seq, t_total);
 }
 
@@ -341,6 +349,8 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, 
     if ((st = check_config(cfg, d)) != GDN_OK) return st;
     if ((st = check_params(params, p)) != GDN_OK) return st;
     if (chunk != 64) return fail(GDN_EUNSUPPORTED, "chunk must be 64 (got %d)", chunk);
+    if (d.chan_decay)
+        return fail(GDN_EUNSUPPORTED, "the chunked prefill has one decay per value head only");
     int max_len = 0;
     if ((st = check_cu(n_seq, t_total, cu_seqlens_host, cu_seqlens_dev, max_len)) != GDN_OK) return st;
     if (max_len > 65535 * 64) return fail(GDN_EUNSUPPORTED, "sequence longer than %d", 65535 * 64);

@@ -17,6 +17,7 @@ struct Dims {
     int out_bf16;   // 1: output is bf16, 0: fp32
     int gate;       // 0: SiLU, 1: sigmoid
     int tiled;      // 0: key head hv / group, 1: key head hv % h_k
+    int chan_decay; // 0: one decay per value head, 1: one per key channel
     float norm_eps, l2_eps;
 };
 

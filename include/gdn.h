@@ -66,6 +66,16 @@ typedef enum { GDN_GATE_SILU = 0, GDN_GATE_SIGMOID = 1 } gdn_gate;
  * conversions use.  The two agree when H_v == H_k. */
 typedef enum { GDN_HEADS_GROUPED = 0, GDN_HEADS_TILED = 1 } gdn_head_map;
 
+/* One decay per value head (Gated DeltaNet), or one per key channel of the
+ * value head (Kimi Delta Attention: "cortiq-engine 0.8.76 pipeline.rs",
+ * AttnKind::Kda, a per-channel decayed delta rule).  With
+ * GDN_DECAY_CHANNEL the gate input a is [T][H_v*d_k] and dt_bias
+ * [H_v*d_k]; g[i] = coef * softplus(a[i] + dt_bias[i]) and the state update
+ * starts with S <- diag(e^g) S.  Supported by gdn_decode_step,
+ * gdn_decode_multi and gdn_rewind; gdn_prefill_chunked returns
+ * GDN_EUNSUPPORTED for it. */
+typedef enum { GDN_DECAY_HEAD = 0, GDN_DECAY_CHANNEL = 1 } gdn_decay_mode;
+
 typedef struct {
     int32_t h_k, h_v;       /* key heads, value heads */
     int32_t d_k, d_v;       /* lanes per key / value head */
@@ -76,6 +86,7 @@ typedef struct {
     float norm_eps;         /* gated RMSNorm epsilon (1e-6 on the pages) */
     float l2_eps;           /* q/k L2-norm epsilon (1e-6 on the pages) */
     int32_t head_map;       /* gdn_head_map */
+    int32_t decay_mode;     /* gdn_decay_mode */
 } gdn_config;
 
 /* Exactly one of a_log and decay_coef is given, the other is NULL: the

@@ -34,7 +34,7 @@ def gpu_config(d: Dims, act_dtype: str, out_dtype=torch.float32):
     import gated_deltanet_linear_causal_amd as gdn
     return gdn.Config(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k,
                       torch.bfloat16 if act_dtype == "bf16" else torch.float32,
-                      out_dtype, d.gate, head_map=d.head_map)
+                      out_dtype, d.gate, head_map=d.head_map, decay=d.decay)
 
 
 def to_dev(t: torch.Tensor, act_dtype: str | None = None, device="cuda"):

@@ -47,7 +47,7 @@ def test_status_strings(lib):
 
 def _cfg(**kw):
     base = dict(h_k=2, h_v=4, d_k=64, d_v=64, conv_k=4, act_dtype=0, out_dtype=1, gate=0,
-                norm_eps=1e-6, l2_eps=1e-6, head_map=0)
+                norm_eps=1e-6, l2_eps=1e-6, head_map=0, decay_mode=0)
     base.update(kw)
     return gdn._Config(**base)
 
@@ -63,6 +63,8 @@ def test_workspace_bytes(lib):
     bad = _cfg(h_v=3)
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(bad), 1, 100, 64) == 0
     assert lib.gdn_prefill_workspace_bytes(None, 1, 100, 64) == 0
+    kda = _cfg(decay_mode=1)
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(kda), 1, 100, 64) == 0
 
 
 no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
@@ -89,7 +91,8 @@ def _decode(lib, cfg=None, params=None, batch=2, ptrs=None):
     (dict(h_v=3), EINVAL), (dict(h_k=0), EINVAL), (dict(d_k=48), EUNSUP),
     (dict(d_v=256), EUNSUP), (dict(conv_k=5), EUNSUP), (dict(conv_k=0), EINVAL),
     (dict(act_dtype=7), EINVAL), (dict(gate=2), EINVAL), (dict(norm_eps=-1.0), EINVAL),
-    (dict(l2_eps=float("nan")), EINVAL), (dict(head_map=2), EINVAL)])
+    (dict(l2_eps=float("nan")), EINVAL), (dict(head_map=2), EINVAL),
+    (dict(decay_mode=2), EINVAL)])
 def test_decode_rejects_bad_config(lib, kw, code):
     assert _decode(lib, _cfg(**kw)) == code
     assert lib.gdn_last_error().decode() != ""
@@ -181,6 +184,8 @@ def test_prefill_rejects_bad_cu_seqlens(lib):
 @no_gpu
 def test_prefill_rejects_chunk_workspace_and_aliases(lib):
     assert _prefill(lib, [0, 10], 10, chunk=32) == EUNSUP
+    assert _prefill(lib, [0, 10], 10, cfg=_cfg(decay_mode=1)) == EUNSUP
+    assert "decay" in lib.gdn_last_error().decode()
     assert _prefill(lib, [0, 10], 10, ws=(_P[9], 100)) == EWS
     assert _prefill(lib, [0, 10], 10, ws=(None, 1 << 40)) == EWS
     assert _prefill(lib, [0, 10], 10, ws=(ctypes.c_void_p(_P[9].value + 8), 1 << 40)) == EINVAL

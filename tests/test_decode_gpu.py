@@ -123,6 +123,29 @@ def test_decode_head_map_and_decay_coef(gdn, v):
     np.testing.assert_array_equal(conv.numpy(), conv_ref)
 
 
+KDA = [
+    # h_k, h_v, d_k, d_v, K, act, gate, head_map
+    (2, 4, 128, 128, 4, "bf16", "sigmoid", "grouped"),
+    (2, 2, 64, 32, 3, "f32", "sigmoid", "tiled"),
+    (1, 3, 32, 64, 4, "bf16", "silu", "grouped"),
+]
+
+
+@pytest.mark.parametrize("v", KDA, ids=lambda v: "hk%d_hv%d_dk%d_dv%d_K%d_%s_%s_%s" % v)
+def test_decode_per_channel_decay(gdn, v):
+    """One decay per key channel (Kimi Delta Attention, "cortiq-engine
+    0.8.76 pipeline.rs", AttnKind::Kda), consecutive single-token steps."""
+    hk, hv, dk, dv, K, act, gate, head_map = v
+    d = Dims(hk, hv, dk, dv, K, gate, head_map, decay="channel")
+    case = make_case(d, [0, 0, 0], act_dtype=act, seed=600 + hk + hv + dk + dv, decay="weak",
+                     s0_std=0.3, conv0_std=1.0, decode_steps=8)
+    y, S, conv = run_decode(gdn, case, 8)
+    y_ref, S_ref, conv_ref = oracle_decode(case, 8)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
 def test_decode_bf16_out_is_rne_of_fp32_out(gdn):
     case = make_case(Dims(2, 4, 128, 128), [0] * 5, act_dtype="bf16", seed=7,
                      s0_std=0.02, conv0_std=1.0, decode_steps=3)

@@ -88,6 +88,9 @@ VARIANTS = [
     (2, 6, 64, 64, 4, "bf16", 4, "tiled", False),
     (2, 4, 32, 128, 1, "f32", 6, "tiled", True),
     (1, 2, 128, 64, 4, "bf16", 7, "grouped", False),
+    # one decay per key channel (Kimi Delta Attention)
+    (2, 4, 128, 128, 4, "bf16", 6, "grouped", "channel"),
+    (2, 2, 64, 64, 2, "f32", 8, "tiled", "channel"),
 ]
 
 
@@ -96,9 +99,11 @@ def test_decode_multi_ragged_counts_and_checkpoints(gdn, v):
     """Per-sequence token counts (0, T and in between), outputs, final
     states, histories and every per-token checkpoint against the oracle."""
     hk, hv, dk, dv, K, act, T, head_map, coef = v
-    d = Dims(hk, hv, dk, dv, K, "silu", head_map)
+    chan = coef == "channel"
+    d = Dims(hk, hv, dk, dv, K, "sigmoid" if chan else "silu", head_map,
+             decay="channel" if chan else "head")
     B = 5
-    case = spec_case(d, B, T, act, seed=500 + hk * 10 + hv + dk + T, coef=coef)
+    case = spec_case(d, B, T, act, seed=500 + hk * 10 + hv + dk + T, coef=coef is True)
     counts = [T, 0, 1, T - 1, max(T // 2, 1)]
     y, S, conv, ck = run_multi(gdn, case, counts, ckpt=True)
     y_ref, S_ref, conv_ref = oracle_prefix(case, counts)
@@ -164,6 +169,28 @@ def test_verify_then_rewind(gdn):
     gdn.rewind(cfg, prm, qkv, a, b, S0, C0, keep=keep, state=S0, conv_state=C0)
     torch.cuda.synchronize()
     assert torch.equal(S0, S_k) and torch.equal(C0, C_k)
+
+
+def test_verify_then_rewind_per_channel_decay(gdn):
+    """The rewind contract with one decay per key channel."""
+    d = Dims(2, 4, 64, 64, 4, "sigmoid", decay="channel")
+    B, T = 3, 5
+    case = spec_case(d, B, T, "bf16", seed=22)
+    cfg = P.gpu_config(d, "bf16")
+    prm = P.dev_params(case)
+    qkv, a, b = (P.to_dev(bt(case, k), "bf16") for k in ("qkv", "a", "b"))
+    z = P.to_dev(bt(case, "z"), "bf16")
+    S0, C0 = case.S0.clone().cuda(), case.conv0.clone().cuda()
+    S, C = S0.clone(), C0.clone()
+    gdn.decode_multi(cfg, prm, qkv, z, a, b, C, S)
+    S_all, C_all = gdn.rewind(cfg, prm, qkv, a, b, S0, C0)
+    keep = [1, 3, 5]
+    S_k, C_k = gdn.rewind(cfg, prm, qkv, a, b, S0, C0, keep=keep)
+    torch.cuda.synchronize()
+    assert torch.equal(S_all, S) and torch.equal(C_all, C)
+    _, S_ref, C_ref = oracle_prefix(case, keep)
+    P.assert_state_close(S_k.cpu(), S_ref)
+    np.testing.assert_array_equal(C_k.cpu().numpy(), C_ref)
 
 
 def test_decode_multi_one_token_matches_decode_step(gdn):
