@@ -56,12 +56,14 @@ def decode_bytes(d, batch):
 def decode_multi_bytes(d, batch, t_new):
     """Algorithmic HBM bytes of one multi-token decode call: the state and
     conv history cross HBM once (read + write) whatever t_new is; inputs and
-    outputs scale with the tokens."""
+    outputs scale with the tokens.  With one decay per key channel the gate
+    input a and dt_bias carry d_k values per value head."""
+    gw = d.gate_width
     state = batch * d.h_v * d.d_k * d.d_v * 4 * 2
     conv = batch * (d.conv_k - 1) * d.conv_dim * 4 * 2
-    inp = batch * t_new * (d.conv_dim + d.value_dim + 2 * d.h_v) * 2
+    inp = batch * t_new * (d.conv_dim + d.value_dim + d.h_v + d.h_v * gw) * 2
     out = batch * t_new * d.value_dim * 2
-    params = (d.conv_dim * d.conv_k + 2 * d.h_v + d.d_v) * 4
+    params = (d.conv_dim * d.conv_k + d.h_v + d.h_v * gw + d.d_v) * 4
     return state + conv + inp + out + params
 
 
@@ -338,6 +340,34 @@ def main():
         torch.cuda.synchronize()
         multi[t_new] = (ev_m[0].elapsed_time(ev_m[1]) / calls, calls)
 
+    # The per-channel-decay variant (Kimi Delta Attention) on the same batch:
+    # one token per sequence and four.
+    from gdn_inputs import make_case
+    kd = BIG.__class__(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, "sigmoid", decay="channel")
+    kcase = None if args.no_multi else make_case(kd, [0] * B, act_dtype="bf16", seed=5,
+                                                  s0_std=0.02, conv0_std=1.0, decode_steps=4)
+    kda = {}
+    if kcase is not None:
+        kcfg = gdn.Config(kd.h_k, kd.h_v, kd.d_k, kd.d_v, kd.conv_k, bf, bf, "sigmoid",
+                          decay="channel")
+        kparams = {k: v.to(dev) for k, v in kcase.params.items()}
+        S_k, c_k = kcase.S0.to(dev), kcase.conv0.to(dev)
+        for t_new in (1, 4):
+            xm = [kcase.dec[k][:t_new].transpose(0, 1).to(bf).to(dev).contiguous()
+                  for k in ("qkv", "z", "a", "b")]
+            out_m = torch.empty((B, t_new, d.value_dim), dtype=bf, device=dev)
+            calls = 50
+            for _ in range(3):
+                gdn.decode_multi(kcfg, kparams, *xm, c_k, S_k, out=out_m, stream=stream)
+            ev_m = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev_m[0].record(stream)
+            for _ in range(calls):
+                gdn.decode_multi(kcfg, kparams, *xm, c_k, S_k, out=out_m, stream=stream)
+            ev_m[1].record(stream)
+            torch.cuda.synchronize()
+            kda[t_new] = (ev_m[0].elapsed_time(ev_m[1]) / calls, calls)
+        del S_k, c_k
+
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -371,6 +401,16 @@ def main():
                "mfma_busy": load_counter("prefill_call", "mfma_busy"),
                "hbm_frac": round(pbytes / (pf_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     roof_multi = {}
+    for t_new, (ms, calls) in kda.items():
+        mb = decode_multi_bytes(kd, B, t_new)
+        gbs = mb / (ms * 1e-3) / 1e9
+        roof_multi[f"kda_decode_t{t_new}"] = {
+            "kernel": f"gdn::decode_multi_kernel, one decay per key channel "
+                      f"(gdn_decode_multi, {t_new} tokens/sequence)",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": mb, "duration_us": round(ms * 1e3, 2),
+            "launches_timed": calls, "tokens_per_s": round(B * t_new / (ms * 1e-3), 1)}
     for t_new, (ms, calls) in multi.items():
         mb = decode_multi_bytes(d, B, t_new)
         gbs = mb / (ms * 1e-3) / 1e9

@@ -67,7 +67,7 @@ __device__ __forceinline__ float pick3(const float (&w)[3], int i)
 }
 
 template <typename TIn, int DK, int DV, int NSLOT, bool CH>
-__global__ void __launch_bounds__(2 * DV * NSLOT)
+__global__ void __launch_bounds__(2 * DV * NSLOT) __attribute__((amdgpu_waves_per_eu(4)))
 decode_multi_kernel(const MultiArgs p)
 {
     constexpr int TPH = 2 * DV;     // threads per value head
@@ -131,7 +131,7 @@ decode_multi_kernel(const MultiArgs p)
     }
     // per-channel decay inputs: element e = (pair, channel) of a [.][H_v*d_k]
     auto alpha_index = [&](int e) { return gate_index(e / DK) * DK + e % DK; };
-    constexpr int kAlphaPre = 4; // elements per thread loaded up front
+    constexpr int kAlphaPre = 2; // elements per thread loaded up front
     TIn gac[kAlphaPre];
 #pragma unroll
     for (int k = 0; k < kAlphaPre; ++k) {
