@@ -347,6 +347,7 @@ def main():
     kcase = None if args.no_multi else make_case(kd, [0] * B, act_dtype="bf16", seed=5,
                                                   s0_std=0.02, conv0_std=1.0, decode_steps=4)
     kda = {}
+    kda_pf = None
     if kcase is not None:
         kcfg = gdn.Config(kd.h_k, kd.h_v, kd.d_k, kd.d_v, kd.conv_k, bf, bf, "sigmoid",
                           decay="channel")
@@ -367,6 +368,24 @@ def main():
             torch.cuda.synchronize()
             kda[t_new] = (ev_m[0].elapsed_time(ev_m[1]) / calls, calls)
         del S_k, c_k
+        # chunked prefill with one decay per key channel, T=4096, zero state
+        kpf = make_case(kd, [T], act_dtype="bf16", seed=6)
+        kx = [getattr(kpf, k).to(bf).to(dev).contiguous() for k in ("qkv", "z", "a", "b")]
+        kpp = {k: v.to(dev) for k, v in kpf.params.items()}
+        kws = gdn.alloc_workspace(kcfg, 1, T, dev)
+        for _ in range(3):
+            gdn.prefill_chunked(kcfg, kpp, seq, *kx, state_out=S_pf, conv_out=c_pf, out=out_pf,
+                                workspace=kws, stream=stream)
+        ev_m = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        calls = 20
+        ev_m[0].record(stream)
+        for _ in range(calls):
+            gdn.prefill_chunked(kcfg, kpp, seq, *kx, state_out=S_pf, conv_out=c_pf, out=out_pf,
+                                workspace=kws, stream=stream)
+        ev_m[1].record(stream)
+        torch.cuda.synchronize()
+        kda_pf = (ev_m[0].elapsed_time(ev_m[1]) / calls, calls)
+        del kws
 
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -411,6 +430,16 @@ def main():
             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
             "algorithmic_bytes_per_launch": mb, "duration_us": round(ms * 1e3, 2),
             "launches_timed": calls, "tokens_per_s": round(B * t_new / (ms * 1e-3), 1)}
+    if kda_pf is not None:
+        ms, calls = kda_pf
+        tf = pflops / (ms * 1e-3) / 1e12
+        roof_multi["kda_prefill"] = {
+            "kernel": "gdn_prefill_chunked, one decay per key channel (kda_intra, tri, scan, "
+                      "norm, conv_final launches)",
+            "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": pflops, "duration_us": round(ms * 1e3, 2),
+            "launches_timed": calls, "tokens_per_s": round(T / (ms * 1e-3), 1)}
     for t_new, (ms, calls) in multi.items():
         mb = decode_multi_bytes(d, B, t_new)
         gbs = mb / (ms * 1e-3) / 1e9

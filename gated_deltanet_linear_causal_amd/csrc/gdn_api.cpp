@@ -331,8 +331,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seq, int32_t
                                    int32_t chunk)
 {
     gdn::Dims d;
-    if (check_config(cfg, d) != GDN_OK || n_seq < 0 || t_total < 0 || chunk != 64 || d.chan_decay)
-        return 0;
+    if (check_config(cfg, d) != GDN_OK || n_seq < 0 || t_total < 0 || chunk != 64) return 0;
     return gdn::prefill_workspace_bytes(d, n_seq, t_total);
 }
 
@@ -349,8 +348,6 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, 
     if ((st = check_config(cfg, d)) != GDN_OK) return st;
     if ((st = check_params(params, p)) != GDN_OK) return st;
     if (chunk != 64) return fail(GDN_EUNSUPPORTED, "chunk must be 64 (got %d)", chunk);
-    if (d.chan_decay)
-        return fail(GDN_EUNSUPPORTED, "the chunked prefill has one decay per value head only");
     int max_len = 0;
     if ((st = check_cu(n_seq, t_total, cu_seqlens_host, cu_seqlens_dev, max_len)) != GDN_OK) return st;
     if (max_len > 65535 * 64) return fail(GDN_EUNSUPPORTED, "sequence longer than %d", 65535 * 64);
@@ -369,7 +366,7 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, 
     const size_t cbytes = (size_t)n_seq * (d.conv_k - 1) * d.conv_dim * 4;
     const Range ins[] = {{qkv, (size_t)t_total * d.conv_dim * esz},
                          {z, (size_t)t_total * d.value_dim * esz},
-                         {a, (size_t)t_total * d.h_v * esz},
+                         {a, (size_t)t_total * d.h_v * (d.chan_decay ? d.d_k : 1) * esz},
                          {b, (size_t)t_total * d.h_v * esz}};
     const Range ro{out, (size_t)t_total * d.value_dim * osz};
     const Range rsi{state_in, sbytes}, rso{state_out, sbytes};

@@ -198,9 +198,15 @@ __device__ __forceinline__ void lds_barrier()
 //        16 slice + l%16)
 //   gf   [H_v][slot][e^G, e^{G_C-G}][64] fp32
 //   o    [H_v][T][d_v] fp32 pre-norm readout
+//
+// With one decay per key channel (Kimi Delta Attention) the decay sits
+// inside the q/k operands, so qf, ktf and gram are per value head and hold
+// q^ (.) e^G, (k^ (.) e^{G_C-G})^T and the decayed Gram tiles; kw
+// [H_v][slot] (ktf layout) holds (k^ (.) e^G)^T for W, and gf the chunk
+// decay e^{G_C} of each key channel ([d_k] of the 128 floats).
 // ---------------------------------------------------------------------------
 struct WsLayout {
-    size_t qf, ktf, gram, wf, pf, uf, gf, o, total;
+    size_t qf, ktf, gram, wf, pf, uf, gf, o, kw, total;
     int ns;
 };
 
@@ -214,13 +220,16 @@ static WsLayout ws_layout(const Dims &d, int n_seq, int t_total)
     w.ns = chunk_slots(n_seq, t_total);
     const size_t NS = (size_t)w.ns;
     const size_t frag_dk = (size_t)kC * d.d_k * 2 * 2; // bytes of a 64 x d_k hi/lo block
+    // With one decay per key channel the q/k operands and the Gram tiles
+    // carry that decay, so they exist per value head.
+    const size_t hq = d.chan_decay ? d.h_v : d.h_k;
     size_t off = 0;
     w.qf = off;
-    off = align256(off + d.h_k * NS * frag_dk);
+    off = align256(off + hq * NS * frag_dk);
     w.ktf = off;
-    off = align256(off + d.h_k * NS * frag_dk);
+    off = align256(off + hq * NS * frag_dk);
     w.gram = off;
-    off = align256(off + d.h_k * NS * 2 * kC * kC * sizeof(float));
+    off = align256(off + hq * NS * 2 * kC * kC * sizeof(float));
     w.wf = off;
     off = align256(off + d.h_v * NS * frag_dk);
     w.pf = off;
@@ -231,6 +240,8 @@ static WsLayout ws_layout(const Dims &d, int n_seq, int t_total)
     off = align256(off + d.h_v * NS * 2 * kC * sizeof(float));
     w.o = off;
     off = align256(off + (size_t)t_total * d.value_dim * sizeof(float));
+    w.kw = off; // per-channel decay only: k^ (.) e^G fragments for W
+    off = align256(off + (d.chan_decay ? d.h_v * NS * frag_dk : 0));
     w.total = off;
     return w;
 }
@@ -250,11 +261,11 @@ struct PrefillArgs {
     const float *conv_in;
     float *conv_out;
     void *out;
-    __bf16 *ws_qf, *ws_ktf, *ws_wf, *ws_pf;
+    __bf16 *ws_qf, *ws_ktf, *ws_wf, *ws_pf, *ws_kw;
     float *ws_gram, *ws_uf, *ws_gf, *ws_o;
     int ns, t_total;
     int h_k, h_v, d_v, group, conv_k, conv_dim, value_dim;
-    int gate, out_bf16, tiled;
+    int gate, out_bf16, tiled, kda;
     float norm_eps, l2_eps;
 };
 
@@ -481,6 +492,266 @@ qknorm_kernel(const PrefillArgs p)
 }
 
 // ---------------------------------------------------------------------------
+// kda_intra: the intra-chunk operands when each key channel has its own
+// decay (Kimi Delta Attention, "cortiq-engine 0.8.76 pipeline.rs",
+// AttnKind::Kda).  The decay then sits inside the key/query dot products,
+//   A'[i][j] = sum_d k[i][d] k[j][d] e^{G[i][d] - G[j][d]},
+//   P'[i][j] = sum_d q[i][d] k[j][d] e^{G[i][d] - G[j][d]}     (j <= i),
+// with G[t][d] the prefix over the chunk of g[t][d] = c softplus(a + dt_bias)
+// (G <= 0, non-increasing in t), so no Gram matrix can be shared by the
+// value heads of a group.  One workgroup per (chunk, value head, sequence),
+// 512 threads (the fp32 rows fill 100 KB of LDS, so one workgroup per CU;
+// eight waves keep two per SIMD):
+//   1. conv + SiLU + L2 norm of the chunk's q and k rows (fp32 in LDS) and
+//      the per-channel prefix G;
+//   2. A' and P': 16x16 blocks below the diagonal on the matrix cores with
+//      both factors taken relative to the last row r of the column block
+//      (e^{G[i]-G[r]} <= 1 for i > r, e^{G[r]-G[j]} <= 1 for j <= r, so
+//      nothing overflows), diagonal blocks with one exponential per
+//      (i, j, d);
+//   3. the fragments the later kernels read: (k^ (.) e^G)^T for W, q^ (.) e^G
+//      for the read-out, (k^ (.) e^{G_C-G})^T for the state update, and the
+//      chunk decay e^{G_C} of each channel.
+// ---------------------------------------------------------------------------
+template <int DK> constexpr size_t kda_smem_bytes() { return 3 * (size_t)kC * (DK + 4) * 4; }
+
+template <typename TIn, int DK>
+__global__ void __launch_bounds__(512)
+kda_intra_kernel(const PrefillArgs p)
+{
+    constexpr int NW = 8;                    // waves
+    constexpr int RQ = DK + 4;               // fp32 LDS row stride
+    constexpr int LPT = DK / 4;              // lanes per token row (8 channels each)
+    constexpr int TPI = 64 / LPT;            // token rows per wave pass
+    constexpr int TPL = kC / (NW * TPI);     // consecutive tokens per lane
+    constexpr int WIN = TPL + 3;             // raw rows a lane reads
+    constexpr int KS = DK / 32, MTS = DK / 16;
+    constexpr int NPART = 64 * NW / DK, TPP = kC / NPART; // gate prefix: parts of the chunk
+    const int c = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
+    const int s0 = p.cu[n], L = p.cu[n + 1] - s0;
+    if (c * kC >= L) return;
+    const int t0 = s0 + c * kC;
+    const int Lc = min(kC, L - c * kC);
+    const int hk = key_head_of(hv, p.h_k, p.group, p.tiled);
+    const int slot = s0 / kC + n + c;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kq = lane >> 4;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float *sQ = reinterpret_cast<float *>(smem);
+    float *sK = sQ + kC * RQ;
+    float *sG = sK + kC * RQ;
+
+    // ---- loads: raw q/k rows (as the scalar-decay path) and gate inputs
+    const int sub = lane / LPT, ll = lane % LPT;
+    const bool isk = ll >= DK / 8;
+    const int c8 = (isk ? ll - DK / 8 : ll) * 8;
+    const int ch = (isk ? p.h_k * DK : 0) + hk * DK + c8;
+    const TIn *x = static_cast<const TIn *>(p.qkv);
+    const int r0 = kC / NW * wave + TPL * sub;
+    const int tl0 = c * kC + r0;
+    typedef typename RawAct<TIn>::type RawT;
+    RawT raw[WIN][2];
+#pragma unroll
+    for (int j = 0; j < WIN; ++j) {
+        const int tau = min(max(tl0 - 3 + j, 0), L - 1);
+        const size_t base = (size_t)(s0 + tau) * p.conv_dim + ch;
+        raw[j][0] = RawAct<TIn>::load(x, base);
+        raw[j][1] = RawAct<TIn>::load(x, base + 4);
+    }
+    const TIn *pa = static_cast<const TIn *>(p.a);
+    const int gd = tid % DK, gpart = tid / DK;
+    float araw[TPP];
+#pragma unroll
+    for (int tt = 0; tt < TPP; ++tt) {
+        const int t = gpart * TPP + tt;
+        araw[tt] = t < Lc ? load_act(pa, (size_t)(t0 + t) * p.h_v * DK + (size_t)hv * DK + gd) : 0.0f;
+    }
+    float w0[4][4], w1[4][4];
+    load_taps4(p, ch, w0);
+    load_taps4(p, ch + 4, w1);
+    const float extra = isk ? 1.0f : rsqrtf((float)DK);
+
+    // ---- 1. conv + SiLU + L2 norm, fp32 rows (zero past the sequence end)
+    {
+        f32x4 xv[WIN][2];
+#pragma unroll
+        for (int j = 0; j < WIN; ++j) {
+            xv[j][0] = RawAct<TIn>::to_f32(raw[j][0]);
+            xv[j][1] = RawAct<TIn>::to_f32(raw[j][1]);
+        }
+        if (tl0 < 3) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                if (tl0 - 3 + j < 0) {
+                    xv[j][0] = raw4(p, x, n, s0, tl0 - 3 + j, ch);
+                    xv[j][1] = raw4(p, x, n, s0, tl0 - 3 + j, ch + 4);
+                }
+        }
+#pragma unroll
+        for (int k = 0; k < TPL; ++k) {
+            const int r = r0 + k, tl = tl0 + k;
+            const f32x4 xa[4] = {xv[k][0], xv[k + 1][0], xv[k + 2][0], xv[k + 3][0]};
+            const f32x4 xb[4] = {xv[k][1], xv[k + 1][1], xv[k + 2][1], xv[k + 3][1]};
+            const f32x4 ca = conv4(w0, xa), cb = conv4(w1, xb);
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += ca[e] * ca[e] + cb[e] * cb[e];
+            ss = row_sum<DK / 8>(ss);
+            const float sc = tl < L ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
+            float *dst = (isk ? sK : sQ) + r * RQ + c8;
+            *reinterpret_cast<f32x4 *>(dst) = ca * sc;
+            *reinterpret_cast<f32x4 *>(dst + 4) = cb * sc;
+        }
+    }
+    // per-channel log-decays and their prefix within each part of the chunk
+    {
+        const float coef = decay_coef_of(p.a_log, p.decay_coef, hv);
+        const float dtb = p.dt_bias[(size_t)hv * DK + gd];
+        float G = 0.0f;
+#pragma unroll
+        for (int tt = 0; tt < TPP; ++tt) {
+            const int t = gpart * TPP + tt;
+            if (t < Lc) { // g = 0 past the end
+                // softplus(x) = max(x, 0) + log(1 + e^{-|x|}): the hardware
+                // exp/log, absolute error ~1e-7 (8192 of them per workgroup)
+                const float x = araw[tt] + dtb;
+                G += coef * (fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))));
+            }
+            sG[t * RQ + gd] = G;
+        }
+    }
+    __syncthreads();
+    {
+        float off = 0.0f;
+        for (int pp = 0; pp < gpart; ++pp) off += sG[((pp + 1) * TPP - 1) * RQ + gd];
+        __syncthreads();
+        if (gpart > 0)
+#pragma unroll
+            for (int tt = 0; tt < TPP; ++tt) sG[(gpart * TPP + tt) * RQ + gd] += off;
+    }
+    __syncthreads();
+
+    // ---- 2. decayed Gram tiles
+    float *gram = p.ws_gram + ((size_t)hv * p.ns + slot) * (2 * kC * kC);
+    {
+        // blocks (I, J), I > J, on the matrix cores: wave w < 6 takes pair
+        // w of (1,0) (2,0) (3,0) (2,1) (3,1) (3,2)
+        if (wave < 6) {
+            const int pr = wave;
+            const int bI = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
+            const int bJ = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
+            const int r = 16 * bJ + 15, i = 16 * bI + col, j = 16 * bJ + col;
+            f32x4 aa = {0.f, 0.f, 0.f, 0.f}, ap = aa;
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+                const int d0 = 32 * st + 8 * kq;
+                float va[8], vq[8], vb[8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4 gr = ld4(sG + r * RQ + d0 + 4 * h);
+                    const f32x4 gi = ld4(sG + i * RQ + d0 + 4 * h), gj = ld4(sG + j * RQ + d0 + 4 * h);
+                    const f32x4 ki = ld4(sK + i * RQ + d0 + 4 * h), qi = ld4(sQ + i * RQ + d0 + 4 * h);
+                    const f32x4 kj = ld4(sK + j * RQ + d0 + 4 * h);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float ei = __expf(gi[e] - gr[e]), ej = __expf(gr[e] - gj[e]);
+                        va[4 * h + e] = ki[e] * ei;
+                        vq[4 * h + e] = qi[e] * ei;
+                        vb[4 * h + e] = kj[e] * ej;
+                    }
+                }
+                const Frag fb = split8(vb);
+                aa = mma3(split8(va), fb, aa);
+                ap = mma3(split8(vq), fb, ap);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ri = 16 * bI + 4 * kq + e, cj = 16 * bJ + col;
+                gram[ri * kC + cj] = aa[e];
+                gram[kC * kC + ri * kC + cj] = ap[e];
+            }
+        }
+        // diagonal blocks: wave w takes block w % 4 and columns 2 (w / 4),
+        // 2 (w / 4) + 1 of each column quad; lane (row col, quad kq); one
+        // exponential per (i, j, d), computed for every lane and masked (a
+        // term with j > i may overflow, so it is selected away, never
+        // multiplied); zero above the diagonal
+        const int b = wave & 3, jh = wave >> 2, i = 16 * b + col;
+        float acc_a[2] = {0.f, 0.f}, acc_p[2] = {0.f, 0.f};
+        bool live[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) live[jj] = 4 * kq + 2 * jh + jj <= col;
+        for (int d4 = 0; d4 < DK / 4; ++d4) {
+            const f32x4 ki = ld4(sK + i * RQ + 4 * d4), qi = ld4(sQ + i * RQ + 4 * d4);
+            const f32x4 gi = ld4(sG + i * RQ + 4 * d4);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 16 * b + 4 * kq + 2 * jh + jj;
+                const f32x4 kj = ld4(sK + j * RQ + 4 * d4), gj = ld4(sG + j * RQ + 4 * d4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ex = __expf(gi[e] - gj[e]);
+                    const float w = live[jj] ? kj[e] * ex : 0.0f;
+                    acc_a[jj] = fmaf(ki[e], w, acc_a[jj]);
+                    acc_p[jj] = fmaf(qi[e], w, acc_p[jj]);
+                }
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 16 * b + 4 * kq + 2 * jh + jj;
+            gram[i * kC + j] = live[jj] ? acc_a[jj] : 0.0f;
+            gram[kC * kC + i * kC + j] = live[jj] ? acc_p[jj] : 0.0f;
+        }
+    }
+
+    // ---- 3. decayed operand fragments and the chunk decay
+    {
+        const size_t fbase = ((size_t)hv * p.ns + slot) * (2 * kC * DK) + lane * 8;
+        // (k^ (.) e^G)^T for W, and (k^ (.) e^{G_C - G})^T for the state
+        // update: lane (i, q) of fragment (rb, s) holds tokens 32 s + 8 q + e
+        // of channel 16 rb + i
+        for (int f = wave; f < MTS * 2; f += NW) {
+            const int st = f & 1, rb = f >> 1;
+            const int d = 16 * rb + col, t = 32 * st + 8 * kq;
+            const float gC = sG[(kC - 1) * RQ + d];
+            float vw[8], vs[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kv = sK[(t + e) * RQ + d], g = sG[(t + e) * RQ + d];
+                vw[e] = kv * __expf(g);
+                vs[e] = kv * __expf(gC - g);
+            }
+            const Frag a = split8(vw), bq = split8(vs);
+            const int fi = (rb * 2 + st) * 2;
+            *reinterpret_cast<bf16x8 *>(p.ws_kw + fbase + (size_t)fi * 512) = a.hi;
+            *reinterpret_cast<bf16x8 *>(p.ws_kw + fbase + (size_t)(fi + 1) * 512) = a.lo;
+            *reinterpret_cast<bf16x8 *>(p.ws_ktf + fbase + (size_t)fi * 512) = bq.hi;
+            *reinterpret_cast<bf16x8 *>(p.ws_ktf + fbase + (size_t)(fi + 1) * 512) = bq.lo;
+        }
+        // q^ (.) e^G, d_k-permuted: lane (row col, q) of fragment (rb, s) holds
+        // channels 32 s + 4 q + e and 32 s + 16 + 4 q + e of row 16 rb + col
+        for (int f = wave; f < 4 * KS; f += NW) {
+            const int st = f % KS, rb = f / KS;
+            const int t = 16 * rb + col, d0 = 32 * st + 4 * kq;
+            const f32x4 q0 = ld4(sQ + t * RQ + d0), q1 = ld4(sQ + t * RQ + d0 + 16);
+            const f32x4 g0 = ld4(sG + t * RQ + d0), g1 = ld4(sG + t * RQ + d0 + 16);
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = q0[e] * __expf(g0[e]);
+                v[4 + e] = q1[e] * __expf(g1[e]);
+            }
+            const Frag fq = split8(v);
+            *reinterpret_cast<bf16x8 *>(p.ws_qf + fbase + (size_t)(2 * f) * 512) = fq.hi;
+            *reinterpret_cast<bf16x8 *>(p.ws_qf + fbase + (size_t)(2 * f + 1) * 512) = fq.lo;
+        }
+        if (tid < DK)
+            p.ws_gf[((size_t)hv * p.ns + slot) * (2 * kC) + tid] = __expf(sG[(kC - 1) * RQ + tid]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // tri: one workgroup per (chunk, value head, sequence), 256 threads.
 // ---------------------------------------------------------------------------
 template <int DV> struct TriLds {
@@ -492,7 +763,7 @@ template <int DV> struct TriLds {
     static constexpr int total = o_u + (ap > vt ? ap : vt);
 };
 
-template <typename TIn, int DK, int DV>
+template <typename TIn, int DK, int DV, bool KDA>
 __global__ void __launch_bounds__(256)
 tri_kernel(const PrefillArgs p)
 {
@@ -525,7 +796,7 @@ tri_kernel(const PrefillArgs p)
     float a_raw = 0.0f, b_raw = 0.0f;
     if (wave == 0 && lane < Lc) {
         const size_t gi = (size_t)(t0 + lane) * p.h_v + hv;
-        a_raw = load_act(pa, gi);
+        if (!KDA) a_raw = load_act(pa, gi);
         b_raw = load_act(pb, gi);
     }
     // Gram rows: thread (i, jq) holds row i, columns 16 jq .. 16 jq + 15 of
@@ -534,7 +805,8 @@ tri_kernel(const PrefillArgs p)
     const bool glive = gq <= (gi_ >> 4);
     f32x4 gkk[4], gqk[4];
     {
-        const float *g = p.ws_gram + ((size_t)hk * p.ns + slot) * (2 * kC * kC) + gi_ * kC + 16 * gq;
+        const float *g = p.ws_gram + ((size_t)(KDA ? hv : hk) * p.ns + slot) * (2 * kC * kC) +
+                         gi_ * kC + 16 * gq;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             gkk[m] = glive ? ld4(g + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -544,7 +816,15 @@ tri_kernel(const PrefillArgs p)
     // ---- gates ("cherenkov qwen4_exp/cpu.rs" fn deltanet) and their
     // inclusive prefix sum over the chunk (wave 0); past the chunk end
     // g = 0 and b = 0.
-    if (wave == 0) {
+    // (with one decay per key channel the decay is already inside the Gram
+    // tiles and the k operand: only beta is needed here)
+    if (KDA && wave == 0) {
+        const float beta = lane < Lc ? sigmoidf_(b_raw) : 0.0f;
+        sG[lane] = 0.0f;
+        sB[lane] = beta;
+        sBE[lane] = beta;
+    }
+    if (!KDA && wave == 0) {
         float beta = 0.0f, g = 0.0f;
         if (lane < Lc) {
             beta = sigmoidf_(b_raw);
@@ -576,7 +856,7 @@ tri_kernel(const PrefillArgs p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 16 * gq + 4 * m + e;
-                const float md = j <= i ? expf(Gi - sG[j]) : 0.0f;
+                const float md = j <= i ? (KDA ? 1.0f : expf(Gi - sG[j])) : 0.0f;
                 av[e] = j < i ? bi * md * gkk[m][e] : 0.0f;
                 pv[e] = md * gqk[m][e];
             }
@@ -621,7 +901,8 @@ tri_kernel(const PrefillArgs p)
     const bool wact = sp < KS;
     Frag kA[2][2];
     if (wact) {
-        const __bf16 *kt = p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK) + lane * 8;
+        const __bf16 *kt = (KDA ? p.ws_kw + ((size_t)hv * p.ns + slot) * (2 * kC * DK)
+                                : p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK)) + lane * 8;
 #pragma unroll
         for (int n2 = 0; n2 < 2; ++n2)
 #pragma unroll
@@ -784,7 +1065,7 @@ tri_kernel(const PrefillArgs p)
 // double-buffered by chunk parity), D (double-buffered) and e^{G_C-G} D.
 // Both roles meet at the same two barriers per chunk.
 // ---------------------------------------------------------------------------
-template <int DK>
+template <int DK, bool KDA>
 __global__ void __launch_bounds__(512)
 scan_kernel(const PrefillArgs p, int slices)
 {
@@ -826,7 +1107,9 @@ scan_kernel(const PrefillArgs p, int slices)
 
     if (wave < 4) {
         // ================= chain waves ===================================
-        const __bf16 *ktf = p.ws_ktf + ((size_t)hk * p.ns + slot0) * (2 * kC * DK) + lane * 8;
+        // (per value head when each key channel has its own decay)
+        const int hq = KDA ? hv : hk;
+        const __bf16 *ktf = p.ws_ktf + ((size_t)hq * p.ns + slot0) * (2 * kC * DK) + lane * 8;
         const __bf16 *wf = p.ws_wf + ((size_t)hv * p.ns + slot0) * (2 * kC * DK) + lane * 8;
         const float *uf = p.ws_uf + ((size_t)hv * p.ns + slot0) * ((size_t)kC * p.d_v) +
                           (size_t)slice * 4 * 256 + w * 256 + lane * 4;
@@ -835,6 +1118,9 @@ scan_kernel(const PrefillArgs p, int slices)
         Frag cW[KS], cK[MTW][2];
         f32x4 cU, cEGC;
         float gam = 0.0f;
+        f32x4 gam4[MTW]; // per-channel chunk decay of this wave's state rows
+#pragma unroll
+        for (int u = 0; u < MTW; ++u) gam4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         // Load groups, each issued right after the last use of what it
         // replaces: W rows and U (phase 1), e^{G_C-G} rows (after E), k^T rows
         // and e^{G_C} (phase 2).  The loads are unconditional (the last chunk
@@ -860,7 +1146,14 @@ scan_kernel(const PrefillArgs p, int slices)
                     cK[u][s] = frag_at(ktf + off + f * 512, ktf + off + (f + 1) * 512);        \
                 }                                                                              \
             }                                                                                  \
-            gam = gf[(size_t)(CH) * (2 * kC) + kC - 1];                                        \
+            if (KDA) {                                                                         \
+                _Pragma("unroll") for (int u = 0; u < MTW; ++u) {                              \
+                    const int mt = min(w + 4 * u, MTS - 1);                                    \
+                    gam4[u] = ld4(gf + (size_t)(CH) * (2 * kC) + 16 * mt + 4 * kq);            \
+                }                                                                              \
+            } else {                                                                           \
+                gam = gf[(size_t)(CH) * (2 * kC) + kC - 1];                                    \
+            }                                                                                  \
         }
         // State tile mt into S^T (buffer par) at its d_k-permuted position.
         auto put_state = [&](int par, int mt, const f32x4 &v) {
@@ -908,7 +1201,7 @@ scan_kernel(const PrefillArgs p, int slices)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     split1(Dv[e], dh[e], dl[e]);
-                    split1(Dv[e] * cEGC[e], eh[e], el[e]);
+                    split1(KDA ? Dv[e] : Dv[e] * cEGC[e], eh[e], el[e]);
                 }
                 const int o = col * RT + 16 * w + 4 * kq;
                 *reinterpret_cast<uint2 *>(&sD[par][0][o]) = make_uint2(pack2(dh[0], dh[1]), pack2(dh[2], dh[3]));
@@ -933,7 +1226,7 @@ scan_kernel(const PrefillArgs p, int slices)
             for (int u = 0; u < MTW; ++u) {
                 const int mt = w + 4 * u;
                 if (mt < MTS) {
-                    f32x4 acc = gam * S[u];
+                    f32x4 acc = KDA ? gam4[u] * S[u] : gam * S[u];
 #pragma unroll
                     for (int s = 0; s < 2; ++s) acc = mma3(cK[u][s], Be[s], acc);
                     S[u] = acc;
@@ -957,7 +1250,7 @@ scan_kernel(const PrefillArgs p, int slices)
         }
     } else {
         // ================= output waves (one chunk behind) ==============
-        const __bf16 *qf = p.ws_qf + ((size_t)hk * p.ns + slot0) * (2 * kC * DK) + lane * 8;
+        const __bf16 *qf = p.ws_qf + ((size_t)(KDA ? hv : hk) * p.ns + slot0) * (2 * kC * DK) + lane * 8;
         const __bf16 *pf = p.ws_pf + ((size_t)hv * p.ns + slot0) * (2 * kC * kC) + lane * 8;
         const float *gf = p.ws_gf + ((size_t)hv * p.ns + slot0) * (2 * kC);
         float *o_head = p.ws_o + (size_t)hv * p.t_total * p.d_v + slice * kBV + col;
@@ -989,7 +1282,7 @@ scan_kernel(const PrefillArgs p, int slices)
                 const int o = col * RK + 32 * s + 8 * kq;
                 acc = mma3(cQ[s], frag_at(&sS[par][0][o], &sS[par][1][o]), acc);
             }
-            return acc * cEG;
+            return KDA ? acc : acc * cEG; // (q already carries e^G per channel)
         };
         // O = Y + P D of chunk cc, stored for its rows inside the sequence.
         auto finish = [&](int cc, f32x4 y) {
@@ -1099,24 +1392,31 @@ static hipError_t launch_norm(const PrefillArgs &a, int rows, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename TIn, int DK, int DV>
+template <typename TIn, int DK, int DV, bool KDA>
 static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total, int max_len,
                                    hipStream_t s)
 {
     hipError_t e;
     if (max_len > 0) {
         const int nch_max = (max_len + kC - 1) / kC;
-        const dim3 grid_k((nch_max + kQkChunks - 1) / kQkChunks, a.h_k, n_seq);
-        hipLaunchKernelGGL((qknorm_kernel<TIn, DK>), grid_k, dim3(256), qknorm_smem_bytes<DK>(), s, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
         const dim3 grid_v((max_len + kC - 1) / kC, a.h_v, n_seq);
-        hipLaunchKernelGGL((tri_kernel<TIn, DK, DV>), grid_v, dim3(256), TriLds<DV>::total, s, a);
+        if (KDA) {
+            hipLaunchKernelGGL((kda_intra_kernel<TIn, DK>), grid_v, dim3(512), kda_smem_bytes<DK>(),
+                               s, a);
+        } else {
+            const dim3 grid_k((nch_max + kQkChunks - 1) / kQkChunks, a.h_k, n_seq);
+            hipLaunchKernelGGL((qknorm_kernel<TIn, DK>), grid_k, dim3(256), qknorm_smem_bytes<DK>(),
+                               s, a);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((tri_kernel<TIn, DK, DV, KDA>), grid_v, dim3(256), TriLds<DV>::total, s,
+                           a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (n_seq > 0) {
         const int slices = DV / kBV;
-        hipLaunchKernelGGL((scan_kernel<DK>), dim3(n_seq * a.h_v * slices), dim3(512), 0, s, a,
-                           slices);
+        hipLaunchKernelGGL((scan_kernel<DK, KDA>), dim3(n_seq * a.h_v * slices), dim3(512), 0, s,
+                           a, slices);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int rows = t_total * a.h_v;
@@ -1139,7 +1439,13 @@ static hipError_t set_smem_limits()
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)qknorm_smem_bytes<DK>());
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(tri_kernel<TIn, DK, DV>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kda_intra_kernel<TIn, DK>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kda_smem_bytes<DK>());
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(tri_kernel<TIn, DK, DV, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)TriLds<DV>::total);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(tri_kernel<TIn, DK, DV, false>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)TriLds<DV>::total);
 }
 
@@ -1149,7 +1455,8 @@ static hipError_t run_prefill(const PrefillArgs &a, int n_seq, int t_total, int 
 {
     static const hipError_t limits = set_smem_limits<TIn, DK, DV>();
     if (limits != hipSuccess) return limits;
-    return launch_prefill_t<TIn, DK, DV>(a, n_seq, t_total, max_len, s);
+    if (a.kda) return launch_prefill_t<TIn, DK, DV, true>(a, n_seq, t_total, max_len, s);
+    return launch_prefill_t<TIn, DK, DV, false>(a, n_seq, t_total, max_len, s);
 }
 
 template <typename TIn, int DK>
@@ -1196,6 +1503,7 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.ws_uf = reinterpret_cast<float *>(base + w.uf);
     A.ws_gf = reinterpret_cast<float *>(base + w.gf);
     A.ws_o = reinterpret_cast<float *>(base + w.o);
+    A.ws_kw = reinterpret_cast<__bf16 *>(base + w.kw);
     A.ns = w.ns;
     A.t_total = t_total;
     A.h_k = d.h_k;
@@ -1207,6 +1515,7 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.value_dim = d.value_dim;
     A.gate = d.gate;
     A.tiled = d.tiled;
+    A.kda = d.chan_decay;
     A.out_bf16 = d.out_bf16;
     A.norm_eps = d.norm_eps;
     A.l2_eps = d.l2_eps;

@@ -71,9 +71,8 @@ typedef enum { GDN_HEADS_GROUPED = 0, GDN_HEADS_TILED = 1 } gdn_head_map;
  * AttnKind::Kda, a per-channel decayed delta rule).  With
  * GDN_DECAY_CHANNEL the gate input a is [T][H_v*d_k] and dt_bias
  * [H_v*d_k]; g[i] = coef * softplus(a[i] + dt_bias[i]) and the state update
- * starts with S <- diag(e^g) S.  Supported by gdn_decode_step,
- * gdn_decode_multi and gdn_rewind; gdn_prefill_chunked returns
- * GDN_EUNSUPPORTED for it. */
+ * starts with S <- diag(e^g) S.  Every entry point supports it (the
+ * chunked prefill then carries the decay inside its q/k operands). */
 typedef enum { GDN_DECAY_HEAD = 0, GDN_DECAY_CHANNEL = 1 } gdn_decay_mode;
 
 typedef struct {

@@ -94,6 +94,48 @@ def test_prefill_head_map_and_decay_coef(gdn, v):
     np.testing.assert_array_equal(conv.numpy(), r["conv"])
 
 
+KDA_SMALL = [
+    # h_k, h_v, d_k, d_v, K, decay, head_map, act, lengths
+    (2, 4, 64, 64, 4, "weak", "grouped", "bf16", [1, 63, 65, 130]),
+    (2, 4, 64, 64, 4, "strong", "tiled", "f32", [130, 64, 7]),
+    (1, 2, 128, 128, 4, "weak", "grouped", "bf16", [200]),
+    (2, 2, 32, 32, 3, "weak", "grouped", "f32", [64, 129, 0, 2]),
+    (1, 2, 128, 32, 2, "strong", "grouped", "bf16", [100, 31]),
+    (2, 2, 32, 128, 4, "weak", "tiled", "bf16", [77]),
+]
+
+
+@pytest.mark.parametrize("v", KDA_SMALL, ids=lambda v: "hk%d_hv%d_dk%d_dv%d_K%d_%s_%s_%s_%s" % (
+    *v[:8], "-".join(map(str, v[8]))))
+def test_prefill_per_channel_decay(gdn, v):
+    """One decay per key channel (Kimi Delta Attention, "cortiq-engine
+    0.8.76 pipeline.rs", AttnKind::Kda), sigmoid output gate, non-zero
+    initial states, ragged chunks."""
+    hk, hv, dk, dv, K, decay, head_map, act, lengths = v
+    d = Dims(hk, hv, dk, dv, K, "sigmoid", head_map, decay="channel")
+    case = make_case(d, lengths, act_dtype=act, seed=700 + sum(lengths) + dk, decay=decay,
+                     s0_std=0.3, conv0_std=1.0)
+    y, S, conv = run_prefill(gdn, case)
+    r = P.run_oracle(case)
+    P.assert_y_close(y, r["y"])
+    P.assert_state_close(S, r["S"])
+    np.testing.assert_array_equal(conv.numpy(), r["conv"])
+
+
+def test_prefill_per_channel_decay_t1024_all_heads(gdn):
+    """The full layer (H_k=16, H_v=32, d=128, K=4, bf16) over T=1024 with one
+    decay per key channel and a weak decay, so that the state carries across
+    all 16 chunks."""
+    d = Dims(16, 32, 128, 128, 4, "sigmoid", decay="channel")
+    case = make_case(d, [1024], act_dtype="bf16", seed=701, decay="weak", s0_std=0.02,
+                     conv0_std=1.0)
+    y, S, conv = run_prefill(gdn, case)
+    r = P.run_oracle(case)
+    P.assert_y_close(y, r["y"])
+    P.assert_state_close(S, r["S"])
+    np.testing.assert_array_equal(conv.numpy(), r["conv"])
+
+
 def test_prefill_zero_state_pointers_and_empty_sequences(gdn):
     """NULL state_in / conv_in mean zeros; empty sequences pass their state
     through unchanged."""
