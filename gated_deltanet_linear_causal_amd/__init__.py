@@ -48,6 +48,11 @@ class _Params(ctypes.Structure):
                 ("decay_coef", ctypes.c_void_p)]
 
 
+class _Proj(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("w_qkv", ctypes.c_void_p), ("w_z", ctypes.c_void_p),
+                ("w_b", ctypes.c_void_p), ("w_a", ctypes.c_void_p), ("w_out", ctypes.c_void_p)]
+
+
 _VP, _I32 = ctypes.c_void_p, ctypes.c_int32
 _SIGNATURES = {
     "gdn_conv_update": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
@@ -64,6 +69,13 @@ _SIGNATURES = {
                                            _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                                            _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
                                            _VP]),
+    "gdn_mixer_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Config), _I32, _I32, _I32]),
+    "gdn_mixer_prefill": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
+                                         ctypes.POINTER(_Proj), _I32, _I32] + [_VP] * 9
+                          + [ctypes.c_size_t, _VP]),
+    "gdn_mixer_decode": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
+                                        ctypes.POINTER(_Proj), _I32] + [_VP] * 5
+                         + [ctypes.c_size_t, _VP]),
     "gdn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdn_last_error": (ctypes.c_char_p, []),
 }
@@ -374,6 +386,81 @@ def prefill_chunked(cfg: Config, params: dict, seqlens: SeqLens, qkv, z, a, b,
     return out, state_out, conv_out
 
 
+def _proj(cfg: Config, proj: dict) -> _Proj:
+    """proj: hidden (int) and bf16 weights w_qkv [conv_dim, H], w_z [value_dim, H],
+    w_b [H_v, H], w_a [H_v * gate_width, H], w_out [H, value_dim]."""
+    H = int(proj["hidden"])
+    bf = torch.bfloat16
+    _check(proj["w_qkv"], "w_qkv", (cfg.conv_dim, H), bf)
+    _check(proj["w_z"], "w_z", (cfg.value_dim, H), bf)
+    _check(proj["w_b"], "w_b", (cfg.h_v, H), bf)
+    _check(proj["w_a"], "w_a", (cfg.h_v * cfg.gate_width, H), bf)
+    _check(proj["w_out"], "w_out", (H, cfg.value_dim), bf)
+    return _Proj(H, *(proj[k].data_ptr() for k in ("w_qkv", "w_z", "w_b", "w_a", "w_out")))
+
+
+def mixer_workspace_bytes(cfg: Config, hidden: int, n_seq: int, t_total: int) -> int:
+    c = cfg.c_struct()
+    return int(load_library().gdn_mixer_workspace_bytes(ctypes.byref(c), hidden, n_seq, t_total))
+
+
+def mixer_prefill(cfg: Config, params: dict, proj: dict, seqlens: SeqLens, x, state_in=None,
+                  state_out=None, conv_in=None, conv_out=None, y=None, workspace=None,
+                  stream=None):
+    """The mixer with its projections over packed sequences: x [T, H] bf16 ->
+    y [T, H] (cfg.out_dtype).  Returns (y, state_out, conv_out)."""
+    lib = load_library()
+    T, N, H = seqlens.t_total, seqlens.n_seq, int(proj["hidden"])
+    dev = x.device
+    _check(x, "x", (T, H), torch.bfloat16)
+    sshape = (N, cfg.h_v, cfg.d_k, cfg.d_v)
+    cshape = (N, cfg.conv_k - 1, cfg.conv_dim)
+    if state_in is not None:
+        _check(state_in, "state_in", sshape, torch.float32)
+    if conv_in is not None:
+        _check(conv_in, "conv_in", cshape, torch.float32)
+    if state_out is None:
+        state_out = torch.empty(sshape, dtype=torch.float32, device=dev)
+    if conv_out is None:
+        conv_out = torch.empty(cshape, dtype=torch.float32, device=dev)
+    if y is None:
+        y = torch.empty((T, H), dtype=cfg.out_dtype, device=dev)
+    _check(y, "y", (T, H), cfg.out_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(mixer_workspace_bytes(cfg, H, N, T), 256), dtype=torch.uint8,
+                                device=dev)
+    c, p, pj = cfg.c_struct(), _params(cfg, params), _proj(cfg, proj)
+    _raise_on(lib.gdn_mixer_prefill(
+        ctypes.byref(c), ctypes.byref(p), ctypes.byref(pj), N, T,
+        ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev), _ptr(x), _ptr(state_in),
+        _ptr(state_out), _ptr(conv_in), _ptr(conv_out), _ptr(y), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y, state_out, conv_out
+
+
+def mixer_decode(cfg: Config, params: dict, proj: dict, x, conv_state, state, y=None,
+                 workspace=None, stream=None):
+    """One mixer decode step with projections: x [B, H] bf16 -> y [B, H];
+    conv_state and state are updated in place."""
+    lib = load_library()
+    B, H = x.shape[0], int(proj["hidden"])
+    _check(x, "x", (B, H), torch.bfloat16)
+    _check(conv_state, "conv_state", (B, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
+    _check(state, "state", (B, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
+    if y is None:
+        y = torch.empty((B, H), dtype=cfg.out_dtype, device=x.device)
+    _check(y, "y", (B, H), cfg.out_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(mixer_workspace_bytes(cfg, H, B, B), 256), dtype=torch.uint8,
+                                device=x.device)
+    c, p, pj = cfg.c_struct(), _params(cfg, params), _proj(cfg, proj)
+    _raise_on(lib.gdn_mixer_decode(ctypes.byref(c), ctypes.byref(p), ctypes.byref(pj), B, _ptr(x),
+                                   _ptr(conv_state), _ptr(state), _ptr(y), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+
+
 __all__ = ["Config", "SeqLens", "GdnError", "load_library", "header_functions",
            "conv_update", "decode_step", "decode_multi", "rewind", "prefill_workspace_bytes",
-           "alloc_workspace", "prefill_chunked", "LIB_PATH", "CHUNK", "MAX_NEW_TOKENS"]
+           "alloc_workspace", "prefill_chunked", "mixer_workspace_bytes", "mixer_prefill",
+           "mixer_decode", "LIB_PATH", "CHUNK", "MAX_NEW_TOKENS"]

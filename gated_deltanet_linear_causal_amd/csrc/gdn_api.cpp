@@ -390,6 +390,137 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, 
                       "gdn_prefill_chunked launch");
 }
 
+} // extern "C"
+
+namespace {
+
+gdn_status check_proj(const gdn::Dims &d, const gdn_config *cfg, const gdn_proj *proj,
+                      gdn::Proj &out)
+{
+    if (!proj) return fail(GDN_EINVAL, "proj is NULL");
+    if (proj->hidden <= 0 || proj->hidden % 8 != 0 || proj->hidden > (1 << 20))
+        return fail(GDN_EINVAL, "hidden must be a positive multiple of 8 (got %d)", proj->hidden);
+    if (!proj->w_qkv || !proj->w_z || !proj->w_b || !proj->w_a || !proj->w_out)
+        return fail(GDN_EINVAL, "every projection weight must be non-NULL");
+    if (cfg->act_dtype != GDN_BF16)
+        return fail(GDN_EUNSUPPORTED, "the mixer takes bf16 hidden states (act_dtype GDN_BF16)");
+    (void)d;
+    out.hidden = proj->hidden;
+    out.w_qkv = proj->w_qkv;
+    out.w_z = proj->w_z;
+    out.w_b = proj->w_b;
+    out.w_a = proj->w_a;
+    out.w_out = proj->w_out;
+    return GDN_OK;
+}
+
+gdn_status check_workspace(void *workspace, size_t ws_bytes, size_t need)
+{
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(GDN_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                    workspace ? ws_bytes : (size_t)0);
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
+    return GDN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+size_t gdn_mixer_workspace_bytes(const gdn_config *cfg, int32_t hidden, int32_t n_seq,
+                                 int32_t t_total)
+{
+    gdn::Dims d;
+    if (check_config(cfg, d) != GDN_OK || hidden <= 0 || hidden % 8 != 0 || n_seq < 0 ||
+        t_total < 0)
+        return 0;
+    return gdn::mixer_workspace_bytes(d, hidden, n_seq, t_total, true);
+}
+
+gdn_status gdn_mixer_prefill(const gdn_config *cfg, const gdn_params *params,
+                             const gdn_proj *proj, int32_t n_seq, int32_t t_total,
+                             const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                             const void *x, const float *state_in, float *state_out,
+                             const float *conv_in, float *conv_out, void *y, void *workspace,
+                             size_t ws_bytes, void *stream)
+{
+    gdn::Dims d;
+    gdn::Params p;
+    gdn::Proj pj;
+    gdn_status st;
+    if ((st = check_config(cfg, d)) != GDN_OK) return st;
+    if ((st = check_params(params, p)) != GDN_OK) return st;
+    if ((st = check_proj(d, cfg, proj, pj)) != GDN_OK) return st;
+    int max_len = 0;
+    if ((st = check_cu(n_seq, t_total, cu_seqlens_host, cu_seqlens_dev, max_len)) != GDN_OK) return st;
+    if (max_len > 65535 * 64) return fail(GDN_EUNSUPPORTED, "sequence longer than %d", 65535 * 64);
+    if (t_total > 0 && (!x || !y)) return fail(GDN_EINVAL, "x and y are required when t_total > 0");
+    if (n_seq > 0 && (!state_out || (d.conv_k > 1 && !conv_out)))
+        return fail(GDN_EINVAL, "state_out (and conv_out when K > 1) are required");
+    const size_t need = gdn::mixer_workspace_bytes(d, pj.hidden, n_seq, t_total, true);
+    if ((st = check_workspace(workspace, ws_bytes, need)) != GDN_OK) return st;
+    const size_t osz = d.out_bf16 ? 2 : 4;
+    const size_t sbytes = (size_t)n_seq * d.h_v * d.d_k * d.d_v * 4;
+    const size_t cbytes = (size_t)n_seq * (d.conv_k - 1) * d.conv_dim * 4;
+    const Range rx{x, (size_t)t_total * pj.hidden * 2}, ry{y, (size_t)t_total * pj.hidden * osz};
+    const Range rsi{state_in, sbytes}, rso{state_out, sbytes}, rci{conv_in, cbytes},
+        rco{conv_out, cbytes}, rws{workspace, need};
+    const Range outs[] = {ry, rso, rco, rws};
+    for (const Range &o : outs)
+        if (overlap(o, rx)) return fail(GDN_EINVAL, "outputs and workspace must not overlap x");
+    if (overlap(ry, rso) || overlap(ry, rco) || overlap(ry, rws) || overlap(rso, rco) ||
+        overlap(rso, rws) || overlap(rco, rws) || overlap(ry, rsi) || overlap(ry, rci) ||
+        overlap(rws, rsi) || overlap(rws, rci) || overlap(rso, rci) || overlap(rco, rsi))
+        return fail(GDN_EINVAL, "y, state_out, conv_out and workspace must be disjoint buffers");
+    if (overlap(rsi, rso) && state_in != state_out)
+        return fail(GDN_EINVAL, "state_out may equal state_in but must not partially overlap it");
+    if (overlap(rci, rco) && conv_in != conv_out)
+        return fail(GDN_EINVAL, "conv_out may equal conv_in but must not partially overlap it");
+    return hip_status(gdn::launch_mixer_prefill(d, p, pj, n_seq, t_total, max_len, cu_seqlens_dev,
+                                                x, state_in, state_out, conv_in, conv_out, y,
+                                                workspace, static_cast<hipStream_t>(stream)),
+                      "gdn_mixer_prefill launch");
+}
+
+gdn_status gdn_mixer_decode(const gdn_config *cfg, const gdn_params *params,
+                            const gdn_proj *proj, int32_t batch, const void *x,
+                            float *conv_state, float *state, void *y, void *workspace,
+                            size_t ws_bytes, void *stream)
+{
+    gdn::Dims d;
+    gdn::Params p;
+    gdn::Proj pj;
+    gdn_status st;
+    if ((st = check_config(cfg, d)) != GDN_OK) return st;
+    if ((st = check_params(params, p)) != GDN_OK) return st;
+    if ((st = check_proj(d, cfg, proj, pj)) != GDN_OK) return st;
+    if (batch < 0) return fail(GDN_EINVAL, "batch must be >= 0 (got %d)", batch);
+    if (batch > 65535) return fail(GDN_EUNSUPPORTED, "batch must be <= 65535 (got %d)", batch);
+    if (batch == 0) return ok();
+    if (!x || !y || !state || (d.conv_k > 1 && !conv_state))
+        return fail(GDN_EINVAL, "x, y, state (and conv_state when K > 1) are required");
+    if (d.chan_decay && gdn::decode_multi_lds_bytes(d, 1) > gdn::kDecodeMultiMaxLds)
+        return fail(GDN_EUNSUPPORTED,
+                    "per-channel decay needs %d conv channels per key head to fit the on-chip "
+                    "buffer", 2 * d.d_k + d.group * d.d_v);
+    const size_t need = gdn::mixer_workspace_bytes(d, pj.hidden, batch, batch, false);
+    if ((st = check_workspace(workspace, ws_bytes, need)) != GDN_OK) return st;
+    const size_t osz = d.out_bf16 ? 2 : 4;
+    const Range rx{x, (size_t)batch * pj.hidden * 2}, ry{y, (size_t)batch * pj.hidden * osz};
+    const Range rs{state, (size_t)batch * d.h_v * d.d_k * d.d_v * 4};
+    const Range rc{conv_state, (size_t)batch * (d.conv_k - 1) * d.conv_dim * 4};
+    const Range rws{workspace, need};
+    const Range all[] = {rx, ry, rs, rc, rws};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(all[i], all[j]))
+                return fail(GDN_EINVAL, "x, y, state, conv_state and workspace must not overlap");
+    return hip_status(gdn::launch_mixer_decode(d, p, pj, batch, x, conv_state, state, y, workspace,
+                                               static_cast<hipStream_t>(stream)),
+                      "gdn_mixer_decode launch");
+}
+
 const char *gdn_status_string(gdn_status s)
 {
     switch (s) {

@@ -45,6 +45,20 @@ hipError_t launch_decode_multi(const Dims &d, const Params &p, int batch, int t_
                                float *conv_out, const float *state_in, float *state_out,
                                float *ckpt, void *out, hipStream_t s);
 
+// The mixer with its projections (hipBLASLt GEMMs around the core).
+struct Proj {
+    int hidden;
+    const void *w_qkv, *w_z, *w_b, *w_a, *w_out;
+};
+size_t mixer_workspace_bytes(const Dims &d, int hidden, int n_seq, int t_total, bool prefill);
+hipError_t launch_mixer_prefill(const Dims &d, const Params &p, const Proj &pj, int n_seq,
+                                int t_total, int max_len, const int32_t *cu_dev, const void *x,
+                                const float *state_in, float *state_out, const float *conv_in,
+                                float *conv_out, void *y, void *ws, hipStream_t s);
+hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, int batch,
+                               const void *x, float *conv_state, float *state, void *y, void *ws,
+                               hipStream_t s);
+
 // Chunked prefill.  Workspace layout and size are owned by prefill.hip.
 size_t prefill_workspace_bytes(const Dims &d, int n_seq, int t_total);
 hipError_t launch_prefill(const Dims &d, const Params &p, int n_seq, int t_total,

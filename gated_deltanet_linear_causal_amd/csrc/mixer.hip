@@ -1,0 +1,268 @@
+// The GDN mixer with its projections: in_proj (qkv, z, b, a) from the
+// model's hidden states, the mixer core, and out_proj back to the hidden
+// size ("oxinfer 0.0.5 src/qwen.rs", Gdn struct and gdn_forward;
+// "cherenkov qwen4_exp/cpu.rs", fn deltanet).
+//
+// The projections are plain dense GEMMs and run on hipBLASLt (bf16
+// operands, fp32 accumulation).  The projected activations stay fp32, so
+// the core runs on fp32 inputs.  The core's fp32 output is split into a
+// bf16 hi part and a bf16 lo part, and out_proj is the sum of the two bf16
+// GEMMs (hi then lo, the second accumulating into the first): rounding the
+// core output to one bf16 alone would cost about as much as the whole error
+// budget of the layer.
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+#include <hipblaslt/hipblaslt.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+namespace gdn {
+
+// ---------------------------------------------------------------------------
+// element-wise kernels
+// ---------------------------------------------------------------------------
+
+// v -> (hi, lo) with hi = bf16(v), lo = bf16(v - hi), four per thread.
+__global__ void __launch_bounds__(256) split_bf16_kernel(const float *__restrict__ v,
+                                                         bf16_t *__restrict__ hi,
+                                                         bf16_t *__restrict__ lo, size_t n4)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const float4 x = reinterpret_cast<const float4 *>(v)[i];
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+    bf16_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = f32_to_bf16(xs[e]);
+        l[e] = f32_to_bf16(xs[e] - bf16_bits_to_f32(h[e]));
+    }
+    reinterpret_cast<uint2 *>(hi)[i] = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+    reinterpret_cast<uint2 *>(lo)[i] = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+}
+
+// fp32 -> bf16 (round to nearest even), four per thread.
+__global__ void __launch_bounds__(256) to_bf16_kernel(const float *__restrict__ v,
+                                                      bf16_t *__restrict__ out, size_t n4)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    store_out4(out, 4 * i, reinterpret_cast<const float4 *>(v)[i], true);
+}
+
+// ---------------------------------------------------------------------------
+// hipBLASLt: one handle per device, algorithms cached per GEMM shape
+// ---------------------------------------------------------------------------
+namespace {
+
+struct Blas {
+    hipblasLtHandle_t handle = nullptr;
+    std::map<std::tuple<int64_t, int64_t, int64_t, float>, hipblasLtMatmulAlgo_t> algos;
+};
+
+std::mutex g_blas_mu;
+Blas g_blas[64];
+
+hipError_t blas_error(hipblasStatus_t st)
+{
+    return st == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorLaunchFailure;
+}
+
+// D[m][n] (fp32, row-major) = beta * D + X[m][k] . W[n][k]^T, X and W bf16
+// row-major.  In column-major terms D^T (n x m) = W (k x n)^T . X^T (k x m).
+hipError_t gemm_bf16_nt(int64_t m, int64_t n, int64_t k, const void *X, const void *W, float beta,
+                        float *D, void *ws, size_t ws_bytes, hipStream_t s)
+{
+    if (m == 0 || n == 0) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_blas_mu);
+    Blas &b = g_blas[dev];
+    if (!b.handle && hipblasLtCreate(&b.handle) != HIPBLAS_STATUS_SUCCESS) {
+        b.handle = nullptr;
+        return hipErrorLaunchFailure;
+    }
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+    hipblasStatus_t st = hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F);
+    const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
+    if (st == HIPBLAS_STATUS_SUCCESS)
+        st = hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT));
+    if (st == HIPBLAS_STATUS_SUCCESS)
+        st = hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN));
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, k, n, k);
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, k, m, k);
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&lc, HIP_R_32F, n, m, n);
+    const auto key = std::make_tuple(m, n, k, beta);
+    auto it = b.algos.find(key);
+    if (st == HIPBLAS_STATUS_SUCCESS && it == b.algos.end()) {
+        hipblasLtMatmulPreference_t pref = nullptr;
+        st = hipblasLtMatmulPreferenceCreate(&pref);
+        const uint64_t cap = ws_bytes;
+        if (st == HIPBLAS_STATUS_SUCCESS)
+            st = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
+                                                       &cap, sizeof(cap));
+        hipblasLtMatmulHeuristicResult_t res[1];
+        int found = 0;
+        if (st == HIPBLAS_STATUS_SUCCESS)
+            st = hipblasLtMatmulAlgoGetHeuristic(b.handle, desc, la, lb, lc, lc, pref, 1, res, &found);
+        if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+        if (st == HIPBLAS_STATUS_SUCCESS && found < 1) st = HIPBLAS_STATUS_NOT_SUPPORTED;
+        if (st == HIPBLAS_STATUS_SUCCESS) it = b.algos.emplace(key, res[0].algo).first;
+    }
+    if (st == HIPBLAS_STATUS_SUCCESS) {
+        const float alpha = 1.0f;
+        st = hipblasLtMatmul(b.handle, desc, &alpha, W, la, X, lb, &beta, D, lc, D, lc, &it->second,
+                             ws, ws_bytes, s);
+    }
+    if (lc) hipblasLtMatrixLayoutDestroy(lc);
+    if (lb) hipblasLtMatrixLayoutDestroy(lb);
+    if (la) hipblasLtMatrixLayoutDestroy(la);
+    if (desc) hipblasLtMatmulDescDestroy(desc);
+    return blas_error(st);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+constexpr size_t kBlasWorkspace = size_t(32) << 20;
+
+struct MixerWs {
+    size_t qkv, z, b, a, core, hi, lo, acc, blas, prefill, total;
+};
+
+// The core runs on fp32 activations: the dims it sees.
+Dims core_dims(const Dims &d)
+{
+    Dims c = d;
+    c.act_bf16 = 0;
+    c.out_bf16 = 0;
+    return c;
+}
+
+MixerWs mixer_ws(const Dims &d, int hidden, int n_seq, int t_total, bool prefill)
+{
+    MixerWs w;
+    const size_t T = (size_t)t_total, gw = d.chan_decay ? d.d_k : 1;
+    size_t off = 0;
+    w.qkv = off;
+    off = align256(off + T * d.conv_dim * 4);
+    w.z = off;
+    off = align256(off + T * d.value_dim * 4);
+    w.b = off;
+    off = align256(off + T * d.h_v * 4);
+    w.a = off;
+    off = align256(off + T * d.h_v * gw * 4);
+    w.core = off;
+    off = align256(off + T * d.value_dim * 4);
+    w.hi = off;
+    off = align256(off + T * d.value_dim * 2);
+    w.lo = off;
+    off = align256(off + T * d.value_dim * 2);
+    w.acc = off;
+    off = align256(off + (d.out_bf16 ? T * hidden * 4 : 0));
+    w.blas = off;
+    off = align256(off + kBlasWorkspace);
+    w.prefill = off;
+    off = align256(off + (prefill ? prefill_workspace_bytes(core_dims(d), n_seq, t_total) : 0));
+    w.total = off;
+    return w;
+}
+
+// in_proj: the four projections of x [T][H] into fp32 qkv, z, b, a.
+hipError_t in_proj(const Dims &d, const Proj &pj, int T, const void *x, char *base,
+                   const MixerWs &w, hipStream_t s)
+{
+    const int64_t H = pj.hidden, gw = d.chan_decay ? d.d_k : 1;
+    void *bw = base + w.blas;
+    hipError_t e;
+    if ((e = gemm_bf16_nt(T, d.conv_dim, H, x, pj.w_qkv, 0.0f,
+                          reinterpret_cast<float *>(base + w.qkv), bw, kBlasWorkspace, s)) != hipSuccess)
+        return e;
+    if ((e = gemm_bf16_nt(T, d.value_dim, H, x, pj.w_z, 0.0f,
+                          reinterpret_cast<float *>(base + w.z), bw, kBlasWorkspace, s)) != hipSuccess)
+        return e;
+    if ((e = gemm_bf16_nt(T, d.h_v, H, x, pj.w_b, 0.0f, reinterpret_cast<float *>(base + w.b), bw,
+                          kBlasWorkspace, s)) != hipSuccess)
+        return e;
+    return gemm_bf16_nt(T, d.h_v * gw, H, x, pj.w_a, 0.0f, reinterpret_cast<float *>(base + w.a),
+                        bw, kBlasWorkspace, s);
+}
+
+// out_proj of the fp32 core output: y = hi . W_out^T + lo . W_out^T.
+hipError_t out_proj(const Dims &d, const Proj &pj, int T, char *base, const MixerWs &w, void *y,
+                    hipStream_t s)
+{
+    if (T == 0) return hipSuccess;
+    const size_t n4 = (size_t)T * d.value_dim / 4;
+    bf16_t *hi = reinterpret_cast<bf16_t *>(base + w.hi), *lo = reinterpret_cast<bf16_t *>(base + w.lo);
+    hipLaunchKernelGGL(split_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const float *>(base + w.core), hi, lo, n4);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    float *acc = d.out_bf16 ? reinterpret_cast<float *>(base + w.acc) : static_cast<float *>(y);
+    void *bw = base + w.blas;
+    if ((e = gemm_bf16_nt(T, pj.hidden, d.value_dim, hi, pj.w_out, 0.0f, acc, bw, kBlasWorkspace,
+                          s)) != hipSuccess)
+        return e;
+    if ((e = gemm_bf16_nt(T, pj.hidden, d.value_dim, lo, pj.w_out, 1.0f, acc, bw, kBlasWorkspace,
+                          s)) != hipSuccess)
+        return e;
+    if (d.out_bf16) {
+        const size_t m4 = (size_t)T * pj.hidden / 4;
+        hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((m4 + 255) / 256)), dim3(256), 0, s, acc,
+                           static_cast<bf16_t *>(y), m4);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+} // namespace
+
+size_t mixer_workspace_bytes(const Dims &d, int hidden, int n_seq, int t_total, bool prefill)
+{
+    return mixer_ws(d, hidden, n_seq, t_total, prefill).total;
+}
+
+hipError_t launch_mixer_prefill(const Dims &d, const Params &p, const Proj &pj, int n_seq,
+                                int t_total, int max_len, const int32_t *cu_dev, const void *x,
+                                const float *state_in, float *state_out, const float *conv_in,
+                                float *conv_out, void *y, void *ws, hipStream_t s)
+{
+    const MixerWs w = mixer_ws(d, pj.hidden, n_seq, t_total, true);
+    char *base = static_cast<char *>(ws);
+    hipError_t e;
+    if ((e = in_proj(d, pj, t_total, x, base, w, s)) != hipSuccess) return e;
+    if ((e = launch_prefill(core_dims(d), p, n_seq, t_total, max_len, cu_dev, base + w.qkv,
+                            base + w.z, base + w.a, base + w.b, state_in, state_out, conv_in,
+                            conv_out, base + w.core, base + w.prefill, s)) != hipSuccess)
+        return e;
+    return out_proj(d, pj, t_total, base, w, y, s);
+}
+
+hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, int batch,
+                               const void *x, float *conv_state, float *state, void *y, void *ws,
+                               hipStream_t s)
+{
+    const MixerWs w = mixer_ws(d, pj.hidden, batch, batch, false);
+    char *base = static_cast<char *>(ws);
+    hipError_t e;
+    if ((e = in_proj(d, pj, batch, x, base, w, s)) != hipSuccess) return e;
+    const Dims c = core_dims(d);
+    if (decode_multi_lds_bytes(c, 1) <= kDecodeMultiMaxLds)
+        e = launch_decode_multi(c, p, batch, 1, nullptr, base + w.qkv, base + w.z, base + w.a,
+                                base + w.b, conv_state, conv_state, state, state, nullptr,
+                                base + w.core, s);
+    else
+        e = launch_decode(c, p, batch, base + w.qkv, base + w.z, base + w.a, base + w.b,
+                          conv_state, state, base + w.core, s);
+    if (e != hipSuccess) return e;
+    return out_proj(d, pj, batch, base, w, y, s);
+}
+
+} // namespace gdn

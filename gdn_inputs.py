@@ -146,6 +146,28 @@ def make_case(dims: Dims, lengths, act_dtype="bf16", seed=0, decay="strong",
                 name)
 
 
+def make_projections(dims: Dims, hidden: int, seed: int) -> dict:
+    """Random projection weights of the mixer (bf16 values held in float32):
+    N(0, 1/sqrt(H)) for in_proj, so the projected activations are about
+    N(0, 1), and N(0, 1/sqrt(value_dim)) for out_proj."""
+    gen = torch.Generator().manual_seed(seed)
+
+    def w(rows, cols):
+        x = torch.randn((rows, cols), generator=gen, dtype=torch.float32) / cols ** 0.5
+        return x.to(torch.bfloat16).to(torch.float32)
+    return {"hidden": hidden,
+            "w_qkv": w(dims.conv_dim, hidden), "w_z": w(dims.value_dim, hidden),
+            "w_b": w(dims.h_v, hidden), "w_a": w(dims.h_v * dims.gate_width, hidden),
+            "w_out": w(hidden, dims.value_dim)}
+
+
+def make_hidden(rows: int, hidden: int, seed: int) -> torch.Tensor:
+    """Model hidden states ~ N(0, 1), rounded to bf16 (held in float32)."""
+    gen = torch.Generator().manual_seed(seed)
+    return torch.randn((rows, hidden), generator=gen, dtype=torch.float32).to(
+        torch.bfloat16).to(torch.float32)
+
+
 # --- the five named workloads ---------------------------------------------
 
 BIG = Dims(h_k=16, h_v=32, d_k=128, d_v=128, conv_k=4)

@@ -234,6 +234,60 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params,
                                void *out, void *workspace, size_t ws_bytes,
                                void *stream);
 
+/*
+ * The mixer with its projections ("oxinfer 0.0.5 src/qwen.rs", Gdn struct
+ * and gdn_forward): in_proj of the model's hidden states x into qkv, z, b
+ * and a, the mixer core above, and out_proj of its output back to the
+ * hidden size.  Weights are bf16, row-major [out features][in features],
+ * owned by the caller:
+ */
+typedef struct {
+    int32_t hidden;          /* model width H, a positive multiple of 8 */
+    const void *w_qkv;       /* [conv_dim][H] */
+    const void *w_z;         /* [H_v*d_v][H] */
+    const void *w_b;         /* [H_v][H] */
+    const void *w_a;         /* [H_v*gate_width][H], gate_width = d_k with
+                                GDN_DECAY_CHANNEL, else 1 */
+    const void *w_out;       /* [H][H_v*d_v] */
+} gdn_proj;
+
+/*
+ * Bytes of device workspace gdn_mixer_prefill needs for these sizes (also
+ * enough for gdn_mixer_decode with batch <= t_total), 0 if invalid.
+ */
+size_t gdn_mixer_workspace_bytes(const gdn_config *cfg, int32_t hidden, int32_t n_seq,
+                                 int32_t t_total);
+
+/*
+ * Mixer over packed sequences (prefill).  The projections are dense GEMMs
+ * (bf16 operands, fp32 accumulation); the projected activations stay fp32
+ * and the core runs on them; out_proj multiplies the core's fp32 output
+ * split into two bf16 parts, so the layer keeps fp32-level accuracy.
+ *   cfg->act_dtype must be GDN_BF16: x [t_total][H] bf16.
+ *   cfg->out_dtype selects y [t_total][H] bf16 or fp32.
+ *   cu_seqlens, state_in/out, conv_in/out: as in gdn_prefill_chunked.
+ *   workspace: gdn_mixer_workspace_bytes(cfg, H, n_seq, t_total) bytes,
+ *     256-byte aligned.  y must not overlap any other buffer.
+ */
+gdn_status gdn_mixer_prefill(const gdn_config *cfg, const gdn_params *params,
+                             const gdn_proj *proj, int32_t n_seq, int32_t t_total,
+                             const int32_t *cu_seqlens_host,
+                             const int32_t *cu_seqlens_dev, const void *x,
+                             const float *state_in, float *state_out,
+                             const float *conv_in, float *conv_out, void *y,
+                             void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Mixer decode step: one token for each of `batch` sequences, x [batch][H]
+ * bf16 -> y [batch][H]; conv_state and state updated in place as in
+ * gdn_decode_step.  workspace: gdn_mixer_workspace_bytes(cfg, H, batch,
+ * batch) bytes.
+ */
+gdn_status gdn_mixer_decode(const gdn_config *cfg, const gdn_params *params,
+                            const gdn_proj *proj, int32_t batch, const void *x,
+                            float *conv_state, float *state, void *y,
+                            void *workspace, size_t ws_bytes, void *stream);
+
 /* Static name of a status code. */
 const char *gdn_status_string(gdn_status status);
 

@@ -207,3 +207,20 @@ def mixer(shape: Shape, cu_seqlens, params, qkv, z, a, b, S0, conv0,
     if want_pre:
         out["o_pre"] = o_pre
     return out
+
+
+def mixer_layer(shape: Shape, cu_seqlens, params, proj, x, S0, conv0, nthreads=1):
+    """The mixer with its projections ("oxinfer 0.0.5 src/qwen.rs", Gdn
+    struct and gdn_forward): qkv, z, b, a = x W^T for the four in_proj
+    weights (matrix products in float64 with numpy), the mixer core above,
+    and out_proj y W_out^T.  proj: hidden and w_qkv [conv_dim, H],
+    w_z [value_dim, H], w_b [H_v, H], w_a [H_v * gate_width, H],
+    w_out [H, value_dim].  Returns dict(out, y, S, conv)."""
+    x = _f64(x)
+    qkv = x @ _f64(proj["w_qkv"]).T
+    z = x @ _f64(proj["w_z"]).T
+    b = x @ _f64(proj["w_b"]).T
+    a = x @ _f64(proj["w_a"]).T
+    r = mixer(shape, cu_seqlens, params, qkv, z, a, b, S0, conv0, nthreads=nthreads)
+    r["out"] = r["y"] @ _f64(proj["w_out"]).T
+    return r

@@ -29,7 +29,9 @@ def test_library_exports_every_header_function(lib):
     names = gdn.header_functions()
     assert set(names) == {"gdn_conv_update", "gdn_decode_step", "gdn_decode_multi",
                           "gdn_rewind", "gdn_prefill_workspace_bytes",
-                          "gdn_prefill_chunked", "gdn_status_string", "gdn_last_error"}
+                          "gdn_prefill_chunked", "gdn_mixer_workspace_bytes",
+                          "gdn_mixer_prefill", "gdn_mixer_decode", "gdn_status_string",
+                          "gdn_last_error"}
     dyn = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in dyn.splitlines() if line.strip()}
@@ -160,6 +162,37 @@ def test_decode_multi_and_rewind_reject_bad_arguments(lib):
     # the rewound state must not overlap the recorded inputs
     assert _rewind(lib, ptrs=[None, _P[0], _P[2], _P[3], _P[6], _P[4], _P[0], _P[5]]) == EINVAL
     assert _rewind(lib, batch=0) == OK
+
+
+def _proj(hidden=64, **kw):
+    base = dict(hidden=hidden, w_qkv=_P[10].value, w_z=_P[11].value, w_b=_P[12].value,
+                w_a=_P[13].value, w_out=_P[15].value)
+    base.update(kw)
+    return gdn._Proj(**base)
+
+
+@no_gpu
+def test_mixer_rejects_bad_arguments(lib):
+    c = _cfg()
+    assert lib.gdn_mixer_workspace_bytes(ctypes.byref(c), 64, 1, 100) > \
+        lib.gdn_prefill_workspace_bytes(ctypes.byref(c), 1, 100, 64)
+    assert lib.gdn_mixer_workspace_bytes(ctypes.byref(c), 60, 1, 100) == 0
+
+    def dec(cfg=None, proj=None, batch=2, ptrs=None, ws=(_P[9], 1 << 40)):
+        p = ptrs or [_P[0], _P[4], _P[5], _P[6]]   # x, conv_state, state, y
+        return lib.gdn_mixer_decode(ctypes.byref(cfg or c), ctypes.byref(_params()),
+                                    ctypes.byref(proj or _proj()), batch, *p, ws[0], ws[1], None)
+    assert dec(proj=_proj(hidden=60)) == EINVAL
+    assert dec(proj=_proj(w_out=None)) == EINVAL
+    assert dec(cfg=_cfg(act_dtype=1)) == EUNSUP
+    assert dec(ws=(_P[9], 10)) == EWS
+    assert dec(ptrs=[_P[0], _P[4], _P[5], _P[0]]) == EINVAL   # y aliasing x
+    assert dec(batch=0) == OK
+    cu = np.asarray([0, 10], dtype=np.int32)
+    st = lib.gdn_mixer_prefill(ctypes.byref(c), ctypes.byref(_params()), ctypes.byref(_proj()),
+                               1, 10, cu.ctypes.data_as(ctypes.c_void_p), _P[14], _P[0], _P[4],
+                               _P[5], _P[6], _P[7], _P[0], _P[9], 1 << 40, None)
+    assert st == EINVAL and "overlap" in lib.gdn_last_error().decode()
 
 
 def _prefill(lib, cu, t_total, cfg=None, chunk=64, ws=(_P[9], 1 << 40), outs=None):

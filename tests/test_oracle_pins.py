@@ -531,3 +531,32 @@ def test_kda_matches_independent_formulation(head_map):
         np.testing.assert_allclose(out["o_pre"][:, hv * DV:(hv + 1) * DV], o_ref,
                                    rtol=1e-11, atol=1e-13)
         np.testing.assert_allclose(out["S"][0, hv], S_ref, rtol=1e-11, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# the mixer with its projections ("oxinfer 0.0.5 src/qwen.rs", Gdn struct,
+# gdn_forward)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("decay", ["head", "channel"])
+def test_mixer_layer_with_selection_weights_is_the_core(decay):
+    """With in_proj weights that select consecutive slices of x (identity
+    blocks) and an identity out_proj, the layer is the core on those slices:
+    a wrong weight for any of qkv, z, b, a or the output fails."""
+    d = Dims(2, 4, 4, 3, conv_k=3, decay=decay)
+    c = _case(d, [6, 4], seed=41, s0_std=0.3, conv0_std=1.0, decay="weak")
+    widths = [d.conv_dim, d.value_dim, d.h_v, d.h_v * d.gate_width]
+    H = sum(widths)
+    x = np.concatenate([np.asarray(c.qkv, np.float64), np.asarray(c.z, np.float64),
+                        np.asarray(c.b, np.float64), np.asarray(c.a, np.float64)], axis=1)
+    eye = np.eye(H)
+    off = np.cumsum([0] + widths)
+    proj = {"hidden": H, "w_qkv": eye[off[0]:off[1]], "w_z": eye[off[1]:off[2]],
+            "w_b": eye[off[2]:off[3]], "w_a": eye[off[3]:off[4]],
+            "w_out": np.eye(d.value_dim)}
+    shape = oracle.Shape(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, d.gate, decay=decay)
+    layer = oracle.mixer_layer(shape, c.cu_seqlens, c.params, proj, x, c.S0, c.conv0)
+    core = oracle.mixer(shape, c.cu_seqlens, c.params, c.qkv, c.z, c.a, c.b, c.S0, c.conv0)
+    np.testing.assert_array_equal(layer["y"], core["y"])
+    np.testing.assert_array_equal(layer["out"], core["y"])
+    np.testing.assert_array_equal(layer["S"], core["S"])
