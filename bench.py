@@ -387,6 +387,36 @@ def main():
         kda_pf = (ev_m[0].elapsed_time(ev_m[1]) / calls, calls)
         del kws
 
+    # The mixer with its projections (hidden 2048): one decode step for the
+    # B=64 batch and the T=4096 prefill, same core inputs' shapes.
+    mix = {}
+    if not args.no_multi:
+        from gdn_inputs import make_hidden, make_projections
+        Hd = 2048
+        proj = make_projections(d, Hd, seed=7)
+        pj = {k: (v if k == "hidden" else v.to(bf).to(dev).contiguous()) for k, v in proj.items()}
+        xd = make_hidden(B, Hd, seed=8).to(bf).to(dev)
+        xp = make_hidden(T, Hd, seed=9).to(bf).to(dev)
+        mws = torch.empty(gdn.mixer_workspace_bytes(cfg, Hd, 1, T), dtype=torch.uint8, device=dev)
+        yd = torch.empty((B, Hd), dtype=bf, device=dev)
+        yp = torch.empty((T, Hd), dtype=bf, device=dev)
+        for name, fn, calls in (
+                ("decode", lambda: gdn.mixer_decode(cfg, dparams, pj, xd, c_dc, S_dc, y=yd,
+                                                    workspace=mws, stream=stream), 50),
+                ("prefill", lambda: gdn.mixer_prefill(cfg, params, pj, seq, xp, state_out=S_pf,
+                                                      conv_out=c_pf, y=yp, workspace=mws,
+                                                      stream=stream), 10)):
+            for _ in range(3):
+                fn()
+            ev_m = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev_m[0].record(stream)
+            for _ in range(calls):
+                fn()
+            ev_m[1].record(stream)
+            torch.cuda.synchronize()
+            mix[name] = (ev_m[0].elapsed_time(ev_m[1]) / calls, calls, Hd)
+        del mws
+
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -439,6 +469,29 @@ def main():
             "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
             "algorithmic_flops_per_launch": pflops, "duration_us": round(ms * 1e3, 2),
+            "launches_timed": calls, "tokens_per_s": round(T / (ms * 1e-3), 1)}
+    if "decode" in mix:
+        ms, calls, Hd = mix["decode"]
+        nproj = d.conv_dim + d.value_dim + 2 * d.h_v
+        mb = dbytes + (nproj + d.value_dim) * Hd * 2 + 2 * B * Hd * 2
+        gbs = mb / (ms * 1e-3) / 1e9
+        roof_multi["mixer_decode"] = {
+            "kernel": "gdn_mixer_decode (in_proj GEMMs, decode kernel, out_proj GEMMs), hidden 2048",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": mb, "duration_us": round(ms * 1e3, 2),
+            "launches_timed": calls, "tokens_per_s": round(B / (ms * 1e-3), 1)}
+    if "prefill" in mix:
+        ms, calls, Hd = mix["prefill"]
+        nproj = d.conv_dim + d.value_dim + 2 * d.h_v
+        mf = pflops + 2 * T * Hd * (nproj + d.value_dim)
+        tf = mf / (ms * 1e-3) / 1e12
+        roof_multi["mixer_prefill"] = {
+            "kernel": "gdn_mixer_prefill (in_proj GEMMs, chunked prefill, out_proj GEMMs), "
+                      "hidden 2048",
+            "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": mf, "duration_us": round(ms * 1e3, 2),
             "launches_timed": calls, "tokens_per_s": round(T / (ms * 1e-3), 1)}
     for t_new, (ms, calls) in multi.items():
         mb = decode_multi_bytes(d, B, t_new)

@@ -59,9 +59,16 @@ __global__ void __launch_bounds__(256) to_bf16_kernel(const float *__restrict__ 
 // ---------------------------------------------------------------------------
 namespace {
 
+// Everything a GEMM shape needs, made once and kept for the process.
+struct GemmPlan {
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+    hipblasLtMatmulAlgo_t algo;
+};
+
 struct Blas {
     hipblasLtHandle_t handle = nullptr;
-    std::map<std::tuple<int64_t, int64_t, int64_t, float>, hipblasLtMatmulAlgo_t> algos;
+    std::map<std::tuple<int64_t, int64_t, int64_t, size_t>, GemmPlan> plans;
 };
 
 std::mutex g_blas_mu;
@@ -72,8 +79,38 @@ hipError_t blas_error(hipblasStatus_t st)
     return st == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorLaunchFailure;
 }
 
+// The plan of D[m][n] = X[m][k] . W[n][k]^T: in column-major terms
+// D^T (n x m) = W (k x n)^T . X^T (k x m); bf16 operands, fp32 D.
+hipblasStatus_t make_plan(hipblasLtHandle_t h, int64_t m, int64_t n, int64_t k, size_t ws_bytes,
+                          GemmPlan &g)
+{
+    hipblasStatus_t st = hipblasLtMatmulDescCreate(&g.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F);
+    const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
+    if (st == HIPBLAS_STATUS_SUCCESS)
+        st = hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT));
+    if (st == HIPBLAS_STATUS_SUCCESS)
+        st = hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN));
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&g.la, HIP_R_16BF, k, n, k);
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&g.lb, HIP_R_16BF, k, m, k);
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&g.lc, HIP_R_32F, n, m, n);
+    hipblasLtMatmulPreference_t pref = nullptr;
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatmulPreferenceCreate(&pref);
+    const uint64_t cap = ws_bytes;
+    if (st == HIPBLAS_STATUS_SUCCESS)
+        st = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
+                                                   &cap, sizeof(cap));
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int found = 0;
+    if (st == HIPBLAS_STATUS_SUCCESS)
+        st = hipblasLtMatmulAlgoGetHeuristic(h, g.desc, g.la, g.lb, g.lc, g.lc, pref, 1, res, &found);
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    if (st == HIPBLAS_STATUS_SUCCESS && found < 1) st = HIPBLAS_STATUS_NOT_SUPPORTED;
+    if (st == HIPBLAS_STATUS_SUCCESS) g.algo = res[0].algo;
+    return st;
+}
+
 // D[m][n] (fp32, row-major) = beta * D + X[m][k] . W[n][k]^T, X and W bf16
-// row-major.  In column-major terms D^T (n x m) = W (k x n)^T . X^T (k x m).
+// row-major.
 hipError_t gemm_bf16_nt(int64_t m, int64_t n, int64_t k, const void *X, const void *W, float beta,
                         float *D, void *ws, size_t ws_bytes, hipStream_t s)
 {
@@ -88,44 +125,24 @@ hipError_t gemm_bf16_nt(int64_t m, int64_t n, int64_t k, const void *X, const vo
         b.handle = nullptr;
         return hipErrorLaunchFailure;
     }
-    hipblasLtMatmulDesc_t desc = nullptr;
-    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
-    hipblasStatus_t st = hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F);
-    const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
-    if (st == HIPBLAS_STATUS_SUCCESS)
-        st = hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT));
-    if (st == HIPBLAS_STATUS_SUCCESS)
-        st = hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN));
-    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, k, n, k);
-    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, k, m, k);
-    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&lc, HIP_R_32F, n, m, n);
-    const auto key = std::make_tuple(m, n, k, beta);
-    auto it = b.algos.find(key);
-    if (st == HIPBLAS_STATUS_SUCCESS && it == b.algos.end()) {
-        hipblasLtMatmulPreference_t pref = nullptr;
-        st = hipblasLtMatmulPreferenceCreate(&pref);
-        const uint64_t cap = ws_bytes;
-        if (st == HIPBLAS_STATUS_SUCCESS)
-            st = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
-                                                       &cap, sizeof(cap));
-        hipblasLtMatmulHeuristicResult_t res[1];
-        int found = 0;
-        if (st == HIPBLAS_STATUS_SUCCESS)
-            st = hipblasLtMatmulAlgoGetHeuristic(b.handle, desc, la, lb, lc, lc, pref, 1, res, &found);
-        if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-        if (st == HIPBLAS_STATUS_SUCCESS && found < 1) st = HIPBLAS_STATUS_NOT_SUPPORTED;
-        if (st == HIPBLAS_STATUS_SUCCESS) it = b.algos.emplace(key, res[0].algo).first;
+    const auto key = std::make_tuple(m, n, k, ws_bytes);
+    auto it = b.plans.find(key);
+    if (it == b.plans.end()) {
+        GemmPlan g;
+        const hipblasStatus_t st = make_plan(b.handle, m, n, k, ws_bytes, g);
+        if (st != HIPBLAS_STATUS_SUCCESS) {
+            if (g.lc) hipblasLtMatrixLayoutDestroy(g.lc);
+            if (g.lb) hipblasLtMatrixLayoutDestroy(g.lb);
+            if (g.la) hipblasLtMatrixLayoutDestroy(g.la);
+            if (g.desc) hipblasLtMatmulDescDestroy(g.desc);
+            return blas_error(st);
+        }
+        it = b.plans.emplace(key, g).first;
     }
-    if (st == HIPBLAS_STATUS_SUCCESS) {
-        const float alpha = 1.0f;
-        st = hipblasLtMatmul(b.handle, desc, &alpha, W, la, X, lb, &beta, D, lc, D, lc, &it->second,
-                             ws, ws_bytes, s);
-    }
-    if (lc) hipblasLtMatrixLayoutDestroy(lc);
-    if (lb) hipblasLtMatrixLayoutDestroy(lb);
-    if (la) hipblasLtMatrixLayoutDestroy(la);
-    if (desc) hipblasLtMatmulDescDestroy(desc);
-    return blas_error(st);
+    const GemmPlan &g = it->second;
+    const float alpha = 1.0f;
+    return blas_error(hipblasLtMatmul(b.handle, g.desc, &alpha, W, g.la, X, g.lb, &beta, D, g.lc, D,
+                                      g.lc, &g.algo, ws, ws_bytes, s));
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
