@@ -146,6 +146,19 @@ def test_decode_per_channel_decay(gdn, v):
     np.testing.assert_array_equal(conv.numpy(), conv_ref)
 
 
+def test_decode_per_channel_decay_b64(gdn):
+    """The full layer with one decay per key channel at B=64, three
+    consecutive steps."""
+    d = Dims(16, 32, 128, 128, 4, "sigmoid", decay="channel")
+    case = make_case(d, [0] * 64, act_dtype="bf16", seed=610, decay="weak", s0_std=0.02,
+                     conv0_std=1.0, decode_steps=3)
+    y, S, conv = run_decode(gdn, case, 3)
+    y_ref, S_ref, conv_ref = oracle_decode(case, 3)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
 def test_decode_bf16_out_is_rne_of_fp32_out(gdn):
     case = make_case(Dims(2, 4, 128, 128), [0] * 5, act_dtype="bf16", seed=7,
                      s0_std=0.02, conv0_std=1.0, decode_steps=3)
