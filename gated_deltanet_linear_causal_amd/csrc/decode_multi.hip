@@ -49,6 +49,8 @@ struct MultiArgs {
     int t_new;
     int h_k, h_v, group, conv_k, conv_dim, value_dim;
     int gate, out_bf16, tiled;
+    int out_split;   // out: bf16 hi parts, then the lo parts at out + split_off
+    size_t split_off;
     float norm_eps, l2_eps;
 };
 // (with one decay per key channel, a is [batch][t_new][H_v*d_k] and dt_bias
@@ -344,7 +346,10 @@ decode_multi_kernel(const MultiArgs p)
             y.y = o[1] * rn * w4.y * gatef_(z4.y, p.gate);
             y.z = o[2] * rn * w4.z * gatef_(z4.z, p.gate);
             y.w = o[3] * rn * w4.w * gatef_(z4.w, p.gate);
-            store_out4(p.out, out_index(q), y, p.out_bf16);
+            if (p.out_split)
+                store_split4(p.out, out_index(q), p.split_off, y);
+            else
+                store_out4(p.out, out_index(q), y, p.out_bf16);
         }
     }
 }
@@ -435,6 +440,8 @@ hipError_t launch_decode_multi(const Dims &d, const Params &p, int batch, int t_
     args.gate = d.gate;
     args.out_bf16 = d.out_bf16;
     args.tiled = d.tiled;
+    args.out_split = d.out_split;
+    args.split_off = (size_t)batch * t_new * d.value_dim;
     args.norm_eps = d.norm_eps;
     args.l2_eps = d.l2_eps;
     if (d.act_bf16) return launch_multi_dims<bf16_t>(args, d.chan_decay, d.d_k, d.d_v, batch, s);

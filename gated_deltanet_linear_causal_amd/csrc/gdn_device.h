@@ -75,6 +75,25 @@ __device__ __forceinline__ void store_out4(void *out, size_t i, float4 v, bool b
     }
 }
 
+// Four fp32 outputs as two bf16 parts, hi = bf16(v) at out[i] and
+// lo = bf16(v - hi) at out[lo_off + i] (the operands of a split-bf16
+// product).
+__device__ __forceinline__ void store_split4(void *out, size_t i, size_t lo_off, float4 v)
+{
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    bf16_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = f32_to_bf16(x[e]);
+        l[e] = f32_to_bf16(x[e] - bf16_bits_to_f32(h[e]));
+    }
+    bf16_t *o = static_cast<bf16_t *>(out);
+    *reinterpret_cast<uint2 *>(o + i) =
+        make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+    *reinterpret_cast<uint2 *>(o + lo_off + i) =
+        make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+}
+
 __device__ __forceinline__ void store_out1(void *out, size_t i, float v, bool bf16)
 {
     if (bf16)

@@ -18,6 +18,7 @@ struct Dims {
     int gate;       // 0: SiLU, 1: sigmoid
     int tiled;      // 0: key head hv / group, 1: key head hv % h_k
     int chan_decay; // 0: one decay per value head, 1: one per key channel
+    int out_split;  // 1: out receives bf16 hi parts, then (after all of them) bf16 lo parts
     float norm_eps, l2_eps;
 };
 

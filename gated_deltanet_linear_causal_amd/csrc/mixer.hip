@@ -4,12 +4,14 @@
 // "cherenkov qwen4_exp/cpu.rs", fn deltanet).
 //
 // The projections are plain dense GEMMs and run on hipBLASLt (bf16
-// operands, fp32 accumulation).  The projected activations stay fp32, so
-// the core runs on fp32 inputs.  The core's fp32 output is split into a
-// bf16 hi part and a bf16 lo part, and out_proj is the sum of the two bf16
-// GEMMs (hi then lo, the second accumulating into the first): rounding the
-// core output to one bf16 alone would cost about as much as the whole error
-// budget of the layer.
+// operands, fp32 accumulation), apart from the two narrow gate projections
+// of a decode step, which a small kernel does.  The projected activations
+// stay fp32, so the core runs on fp32 inputs.  The core writes its output
+// as a bf16 hi part and a bf16 lo part (hi = bf16(o), lo = bf16(o - hi)),
+// stacked as [hi rows; lo rows], and out_proj is one GEMM over the stacked
+// rows whose two halves are then added: rounding the core output to one
+// bf16 alone would cost about as much as the whole error budget of the
+// layer.
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -45,13 +47,63 @@ __global__ void __launch_bounds__(256) split_bf16_kernel(const float *__restrict
     reinterpret_cast<uint2 *>(lo)[i] = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
 }
 
-// fp32 -> bf16 (round to nearest even), four per thread.
-__global__ void __launch_bounds__(256) to_bf16_kernel(const float *__restrict__ v,
-                                                      bf16_t *__restrict__ out, size_t n4)
+// b = x W_b^T and a = x W_a^T for a few rows of x (the decode step), where a
+// library GEMM with this few output columns costs more in launch and tiling
+// than in work.  A wave per (output column, 8 rows of x): its lanes run over
+// the hidden size 8 elements at a time, with the weight row and all 8 rows
+// of x loaded before the sums so that the loads overlap.
+constexpr int kGateRows = 8;
+
+__global__ void __launch_bounds__(256) gates_proj_kernel(const bf16_t *__restrict__ x,
+                                                         const bf16_t *__restrict__ wb,
+                                                         const bf16_t *__restrict__ wa,
+                                                         float *__restrict__ b,
+                                                         float *__restrict__ a, int T, int H, int nb)
+{
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= 2 * nb) return; // whole waves; no barrier below
+    const int t0 = blockIdx.y * kGateRows;
+    const bf16_t *w = j < nb ? wb + (size_t)j * H : wa + (size_t)(j - nb) * H;
+    const bf16_t *xr[kGateRows];
+#pragma unroll
+    for (int r = 0; r < kGateRows; ++r) xr[r] = x + (size_t)min(t0 + r, T - 1) * H;
+    float acc[kGateRows] = {};
+    for (int k = lane * 8; k < H; k += 512) {
+        const uint4 wv = *reinterpret_cast<const uint4 *>(w + k);
+        uint4 xv[kGateRows];
+#pragma unroll
+        for (int r = 0; r < kGateRows; ++r) xv[r] = *reinterpret_cast<const uint4 *>(xr[r] + k);
+        const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int r = 0; r < kGateRows; ++r) {
+            const uint32_t xs[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[r] = fmaf(__uint_as_float(xs[e] << 16), __uint_as_float(ws[e] << 16), acc[r]);
+                acc[r] = fmaf(__uint_as_float(xs[e] & 0xffff0000u),
+                              __uint_as_float(ws[e] & 0xffff0000u), acc[r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kGateRows; ++r) acc[r] = group_sum<64>(acc[r]);
+    float *dst = j < nb ? b + j : a + (j - nb);
+#pragma unroll
+    for (int r = 0; r < kGateRows; ++r)
+        if (lane == r && t0 + r < T) dst[(size_t)(t0 + r) * nb] = acc[r];
+}
+
+// y = p[i] + p[n + i]: the products of the hi and lo parts, stacked as
+// rows 0..T-1 and T..2T-1 of one GEMM, added and stored as fp32 or bf16
+// (round to nearest even), four per thread.
+__global__ void __launch_bounds__(256) add_halves_kernel(const float *__restrict__ v, void *out,
+                                                         size_t n4, int out_bf16)
 {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n4) return;
-    store_out4(out, 4 * i, reinterpret_cast<const float4 *>(v)[i], true);
+    const float4 *v4 = reinterpret_cast<const float4 *>(v);
+    store_out4(out, 4 * i, v4[i] + v4[n4 + i], out_bf16);
 }
 
 // ---------------------------------------------------------------------------
@@ -150,15 +202,17 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t kBlasWorkspace = size_t(32) << 20;
 
 struct MixerWs {
-    size_t qkv, z, b, a, core, hi, lo, acc, blas, prefill, total;
+    size_t qkv, z, b, a, core, hl, acc, blas, prefill, total;
 };
 
-// The core runs on fp32 activations: the dims it sees.
-Dims core_dims(const Dims &d)
+// The core runs on fp32 activations and writes its output as bf16 hi and
+// lo parts (the operands of out_proj): the dims it sees.
+Dims core_dims(const Dims &d, bool split)
 {
     Dims c = d;
     c.act_bf16 = 0;
     c.out_bf16 = 0;
+    c.out_split = split;
     return c;
 }
 
@@ -175,18 +229,16 @@ MixerWs mixer_ws(const Dims &d, int hidden, int n_seq, int t_total, bool prefill
     off = align256(off + T * d.h_v * 4);
     w.a = off;
     off = align256(off + T * d.h_v * gw * 4);
-    w.core = off;
+    w.core = off; // fp32 core output, only where the core cannot split it itself
     off = align256(off + T * d.value_dim * 4);
-    w.hi = off;
-    off = align256(off + T * d.value_dim * 2);
-    w.lo = off;
-    off = align256(off + T * d.value_dim * 2);
-    w.acc = off;
-    off = align256(off + (d.out_bf16 ? T * hidden * 4 : 0));
+    w.hl = off;   // [hi parts][lo parts]
+    off = align256(off + T * d.value_dim * 2 * 2);
+    w.acc = off;  // the two stacked out_proj products
+    off = align256(off + 2 * T * hidden * 4);
     w.blas = off;
     off = align256(off + kBlasWorkspace);
     w.prefill = off;
-    off = align256(off + (prefill ? prefill_workspace_bytes(core_dims(d), n_seq, t_total) : 0));
+    off = align256(off + (prefill ? prefill_workspace_bytes(core_dims(d, true), n_seq, t_total) : 0));
     w.total = off;
     return w;
 }
@@ -204,6 +256,16 @@ hipError_t in_proj(const Dims &d, const Proj &pj, int T, const void *x, char *ba
     if ((e = gemm_bf16_nt(T, d.value_dim, H, x, pj.w_z, 0.0f,
                           reinterpret_cast<float *>(base + w.z), bw, kBlasWorkspace, s)) != hipSuccess)
         return e;
+    const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(pj.w_b) |
+                           reinterpret_cast<uintptr_t>(pj.w_a)) & 15) == 0;
+    if (gw == 1 && T > 0 && T <= 256 && aligned) {
+        const dim3 grid((2 * d.h_v + 3) / 4, (T + kGateRows - 1) / kGateRows);
+        hipLaunchKernelGGL(gates_proj_kernel, grid, dim3(256), 0, s,
+                           static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(pj.w_b),
+                           static_cast<const bf16_t *>(pj.w_a), reinterpret_cast<float *>(base + w.b),
+                           reinterpret_cast<float *>(base + w.a), T, (int)H, d.h_v);
+        return hipGetLastError();
+    }
     if ((e = gemm_bf16_nt(T, d.h_v, H, x, pj.w_b, 0.0f, reinterpret_cast<float *>(base + w.b), bw,
                           kBlasWorkspace, s)) != hipSuccess)
         return e;
@@ -211,32 +273,29 @@ hipError_t in_proj(const Dims &d, const Proj &pj, int T, const void *x, char *ba
                         bw, kBlasWorkspace, s);
 }
 
-// out_proj of the fp32 core output: y = hi . W_out^T + lo . W_out^T.
+// out_proj of the core output split into bf16 parts: y = hi . W_out^T +
+// lo . W_out^T, one GEMM over the stacked [hi; lo] rows and a pass that adds
+// the halves (split here from the fp32 core output when `split_here`).
 hipError_t out_proj(const Dims &d, const Proj &pj, int T, char *base, const MixerWs &w, void *y,
-                    hipStream_t s)
+                    bool split_here, hipStream_t s)
 {
     if (T == 0) return hipSuccess;
     const size_t n4 = (size_t)T * d.value_dim / 4;
-    bf16_t *hi = reinterpret_cast<bf16_t *>(base + w.hi), *lo = reinterpret_cast<bf16_t *>(base + w.lo);
-    hipLaunchKernelGGL(split_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                       reinterpret_cast<const float *>(base + w.core), hi, lo, n4);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    float *acc = d.out_bf16 ? reinterpret_cast<float *>(base + w.acc) : static_cast<float *>(y);
-    void *bw = base + w.blas;
-    if ((e = gemm_bf16_nt(T, pj.hidden, d.value_dim, hi, pj.w_out, 0.0f, acc, bw, kBlasWorkspace,
-                          s)) != hipSuccess)
-        return e;
-    if ((e = gemm_bf16_nt(T, pj.hidden, d.value_dim, lo, pj.w_out, 1.0f, acc, bw, kBlasWorkspace,
-                          s)) != hipSuccess)
-        return e;
-    if (d.out_bf16) {
-        const size_t m4 = (size_t)T * pj.hidden / 4;
-        hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((m4 + 255) / 256)), dim3(256), 0, s, acc,
-                           static_cast<bf16_t *>(y), m4);
-        return hipGetLastError();
+    bf16_t *hi = reinterpret_cast<bf16_t *>(base + w.hl), *lo = hi + (size_t)T * d.value_dim;
+    hipError_t e;
+    if (split_here) {
+        hipLaunchKernelGGL(split_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                           reinterpret_cast<const float *>(base + w.core), hi, lo, n4);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    return hipSuccess;
+    float *acc = reinterpret_cast<float *>(base + w.acc);
+    if ((e = gemm_bf16_nt(2 * (int64_t)T, pj.hidden, d.value_dim, hi, pj.w_out, 0.0f, acc,
+                          base + w.blas, kBlasWorkspace, s)) != hipSuccess)
+        return e;
+    const size_t m4 = (size_t)T * pj.hidden / 4;
+    hipLaunchKernelGGL(add_halves_kernel, dim3((unsigned)((m4 + 255) / 256)), dim3(256), 0, s, acc, y,
+                       m4, d.out_bf16);
+    return hipGetLastError();
 }
 
 } // namespace
@@ -255,11 +314,11 @@ hipError_t launch_mixer_prefill(const Dims &d, const Params &p, const Proj &pj, 
     char *base = static_cast<char *>(ws);
     hipError_t e;
     if ((e = in_proj(d, pj, t_total, x, base, w, s)) != hipSuccess) return e;
-    if ((e = launch_prefill(core_dims(d), p, n_seq, t_total, max_len, cu_dev, base + w.qkv,
+    if ((e = launch_prefill(core_dims(d, true), p, n_seq, t_total, max_len, cu_dev, base + w.qkv,
                             base + w.z, base + w.a, base + w.b, state_in, state_out, conv_in,
-                            conv_out, base + w.core, base + w.prefill, s)) != hipSuccess)
+                            conv_out, base + w.hl, base + w.prefill, s)) != hipSuccess)
         return e;
-    return out_proj(d, pj, t_total, base, w, y, s);
+    return out_proj(d, pj, t_total, base, w, y, false, s);
 }
 
 hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, int batch,
@@ -270,16 +329,17 @@ hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, i
     char *base = static_cast<char *>(ws);
     hipError_t e;
     if ((e = in_proj(d, pj, batch, x, base, w, s)) != hipSuccess) return e;
-    const Dims c = core_dims(d);
-    if (decode_multi_lds_bytes(c, 1) <= kDecodeMultiMaxLds)
+    const Dims c = core_dims(d, true);
+    const bool multi = decode_multi_lds_bytes(c, 1) <= kDecodeMultiMaxLds;
+    if (multi)
         e = launch_decode_multi(c, p, batch, 1, nullptr, base + w.qkv, base + w.z, base + w.a,
                                 base + w.b, conv_state, conv_state, state, state, nullptr,
-                                base + w.core, s);
-    else
-        e = launch_decode(c, p, batch, base + w.qkv, base + w.z, base + w.a, base + w.b,
-                          conv_state, state, base + w.core, s);
+                                base + w.hl, s);
+    else // the persistent kernel (very wide groups) writes fp32
+        e = launch_decode(core_dims(d, false), p, batch, base + w.qkv, base + w.z, base + w.a,
+                          base + w.b, conv_state, state, base + w.core, s);
     if (e != hipSuccess) return e;
-    return out_proj(d, pj, batch, base, w, y, s);
+    return out_proj(d, pj, batch, base, w, y, !multi, s);
 }
 
 } // namespace gdn

@@ -266,6 +266,7 @@ struct PrefillArgs {
     int ns, t_total;
     int h_k, h_v, d_v, group, conv_k, conv_dim, value_dim;
     int gate, out_bf16, tiled, kda;
+    int out_split;   // out: bf16 hi parts, then the lo parts at out + t_total * value_dim
     float norm_eps, l2_eps;
 };
 
@@ -1359,7 +1360,12 @@ norm_kernel(const PrefillArgs p, int rows)
         y.y = o[k][1] * rn * w[1] * gatef_(z[k][1], p.gate);
         y.z = o[k][2] * rn * w[2] * gatef_(z[k][2], p.gate);
         y.w = o[k][3] * rn * w[3] * gatef_(z[k][3], p.gate);
-        if (rbase + k * RPW < rows) store_out4(p.out, base[k], y, p.out_bf16);
+        if (rbase + k * RPW < rows) {
+            if (p.out_split)
+                store_split4(p.out, base[k], (size_t)p.t_total * p.value_dim, y);
+            else
+                store_out4(p.out, base[k], y, p.out_bf16);
+        }
     }
 }
 
@@ -1516,6 +1522,7 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.gate = d.gate;
     A.tiled = d.tiled;
     A.kda = d.chan_decay;
+    A.out_split = d.out_split;
     A.out_bf16 = d.out_bf16;
     A.norm_eps = d.norm_eps;
     A.l2_eps = d.l2_eps;
