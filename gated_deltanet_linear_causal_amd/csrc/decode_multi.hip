@@ -105,13 +105,20 @@ decode_multi_kernel(const MultiArgs p)
     // offset, so that no 64-bit per-lane row addresses stay live.
     const int toff = rg * DV + 4 * c4;
     auto head_base = [&](int hv) { return ((size_t)bs * p.h_v + hv) * DK * DV; };
+    // The first owned channel's history, taps and first input are loaded
+    // before the state: loads complete in issue order, so the conv, the
+    // gates and the L2 scales below run while the state is still arriving.
+    // (Not with one decay per key channel, whose larger register set would
+    // then spill: there the state is loaded first.)
+    constexpr bool kPre = !CH;
     f32x4 s[RPT];
-    {
+    auto load_state = [&]() {
         const float *Sin = p.state_in + head_base(value_head_of(hk, slot, p.h_k, group, p.tiled));
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
             s[r] = *reinterpret_cast<const f32x4 *>(Sin + toff + r * 8 * DV);
-    }
+    };
+    if (!kPre) load_state();
     const TIn *pa = static_cast<const TIn *>(p.a), *pb = static_cast<const TIn *>(p.b);
     const TIn *pz = static_cast<const TIn *>(p.z);
     const int ngate = n * group;                   // (token, value head) pairs
@@ -147,29 +154,49 @@ decode_multi_kernel(const MultiArgs p)
     // three raw inputs, oldest first, and the taps are right-aligned to four
     // (zero taps in front when K < 4), so one code path serves every K <= 4.
     const TIn *qkv = static_cast<const TIn *>(p.qkv);
-    for (int l = tid; l < nch; l += NT) {
-        int ch;
-        if (l < DK) ch = hk * DK + l;
-        else if (l < 2 * DK) ch = p.h_k * DK + hk * DK + (l - DK);
-        else {
-            const int lv = l - 2 * DK;
-            ch = 2 * p.h_k * DK + value_head_of(hk, lv / DV, p.h_k, group, p.tiled) * DV + lv % DV;
-        }
-        float win[3] = {0.f, 0.f, 0.f}, tap[4] = {0.f, 0.f, 0.f, 0.f};
+    auto channel_of = [&](int l) {
+        if (l < DK) return hk * DK + l;
+        if (l < 2 * DK) return p.h_k * DK + hk * DK + (l - DK);
+        const int lv = l - 2 * DK;
+        return 2 * p.h_k * DK + value_head_of(hk, lv / DV, p.h_k, group, p.tiled) * DV + lv % DV;
+    };
+    auto load_conv = [&](int ch, float (&win)[3], float (&tap)[4]) {
         const float *hin = p.conv_in + (size_t)bs * (K - 1) * CD + ch;
 #pragma unroll
         for (int pos = 0; pos < 3; ++pos) {
             const int j = pos - 4 + K; // history slot feeding window position pos
-            if (j >= 0) win[pos] = hin[(size_t)j * CD];
+            win[pos] = j >= 0 ? hin[(size_t)j * CD] : 0.0f;
         }
 #pragma unroll
         for (int pos = 0; pos < 4; ++pos) {
             const int j = pos - 4 + K;
-            if (j >= 0) tap[pos] = p.conv_w[(size_t)ch * K + j];
+            tap[pos] = j >= 0 ? p.conv_w[(size_t)ch * K + j] : 0.0f;
         }
-        float xs[kDecodeMultiMaxTokens];
+    };
+    float win0[3] = {0.f, 0.f, 0.f}, tap0[4] = {0.f, 0.f, 0.f, 0.f};
+    TIn x00 = TIn(0);
+    if (kPre && tid < nch) {
+        const int ch = channel_of(tid);
+        load_conv(ch, win0, tap0);
+        if (n > 0) x00 = qkv[(size_t)bs * T * CD + ch];
+    }
+    if (kPre) load_state();
+
+    for (int l = tid; l < nch; l += NT) {
+        const int ch = channel_of(l);
+        float win[3], tap[4], xs[kDecodeMultiMaxTokens];
+        if (kPre && l == tid) {
 #pragma unroll
-        for (int t = 0; t < kDecodeMultiMaxTokens; ++t)
+            for (int pos = 0; pos < 3; ++pos) win[pos] = win0[pos];
+#pragma unroll
+            for (int pos = 0; pos < 4; ++pos) tap[pos] = tap0[pos];
+            xs[0] = act_to_f32(x00);
+        } else {
+            load_conv(ch, win, tap);
+            xs[0] = n > 0 ? load_act(qkv, (size_t)bs * T * CD + ch) : 0.0f;
+        }
+#pragma unroll
+        for (int t = 1; t < kDecodeMultiMaxTokens; ++t)
             xs[t] = t < n ? load_act(qkv, ((size_t)bs * T + t) * CD + ch) : 0.0f;
 #pragma unroll
         for (int t = 0; t < kDecodeMultiMaxTokens; ++t) {
