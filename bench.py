@@ -92,7 +92,7 @@ def sources_hash():
     return h.hexdigest()[:16]
 
 
-PREFILL_KERNELS = ("qknorm_kernel", "tri_kernel", "scan_kernel", "norm_kernel", "conv_final_kernel")
+PREFILL_KERNELS = ("qknorm_kernel", "tri_kernel", "scan_kernel", "norm_kernel")
 
 
 def _counter_rows(directory):
@@ -441,7 +441,7 @@ def main():
                          frac=round(dec_cold_gbs / PEAK_HBM_GBS, 4),
                          duration_us=round(dc_cold_ms * 1e3, 2), launches_timed=cold_steps,
                          note="4 state sets in rotation (Infinity Cache cold for the state)")
-    roof_pf = {"kernel": "gdn_prefill_chunked (qknorm, tri, scan, norm, conv_final launches)",
+    roof_pf = {"kernel": "gdn_prefill_chunked (qknorm, tri, scan, norm launches)",
                "bound": "mfma", "achieved": round(pf_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                "unit": "TFLOP/s", "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
                "traffic": load_traffic("prefill_call"),
@@ -465,7 +465,7 @@ def main():
         tf = pflops / (ms * 1e-3) / 1e12
         roof_multi["kda_prefill"] = {
             "kernel": "gdn_prefill_chunked, one decay per key channel (kda_intra, tri, scan, "
-                      "norm, conv_final launches)",
+                      "norm launches)",
             "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
             "algorithmic_flops_per_launch": pflops, "duration_us": round(ms * 1e3, 2),

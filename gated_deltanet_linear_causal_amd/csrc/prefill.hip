@@ -29,8 +29,9 @@
 //           carry the chain of chunk states (D = U - W S | S'), four trail
 //           them by a chunk and form O = e^G Q S + P D; every operand of the
 //           next chunk is loaded into registers right after its last use.
-//   norm    grid (rows of (token, value head)): gated RMSNorm + output gate.
-//   conv_final: each sequence's last K-1 raw inputs become its history.
+//   norm    grid (rows of (token, value head)): gated RMSNorm + output gate;
+//           its first workgroups write each sequence's last K-1 raw inputs
+//           as its conv history.
 //
 // Contractions run on v_mfma_f32_16x16x32_bf16 with every fp32 operand
 // split into bf16 hi + lo and three products (hi.hi + hi.lo + lo.hi, fp32
@@ -1324,18 +1325,50 @@ scan_kernel(const PrefillArgs p, int slices)
 }
 
 // ---------------------------------------------------------------------------
+// conv history: each sequence's last K-1 raw inputs, oldest first, reaching
+// into its initial history when it is shorter ("oxinfer 0.0.5 src/qwen.rs"
+// gdn_forward, GdnState).  Thread per (channel, sequence).
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__device__ __forceinline__ void conv_final_channel(const PrefillArgs &p, int ch, int n)
+{
+    if (ch >= p.conv_dim) return;
+    const int K = p.conv_k, CD = p.conv_dim;
+    const int s0 = p.cu[n], L = p.cu[n + 1] - s0;
+    const TIn *x = static_cast<const TIn *>(p.qkv);
+    float old[3];
+    for (int j = 0; j < K - 1; ++j)
+        old[j] = p.conv_in ? p.conv_in[((size_t)n * (K - 1) + j) * CD + ch] : 0.0f;
+    for (int sl = 0; sl < K - 1; ++sl) {
+        const int tau = L - (K - 1) + sl;
+        const float v = tau >= 0 ? load_act(x, (size_t)(s0 + tau) * CD + ch) : old[K - 1 + tau];
+        p.conv_out[((size_t)n * (K - 1) + sl) * CD + ch] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // norm: gated RMSNorm of each (token, value head) row: d_v/4 lanes per row,
 // float4 per lane ("oxinfer 0.0.5 src/qwen.rs" gdn_forward, gated norm).
+// The first conv_blocks workgroups of the launch write the conv history
+// instead (conv_bx blocks of 256 channels per sequence): that work needs
+// only the raw inputs and the initial history, which every earlier launch
+// of the call has finished reading, and it hides under the norm's stream.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DV>
 __global__ void __launch_bounds__(256)
-norm_kernel(const PrefillArgs p, int rows)
+norm_kernel(const PrefillArgs p, int rows, int conv_blocks, int conv_bx)
 {
+    if ((int)blockIdx.x < conv_blocks) {
+        const int b = blockIdx.x;
+        conv_final_channel<TIn>(p, (b % conv_bx) * 256 + threadIdx.x, b / conv_bx);
+        return;
+    }
+    const int blk = blockIdx.x - conv_blocks;
     constexpr int LPR = DV / 4;   // lanes per row
     constexpr int RPW = 64 / LPR; // rows per wave and slot
     constexpr int RPT = 4;        // rows per lane (independent loads in flight)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rbase = (blockIdx.x * 4 + wave) * RPT * RPW + lane / LPR;
+    const int rbase = (blk * 4 + wave) * RPT * RPW + lane / LPR;
     const int c4 = (lane % LPR) * 4;
     const TIn *zp = static_cast<const TIn *>(p.z);
     f32x4 o[RPT], z[RPT];
@@ -1369,32 +1402,18 @@ norm_kernel(const PrefillArgs p, int rows)
     }
 }
 
-template <typename TIn>
-__global__ void __launch_bounds__(256)
-conv_final_kernel(const PrefillArgs p)
-{
-    const int ch = blockIdx.x * 256 + threadIdx.x;
-    const int n = blockIdx.y;
-    if (ch >= p.conv_dim) return;
-    const int K = p.conv_k, CD = p.conv_dim;
-    const int s0 = p.cu[n], L = p.cu[n + 1] - s0;
-    const TIn *x = static_cast<const TIn *>(p.qkv);
-    float old[3];
-    for (int j = 0; j < K - 1; ++j)
-        old[j] = p.conv_in ? p.conv_in[((size_t)n * (K - 1) + j) * CD + ch] : 0.0f;
-    for (int sl = 0; sl < K - 1; ++sl) {
-        const int tau = L - (K - 1) + sl;
-        const float v = tau >= 0 ? load_act(x, (size_t)(s0 + tau) * CD + ch) : old[K - 1 + tau];
-        p.conv_out[((size_t)n * (K - 1) + sl) * CD + ch] = v;
-    }
-}
-
+// The gated norm of `rows` rows, with the conv history of n_seq sequences
+// written by extra workgroups of the same launch (none when conv_k == 1).
 template <typename TIn, int DV>
-static hipError_t launch_norm(const PrefillArgs &a, int rows, hipStream_t s)
+static hipError_t launch_norm(const PrefillArgs &a, int rows, int n_seq, hipStream_t s)
 {
     constexpr int RPB = 4 * 4 * (64 / (DV / 4)); // rows per block
-    hipLaunchKernelGGL((norm_kernel<TIn, DV>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a,
-                       rows);
+    const int conv_bx = (a.conv_dim + 255) / 256;
+    const int conv_blocks = a.conv_k > 1 ? conv_bx * n_seq : 0;
+    const int blocks = conv_blocks + (rows + RPB - 1) / RPB;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((norm_kernel<TIn, DV>), dim3(blocks), dim3(256), 0, s, a, rows,
+                       conv_blocks, conv_bx);
     return hipGetLastError();
 }
 
@@ -1425,16 +1444,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
                            a, slices);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int rows = t_total * a.h_v;
-    if (rows > 0) {
-        if ((e = launch_norm<TIn, DV>(a, rows, s)) != hipSuccess) return e;
-    }
-    if (n_seq > 0 && a.conv_k > 1) {
-        hipLaunchKernelGGL((conv_final_kernel<TIn>), dim3((a.conv_dim + 255) / 256, n_seq),
-                           dim3(256), 0, s, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return launch_norm<TIn, DV>(a, t_total * a.h_v, n_seq, s);
 }
 
 // Dynamic LDS above the default 64 KB needs the attribute raised once.
