@@ -90,6 +90,8 @@ gdn_status check_params(const gdn_params *p, gdn::Params &out)
         return fail(GDN_EINVAL, "conv_w, dt_bias and norm_w must be non-NULL");
     if ((p->a_log == nullptr) == (p->decay_coef == nullptr))
         return fail(GDN_EINVAL, "exactly one of a_log and decay_coef must be given");
+    if ((reinterpret_cast<uintptr_t>(p->conv_w) | reinterpret_cast<uintptr_t>(p->norm_w)) & 15)
+        return fail(GDN_EINVAL, "conv_w and norm_w must be 16-byte aligned");
     out.conv_w = p->conv_w;
     out.a_log = p->a_log;
     out.decay_coef = p->decay_coef;
@@ -354,6 +356,9 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, 
     if (max_len > 65535 * 64) return fail(GDN_EUNSUPPORTED, "sequence longer than %d", 65535 * 64);
     if (t_total > 0 && (!qkv || !z || !a || !b || !out))
         return fail(GDN_EINVAL, "qkv, z, a, b and out are required when t_total > 0");
+    if (t_total > 0 && ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(z) |
+                         reinterpret_cast<uintptr_t>(out)) & 15))
+        return fail(GDN_EINVAL, "qkv, z and out must be 16-byte aligned");
     if (n_seq > 0 && (!state_out || (d.conv_k > 1 && !conv_out)))
         return fail(GDN_EINVAL, "state_out (and conv_out when K > 1) are required");
     const size_t need = gdn::prefill_workspace_bytes(d, n_seq, t_total);

@@ -137,6 +137,13 @@ template <> struct RawAct<bf16_t> {
     {
         return *reinterpret_cast<const uint2 *>(p + i);
     }
+    // channels i..i+7 (16 bytes) as two quads
+    __device__ __forceinline__ static void load8(const bf16_t *p, size_t i, type &a, type &b)
+    {
+        const uint4 v = *reinterpret_cast<const uint4 *>(p + i);
+        a = make_uint2(v.x, v.y);
+        b = make_uint2(v.z, v.w);
+    }
     __device__ __forceinline__ static f32x4 to_f32(type u)
     {
         return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
@@ -148,6 +155,11 @@ template <> struct RawAct<float> {
     __device__ __forceinline__ static type load(const float *p, size_t i)
     {
         return *reinterpret_cast<const f32x4 *>(p + i);
+    }
+    __device__ __forceinline__ static void load8(const float *p, size_t i, type &a, type &b)
+    {
+        a = load(p, i);
+        b = load(p, i + 4);
     }
     __device__ __forceinline__ static f32x4 to_f32(type u) { return u; }
 };
@@ -276,6 +288,15 @@ struct PrefillArgs {
 __device__ __forceinline__ void load_taps4(const PrefillArgs &p, int ch, float (&w)[4][4])
 {
     const int K = p.conv_k;
+    if (K == 4) { // four 16-byte rows (ch is a multiple of 4): one load per channel
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x4 t = ld4(p.conv_w + (size_t)(ch + e) * 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[e][j] = t[j];
+        }
+        return;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -386,8 +407,7 @@ qknorm_kernel(const PrefillArgs p)
         for (int j = 0; j < WIN; ++j) {
             const int tau = min(max(tl0 - 3 + j, 0), L - 1);
             const size_t base = (size_t)(s0 + tau) * p.conv_dim + ch;
-            raw[j][0] = RawAct<TIn>::load(x, base);
-            raw[j][1] = RawAct<TIn>::load(x, base + 4);
+            RawAct<TIn>::load8(x, base, raw[j][0], raw[j][1]);
         }
     };
     RawT rawA[WIN][2], rawB[WIN][2];
@@ -557,8 +577,7 @@ kda_intra_kernel(const PrefillArgs p)
     for (int j = 0; j < WIN; ++j) {
         const int tau = min(max(tl0 - 3 + j, 0), L - 1);
         const size_t base = (size_t)(s0 + tau) * p.conv_dim + ch;
-        raw[j][0] = RawAct<TIn>::load(x, base);
-        raw[j][1] = RawAct<TIn>::load(x, base + 4);
+        RawAct<TIn>::load8(x, base, raw[j][0], raw[j][1]);
     }
     const TIn *pa = static_cast<const TIn *>(p.a);
     const int gd = tid % DK, gpart = tid / DK;
@@ -815,6 +834,39 @@ tri_kernel(const PrefillArgs p)
             gqk[m] = glive ? ld4(g + kC * kC + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
+    // ---- loads needed only after the solve, issued right after the Gram
+    // rows (loads complete in issue order, so they do not delay the Gram
+    // rows) and in flight during the gates, A, P and the solve: raw v
+    // inputs, thread (channel group cg, token group tg)
+    typedef typename RawAct<TIn>::type RawT;
+    const TIn *x = static_cast<const TIn *>(p.qkv);
+    const int cg = tid % CG, tg = tid / CG;
+    const int vch = 2 * p.h_k * DK + hv * DV + 4 * cg;
+    const int vt0 = c * kC + tg * TPG; // first token (sequence position)
+    RawT vraw[VWIN];
+#pragma unroll
+    for (int j = 0; j < VWIN; ++j) {
+        const int tau = min(max(vt0 - 3 + j, 0), L - 1);
+        vraw[j] = RawAct<TIn>::load(x, (size_t)(s0 + tau) * p.conv_dim + vch);
+    }
+    // k^T fragments for the W^T tiles of this wave: column blocks 2 sp and
+    // 2 sp + 1 of d_k (sp = wave), both token steps
+    const int sp = wave;
+    const bool wact = sp < KS;
+    Frag kA[2][2];
+    if (wact) {
+        const __bf16 *kt = (KDA ? p.ws_kw + ((size_t)hv * p.ns + slot) * (2 * kC * DK)
+                                : p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK)) + lane * 8;
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int f = ((2 * sp + n2) * 2 + s) * 2;
+                kA[n2][s] = frag_at(kt + (size_t)f * 512, kt + (size_t)(f + 1) * 512);
+            }
+    }
+    float wv[4][4];
+    load_taps4(p, vch, wv);
     // ---- gates ("cherenkov qwen4_exp/cpu.rs" fn deltanet) and their
     // inclusive prefix sum over the chunk (wave 0); past the chunk end
     // g = 0 and b = 0.
@@ -858,7 +910,9 @@ tri_kernel(const PrefillArgs p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 16 * gq + 4 * m + e;
-                const float md = j <= i ? (KDA ? 1.0f : expf(Gi - sG[j])) : 0.0f;
+                // e^{G_i - G_j} <= 1: the hardware exponential (relative
+                // error ~1e-7 where the factor is not negligible)
+                const float md = j <= i ? (KDA ? 1.0f : __expf(Gi - sG[j])) : 0.0f;
                 av[e] = j < i ? bi * md * gkk[m][e] : 0.0f;
                 pv[e] = md * gqk[m][e];
             }
@@ -883,38 +937,6 @@ tri_kernel(const PrefillArgs p)
         }
     }
 
-    // ---- loads needed only after the solve, issued now so that the solve
-    // hides their latency: raw v inputs, thread (channel group cg, token
-    // group tg)
-    typedef typename RawAct<TIn>::type RawT;
-    const TIn *x = static_cast<const TIn *>(p.qkv);
-    const int cg = tid % CG, tg = tid / CG;
-    const int vch = 2 * p.h_k * DK + hv * DV + 4 * cg;
-    const int vt0 = c * kC + tg * TPG; // first token (sequence position)
-    RawT vraw[VWIN];
-#pragma unroll
-    for (int j = 0; j < VWIN; ++j) {
-        const int tau = min(max(vt0 - 3 + j, 0), L - 1);
-        vraw[j] = RawAct<TIn>::load(x, (size_t)(s0 + tau) * p.conv_dim + vch);
-    }
-    // k^T fragments for the W^T tiles of this wave: column blocks 2 sp and
-    // 2 sp + 1 of d_k (sp = wave), both token steps
-    const int sp = wave;
-    const bool wact = sp < KS;
-    Frag kA[2][2];
-    if (wact) {
-        const __bf16 *kt = (KDA ? p.ws_kw + ((size_t)hv * p.ns + slot) * (2 * kC * DK)
-                                : p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK)) + lane * 8;
-#pragma unroll
-        for (int n2 = 0; n2 < 2; ++n2)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int f = ((2 * sp + n2) * 2 + s) * 2;
-                kA[n2][s] = frag_at(kt + (size_t)f * 512, kt + (size_t)(f + 1) * 512);
-            }
-    }
-    float wv[4][4];
-    load_taps4(p, vch, wv);
 
     // ---- T = (I + A)^-1, blocked over 16x16 blocks, fp32.
     // Diagonal blocks by forward substitution: wave b owns block b; lane

@@ -92,7 +92,9 @@ typedef struct {
  * log-decay is g = -exp(a_log[hv]) * softplus(a + dt_bias[hv]), or
  * g = decay_coef[hv] * softplus(a + dt_bias[hv]) for layers that store the
  * coefficient -exp(A_log) itself (GGUF ssm_a; "oxinfer 0.0.5 src/qwen.rs",
- * weight loading). */
+ * weight loading).
+ * conv_w and norm_w must be 16-byte aligned (the kernels read them in
+ * 16-byte rows; every torch allocation is); a misaligned one is GDN_EINVAL. */
 typedef struct {
     const float *conv_w;    /* [conv_dim][K] depthwise conv taps, no bias */
     const float *a_log;     /* [H_v]  decay magnitude, g = -exp(a_log)... */
@@ -212,7 +214,9 @@ size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seq,
  * start; the last chunk of a sequence may be partial.
  *   chunk: tokens per chunk (64).
  *   cu_seqlens_host / _dev: as in gdn_conv_update.
- *   qkv [t_total][conv_dim], z [t_total][H_v*d_v], a, b [t_total][H_v].
+ *   qkv [t_total][conv_dim], z [t_total][H_v*d_v], a, b [t_total][H_v];
+ *     qkv, z and out are read and written in 16-byte pieces and must be
+ *     16-byte aligned (GDN_EINVAL otherwise).
  *   state_in [n_seq][H_v][d_k][d_v] fp32, or NULL for zeros;
  *   state_out, same shape: each sequence's final state.  May equal
  *     state_in (in place) but must not partially overlap it.

@@ -112,6 +112,12 @@ def test_decode_rejects_bad_arguments(lib):
     assert "a_log" in lib.gdn_last_error().decode()
     assert _decode(lib, params=gdn._Params(_P[10].value, None, _P[12].value,
                                            _P[13].value, None)) == EINVAL
+    # conv_w and norm_w are read in 16-byte rows
+    assert _decode(lib, params=gdn._Params(_P[10].value + 4, _P[11].value, _P[12].value,
+                                           _P[13].value, None)) == EINVAL
+    assert "16-byte" in lib.gdn_last_error().decode()
+    assert _decode(lib, params=gdn._Params(_P[10].value, _P[11].value, _P[12].value,
+                                           _P[13].value + 8, None)) == EINVAL
     assert _decode(lib, batch=-1) == EINVAL
     assert _decode(lib, ptrs=[None] + _P[1:7]) == EINVAL
     # out aliasing the state
@@ -195,14 +201,14 @@ def test_mixer_rejects_bad_arguments(lib):
     assert st == EINVAL and "overlap" in lib.gdn_last_error().decode()
 
 
-def _prefill(lib, cu, t_total, cfg=None, chunk=64, ws=(_P[9], 1 << 40), outs=None):
+def _prefill(lib, cu, t_total, cfg=None, chunk=64, ws=(_P[9], 1 << 40), outs=None, qkv=_P[0]):
     c = cfg or _cfg()
     cu_h = np.asarray(cu, dtype=np.int32)
     n = len(cu) - 1
     o = outs or dict(state_in=_P[4], state_out=_P[5], conv_in=_P[6], conv_out=_P[7], out=_P[8])
     return lib.gdn_prefill_chunked(
         ctypes.byref(c), ctypes.byref(_params()), chunk, n, t_total,
-        cu_h.ctypes.data_as(ctypes.c_void_p), _P[14], _P[0], _P[1], _P[2], _P[3],
+        cu_h.ctypes.data_as(ctypes.c_void_p), _P[14], qkv, _P[1], _P[2], _P[3],
         o["state_in"], o["state_out"], o["conv_in"], o["conv_out"], o["out"], ws[0],
         ws[1], None)
 
@@ -226,6 +232,9 @@ def test_prefill_rejects_chunk_workspace_and_aliases(lib):
     o = dict(state_in=_P[4], state_out=ctypes.c_void_p(_P[4].value + 4), conv_in=_P[6],
              conv_out=_P[7], out=_P[8])
     assert _prefill(lib, [0, 10], 10, outs=o) == EINVAL   # partial state overlap
+    # activations are read in 16-byte pieces
+    assert _prefill(lib, [0, 10], 10, qkv=ctypes.c_void_p(_P[0].value + 8)) == EINVAL
+    assert "16-byte" in lib.gdn_last_error().decode()
 
 
 def test_last_error_is_thread_local(lib):
