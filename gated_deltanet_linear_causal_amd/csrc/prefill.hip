@@ -536,12 +536,15 @@ qknorm_kernel(const PrefillArgs p)
 //      chunk decay e^{G_C} of each channel.
 // ---------------------------------------------------------------------------
 template <int DK> constexpr size_t kda_smem_bytes() { return 3 * (size_t)kC * (DK + 4) * 4; }
+// Waves of kda_intra: its LDS rows allow one workgroup per CU, so at d_k = 128
+// it runs 16 waves (twice the latency hiding of 8 for the same LDS).
+template <int DK> constexpr int kda_waves() { return DK == 128 ? 16 : 8; }
 
 template <typename TIn, int DK>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(64 * kda_waves<DK>())
 kda_intra_kernel(const PrefillArgs p)
 {
-    constexpr int NW = 8;                    // waves
+    constexpr int NW = kda_waves<DK>();      // waves
     constexpr int RQ = DK + 4;               // fp32 LDS row stride
     constexpr int LPT = DK / 4;              // lanes per token row (8 channels each)
     constexpr int TPI = 64 / LPT;            // token rows per wave pass
@@ -697,17 +700,22 @@ kda_intra_kernel(const PrefillArgs p)
         // exponential per (i, j, d), computed for every lane and masked (a
         // term with j > i may overflow, so it is selected away, never
         // multiplied); zero above the diagonal
+        // (with 16 waves, one column of each quad per wave)
+        constexpr int JJ = 16 / NW;
         const int b = wave & 3, jh = wave >> 2, i = 16 * b + col;
-        float acc_a[2] = {0.f, 0.f}, acc_p[2] = {0.f, 0.f};
-        bool live[2];
+        float acc_a[JJ], acc_p[JJ];
+        bool live[JJ];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) live[jj] = 4 * kq + 2 * jh + jj <= col;
+        for (int jj = 0; jj < JJ; ++jj) {
+            acc_a[jj] = acc_p[jj] = 0.0f;
+            live[jj] = 4 * kq + JJ * jh + jj <= col;
+        }
         for (int d4 = 0; d4 < DK / 4; ++d4) {
             const f32x4 ki = ld4(sK + i * RQ + 4 * d4), qi = ld4(sQ + i * RQ + 4 * d4);
             const f32x4 gi = ld4(sG + i * RQ + 4 * d4);
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = 16 * b + 4 * kq + 2 * jh + jj;
+            for (int jj = 0; jj < JJ; ++jj) {
+                const int j = 16 * b + 4 * kq + JJ * jh + jj;
                 const f32x4 kj = ld4(sK + j * RQ + 4 * d4), gj = ld4(sG + j * RQ + 4 * d4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -719,8 +727,8 @@ kda_intra_kernel(const PrefillArgs p)
             }
         }
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int j = 16 * b + 4 * kq + 2 * jh + jj;
+        for (int jj = 0; jj < JJ; ++jj) {
+            const int j = 16 * b + 4 * kq + JJ * jh + jj;
             gram[i * kC + j] = live[jj] ? acc_a[jj] : 0.0f;
             gram[kC * kC + i * kC + j] = live[jj] ? acc_p[jj] : 0.0f;
         }
@@ -1448,7 +1456,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
         const int nch_max = (max_len + kC - 1) / kC;
         const dim3 grid_v((max_len + kC - 1) / kC, a.h_v, n_seq);
         if (KDA) {
-            hipLaunchKernelGGL((kda_intra_kernel<TIn, DK>), grid_v, dim3(512), kda_smem_bytes<DK>(),
+            hipLaunchKernelGGL((kda_intra_kernel<TIn, DK>), grid_v, dim3(64 * kda_waves<DK>()),
+                               kda_smem_bytes<DK>(),
                                s, a);
         } else {
             const dim3 grid_k((nch_max + kQkChunks - 1) / kQkChunks, a.h_k, n_seq);
