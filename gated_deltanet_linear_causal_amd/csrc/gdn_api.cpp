@@ -157,6 +157,8 @@ gdn_status gdn_conv_update(const gdn_config *cfg, const gdn_params *params, int3
     if ((st = check_params(params, p)) != GDN_OK) return st;
     int max_len = 0;
     if ((st = check_cu(n_seq, t_total, cu_seqlens_host, cu_seqlens_dev, max_len)) != GDN_OK) return st;
+    if ((long long)t_total * d.h_v > (1LL << 30)) // (token, value head) rows are counted in int
+        return fail(GDN_EUNSUPPORTED, "t_total * H_v must be <= 2^30 (got %lld)", (long long)t_total * d.h_v);
     if (t_total > 0 && (!x || !y)) return fail(GDN_EINVAL, "x and y are required when t_total > 0");
     if (n_seq > 0 && d.conv_k > 1 && !conv_state) return fail(GDN_EINVAL, "conv_state is required");
     const size_t esz = d.act_bf16 ? 2 : 4;
@@ -182,6 +184,8 @@ gdn_status gdn_decode_step(const gdn_config *cfg, const gdn_params *params, int3
     if ((st = check_params(params, p)) != GDN_OK) return st;
     if (batch < 0) return fail(GDN_EINVAL, "batch must be >= 0 (got %d)", batch);
     if (batch > 65535) return fail(GDN_EUNSUPPORTED, "batch must be <= 65535 (got %d)", batch);
+    if ((long long)batch * d.h_k > (1LL << 30)) // one workgroup per (sequence, key head)
+        return fail(GDN_EUNSUPPORTED, "batch * H_k must be <= 2^30 (got %lld)", (long long)batch * d.h_k);
     if (batch == 0) return ok();
     if (!qkv || !z || !a || !b || !state || !out || (d.conv_k > 1 && !conv_state))
         return fail(GDN_EINVAL, "qkv, z, a, b, state, out (and conv_state when K > 1) are required");
@@ -229,6 +233,8 @@ gdn_status check_multi(const gdn::Dims &d, int32_t batch, int32_t t_new, const v
 {
     if (batch < 0) return fail(GDN_EINVAL, "batch must be >= 0 (got %d)", batch);
     if (batch > 65535) return fail(GDN_EUNSUPPORTED, "batch must be <= 65535 (got %d)", batch);
+    if ((long long)batch * d.h_k > (1LL << 30)) // one workgroup per (sequence, key head)
+        return fail(GDN_EUNSUPPORTED, "batch * H_k must be <= 2^30 (got %lld)", (long long)batch * d.h_k);
     if (t_new < 1 || t_new > gdn::kDecodeMultiMaxTokens)
         return fail(GDN_EUNSUPPORTED, "tokens per sequence must be in [1, %d] (got %d)",
                     gdn::kDecodeMultiMaxTokens, t_new);
@@ -353,6 +359,8 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, 
     if (chunk != 64) return fail(GDN_EUNSUPPORTED, "chunk must be 64 (got %d)", chunk);
     int max_len = 0;
     if ((st = check_cu(n_seq, t_total, cu_seqlens_host, cu_seqlens_dev, max_len)) != GDN_OK) return st;
+    if ((long long)t_total * d.h_v > (1LL << 30)) // (token, value head) rows are counted in int
+        return fail(GDN_EUNSUPPORTED, "t_total * H_v must be <= 2^30 (got %lld)", (long long)t_total * d.h_v);
     if (max_len > 65535 * 64) return fail(GDN_EUNSUPPORTED, "sequence longer than %d", 65535 * 64);
     if (t_total > 0 && (!qkv || !z || !a || !b || !out))
         return fail(GDN_EINVAL, "qkv, z, a, b and out are required when t_total > 0");
@@ -460,6 +468,8 @@ gdn_status gdn_mixer_prefill(const gdn_config *cfg, const gdn_params *params,
     if ((st = check_proj(d, cfg, proj, pj)) != GDN_OK) return st;
     int max_len = 0;
     if ((st = check_cu(n_seq, t_total, cu_seqlens_host, cu_seqlens_dev, max_len)) != GDN_OK) return st;
+    if ((long long)t_total * d.h_v > (1LL << 30)) // (token, value head) rows are counted in int
+        return fail(GDN_EUNSUPPORTED, "t_total * H_v must be <= 2^30 (got %lld)", (long long)t_total * d.h_v);
     if (max_len > 65535 * 64) return fail(GDN_EUNSUPPORTED, "sequence longer than %d", 65535 * 64);
     if (t_total > 0 && (!x || !y)) return fail(GDN_EINVAL, "x and y are required when t_total > 0");
     if (n_seq > 0 && (!state_out || (d.conv_k > 1 && !conv_out)))
@@ -503,6 +513,8 @@ gdn_status gdn_mixer_decode(const gdn_config *cfg, const gdn_params *params,
     if ((st = check_proj(d, cfg, proj, pj)) != GDN_OK) return st;
     if (batch < 0) return fail(GDN_EINVAL, "batch must be >= 0 (got %d)", batch);
     if (batch > 65535) return fail(GDN_EUNSUPPORTED, "batch must be <= 65535 (got %d)", batch);
+    if ((long long)batch * d.h_k > (1LL << 30)) // one workgroup per (sequence, key head)
+        return fail(GDN_EUNSUPPORTED, "batch * H_k must be <= 2^30 (got %lld)", (long long)batch * d.h_k);
     if (batch == 0) return ok();
     if (!x || !y || !state || (d.conv_k > 1 && !conv_state))
         return fail(GDN_EINVAL, "x, y, state (and conv_state when K > 1) are required");

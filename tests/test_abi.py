@@ -237,6 +237,19 @@ def test_prefill_rejects_chunk_workspace_and_aliases(lib):
     assert "16-byte" in lib.gdn_last_error().decode()
 
 
+@no_gpu
+def test_shapes_beyond_the_launch_grids_are_rejected(lib):
+    # (token, value head) rows and (sequence, key head) workgroups are counted in 32 bits
+    t = (1 << 25) + 64
+    assert _prefill(lib, [0, t], t, cfg=_cfg(h_k=16, h_v=32)) == EUNSUP
+    assert "t_total * H_v" in lib.gdn_last_error().decode()
+    wide = _cfg(h_k=32768, h_v=32768)
+    assert _decode(lib, wide, batch=65535) == EUNSUP
+    assert "batch * H_k" in lib.gdn_last_error().decode()
+    assert _multi(lib, wide, batch=65535, t_new=1) == EUNSUP
+    assert "batch * H_k" in lib.gdn_last_error().decode()
+
+
 def test_last_error_is_thread_local(lib):
     c = _cfg(h_v=3)
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(c), 1, 10, 64) == 0
