@@ -931,11 +931,14 @@ tri_kernel(const PrefillArgs p)
     __syncthreads();
 
     // ---- P fragments (natural order): wave w takes (rb, s) = pairs w, w+4.
+    // Rows 0-31 are zero in columns 32-63 (P is lower triangular): those two
+    // fragments are never read, so they are not written.
     {
         __bf16 *pf = p.ws_pf + ((size_t)hv * p.ns + slot) * (2 * kC * kC) + lane * 8;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int pr = wave + 4 * k, rb = pr >> 1, s = pr & 1;
+            if (rb < 2 && s == 1) continue;
             const float *src = sP + (16 * rb + col) * LC + 32 * s + 8 * kq;
             const f32x4 u = ld4(src), v = ld4(src + 4);
             const float vals[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
@@ -1302,7 +1305,8 @@ scan_kernel(const PrefillArgs p, int slices)
             const size_t off = (size_t)(CH) * (2 * kC * kC);                                   \
             _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                    \
                 const int f = (w * 2 + s) * 2;                                                 \
-                cP[s] = frag_at(pf + off + f * 512, pf + off + (f + 1) * 512);                 \
+                if (s == 0 || w >= 2) /* rows 0-31 of P are zero in columns 32-63 */           \
+                    cP[s] = frag_at(pf + off + f * 512, pf + off + (f + 1) * 512);             \
             }                                                                                  \
         }
         // Y = e^G (Q S) of chunk cc from the state buffer of its parity.
