@@ -412,11 +412,13 @@ qknorm_kernel(const PrefillArgs p)
     };
     RawT rawA[WIN][2], rawB[WIN][2];
     const bool second = (cfirst + 1) * kC < L;
+    // (the taps, which the first chunk's conv needs, go ahead of the second
+    // chunk's rows: loads complete in issue order)
     load_raw(cfirst, rawA);
-    if (second) load_raw(cfirst + 1, rawB);
     float w0[4][4], w1[4][4];
     load_taps4(p, ch, w0);
     load_taps4(p, ch + 4, w1);
+    if (second) load_raw(cfirst + 1, rawB);
     const float extra = isk ? 1.0f : rsqrtf((float)DK);
 
     auto process = [&](int c, const RawT (&raw)[WIN][2]) {
