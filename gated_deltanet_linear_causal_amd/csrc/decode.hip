@@ -301,6 +301,23 @@ decode_kernel(const DecodeArgs p)
     }
 }
 
+hipError_t device_cu_count(int *n)
+{
+    static int ncu[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (ncu[dev] == 0) {
+        int c = 0;
+        e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        ncu[dev] = c > 0 ? c : 1;
+    }
+    *n = ncu[dev];
+    return hipSuccess;
+}
+
 template <typename TIn, int DK, int DV, int NSLOT>
 static hipError_t launch_t(const DecodeArgs &a, int batch, hipStream_t s)
 {
@@ -308,20 +325,12 @@ static hipError_t launch_t(const DecodeArgs &a, int batch, hipStream_t s)
     const size_t shmem = sizeof(float) * (2 * DK + a.group * DV) +
                          sizeof(f32x4) * NSLOT * 8 * (DV / 4) * 2 + 4 * sizeof(float);
     // One workgroup per CU at most (each holds two state slabs in registers).
-    static int ncu[64] = {0};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    int ncu = 0;
+    const hipError_t e = device_cu_count(&ncu);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (ncu[dev] == 0) {
-        int n = 0;
-        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        ncu[dev] = n > 0 ? n : 1;
-    }
     DecodeArgs args = a;
     args.units = batch * a.h_k;
-    const int grid = args.units < ncu[dev] ? args.units : ncu[dev];
+    const int grid = args.units < ncu ? args.units : ncu;
     hipLaunchKernelGGL((decode_kernel<TIn, DK, DV, NSLOT>), dim3(grid), dim3(NT), shmem, s, args);
     return hipGetLastError();
 }

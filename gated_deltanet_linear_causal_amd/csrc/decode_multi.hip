@@ -412,16 +412,22 @@ static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int batch, hipStre
     return hipGetLastError();
 }
 
-// One value head at a time (NSLOT = 1) for every group size: at d_k = d_v =
-// 128 four such workgroups share a CU, so every (sequence, key head) of a
-// B=64 call is resident at once and one head's state stores overlap another
-// head's loads.  Two heads side by side (NSLOT = 2, 512 threads, two
-// resident generations of workgroups) measured slower at B=64: 63.2 against
-// 65.4 us per step with the state out of cache, 77 against 82 us with 8
-// tokens, and within 0.4 us with the state cached.
+// Two value heads side by side (NSLOT = 2, 512 threads at d_v = 128, two
+// workgroups per CU) while every (sequence, key head) still fits on the chip
+// at once; beyond that, one head at a time (NSLOT = 1, four workgroups per
+// CU), so that the grid stays resident in one generation and one head's
+// state stores overlap another head's loads.  At d_k = d_v = 128, H_k = 16:
+// B=16 13.9 against 17.2 us, B=32 24.7 against 28.0 us (side by side
+// better); B=64 with the state out of cache 62.1 against 65.4 us and with
+// 8 tokens 76 against 82 us (one at a time better).
 template <typename TIn, int DK, int DV>
 static hipError_t launch_multi_slots(const MultiArgs &a, bool ch, int batch, hipStream_t s)
 {
+    int ncu = 0;
+    const hipError_t e = device_cu_count(&ncu);
+    if (e != hipSuccess) return e;
+    if (a.group % 2 == 0 && (long long)batch * a.h_k <= 2LL * ncu)
+        return launch_multi_t<TIn, DK, DV, 2>(a, ch, batch, s);
     return launch_multi_t<TIn, DK, DV, 1>(a, ch, batch, s);
 }
 

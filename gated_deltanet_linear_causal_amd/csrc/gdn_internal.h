@@ -27,6 +27,9 @@ struct Params {
     const float *decay_coef; // replaces -exp(a_log) when not NULL (a_log is then NULL)
 };
 
+// Compute units of the current device (queried once per device and kept).
+hipError_t device_cu_count(int *n);
+
 hipError_t launch_conv_update(const Dims &d, const Params &p, int n_seq, int max_len,
                               const int32_t *cu_dev, const void *x, float *conv_state,
                               float *y, hipStream_t s);
