@@ -658,6 +658,10 @@ kda_intra_kernel(const PrefillArgs p)
     __syncthreads();
 
     // ---- 2. decayed Gram tiles
+    // (waves 0-5 also take the off-diagonal blocks, so they set the end of
+    // this phase: issue priority 3 for them took kda_intra 211 -> 205 us at
+    // T=4096)
+    if (wave < 6) __builtin_amdgcn_s_setprio(3);
     float *gram = p.ws_gram + ((size_t)hv * p.ns + slot) * (2 * kC * kC);
     {
         // blocks (I, J), I > J, on the matrix cores: wave w < 6 takes pair
@@ -737,6 +741,7 @@ kda_intra_kernel(const PrefillArgs p)
     }
 
     // ---- 3. decayed operand fragments and the chunk decay
+    __builtin_amdgcn_s_setprio(0);
     {
         const size_t fbase = ((size_t)hv * p.ns + slot) * (2 * kC * DK) + lane * 8;
         // (k^ (.) e^G)^T for W, and (k^ (.) e^{G_C - G})^T for the state
