@@ -15,6 +15,14 @@ run on, so the line reports prefill tokens/s (``value``) and the decode-step
 latency separately; a second decode measurement rotates four state sets so
 that the states do not stay in the 256 MB Infinity Cache.
 
+Beside the step, ``workloads`` reports the other workloads on their own:
+the tiny recurrent case (64 single-token steps, H=2, d=32, fp32: us/step),
+the packed varlen prefill (8 sequences of U{512..8192} tokens: tokens/s and
+its MFMA and HBM fractions) and the long-context hand-off (T=65536 prefill,
+then 256 decode steps at B=1: tokens/s and us/step).  ``cpu_baseline``
+times the oracle on the step's prefill and decode workloads, on one thread
+and on all host threads given to the run.
+
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this build is a
 one-GPU build (the sharding design is written up, not launched).
 """
@@ -76,12 +84,13 @@ def prefill_flops(d, T, C=64):
     return T * per_tok
 
 
-def prefill_bytes(d, T, n_seq=1):
+def prefill_bytes(d, T, n_seq=1, state_in=False):
     """Algorithmic HBM bytes of one prefill call: bf16 inputs and output,
-    final fp32 state and conv history written (zero initial state)."""
+    each sequence's final fp32 state and conv history written, and its
+    initial ones read when the call is given them."""
     io = T * ((d.conv_dim + d.value_dim + 2 * d.h_v) * 2 + d.value_dim * 2)
     states = n_seq * (d.h_v * d.d_k * d.d_v + (d.conv_k - 1) * d.conv_dim) * 4
-    return io + states
+    return io + states * (2 if state_in else 1)
 
 
 def sources_hash():
@@ -194,28 +203,64 @@ def load_traffic(kernel):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
-def cpu_baseline(case, threads, min_seconds=10.0, max_reps=100):
-    """The oracle, untuned, on the host cores: the full T=4096 prefill over
-    every head, repeated until at least min_seconds of wall time (a short
-    warm-up call loads the library first)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(pf_case, dc_case, threads, reps=3):
+    """The oracle, untuned, on the host cores, on the two workloads of the
+    step: the T=4096 prefill over every head, and the B=64 x 100 decode
+    steps (run as 64 sequences of 100 tokens: the oracle steps token by
+    token either way).  Each is timed on one thread (one run) and on
+    `threads` threads (median of `reps`), after an untimed warm-up call."""
+    import statistics
+
     import oracle
-    shape = oracle.Shape(case.dims.h_k, case.dims.h_v, case.dims.d_k, case.dims.d_v,
-                         case.dims.conv_k, case.dims.gate)
-    oracle.mixer(shape, [0, 1], case.params, case.qkv[:1], case.z[:1], case.a[:1],
-                 case.b[:1], case.S0, case.conv0, nthreads=threads)
-    reps = 0
-    t = time.perf_counter()
-    while True:
-        oracle.mixer(shape, case.cu_seqlens, case.params, case.qkv, case.z, case.a, case.b,
-                     case.S0, case.conv0, nthreads=threads)
-        reps += 1
-        dt = time.perf_counter() - t
-        if dt >= min_seconds or reps >= max_reps:
-            break
-    T = case.t_total
-    return {"value": reps * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} x the full prefill T={T} (all {case.dims.h_v} value heads), "
-                      f"float64 token-by-token C oracle on {threads} threads, {dt:.1f} s wall"}
+    shape = oracle.Shape(pf_case.dims.h_k, pf_case.dims.h_v, pf_case.dims.d_k, pf_case.dims.d_v,
+                         pf_case.dims.conv_k, pf_case.dims.gate)
+    B, steps = dc_case.dec["qkv"].shape[1], dc_case.dec["qkv"].shape[0]
+
+    def pack(x):
+        return x.transpose(0, 1).reshape(B * steps, -1)
+    dcu = [i * steps for i in range(B + 1)]
+    runs = {
+        "prefill": (lambda nt: oracle.mixer(shape, pf_case.cu_seqlens, pf_case.params, pf_case.qkv,
+                                            pf_case.z, pf_case.a, pf_case.b, pf_case.S0,
+                                            pf_case.conv0, nthreads=nt), pf_case.t_total),
+        "decode": (lambda nt: oracle.mixer(shape, dcu, dc_case.params, pack(dc_case.dec["qkv"]),
+                                           pack(dc_case.dec["z"]), pack(dc_case.dec["a"]),
+                                           pack(dc_case.dec["b"]), dc_case.S0, dc_case.conv0,
+                                           nthreads=nt), B * steps),
+    }
+    oracle.mixer(shape, [0, 1], pf_case.params, pf_case.qkv[:1], pf_case.z[:1], pf_case.a[:1],
+                 pf_case.b[:1], pf_case.S0, pf_case.conv0, nthreads=threads)
+    legs = {}
+    for name, (fn, tokens) in runs.items():
+        for nt, n in ((1, 1), (threads, reps)):
+            times = []
+            for _ in range(n):
+                t = time.perf_counter()
+                fn(nt)
+                times.append(time.perf_counter() - t)
+            dt = statistics.median(times)
+            legs[f"{name}_{nt}t"] = {"tokens_per_s": round(tokens / dt, 1), "seconds": round(dt, 3),
+                                     "threads": nt, "runs": n}
+    dec_all = legs[f"decode_{threads}t"]
+    return {"value": legs[f"prefill_{threads}t"]["tokens_per_s"], "unit": "tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"the full T={pf_case.t_total} prefill (all {pf_case.dims.h_v} value heads) "
+                      f"and the B={B} x {steps}-step decode, float64 token-by-token C oracle; "
+                      f"value = prefill on {threads} threads (median of {reps}); decode on "
+                      f"{threads} threads: {dec_all['tokens_per_s']} tokens/s = "
+                      f"{round(dec_all['seconds'] / steps * 1e6, 1)} us per B={B} step",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(), "legs": legs}
 
 
 def main():
@@ -227,6 +272,8 @@ def main():
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the multi-token decode legs (profiling runs: every "
                          "decode_multi_kernel launch is then a gdn_decode_step)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the tiny-recurrent, varlen and T=65536 hand-off legs")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -322,6 +369,80 @@ def main():
     torch.cuda.synchronize()
     dc_cold_ms = ev_c[0].elapsed_time(ev_c[1]) / cold_steps
     del S_rot, c_rot
+
+    def time_calls(fn, calls, warm=2):
+        for _ in range(warm):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(calls):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / calls
+
+    work = {}
+    if not args.no_workloads:
+        from gdn_inputs import long_handoff, tiny_recurrent, varlen_prefill
+        # Tiny recurrent workload: 1 sequence, 64 tokens one at a time
+        # through gdn_decode_step, H=2, d=32, fp32 (launch-latency bound).
+        tc = tiny_recurrent()
+        td = tc.dims
+        tcfg = gdn.Config(td.h_k, td.h_v, td.d_k, td.d_v, td.conv_k, torch.float32,
+                          torch.float32)
+        tp = {k: v.to(dev) for k, v in tc.params.items()}
+        tx = [tc.dec[k].to(dev).contiguous() for k in ("qkv", "z", "a", "b")]
+        tS, tC = tc.S0.to(dev), tc.conv0.to(dev)
+        tout = torch.empty((1, td.value_dim), dtype=torch.float32, device=dev)
+        nst = tx[0].shape[0]
+
+        def tiny_run():
+            for j in range(nst):
+                gdn.decode_step(tcfg, tp, tx[0][j], tx[1][j], tx[2][j], tx[3][j], tC, tS,
+                                out=tout, stream=stream)
+        work["tiny"] = (time_calls(tiny_run, 20) / nst, nst, td)
+
+        # Varlen packed prefill: 8 sequences of U{512..8192} tokens, random
+        # initial states and histories.
+        vc = varlen_prefill()
+        vx = [getattr(vc, k).to(bf).to(dev).contiguous() for k in ("qkv", "z", "a", "b")]
+        vseq = gdn.SeqLens(vc.cu_seqlens, dev)
+        vS0, vC0 = vc.S0.to(dev), vc.conv0.to(dev)
+        vS, vC = torch.empty_like(vS0), torch.empty_like(vC0)
+        vout = torch.empty((vc.t_total, d.value_dim), dtype=bf, device=dev)
+        vws = gdn.alloc_workspace(cfg, vc.n_seq, vc.t_total, dev)
+        vp = {k: v.to(dev) for k, v in vc.params.items()}
+        work["varlen"] = (time_calls(lambda: gdn.prefill_chunked(
+            cfg, vp, vseq, *vx, state_in=vS0, state_out=vS, conv_in=vC0, conv_out=vC, out=vout,
+            workspace=vws, stream=stream), 5), vc)
+        del vx, vws, vout
+
+        # Long-context hand-off: B=1 prefill of T=65536 (sigmoid gate), then
+        # 256 decode steps from the returned state and history.
+        lc = long_handoff()
+        ld = lc.dims
+        lcfg = gdn.Config(ld.h_k, ld.h_v, ld.d_k, ld.d_v, ld.conv_k, bf, bf, ld.gate)
+        lp = {k: v.to(dev) for k, v in lc.params.items()}
+        lx = [getattr(lc, k).to(bf).to(dev).contiguous() for k in ("qkv", "z", "a", "b")]
+        lseq = gdn.SeqLens(lc.cu_seqlens, dev)
+        lS = torch.empty((1, ld.h_v, ld.d_k, ld.d_v), dtype=torch.float32, device=dev)
+        lC = torch.empty((1, ld.conv_k - 1, ld.conv_dim), dtype=torch.float32, device=dev)
+        lout = torch.empty((lc.t_total, ld.value_dim), dtype=bf, device=dev)
+        lws = gdn.alloc_workspace(lcfg, 1, lc.t_total, dev)
+        lpf_ms = time_calls(lambda: gdn.prefill_chunked(lcfg, lp, lseq, *lx, state_out=lS,
+                                                        conv_out=lC, out=lout, workspace=lws,
+                                                        stream=stream), 3, warm=1)
+        del lx, lws, lout
+        ldx = [lc.dec[k].to(bf).to(dev).contiguous() for k in ("qkv", "z", "a", "b")]
+        ldo = torch.empty((1, ld.value_dim), dtype=bf, device=dev)
+        nld = ldx[0].shape[0]
+
+        def long_decode():
+            for j in range(nld):
+                gdn.decode_step(lcfg, lp, ldx[0][j], ldx[1][j], ldx[2][j], ldx[3][j], lC, lS,
+                                out=ldo, stream=stream)
+        work["long"] = (lpf_ms, time_calls(long_decode, 2, warm=1) / nld, nld, lc)
+        del ldx
 
     # Multi-token decode (speculative verification of t_new drafted tokens per
     # sequence, gdn_decode_multi), same batch, states updated in place.
@@ -502,6 +623,44 @@ def main():
             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
             "algorithmic_bytes_per_launch": mb, "duration_us": round(ms * 1e3, 2),
             "launches_timed": calls, "tokens_per_s": round(B * t_new / (ms * 1e-3), 1)}
+    workloads = {}
+    if "tiny" in work:
+        us, nst, td = work["tiny"]
+        tb = decode_bytes(td, 1)
+        workloads["tiny_recurrent"] = {
+            "config": "1 sequence, 64 tokens one at a time (gdn_decode_step), H_k=H_v=2, "
+                      "d_k=d_v=32, K=4, fp32 in/out",
+            "us_per_step": round(us * 1e3, 2), "steps_timed": 20 * nst,
+            "bound": "launch latency", "algorithmic_bytes_per_step": tb,
+            "hbm_frac": round(tb / (us * 1e-3) / 1e9 / PEAK_HBM_GBS, 6)}
+    if "varlen" in work:
+        ms, vc = work["varlen"]
+        vflops = prefill_flops(d, vc.t_total)
+        vbytes = prefill_bytes(d, vc.t_total, vc.n_seq, state_in=True)
+        lens = [vc.cu_seqlens[i + 1] - vc.cu_seqlens[i] for i in range(vc.n_seq)]
+        workloads["varlen_prefill"] = {
+            "config": f"{vc.n_seq} packed sequences, lengths {lens} ({vc.t_total} tokens), "
+                      "random initial states, bf16",
+            "tokens_per_s": round(vc.t_total / (ms * 1e-3), 1), "ms_per_call": round(ms, 4),
+            "calls_timed": 5, "algorithmic_flops_per_call": vflops,
+            "mfma_frac": round(vflops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_bytes_per_call": vbytes,
+            "hbm_frac": round(vbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if "long" in work:
+        pms, dms, nld, lc = work["long"]
+        lflops = prefill_flops(lc.dims, lc.t_total)
+        lbytes = prefill_bytes(lc.dims, lc.t_total)
+        db1 = decode_bytes(lc.dims, 1)
+        workloads["long_handoff"] = {
+            "config": f"B=1 prefill T={lc.t_total} (sigmoid gate), then {nld} decode steps "
+                      "from its state, B=1",
+            "prefill_tokens_per_s": round(lc.t_total / (pms * 1e-3), 1),
+            "prefill_ms": round(pms, 4), "prefill_calls_timed": 3,
+            "prefill_mfma_frac": round(lflops / (pms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "prefill_hbm_frac": round(lbytes / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "decode_us_per_step": round(dms * 1e3, 2), "decode_steps_timed": 2 * nld,
+            "decode_algorithmic_bytes_per_step": db1,
+            "decode_hbm_frac": round(db1 / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     # the kernel that takes most of a step's time
     dominant = roof_pf if pf_ms >= dc_ms * n_sets else roof_dec
 
@@ -512,7 +671,11 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "f32+bf16x3",
+        "dtype_note": "decode: fp32 vector FMA; prefill contractions: fp32 operands split into "
+                      "bf16 hi + lo parts, three MFMAs (hi.hi + hi.lo + lo.hi; lo.lo dropped), "
+                      "fp32 accumulation; conv, norms and gates fp32; activations bf16 in and out",
+        "data": "synthetic",
         "config": {"workload": "GDN mixer: prefill B=1 T=4096 + 100 consecutive decode "
                                "steps B=64; H_k=16 H_v=32 d_k=d_v=128 K=4 C=64; bf16 "
                                "activations/output, fp32 state", "global_batch": 64, "seq_len": T,
@@ -522,13 +685,19 @@ def main():
         "decode_cold_us_per_step": round(dc_cold_ms * 1e3, 2),
         "decode_tokens_per_s": round(B / (dc_ms * 1e-3), 1),
         "roofline": dominant,
+        "roofline_note": "roofline is the kernel that takes most of the step's time (the 100 "
+                         "decode steps); the prefill's own roofline is rooflines.prefill. The "
+                         "100 decode steps (28 GB of state traffic) evict the prefill's data "
+                         "from the 256 MB Infinity Cache between prefills, in place of an "
+                         "explicit flush",
+        "workloads": workloads,
         "rooflines": {"decode": roof_dec, "decode_cold": roof_dec_cold, "prefill": roof_pf,
                       **roof_multi},
         "note": "the pages quote no throughput for this path on any hardware",
     }
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
-        line["cpu_baseline"] = cpu_baseline(pf, threads)
+        line["cpu_baseline"] = cpu_baseline(pf, dc, threads)
     print(json.dumps(line), flush=True)
 
 

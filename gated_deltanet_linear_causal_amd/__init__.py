@@ -7,6 +7,7 @@ import of any entry point raises: there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -196,6 +197,16 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc_on(stream):
+    """Context in which the binding allocates its default outputs and
+    temporary workspaces: the stream the kernels are enqueued on.  The caching
+    allocator then ties each block to that stream, so a temporary dropped on
+    return is reused only by work ordered after the kernels that use it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
+
+
 def _raise_on(status: int):
     if status != 0:
         raise GdnError(status, load_library().gdn_last_error().decode())
@@ -218,17 +229,18 @@ def conv_update(cfg: Config, params: dict, seqlens: SeqLens, x, conv_state, y=No
     """silu(causal conv) of packed raw inputs; conv_state updated in place.
     Returns y [T, conv_dim] fp32."""
     lib = load_library()
-    T, N = seqlens.t_total, seqlens.n_seq
-    _check(x, "x", (T, cfg.conv_dim), cfg.act_dtype)
-    _check(conv_state, "conv_state", (N, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
-    if y is None:
-        y = torch.empty((T, cfg.conv_dim), dtype=torch.float32, device=x.device)
-    _check(y, "y", (T, cfg.conv_dim), torch.float32)
-    c, p = cfg.c_struct(), _params(cfg, params)
-    _raise_on(lib.gdn_conv_update(ctypes.byref(c), ctypes.byref(p), N, T,
-                                  ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev),
-                                  _ptr(x), _ptr(conv_state), _ptr(y), _stream(stream)))
-    return y
+    with _alloc_on(stream):
+        T, N = seqlens.t_total, seqlens.n_seq
+        _check(x, "x", (T, cfg.conv_dim), cfg.act_dtype)
+        _check(conv_state, "conv_state", (N, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
+        if y is None:
+            y = torch.empty((T, cfg.conv_dim), dtype=torch.float32, device=x.device)
+        _check(y, "y", (T, cfg.conv_dim), torch.float32)
+        c, p = cfg.c_struct(), _params(cfg, params)
+        _raise_on(lib.gdn_conv_update(ctypes.byref(c), ctypes.byref(p), N, T,
+                                      ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev),
+                                      _ptr(x), _ptr(conv_state), _ptr(y), _stream(stream)))
+        return y
 
 
 def decode_step(cfg: Config, params: dict, qkv, z, a, b, conv_state, state, out=None,
@@ -236,24 +248,25 @@ def decode_step(cfg: Config, params: dict, qkv, z, a, b, conv_state, state, out=
     """One token per sequence; conv_state and state are updated in place.
     Returns out [B, H_v*d_v] (cfg.out_dtype)."""
     lib = load_library()
-    B = qkv.shape[0]
-    _check(qkv, "qkv", (B, cfg.conv_dim), cfg.act_dtype)
-    _check(z, "z", (B, cfg.value_dim), cfg.act_dtype)
-    _check(a, "a", (B, cfg.h_v * cfg.gate_width), cfg.act_dtype)
-    _check(b, "b", (B, cfg.h_v), cfg.act_dtype)
-    _check(conv_state, "conv_state", (B, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
-    _check(state, "state", (B, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
-    if out is None:
-        out = torch.empty((B, cfg.value_dim), dtype=cfg.out_dtype, device=qkv.device)
-    _check(out, "out", (B, cfg.value_dim), cfg.out_dtype)
-    c, p = cfg.c_struct(), _params(cfg, params)
-    _raise_on(lib.gdn_decode_step(ctypes.byref(c), ctypes.byref(p), B, _ptr(qkv), _ptr(z),
-                                  _ptr(a), _ptr(b), _ptr(conv_state), _ptr(state), _ptr(out),
-                                  _stream(stream)))
-    return out
+    with _alloc_on(stream):
+        B = qkv.shape[0]
+        _check(qkv, "qkv", (B, cfg.conv_dim), cfg.act_dtype)
+        _check(z, "z", (B, cfg.value_dim), cfg.act_dtype)
+        _check(a, "a", (B, cfg.h_v * cfg.gate_width), cfg.act_dtype)
+        _check(b, "b", (B, cfg.h_v), cfg.act_dtype)
+        _check(conv_state, "conv_state", (B, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
+        _check(state, "state", (B, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
+        if out is None:
+            out = torch.empty((B, cfg.value_dim), dtype=cfg.out_dtype, device=qkv.device)
+        _check(out, "out", (B, cfg.value_dim), cfg.out_dtype)
+        c, p = cfg.c_struct(), _params(cfg, params)
+        _raise_on(lib.gdn_decode_step(ctypes.byref(c), ctypes.byref(p), B, _ptr(qkv), _ptr(z),
+                                      _ptr(a), _ptr(b), _ptr(conv_state), _ptr(state), _ptr(out),
+                                      _stream(stream)))
+        return out
 
 
-MAX_NEW_TOKENS = 8
+    MAX_NEW_TOKENS = 8
 
 
 def _check_counts(n, B, device):
@@ -277,35 +290,36 @@ def decode_multi(cfg: Config, params: dict, qkv, z, a, b, conv_state, state, out
     [B, t_new, H_v, d_k, d_v] fp32 per-token states.  Returns out
     [B, t_new, value_dim] (None when want_out is False)."""
     lib = load_library()
-    B, T = qkv.shape[0], qkv.shape[1]
-    dev = qkv.device
-    _check(qkv, "qkv", (B, T, cfg.conv_dim), cfg.act_dtype)
-    _check(a, "a", (B, T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
-    _check(b, "b", (B, T, cfg.h_v), cfg.act_dtype)
-    sshape = (B, cfg.h_v, cfg.d_k, cfg.d_v)
-    cshape = (B, cfg.conv_k - 1, cfg.conv_dim)
-    _check(conv_state, "conv_state", cshape, torch.float32)
-    _check(state, "state", sshape, torch.float32)
-    conv_out = conv_state if conv_out is None else conv_out
-    state_out = state if state_out is None else state_out
-    _check(conv_out, "conv_out", cshape, torch.float32)
-    _check(state_out, "state_out", sshape, torch.float32)
-    if ckpt is not None:
-        _check(ckpt, "ckpt", (B, T, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
-    if want_out:
-        _check(z, "z", (B, T, cfg.value_dim), cfg.act_dtype)
-        if out is None:
-            out = torch.empty((B, T, cfg.value_dim), dtype=cfg.out_dtype, device=dev)
-        _check(out, "out", (B, T, cfg.value_dim), cfg.out_dtype)
-    else:
-        out = None
-    n = _check_counts(n_tok, B, dev)
-    c, p = cfg.c_struct(), _params(cfg, params)
-    _raise_on(lib.gdn_decode_multi(ctypes.byref(c), ctypes.byref(p), B, T, _ptr(n), _ptr(qkv),
-                                   _ptr(z) if want_out else None, _ptr(a), _ptr(b),
-                                   _ptr(conv_state), _ptr(conv_out), _ptr(state),
-                                   _ptr(state_out), _ptr(ckpt), _ptr(out), _stream(stream)))
-    return out
+    with _alloc_on(stream):
+        B, T = qkv.shape[0], qkv.shape[1]
+        dev = qkv.device
+        _check(qkv, "qkv", (B, T, cfg.conv_dim), cfg.act_dtype)
+        _check(a, "a", (B, T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
+        _check(b, "b", (B, T, cfg.h_v), cfg.act_dtype)
+        sshape = (B, cfg.h_v, cfg.d_k, cfg.d_v)
+        cshape = (B, cfg.conv_k - 1, cfg.conv_dim)
+        _check(conv_state, "conv_state", cshape, torch.float32)
+        _check(state, "state", sshape, torch.float32)
+        conv_out = conv_state if conv_out is None else conv_out
+        state_out = state if state_out is None else state_out
+        _check(conv_out, "conv_out", cshape, torch.float32)
+        _check(state_out, "state_out", sshape, torch.float32)
+        if ckpt is not None:
+            _check(ckpt, "ckpt", (B, T, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
+        if want_out:
+            _check(z, "z", (B, T, cfg.value_dim), cfg.act_dtype)
+            if out is None:
+                out = torch.empty((B, T, cfg.value_dim), dtype=cfg.out_dtype, device=dev)
+            _check(out, "out", (B, T, cfg.value_dim), cfg.out_dtype)
+        else:
+            out = None
+        n = _check_counts(n_tok, B, dev)
+        c, p = cfg.c_struct(), _params(cfg, params)
+        _raise_on(lib.gdn_decode_multi(ctypes.byref(c), ctypes.byref(p), B, T, _ptr(n), _ptr(qkv),
+                                       _ptr(z) if want_out else None, _ptr(a), _ptr(b),
+                                       _ptr(conv_state), _ptr(conv_out), _ptr(state),
+                                       _ptr(state_out), _ptr(ckpt), _ptr(out), _stream(stream)))
+        return out
 
 
 def rewind(cfg: Config, params: dict, qkv_rec, a_rec, b_rec, state0, conv0, keep=None,
@@ -314,27 +328,28 @@ def rewind(cfg: Config, params: dict, qkv_rec, a_rec, b_rec, state0, conv0, keep
     replaying its first keep[i] recorded tokens (all when keep is None).
     Returns (state, conv_state)."""
     lib = load_library()
-    B, T = qkv_rec.shape[0], qkv_rec.shape[1]
-    dev = qkv_rec.device
-    _check(qkv_rec, "qkv_rec", (B, T, cfg.conv_dim), cfg.act_dtype)
-    _check(a_rec, "a_rec", (B, T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
-    _check(b_rec, "b_rec", (B, T, cfg.h_v), cfg.act_dtype)
-    sshape = (B, cfg.h_v, cfg.d_k, cfg.d_v)
-    cshape = (B, cfg.conv_k - 1, cfg.conv_dim)
-    _check(state0, "state0", sshape, torch.float32)
-    _check(conv0, "conv0", cshape, torch.float32)
-    if state is None:
-        state = torch.empty(sshape, dtype=torch.float32, device=dev)
-    if conv_state is None:
-        conv_state = torch.empty(cshape, dtype=torch.float32, device=dev)
-    _check(state, "state", sshape, torch.float32)
-    _check(conv_state, "conv_state", cshape, torch.float32)
-    n = _check_counts(keep, B, dev)
-    c, p = cfg.c_struct(), _params(cfg, params)
-    _raise_on(lib.gdn_rewind(ctypes.byref(c), ctypes.byref(p), B, T, _ptr(n), _ptr(qkv_rec),
-                             _ptr(a_rec), _ptr(b_rec), _ptr(state0), _ptr(conv0), _ptr(state),
-                             _ptr(conv_state), _stream(stream)))
-    return state, conv_state
+    with _alloc_on(stream):
+        B, T = qkv_rec.shape[0], qkv_rec.shape[1]
+        dev = qkv_rec.device
+        _check(qkv_rec, "qkv_rec", (B, T, cfg.conv_dim), cfg.act_dtype)
+        _check(a_rec, "a_rec", (B, T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
+        _check(b_rec, "b_rec", (B, T, cfg.h_v), cfg.act_dtype)
+        sshape = (B, cfg.h_v, cfg.d_k, cfg.d_v)
+        cshape = (B, cfg.conv_k - 1, cfg.conv_dim)
+        _check(state0, "state0", sshape, torch.float32)
+        _check(conv0, "conv0", cshape, torch.float32)
+        if state is None:
+            state = torch.empty(sshape, dtype=torch.float32, device=dev)
+        if conv_state is None:
+            conv_state = torch.empty(cshape, dtype=torch.float32, device=dev)
+        _check(state, "state", sshape, torch.float32)
+        _check(conv_state, "conv_state", cshape, torch.float32)
+        n = _check_counts(keep, B, dev)
+        c, p = cfg.c_struct(), _params(cfg, params)
+        _raise_on(lib.gdn_rewind(ctypes.byref(c), ctypes.byref(p), B, T, _ptr(n), _ptr(qkv_rec),
+                                 _ptr(a_rec), _ptr(b_rec), _ptr(state0), _ptr(conv0), _ptr(state),
+                                 _ptr(conv_state), _stream(stream)))
+        return state, conv_state
 
 
 def prefill_workspace_bytes(cfg: Config, n_seq: int, t_total: int, chunk: int = CHUNK) -> int:
@@ -353,37 +368,38 @@ def prefill_chunked(cfg: Config, params: dict, seqlens: SeqLens, qkv, z, a, b,
                     workspace=None, chunk: int = CHUNK, stream=None):
     """Chunked prefill over packed sequences.  Returns (out, state_out, conv_out)."""
     lib = load_library()
-    T, N = seqlens.t_total, seqlens.n_seq
-    dev = qkv.device
-    _check(qkv, "qkv", (T, cfg.conv_dim), cfg.act_dtype)
-    _check(z, "z", (T, cfg.value_dim), cfg.act_dtype)
-    _check(a, "a", (T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
-    _check(b, "b", (T, cfg.h_v), cfg.act_dtype)
-    sshape = (N, cfg.h_v, cfg.d_k, cfg.d_v)
-    cshape = (N, cfg.conv_k - 1, cfg.conv_dim)
-    if state_in is not None:
-        _check(state_in, "state_in", sshape, torch.float32)
-    if conv_in is not None:
-        _check(conv_in, "conv_in", cshape, torch.float32)
-    if state_out is None:
-        state_out = torch.empty(sshape, dtype=torch.float32, device=dev)
-    if conv_out is None:
-        conv_out = torch.empty(cshape, dtype=torch.float32, device=dev)
-    if out is None:
-        out = torch.empty((T, cfg.value_dim), dtype=cfg.out_dtype, device=dev)
-    _check(state_out, "state_out", sshape, torch.float32)
-    _check(conv_out, "conv_out", cshape, torch.float32)
-    _check(out, "out", (T, cfg.value_dim), cfg.out_dtype)
-    if workspace is None:
-        workspace = alloc_workspace(cfg, N, T, dev, chunk)
-    c, p = cfg.c_struct(), _params(cfg, params)
-    _raise_on(lib.gdn_prefill_chunked(
-        ctypes.byref(c), ctypes.byref(p), chunk, N, T,
-        ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev),
-        _ptr(qkv), _ptr(z), _ptr(a), _ptr(b), _ptr(state_in), _ptr(state_out),
-        _ptr(conv_in), _ptr(conv_out), _ptr(out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
-    return out, state_out, conv_out
+    with _alloc_on(stream):
+        T, N = seqlens.t_total, seqlens.n_seq
+        dev = qkv.device
+        _check(qkv, "qkv", (T, cfg.conv_dim), cfg.act_dtype)
+        _check(z, "z", (T, cfg.value_dim), cfg.act_dtype)
+        _check(a, "a", (T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
+        _check(b, "b", (T, cfg.h_v), cfg.act_dtype)
+        sshape = (N, cfg.h_v, cfg.d_k, cfg.d_v)
+        cshape = (N, cfg.conv_k - 1, cfg.conv_dim)
+        if state_in is not None:
+            _check(state_in, "state_in", sshape, torch.float32)
+        if conv_in is not None:
+            _check(conv_in, "conv_in", cshape, torch.float32)
+        if state_out is None:
+            state_out = torch.empty(sshape, dtype=torch.float32, device=dev)
+        if conv_out is None:
+            conv_out = torch.empty(cshape, dtype=torch.float32, device=dev)
+        if out is None:
+            out = torch.empty((T, cfg.value_dim), dtype=cfg.out_dtype, device=dev)
+        _check(state_out, "state_out", sshape, torch.float32)
+        _check(conv_out, "conv_out", cshape, torch.float32)
+        _check(out, "out", (T, cfg.value_dim), cfg.out_dtype)
+        if workspace is None:
+            workspace = alloc_workspace(cfg, N, T, dev, chunk)
+        c, p = cfg.c_struct(), _params(cfg, params)
+        _raise_on(lib.gdn_prefill_chunked(
+            ctypes.byref(c), ctypes.byref(p), chunk, N, T,
+            ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev),
+            _ptr(qkv), _ptr(z), _ptr(a), _ptr(b), _ptr(state_in), _ptr(state_out),
+            _ptr(conv_in), _ptr(conv_out), _ptr(out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)))
+        return out, state_out, conv_out
 
 
 def _proj(cfg: Config, proj: dict) -> _Proj:
@@ -410,32 +426,33 @@ def mixer_prefill(cfg: Config, params: dict, proj: dict, seqlens: SeqLens, x, st
     """The mixer with its projections over packed sequences: x [T, H] bf16 ->
     y [T, H] (cfg.out_dtype).  Returns (y, state_out, conv_out)."""
     lib = load_library()
-    T, N, H = seqlens.t_total, seqlens.n_seq, int(proj["hidden"])
-    dev = x.device
-    _check(x, "x", (T, H), torch.bfloat16)
-    sshape = (N, cfg.h_v, cfg.d_k, cfg.d_v)
-    cshape = (N, cfg.conv_k - 1, cfg.conv_dim)
-    if state_in is not None:
-        _check(state_in, "state_in", sshape, torch.float32)
-    if conv_in is not None:
-        _check(conv_in, "conv_in", cshape, torch.float32)
-    if state_out is None:
-        state_out = torch.empty(sshape, dtype=torch.float32, device=dev)
-    if conv_out is None:
-        conv_out = torch.empty(cshape, dtype=torch.float32, device=dev)
-    if y is None:
-        y = torch.empty((T, H), dtype=cfg.out_dtype, device=dev)
-    _check(y, "y", (T, H), cfg.out_dtype)
-    if workspace is None:
-        workspace = torch.empty(max(mixer_workspace_bytes(cfg, H, N, T), 256), dtype=torch.uint8,
-                                device=dev)
-    c, p, pj = cfg.c_struct(), _params(cfg, params), _proj(cfg, proj)
-    _raise_on(lib.gdn_mixer_prefill(
-        ctypes.byref(c), ctypes.byref(p), ctypes.byref(pj), N, T,
-        ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev), _ptr(x), _ptr(state_in),
-        _ptr(state_out), _ptr(conv_in), _ptr(conv_out), _ptr(y), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
-    return y, state_out, conv_out
+    with _alloc_on(stream):
+        T, N, H = seqlens.t_total, seqlens.n_seq, int(proj["hidden"])
+        dev = x.device
+        _check(x, "x", (T, H), torch.bfloat16)
+        sshape = (N, cfg.h_v, cfg.d_k, cfg.d_v)
+        cshape = (N, cfg.conv_k - 1, cfg.conv_dim)
+        if state_in is not None:
+            _check(state_in, "state_in", sshape, torch.float32)
+        if conv_in is not None:
+            _check(conv_in, "conv_in", cshape, torch.float32)
+        if state_out is None:
+            state_out = torch.empty(sshape, dtype=torch.float32, device=dev)
+        if conv_out is None:
+            conv_out = torch.empty(cshape, dtype=torch.float32, device=dev)
+        if y is None:
+            y = torch.empty((T, H), dtype=cfg.out_dtype, device=dev)
+        _check(y, "y", (T, H), cfg.out_dtype)
+        if workspace is None:
+            workspace = torch.empty(max(mixer_workspace_bytes(cfg, H, N, T), 256), dtype=torch.uint8,
+                                    device=dev)
+        c, p, pj = cfg.c_struct(), _params(cfg, params), _proj(cfg, proj)
+        _raise_on(lib.gdn_mixer_prefill(
+            ctypes.byref(c), ctypes.byref(p), ctypes.byref(pj), N, T,
+            ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev), _ptr(x), _ptr(state_in),
+            _ptr(state_out), _ptr(conv_in), _ptr(conv_out), _ptr(y), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)))
+        return y, state_out, conv_out
 
 
 def mixer_decode(cfg: Config, params: dict, proj: dict, x, conv_state, state, y=None,
@@ -443,24 +460,25 @@ def mixer_decode(cfg: Config, params: dict, proj: dict, x, conv_state, state, y=
     """One mixer decode step with projections: x [B, H] bf16 -> y [B, H];
     conv_state and state are updated in place."""
     lib = load_library()
-    B, H = x.shape[0], int(proj["hidden"])
-    _check(x, "x", (B, H), torch.bfloat16)
-    _check(conv_state, "conv_state", (B, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
-    _check(state, "state", (B, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
-    if y is None:
-        y = torch.empty((B, H), dtype=cfg.out_dtype, device=x.device)
-    _check(y, "y", (B, H), cfg.out_dtype)
-    if workspace is None:
-        workspace = torch.empty(max(mixer_workspace_bytes(cfg, H, B, B), 256), dtype=torch.uint8,
-                                device=x.device)
-    c, p, pj = cfg.c_struct(), _params(cfg, params), _proj(cfg, proj)
-    _raise_on(lib.gdn_mixer_decode(ctypes.byref(c), ctypes.byref(p), ctypes.byref(pj), B, _ptr(x),
-                                   _ptr(conv_state), _ptr(state), _ptr(y), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(stream)))
-    return y
+    with _alloc_on(stream):
+        B, H = x.shape[0], int(proj["hidden"])
+        _check(x, "x", (B, H), torch.bfloat16)
+        _check(conv_state, "conv_state", (B, cfg.conv_k - 1, cfg.conv_dim), torch.float32)
+        _check(state, "state", (B, cfg.h_v, cfg.d_k, cfg.d_v), torch.float32)
+        if y is None:
+            y = torch.empty((B, H), dtype=cfg.out_dtype, device=x.device)
+        _check(y, "y", (B, H), cfg.out_dtype)
+        if workspace is None:
+            workspace = torch.empty(max(mixer_workspace_bytes(cfg, H, B, B), 256), dtype=torch.uint8,
+                                    device=x.device)
+        c, p, pj = cfg.c_struct(), _params(cfg, params), _proj(cfg, proj)
+        _raise_on(lib.gdn_mixer_decode(ctypes.byref(c), ctypes.byref(p), ctypes.byref(pj), B, _ptr(x),
+                                       _ptr(conv_state), _ptr(state), _ptr(y), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+        return y
 
 
-__all__ = ["Config", "SeqLens", "GdnError", "load_library", "header_functions",
-           "conv_update", "decode_step", "decode_multi", "rewind", "prefill_workspace_bytes",
-           "alloc_workspace", "prefill_chunked", "mixer_workspace_bytes", "mixer_prefill",
-           "mixer_decode", "LIB_PATH", "CHUNK", "MAX_NEW_TOKENS"]
+    __all__ = ["Config", "SeqLens", "GdnError", "load_library", "header_functions",
+               "conv_update", "decode_step", "decode_multi", "rewind", "prefill_workspace_bytes",
+               "alloc_workspace", "prefill_chunked", "mixer_workspace_bytes", "mixer_prefill",
+               "mixer_decode", "LIB_PATH", "CHUNK", "MAX_NEW_TOKENS"]

@@ -27,6 +27,8 @@
 // 4*c4 .. 4*c4+3.  A wavefront load instruction therefore reads two adjacent
 // 512-byte state rows (d_v = 128).
 
+#include <atomic>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -301,20 +303,24 @@ decode_kernel(const DecodeArgs p)
     }
 }
 
+// Compute units per device, queried on first use.  Concurrent first calls
+// may both query; they store the same value, and the atomics make the
+// cache safe to read from any thread.
 hipError_t device_cu_count(int *n)
 {
-    static int ncu[64] = {0};
+    static std::atomic<int> ncu[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (ncu[dev] == 0) {
-        int c = 0;
+    int c = ncu[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        ncu[dev] = c > 0 ? c : 1;
+        c = c > 0 ? c : 1;
+        ncu[dev].store(c, std::memory_order_relaxed);
     }
-    *n = ncu[dev];
+    *n = c;
     return hipSuccess;
 }
 

@@ -161,12 +161,13 @@ hipblasStatus_t make_plan(hipblasLtHandle_t h, int64_t m, int64_t n, int64_t k, 
     return st;
 }
 
-// D[m][n] (fp32, row-major) = beta * D + X[m][k] . W[n][k]^T, X and W bf16
-// row-major.
-hipError_t gemm_bf16_nt(int64_t m, int64_t n, int64_t k, const void *X, const void *W, float beta,
-                        float *D, void *ws, size_t ws_bytes, hipStream_t s)
+// The plan of D[m][n] = X[m][k] . W[n][k]^T on the current device: the
+// device's handle and the shape's plan are made on first use (under the
+// lock) and kept for the process; the returned plan is never modified or
+// freed afterwards, so it is used without the lock.
+hipError_t get_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes, hipblasLtHandle_t &handle,
+                    const GemmPlan *&plan)
 {
-    if (m == 0 || n == 0) return hipSuccess;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -189,13 +190,35 @@ hipError_t gemm_bf16_nt(int64_t m, int64_t n, int64_t k, const void *X, const vo
             if (g.desc) hipblasLtMatmulDescDestroy(g.desc);
             return blas_error(st);
         }
-        it = b.plans.emplace(key, g).first;
+        it = b.plans.emplace(key, g).first; // std::map nodes never move
     }
-    const GemmPlan &g = it->second;
-    const float alpha = 1.0f;
-    return blas_error(hipblasLtMatmul(b.handle, g.desc, &alpha, W, g.la, X, g.lb, &beta, D, g.lc, D,
-                                      g.lc, &g.algo, ws, ws_bytes, s));
+    handle = b.handle;
+    plan = &it->second;
+    return hipSuccess;
 }
+
+// One GEMM of a call, with its plan resolved before the call's first launch.
+struct Gemm {
+    int64_t m = 0, n = 0, k = 0;
+    hipblasLtHandle_t handle = nullptr;
+    const GemmPlan *plan = nullptr;
+    hipError_t prepare(int64_t m_, int64_t n_, int64_t k_, size_t ws_bytes)
+    {
+        m = m_, n = n_, k = k_;
+        if (m == 0 || n == 0) return hipSuccess;
+        return get_plan(m, n, k, ws_bytes, handle, plan);
+    }
+    // D[m][n] (fp32, row-major) = X[m][k] . W[n][k]^T, X and W bf16 row-major.
+    hipError_t run(const void *X, const void *W, float *D, void *ws, size_t ws_bytes,
+                   hipStream_t s) const
+    {
+        if (m == 0 || n == 0) return hipSuccess;
+        const float alpha = 1.0f, beta = 0.0f;
+        return blas_error(hipblasLtMatmul(handle, plan->desc, &alpha, W, plan->la, X, plan->lb,
+                                          &beta, D, plan->lc, D, plan->lc, &plan->algo, ws,
+                                          ws_bytes, s));
+    }
+};
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -243,41 +266,62 @@ MixerWs mixer_ws(const Dims &d, int hidden, int n_seq, int t_total, bool prefill
     return w;
 }
 
-// in_proj: the four projections of x [T][H] into fp32 qkv, z, b, a.
-hipError_t in_proj(const Dims &d, const Proj &pj, int T, const void *x, char *base,
-                   const MixerWs &w, hipStream_t s)
+// The GEMMs of one mixer call: in_proj (qkv, z and, unless the small gate
+// kernel takes them, b and a) and the stacked out_proj.
+struct MixerGemms {
+    Gemm qkv, z, b, a, out;
+    bool gate_kernel = false;
+};
+
+// Resolves every GEMM plan the call needs, so that a failure is reported
+// before anything is enqueued (the call then has written nothing).
+hipError_t prepare_gemms(const Dims &d, const Proj &pj, int T, const void *x, MixerGemms &g)
 {
     const int64_t H = pj.hidden, gw = d.chan_decay ? d.d_k : 1;
-    void *bw = base + w.blas;
-    hipError_t e;
-    if ((e = gemm_bf16_nt(T, d.conv_dim, H, x, pj.w_qkv, 0.0f,
-                          reinterpret_cast<float *>(base + w.qkv), bw, kBlasWorkspace, s)) != hipSuccess)
-        return e;
-    if ((e = gemm_bf16_nt(T, d.value_dim, H, x, pj.w_z, 0.0f,
-                          reinterpret_cast<float *>(base + w.z), bw, kBlasWorkspace, s)) != hipSuccess)
-        return e;
     const bool aligned = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(pj.w_b) |
                            reinterpret_cast<uintptr_t>(pj.w_a)) & 15) == 0;
-    if (gw == 1 && T > 0 && T <= 256 && aligned) {
+    g.gate_kernel = gw == 1 && T > 0 && T <= 256 && aligned;
+    hipError_t e;
+    if ((e = g.qkv.prepare(T, d.conv_dim, H, kBlasWorkspace)) != hipSuccess) return e;
+    if ((e = g.z.prepare(T, d.value_dim, H, kBlasWorkspace)) != hipSuccess) return e;
+    if (!g.gate_kernel) {
+        if ((e = g.b.prepare(T, d.h_v, H, kBlasWorkspace)) != hipSuccess) return e;
+        if ((e = g.a.prepare(T, d.h_v * gw, H, kBlasWorkspace)) != hipSuccess) return e;
+    }
+    return g.out.prepare(2 * (int64_t)T, pj.hidden, d.value_dim, kBlasWorkspace);
+}
+
+// in_proj: the four projections of x [T][H] into fp32 qkv, z, b, a.
+hipError_t in_proj(const Dims &d, const Proj &pj, const MixerGemms &g, int T, const void *x,
+                   char *base, const MixerWs &w, hipStream_t s)
+{
+    void *bw = base + w.blas;
+    hipError_t e;
+    if ((e = g.qkv.run(x, pj.w_qkv, reinterpret_cast<float *>(base + w.qkv), bw, kBlasWorkspace,
+                       s)) != hipSuccess)
+        return e;
+    if ((e = g.z.run(x, pj.w_z, reinterpret_cast<float *>(base + w.z), bw, kBlasWorkspace, s)) !=
+        hipSuccess)
+        return e;
+    if (g.gate_kernel) {
         const dim3 grid((2 * d.h_v + 3) / 4, (T + kGateRows - 1) / kGateRows);
         hipLaunchKernelGGL(gates_proj_kernel, grid, dim3(256), 0, s,
                            static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(pj.w_b),
                            static_cast<const bf16_t *>(pj.w_a), reinterpret_cast<float *>(base + w.b),
-                           reinterpret_cast<float *>(base + w.a), T, (int)H, d.h_v);
+                           reinterpret_cast<float *>(base + w.a), T, pj.hidden, d.h_v);
         return hipGetLastError();
     }
-    if ((e = gemm_bf16_nt(T, d.h_v, H, x, pj.w_b, 0.0f, reinterpret_cast<float *>(base + w.b), bw,
-                          kBlasWorkspace, s)) != hipSuccess)
+    if ((e = g.b.run(x, pj.w_b, reinterpret_cast<float *>(base + w.b), bw, kBlasWorkspace, s)) !=
+        hipSuccess)
         return e;
-    return gemm_bf16_nt(T, d.h_v * gw, H, x, pj.w_a, 0.0f, reinterpret_cast<float *>(base + w.a),
-                        bw, kBlasWorkspace, s);
+    return g.a.run(x, pj.w_a, reinterpret_cast<float *>(base + w.a), bw, kBlasWorkspace, s);
 }
 
 // out_proj of the core output split into bf16 parts: y = hi . W_out^T +
 // lo . W_out^T, one GEMM over the stacked [hi; lo] rows and a pass that adds
 // the halves (split here from the fp32 core output when `split_here`).
-hipError_t out_proj(const Dims &d, const Proj &pj, int T, char *base, const MixerWs &w, void *y,
-                    bool split_here, hipStream_t s)
+hipError_t out_proj(const Dims &d, const Proj &pj, const MixerGemms &g, int T, char *base,
+                    const MixerWs &w, void *y, bool split_here, hipStream_t s)
 {
     if (T == 0) return hipSuccess;
     const size_t n4 = (size_t)T * d.value_dim / 4;
@@ -289,8 +333,7 @@ hipError_t out_proj(const Dims &d, const Proj &pj, int T, char *base, const Mixe
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     float *acc = reinterpret_cast<float *>(base + w.acc);
-    if ((e = gemm_bf16_nt(2 * (int64_t)T, pj.hidden, d.value_dim, hi, pj.w_out, 0.0f, acc,
-                          base + w.blas, kBlasWorkspace, s)) != hipSuccess)
+    if ((e = g.out.run(hi, pj.w_out, acc, base + w.blas, kBlasWorkspace, s)) != hipSuccess)
         return e;
     const size_t m4 = (size_t)T * pj.hidden / 4;
     hipLaunchKernelGGL(add_halves_kernel, dim3((unsigned)((m4 + 255) / 256)), dim3(256), 0, s, acc, y,
@@ -312,13 +355,15 @@ hipError_t launch_mixer_prefill(const Dims &d, const Params &p, const Proj &pj, 
 {
     const MixerWs w = mixer_ws(d, pj.hidden, n_seq, t_total, true);
     char *base = static_cast<char *>(ws);
+    MixerGemms g;
     hipError_t e;
-    if ((e = in_proj(d, pj, t_total, x, base, w, s)) != hipSuccess) return e;
+    if ((e = prepare_gemms(d, pj, t_total, x, g)) != hipSuccess) return e;
+    if ((e = in_proj(d, pj, g, t_total, x, base, w, s)) != hipSuccess) return e;
     if ((e = launch_prefill(core_dims(d, true), p, n_seq, t_total, max_len, cu_dev, base + w.qkv,
                             base + w.z, base + w.a, base + w.b, state_in, state_out, conv_in,
                             conv_out, base + w.hl, base + w.prefill, s)) != hipSuccess)
         return e;
-    return out_proj(d, pj, t_total, base, w, y, false, s);
+    return out_proj(d, pj, g, t_total, base, w, y, false, s);
 }
 
 hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, int batch,
@@ -327,8 +372,10 @@ hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, i
 {
     const MixerWs w = mixer_ws(d, pj.hidden, batch, batch, false);
     char *base = static_cast<char *>(ws);
+    MixerGemms g;
     hipError_t e;
-    if ((e = in_proj(d, pj, batch, x, base, w, s)) != hipSuccess) return e;
+    if ((e = prepare_gemms(d, pj, batch, x, g)) != hipSuccess) return e;
+    if ((e = in_proj(d, pj, g, batch, x, base, w, s)) != hipSuccess) return e;
     const Dims c = core_dims(d, true);
     const bool multi = decode_multi_lds_bytes(c, 1) <= kDecodeMultiMaxLds;
     if (multi)
@@ -339,7 +386,7 @@ hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, i
         e = launch_decode(core_dims(d, false), p, batch, base + w.qkv, base + w.z, base + w.a,
                           base + w.b, conv_state, state, base + w.core, s);
     if (e != hipSuccess) return e;
-    return out_proj(d, pj, batch, base, w, y, !multi, s);
+    return out_proj(d, pj, g, batch, base, w, y, !multi, s);
 }
 
 } // namespace gdn

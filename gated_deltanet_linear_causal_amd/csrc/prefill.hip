@@ -638,10 +638,11 @@ kda_intra_kernel(const PrefillArgs p)
         for (int tt = 0; tt < TPP; ++tt) {
             const int t = gpart * TPP + tt;
             if (t < Lc) { // g = 0 past the end
-                // softplus(x) = max(x, 0) + log(1 + e^{-|x|}): the hardware
-                // exp/log, absolute error ~1e-7 (8192 of them per workgroup)
+                // softplus as everywhere else: x above 20, below it
+                // max(x, 0) + log(1 + e^{-|x|}) with the hardware exp/log
+                // (absolute error ~1e-7; 8192 of them per workgroup)
                 const float x = araw[tt] + dtb;
-                G += coef * (fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))));
+                G += coef * (x > 20.0f ? x : fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))));
             }
             sG[t * RQ + gd] = G;
         }
@@ -1468,12 +1469,35 @@ static hipError_t launch_norm(const PrefillArgs &a, int rows, int n_seq, hipStre
     return hipGetLastError();
 }
 
+// Every sequence of the call is empty: each final state is its initial
+// state (zeros when none is given).  One thread per float (the state
+// pointers carry no alignment promise beyond 4 bytes); nothing to do when the
+// update is in place.
+__global__ void __launch_bounds__(256) state_pass_kernel(const float *__restrict__ sin,
+                                                         float *__restrict__ sout, size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    sout[i] = sin ? sin[i] : 0.0f;
+}
+
 template <typename TIn, int DK, int DV, bool KDA>
 static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total, int max_len,
                                    hipStream_t s)
 {
     hipError_t e;
-    if (max_len > 0) {
+    if (max_len == 0) {
+        // No chunk exists, so there is no workspace to read: the scan (whose
+        // prologue loads chunk 0's operands) must not run.
+        const size_t n = (size_t)n_seq * a.h_v * DK * DV;
+        if (n > 0 && a.state_in != a.state_out) {
+            hipLaunchKernelGGL(state_pass_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                               s, a.state_in, a.state_out, n);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        return launch_norm<TIn, DV>(a, 0, n_seq, s);
+    }
+    {
         const int nch_max = (max_len + kC - 1) / kC;
         const dim3 grid_v((max_len + kC - 1) / kC, a.h_v, n_seq);
         if (KDA) {

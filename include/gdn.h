@@ -18,8 +18,18 @@
  * gate = SiLU or sigmoid.
  *
  * Conventions shared by every entry point
- *   - Every tensor pointer is device memory owned by the caller; the library
- *     never allocates or frees memory and keeps no mutable global state.
+ *   - Every tensor pointer is device memory owned by the caller.  The core
+ *     entry points (all but gdn_mixer_*) allocate and free nothing; their
+ *     only process-wide state is set once and never changes afterwards: a
+ *     per-device cache of the compute-unit count (atomic) and the kernels'
+ *     LDS-size attributes (set on a kernel's first use, in a thread-safe
+ *     static initialiser).
+ *   - The mixer entry points (gdn_mixer_prefill, gdn_mixer_decode) also keep,
+ *     per device, one hipBLASLt handle and one GEMM plan per problem shape.
+ *     Both are made on first use, under a lock, and kept until the process
+ *     ends; making them allocates host memory and, inside hipBLASLt, device
+ *     memory.  Every plan a call needs is resolved before its first launch,
+ *     so a failure there still leaves the caller's buffers untouched.
  *   - Layouts are dense row-major with the innermost index last:
  *       qkv   [T][conv_dim], conv_dim = 2*H_k*d_k + H_v*d_v, channels
  *             ordered q (H_k heads) | k (H_k heads) | v (H_v heads), each

@@ -68,6 +68,44 @@ def test_decode_batch_64x100_steps(gdn):
     np.testing.assert_array_equal(conv.numpy(), conv_ref)
 
 
+def test_decode_batch_64x100_steps_weak_decay(gdn):
+    """The B=64 decode batch with a weak decay (A_log = log U[0.001, 0.01]),
+    so the prefilled states and every step's writes carry through all 100
+    steps; every output and the final states are compared."""
+    base = decode_batch(steps=100)
+    case = make_case(base.dims, [0] * 64, act_dtype="bf16", seed=11, decay="weak",
+                     s0_std=0.02, conv0_std=1.0, decode_steps=100)
+    y, S, conv = run_decode(gdn, case, 100)
+    y_ref, S_ref, conv_ref = oracle_decode(case, 100)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
+@pytest.mark.parametrize("decay", ["head", "channel"])
+def test_decode_gate_edge_inputs(gdn, decay):
+    """Gate inputs on the gates' edges: a + dt_bias straddling the softplus
+    threshold (20) and b = +-30, over 8 steps for 3 sequences."""
+    d = Dims(2, 4, 64, 64, 4, "silu" if decay == "head" else "sigmoid", decay=decay)
+    case = make_case(d, [0, 0, 0], act_dtype="bf16", seed=12, decay="weak", s0_std=0.3,
+                     conv0_std=1.0, decode_steps=8)
+    a_vals = torch.tensor([19.875, 20.0, 20.125, 24.0, -30.0, 30.0, 0.5])
+    b_vals = torch.tensor([30.0, -30.0, 0.0, 5.0, -30.0])
+    sa = case.dec["a"].shape
+    sb = case.dec["b"].shape
+    case.dec["a"] = a_vals[torch.arange(sa.numel()).view(sa) % len(a_vals)].clone()
+    case.dec["b"] = b_vals[torch.arange(sb.numel()).view(sb) % len(b_vals)].clone()
+    dtb = case.params["dt_bias"].clone()
+    dtb[: dtb.numel() // 2] = 0.0
+    dtb[dtb.numel() // 2:] = 0.0625
+    case.params["dt_bias"] = dtb
+    y, S, conv = run_decode(gdn, case, 8)
+    y_ref, S_ref, conv_ref = oracle_decode(case, 8)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
 VARIANTS = [
     # h_k, h_v, d_k, d_v, K, gate, decay
     (2, 2, 32, 32, 4, "silu", "weak"),

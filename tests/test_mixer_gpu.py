@@ -108,3 +108,43 @@ def test_mixer_decode_full_layer_b64(gdn):
     P.assert_y_close(y32.float(), r["out"], "mixer out")
     P.assert_state_close(S, r["S"])
     conv_close(C, r["conv"])
+
+
+@pytest.mark.slow
+def test_mixer_prefill_full_layer_hidden_2048(gdn):
+    """The full layer (hidden 2048, H_k=16, H_v=32, d=128, K=4) over two
+    sequences (1024 and 300 tokens) with a weak decay and random initial
+    states: the GEMM shapes hipBLASLt plans at full size, every output and
+    head compared."""
+    H = 2048
+    case = make_case(BIG, [1024, 300], act_dtype="bf16", seed=830, decay="weak", s0_std=0.02,
+                     conv0_std=1.0)
+    proj = make_projections(BIG, H, seed=831)
+    x = make_hidden(case.t_total, H, seed=832)
+    cfg = P.gpu_config(BIG, "bf16", torch.float32)
+    out, S, conv = gdn.mixer_prefill(cfg, P.dev_params(case), dev_proj(proj),
+                                     gdn.SeqLens(case.cu_seqlens),
+                                     x.to(torch.bfloat16).cuda(), state_in=case.S0.cuda(),
+                                     conv_in=case.conv0.cuda())
+    torch.cuda.synchronize()
+    r = oracle.mixer_layer(P.oracle_shape(BIG), case.cu_seqlens, case.params, proj, x, case.S0,
+                           case.conv0, nthreads=P.n_threads())
+    P.assert_y_close(out.cpu(), r["out"], "mixer out")
+    P.assert_state_close(S.cpu(), r["S"])
+    conv_close(conv.cpu(), r["conv"])
+
+
+def test_mixer_prefill_all_sequences_empty(gdn):
+    """t_total = 0 with three sequences: states and histories pass through."""
+    d = Dims(2, 4, 64, 64)
+    H = 128
+    case = make_case(d, [0, 0, 0], act_dtype="bf16", seed=840, s0_std=0.5, conv0_std=1.0)
+    proj = make_projections(d, H, seed=841)
+    cfg = P.gpu_config(d, "bf16", torch.float32)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    out, S, conv = gdn.mixer_prefill(cfg, P.dev_params(case), dev_proj(proj),
+                                     gdn.SeqLens(case.cu_seqlens), x, state_in=case.S0.cuda(),
+                                     conv_in=case.conv0.cuda())
+    torch.cuda.synchronize()
+    assert out.numel() == 0
+    assert torch.equal(S.cpu(), case.S0) and torch.equal(conv.cpu(), case.conv0)

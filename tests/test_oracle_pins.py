@@ -54,10 +54,11 @@ def test_conv_current_tap_only_is_silu():
     np.testing.assert_allclose(c, F.silu(_t(x)).numpy(), rtol=1e-15, atol=0)
 
 
-@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
 def test_conv_is_textbook_fir_filter(K):
     """With a history, each channel equals scipy's causal FIR filter run over
-    [history, x] (taps reversed: the newest input meets w[K-1])."""
+    [history, x] (taps reversed: the newest input meets w[K-1]).  K = 1 is a
+    per-channel scale with an empty history."""
     d = Dims(1, 2, 3, 5, conv_k=K)
     rng = np.random.default_rng(K)
     L = 11
@@ -70,8 +71,10 @@ def test_conv_is_textbook_fir_filter(K):
         h = lfilter(w[ch, ::-1], [1.0], full[:, ch])[K - 1:]
         ref = F.silu(_t(h)).numpy()
         np.testing.assert_allclose(c[:, ch], ref, rtol=1e-13, atol=1e-15)
-    # new history: last K-1 raw inputs, oldest first
-    np.testing.assert_array_equal(st[0], full[-(K - 1):])
+    # new history: last K-1 raw inputs, oldest first (none when K = 1)
+    assert st.shape == (1, K - 1, d.conv_dim)
+    if K > 1:
+        np.testing.assert_array_equal(st[0], full[-(K - 1):])
 
 
 @pytest.mark.parametrize("L", [0, 1, 2, 3, 5])
@@ -541,8 +544,11 @@ def test_kda_matches_independent_formulation(head_map):
 @pytest.mark.parametrize("decay", ["head", "channel"])
 def test_mixer_layer_with_selection_weights_is_the_core(decay):
     """With in_proj weights that select consecutive slices of x (identity
-    blocks) and an identity out_proj, the layer is the core on those slices:
-    a wrong weight for any of qkv, z, b, a or the output fails."""
+    blocks) the layer's core runs on those slices: a wrong weight for any of
+    qkv, z, b or a fails.  out_proj is a rectangular, non-symmetric
+    selection ([value_dim + 1][value_dim]: output column r is core column
+    r + 1 cyclically, the extra column 2 y_0 - y_1), so the orientation of
+    the output weight is fixed too: applying it transposed fails."""
     d = Dims(2, 4, 4, 3, conv_k=3, decay=decay)
     c = _case(d, [6, 4], seed=41, s0_std=0.3, conv0_std=1.0, decay="weak")
     widths = [d.conv_dim, d.value_dim, d.h_v, d.h_v * d.gate_width]
@@ -551,12 +557,19 @@ def test_mixer_layer_with_selection_weights_is_the_core(decay):
                         np.asarray(c.b, np.float64), np.asarray(c.a, np.float64)], axis=1)
     eye = np.eye(H)
     off = np.cumsum([0] + widths)
+    V = d.value_dim
+    w_out = np.zeros((V + 1, V))
+    for r in range(V):
+        w_out[r, (r + 1) % V] = 1.0
+    w_out[V, 0], w_out[V, 1] = 2.0, -1.0
     proj = {"hidden": H, "w_qkv": eye[off[0]:off[1]], "w_z": eye[off[1]:off[2]],
-            "w_b": eye[off[2]:off[3]], "w_a": eye[off[3]:off[4]],
-            "w_out": np.eye(d.value_dim)}
+            "w_b": eye[off[2]:off[3]], "w_a": eye[off[3]:off[4]], "w_out": w_out}
     shape = oracle.Shape(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, d.gate, decay=decay)
     layer = oracle.mixer_layer(shape, c.cu_seqlens, c.params, proj, x, c.S0, c.conv0)
     core = oracle.mixer(shape, c.cu_seqlens, c.params, c.qkv, c.z, c.a, c.b, c.S0, c.conv0)
     np.testing.assert_array_equal(layer["y"], core["y"])
-    np.testing.assert_array_equal(layer["out"], core["y"])
+    y = core["y"]
+    assert layer["out"].shape == (y.shape[0], V + 1)
+    np.testing.assert_array_equal(layer["out"][:, :V], np.roll(y, -1, axis=1))
+    np.testing.assert_array_equal(layer["out"][:, V], 2.0 * y[:, 0] - y[:, 1])
     np.testing.assert_array_equal(layer["S"], core["S"])
