@@ -70,6 +70,8 @@ _SIGNATURES = {
                                            _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                                            _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
                                            _VP]),
+    "gdn_prefill_chunked_noalloc": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
+                                                   _I32, _I32, _I32] + [_VP] * 11 + [_VP]),
     "gdn_mixer_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Config), _I32, _I32, _I32]),
     "gdn_mixer_prefill": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_Params),
                                          ctypes.POINTER(_Proj), _I32, _I32] + [_VP] * 9
@@ -402,6 +404,48 @@ def prefill_chunked(cfg: Config, params: dict, seqlens: SeqLens, qkv, z, a, b,
         return out, state_out, conv_out
 
 
+PREFILL_NOALLOC_MAX_BYTES = 64 << 20   # GDN_PREFILL_NOALLOC_MAX_BYTES
+
+
+def prefill_chunked_noalloc(cfg: Config, params: dict, seqlens: SeqLens, qkv, z, a, b,
+                            state_in=None, state_out=None, conv_in=None, conv_out=None,
+                            out=None, chunk: int = CHUNK, stream=None):
+    """gdn_prefill_chunked_noalloc: the chunked prefill with its workspace in
+    the library's static device scratch (no workspace argument; the C call
+    allocates nothing).  Pass state_out, conv_out and out to keep this
+    wrapper from allocating them.  Returns (out, state_out, conv_out)."""
+    lib = load_library()
+    with _alloc_on(stream):
+        T, N = seqlens.t_total, seqlens.n_seq
+        dev = qkv.device
+        _check(qkv, "qkv", (T, cfg.conv_dim), cfg.act_dtype)
+        _check(z, "z", (T, cfg.value_dim), cfg.act_dtype)
+        _check(a, "a", (T, cfg.h_v * cfg.gate_width), cfg.act_dtype)
+        _check(b, "b", (T, cfg.h_v), cfg.act_dtype)
+        sshape = (N, cfg.h_v, cfg.d_k, cfg.d_v)
+        cshape = (N, cfg.conv_k - 1, cfg.conv_dim)
+        if state_in is not None:
+            _check(state_in, "state_in", sshape, torch.float32)
+        if conv_in is not None:
+            _check(conv_in, "conv_in", cshape, torch.float32)
+        if state_out is None:
+            state_out = torch.empty(sshape, dtype=torch.float32, device=dev)
+        if conv_out is None:
+            conv_out = torch.empty(cshape, dtype=torch.float32, device=dev)
+        if out is None:
+            out = torch.empty((T, cfg.value_dim), dtype=cfg.out_dtype, device=dev)
+        _check(state_out, "state_out", sshape, torch.float32)
+        _check(conv_out, "conv_out", cshape, torch.float32)
+        _check(out, "out", (T, cfg.value_dim), cfg.out_dtype)
+        c, p = cfg.c_struct(), _params(cfg, params)
+        _raise_on(lib.gdn_prefill_chunked_noalloc(
+            ctypes.byref(c), ctypes.byref(p), chunk, N, T,
+            ctypes.c_void_p(seqlens.host.data_ptr()), _ptr(seqlens.dev),
+            _ptr(qkv), _ptr(z), _ptr(a), _ptr(b), _ptr(state_in), _ptr(state_out),
+            _ptr(conv_in), _ptr(conv_out), _ptr(out), _stream(stream)))
+        return out, state_out, conv_out
+
+
 def _proj(cfg: Config, proj: dict) -> _Proj:
     """proj: hidden (int) and bf16 weights w_qkv [conv_dim, H], w_z [value_dim, H],
     w_b [H_v, H], w_a [H_v * gate_width, H], w_out [H, value_dim]."""
@@ -480,5 +524,6 @@ def mixer_decode(cfg: Config, params: dict, proj: dict, x, conv_state, state, y=
 
     __all__ = ["Config", "SeqLens", "GdnError", "load_library", "header_functions",
                "conv_update", "decode_step", "decode_multi", "rewind", "prefill_workspace_bytes",
-               "alloc_workspace", "prefill_chunked", "mixer_workspace_bytes", "mixer_prefill",
+               "alloc_workspace", "prefill_chunked", "prefill_chunked_noalloc",
+           "PREFILL_NOALLOC_MAX_BYTES", "mixer_workspace_bytes", "mixer_prefill",
                "mixer_decode", "LIB_PATH", "CHUNK", "MAX_NEW_TOKENS"]

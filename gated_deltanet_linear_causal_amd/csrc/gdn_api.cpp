@@ -344,12 +344,18 @@ size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seq, int32_t
     return gdn::prefill_workspace_bytes(d, n_seq, t_total);
 }
 
-gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, int32_t chunk,
-                               int32_t n_seq, int32_t t_total, const int32_t *cu_seqlens_host,
-                               const int32_t *cu_seqlens_dev, const void *qkv, const void *z,
-                               const void *a, const void *b, const float *state_in,
-                               float *state_out, const float *conv_in, float *conv_out, void *out,
-                               void *workspace, size_t ws_bytes, void *stream)
+} // extern "C"
+
+namespace {
+
+// The chunked prefill with its workspace either given by the caller
+// (static_ws false) or taken from the library's static scratch.
+gdn_status prefill_common(const gdn_config *cfg, const gdn_params *params, int32_t chunk,
+                          int32_t n_seq, int32_t t_total, const int32_t *cu_seqlens_host,
+                          const int32_t *cu_seqlens_dev, const void *qkv, const void *z,
+                          const void *a, const void *b, const float *state_in, float *state_out,
+                          const float *conv_in, float *conv_out, void *out, void *workspace,
+                          size_t ws_bytes, bool static_ws, void *stream)
 {
     gdn::Dims d;
     gdn::Params p;
@@ -370,11 +376,19 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, 
     if (n_seq > 0 && (!state_out || (d.conv_k > 1 && !conv_out)))
         return fail(GDN_EINVAL, "state_out (and conv_out when K > 1) are required");
     const size_t need = gdn::prefill_workspace_bytes(d, n_seq, t_total);
-    if (need > 0 && (!workspace || ws_bytes < need))
-        return fail(GDN_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                    workspace ? ws_bytes : (size_t)0);
-    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255))
-        return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
+    if (static_ws) {
+        if (need > gdn::kStaticScratchBytes)
+            return fail(GDN_EUNSUPPORTED,
+                        "this call needs %zu bytes of scratch; the allocation-free prefill holds "
+                        "%zu (use gdn_prefill_chunked with a workspace)",
+                        need, gdn::kStaticScratchBytes);
+    } else {
+        if (need > 0 && (!workspace || ws_bytes < need))
+            return fail(GDN_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                        workspace ? ws_bytes : (size_t)0);
+        if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255))
+            return fail(GDN_EINVAL, "workspace must be 256-byte aligned");
+    }
     const size_t esz = d.act_bf16 ? 2 : 4, osz = d.out_bf16 ? 2 : 4;
     const size_t sbytes = (size_t)n_seq * d.h_v * d.d_k * d.d_v * 4;
     const size_t cbytes = (size_t)n_seq * (d.conv_k - 1) * d.conv_dim * 4;
@@ -385,7 +399,7 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, 
     const Range ro{out, (size_t)t_total * d.value_dim * osz};
     const Range rsi{state_in, sbytes}, rso{state_out, sbytes};
     const Range rci{conv_in, cbytes}, rco{conv_out, cbytes};
-    const Range rws{workspace, need};
+    const Range rws{static_ws ? nullptr : workspace, need};
     const Range outs[] = {ro, rso, rco, rws};
     for (const Range &o : outs)
         for (const Range &r : ins)
@@ -398,10 +412,47 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, 
         return fail(GDN_EINVAL, "state_out may equal state_in but must not partially overlap it");
     if (overlap(rci, rco) && conv_in != conv_out)
         return fail(GDN_EINVAL, "conv_out may equal conv_in but must not partially overlap it");
+    if (static_ws) {
+        hipError_t e = gdn::static_scratch(&workspace);
+        if (e != hipSuccess) return hip_status(e, "static scratch address");
+    }
     return hip_status(gdn::launch_prefill(d, p, n_seq, t_total, max_len, cu_seqlens_dev, qkv, z, a,
                                           b, state_in, state_out, conv_in, conv_out, out, workspace,
                                           static_cast<hipStream_t>(stream)),
-                      "gdn_prefill_chunked launch");
+                      static_ws ? "gdn_prefill_chunked_noalloc launch" : "gdn_prefill_chunked launch");
+}
+
+} // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params, int32_t chunk,
+                               int32_t n_seq, int32_t t_total, const int32_t *cu_seqlens_host,
+                               const int32_t *cu_seqlens_dev, const void *qkv, const void *z,
+                               const void *a, const void *b, const float *state_in,
+                               float *state_out, const float *conv_in, float *conv_out, void *out,
+                               void *workspace, size_t ws_bytes, void *stream)
+{
+    return prefill_common(cfg, params, chunk, n_seq, t_total, cu_seqlens_host, cu_seqlens_dev, qkv,
+                          z, a, b, state_in, state_out, conv_in, conv_out, out, workspace, ws_bytes,
+                          false, stream);
+}
+
+static_assert(GDN_PREFILL_NOALLOC_MAX_BYTES == gdn::kStaticScratchBytes,
+              "the header states the static scratch size");
+
+gdn_status gdn_prefill_chunked_noalloc(const gdn_config *cfg, const gdn_params *params,
+                                       int32_t chunk, int32_t n_seq, int32_t t_total,
+                                       const int32_t *cu_seqlens_host,
+                                       const int32_t *cu_seqlens_dev, const void *qkv,
+                                       const void *z, const void *a, const void *b,
+                                       const float *state_in, float *state_out,
+                                       const float *conv_in, float *conv_out, void *out,
+                                       void *stream)
+{
+    return prefill_common(cfg, params, chunk, n_seq, t_total, cu_seqlens_host, cu_seqlens_dev, qkv,
+                          z, a, b, state_in, state_out, conv_in, conv_out, out, nullptr, 0, true,
+                          stream);
 }
 
 } // extern "C"

@@ -71,4 +71,9 @@ hipError_t launch_prefill(const Dims &d, const Params &p, int n_seq, int t_total
                           const float *state_in, float *state_out, const float *conv_in,
                           float *conv_out, void *out, void *ws, hipStream_t s);
 
+// Workspace of the allocation-free prefill: a static device array of this
+// many bytes per device, its address resolved once per device.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(void **ptr);
+
 } // namespace gdn

@@ -41,6 +41,8 @@
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
+#include <mutex>
+
 namespace gdn {
 
 constexpr int kC = 64;       // tokens per chunk
@@ -1622,6 +1624,38 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     GDN_PF_CASE(128)
 #undef GDN_PF_CASE
     return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate: the workspace of the
+// allocation-free prefill entry point.  One copy per device, held until the
+// process ends; every call on a device shares it, so calls that overlap on
+// one device race.  Every workspace value the prefill uses was written
+// earlier in the same call (a few loads whose values go unused may read what
+// an earlier call left), so nothing needs clearing between calls.  Host code
+// never uses the array's name as a device address: the address comes from
+// hipGetSymbolAddress, once per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 } // namespace gdn

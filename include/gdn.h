@@ -21,9 +21,10 @@
  *   - Every tensor pointer is device memory owned by the caller.  The core
  *     entry points (all but gdn_mixer_*) allocate and free nothing; their
  *     only process-wide state is set once and never changes afterwards: a
- *     per-device cache of the compute-unit count (atomic) and the kernels'
+ *     per-device cache of the compute-unit count (atomic), the kernels'
  *     LDS-size attributes (set on a kernel's first use, in a thread-safe
- *     static initialiser).
+ *     static initialiser) and the per-device address of the static scratch
+ *     array that gdn_prefill_chunked_noalloc uses as its workspace.
  *   - The mixer entry points (gdn_mixer_prefill, gdn_mixer_decode) also keep,
  *     per device, one hipBLASLt handle and one GEMM plan per problem shape.
  *     Both are made on first use, under a lock, and kept until the process
@@ -247,6 +248,34 @@ gdn_status gdn_prefill_chunked(const gdn_config *cfg, const gdn_params *params,
                                const float *conv_in, float *conv_out,
                                void *out, void *workspace, size_t ws_bytes,
                                void *stream);
+
+/*
+ * gdn_prefill_chunked for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, layouts and results as gdn_prefill_chunked
+ * (it runs the same kernels), without the workspace: the library takes it
+ * from a static device array of GDN_PREFILL_NOALLOC_MAX_BYTES bytes that
+ * each device holds from the library's first use until the process ends.
+ * The call allocates and frees nothing (the array's address is looked up
+ * once per device, on the first call there).
+ *   A call whose gdn_prefill_workspace_bytes(cfg, n_seq, t_total, chunk)
+ *   exceeds GDN_PREFILL_NOALLOC_MAX_BYTES returns GDN_EUNSUPPORTED and
+ *   enqueues nothing (at H_k=16, H_v=32, d=128 the limit is reached near
+ *   700 tokens per call).
+ *   Every call on one device shares that device's array: calls that
+ *   overlap in time on one device (other streams, other threads) race and
+ *   must be serialised by the caller.  Nothing in the array needs clearing
+ *   between calls.
+ */
+#define GDN_PREFILL_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+gdn_status gdn_prefill_chunked_noalloc(const gdn_config *cfg, const gdn_params *params,
+                                       int32_t chunk, int32_t n_seq, int32_t t_total,
+                                       const int32_t *cu_seqlens_host,
+                                       const int32_t *cu_seqlens_dev, const void *qkv,
+                                       const void *z, const void *a, const void *b,
+                                       const float *state_in, float *state_out,
+                                       const float *conv_in, float *conv_out, void *out,
+                                       void *stream);
 
 /*
  * The mixer with its projections ("oxinfer 0.0.5 src/qwen.rs", Gdn struct

@@ -29,7 +29,8 @@ def test_library_exports_every_header_function(lib):
     names = gdn.header_functions()
     assert set(names) == {"gdn_conv_update", "gdn_decode_step", "gdn_decode_multi",
                           "gdn_rewind", "gdn_prefill_workspace_bytes",
-                          "gdn_prefill_chunked", "gdn_mixer_workspace_bytes",
+                          "gdn_prefill_chunked", "gdn_prefill_chunked_noalloc",
+                          "gdn_mixer_workspace_bytes",
                           "gdn_mixer_prefill", "gdn_mixer_decode", "gdn_status_string",
                           "gdn_last_error"}
     dyn = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
@@ -235,6 +236,33 @@ def test_prefill_rejects_chunk_workspace_and_aliases(lib):
     # activations are read in 16-byte pieces
     assert _prefill(lib, [0, 10], 10, qkv=ctypes.c_void_p(_P[0].value + 8)) == EINVAL
     assert "16-byte" in lib.gdn_last_error().decode()
+
+
+def _prefill_noalloc(lib, cu, t_total, cfg=None, chunk=64, outs=None, qkv=_P[0]):
+    c = cfg or _cfg()
+    cu_h = np.asarray(cu, dtype=np.int32)
+    n = len(cu) - 1
+    o = outs or dict(state_in=_P[4], state_out=_P[5], conv_in=_P[6], conv_out=_P[7], out=_P[8])
+    return lib.gdn_prefill_chunked_noalloc(
+        ctypes.byref(c), ctypes.byref(_params()), chunk, n, t_total,
+        cu_h.ctypes.data_as(ctypes.c_void_p), _P[14], qkv, _P[1], _P[2], _P[3],
+        o["state_in"], o["state_out"], o["conv_in"], o["conv_out"], o["out"], None)
+
+
+@no_gpu
+def test_prefill_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """The allocation-free prefill refuses, before anything is enqueued, a
+    call whose workspace would not fit its static scratch, and validates
+    like gdn_prefill_chunked otherwise."""
+    big = _cfg(h_k=16, h_v=32, d_k=128, d_v=128)
+    t = 4096
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(big), 1, t, 64) > gdn.PREFILL_NOALLOC_MAX_BYTES
+    assert _prefill_noalloc(lib, [0, t], t, cfg=big) == EUNSUP
+    assert "scratch" in lib.gdn_last_error().decode()
+    assert _prefill_noalloc(lib, [0, 10], 10, chunk=32) == EUNSUP
+    assert _prefill_noalloc(lib, [0, 5, 9], 10) == EINVAL
+    o = dict(state_in=_P[4], state_out=_P[5], conv_in=_P[6], conv_out=_P[7], out=_P[0])
+    assert _prefill_noalloc(lib, [0, 10], 10, outs=o) == EINVAL
 
 
 @no_gpu
