@@ -46,7 +46,7 @@
 namespace gdn {
 
 constexpr int kC = 64;       // tokens per chunk
-constexpr int kBV = 16;      // d_v columns per scan workgroup
+constexpr int kBV = 16;      // d_v columns per scan tile
 constexpr int kQkChunks = 2; // chunks per qknorm workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1098,19 +1098,23 @@ tri_kernel(const PrefillArgs p)
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup per (sequence, value head, 16-column slice), 8 waves
-// in two roles, one wave of each per SIMD:
+// scan: one workgroup per (sequence, value head, slice of NT 16-column tiles
+// of d_v), 8 waves in two roles, one wave of each per SIMD:
 //   chain waves 0-3: wave w carries rows 16w..16w+15 of D = U - W S and the
-//     state rows of M-tiles w, w+4, ... through S' = e^{G_C} S + K^T E;
+//     state rows of M-tiles w, w+4, ... through S' = e^{G_C} S + K^T E, for
+//     every column tile of the slice;
 //   output waves 4-7: one chunk behind, wave w forms rows 16w.. of
 //     O = e^G (Q S) + P D from the state and D the chain left in LDS.
 // Each role loads only its own operands, pre-split, into registers, each
 // reloaded with the next chunk's data right after its last use; LDS holds
 // what the roles exchange: the state slice S^T (d_k-permuted, B operand,
 // double-buffered by chunk parity), D (double-buffered) and e^{G_C-G} D.
-// Both roles meet at the same two barriers per chunk.
+// Both roles meet at the same two barriers per chunk.  Every operand
+// fragment a wave loads serves all NT column tiles, so wider slices cut the
+// operand stream per column (the slices of one head all read the same W,
+// K^T, Q and P of a chunk).
 // ---------------------------------------------------------------------------
-template <int DK, bool KDA>
+template <int DK, bool KDA, int NT>
 __global__ void __launch_bounds__(512)
 scan_kernel(const PrefillArgs p, int slices)
 {
@@ -1119,6 +1123,7 @@ scan_kernel(const PrefillArgs p, int slices)
     constexpr int KS = DK / 32;        // k-steps over d_k
     constexpr int MTS = DK / 16;       // state M-tiles
     constexpr int MTW = (MTS + 3) / 4; // per chain wave
+    constexpr int NC = kBV * NT;       // columns of the slice
 
     // Map the block index so the slices of one head share an XCD (blocks
     // are dealt round-robin over 8 XCDs): they read the same chunk data.
@@ -1126,10 +1131,10 @@ scan_kernel(const PrefillArgs p, int slices)
     int hidx, slice;
     {
         const int b = blockIdx.x;
-        if (slices == 8 && nheads % 8 == 0) {
+        if (slices > 1 && nheads % 8 == 0) {
             const int x8 = b % 8, rest = b / 8;
-            slice = rest % 8;
-            hidx = (rest / 8) * 8 + x8;
+            slice = rest % slices;
+            hidx = (rest / slices) * 8 + x8;
         } else {
             slice = b % slices;
             hidx = b / slices;
@@ -1145,10 +1150,11 @@ scan_kernel(const PrefillArgs p, int slices)
     const int L = p.cu[n + 1] - s0;
     const int nchunks = (L + kC - 1) / kC;
     const int slot0 = s0 / kC + n;
+    const int c0 = slice * NC; // first d_v column of the slice
 
-    __shared__ __attribute__((aligned(16))) __bf16 sS[2][2][kBV * RK]; // [parity][hi,lo]
-    __shared__ __attribute__((aligned(16))) __bf16 sD[2][2][kBV * RT]; // [parity][hi,lo]
-    __shared__ __attribute__((aligned(16))) __bf16 sE[2][kBV * RT];    // [hi,lo]
+    __shared__ __attribute__((aligned(16))) __bf16 sS[2][2][NC * RK]; // [parity][hi,lo]
+    __shared__ __attribute__((aligned(16))) __bf16 sD[2][2][NC * RT]; // [parity][hi,lo]
+    __shared__ __attribute__((aligned(16))) __bf16 sE[2][NC * RT];    // [hi,lo]
 
     if (wave < 4) {
         // ================= chain waves ===================================
@@ -1157,11 +1163,11 @@ scan_kernel(const PrefillArgs p, int slices)
         const __bf16 *ktf = p.ws_ktf + ((size_t)hq * p.ns + slot0) * (2 * kC * DK) + lane * 8;
         const __bf16 *wf = p.ws_wf + ((size_t)hv * p.ns + slot0) * (2 * kC * DK) + lane * 8;
         const float *uf = p.ws_uf + ((size_t)hv * p.ns + slot0) * ((size_t)kC * p.d_v) +
-                          (size_t)slice * 4 * 256 + w * 256 + lane * 4;
+                          (size_t)slice * NT * 4 * 256 + w * 256 + lane * 4;
         const float *gf = p.ws_gf + ((size_t)hv * p.ns + slot0) * (2 * kC);
-        f32x4 S[MTW];
+        f32x4 S[MTW][NT];
         Frag cW[KS], cK[MTW][2];
-        f32x4 cU, cEGC;
+        f32x4 cU[NT], cEGC;
         float gam = 0.0f;
         f32x4 gam4[MTW]; // per-channel chunk decay of this wave's state rows
 #pragma unroll
@@ -1178,7 +1184,8 @@ scan_kernel(const PrefillArgs p, int slices)
                 const int f = (w * KS + s) * 2;                                                \
                 cW[s] = frag_at(wf + off + f * 512, wf + off + (f + 1) * 512);                 \
             }                                                                                  \
-            cU = ld4(uf + (size_t)(CH) * kC * p.d_v);                                          \
+            _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                  \
+                cU[nt] = ld4(uf + (size_t)(CH) * kC * p.d_v + nt * 4 * 256);                   \
         }
 #define GDN_CHAIN_LOAD1B(CH) cEGC = ld4(gf + (size_t)(CH) * (2 * kC) + kC + 16 * w + 4 * kq);
 #define GDN_CHAIN_LOAD2(CH)                                                                    \
@@ -1200,12 +1207,13 @@ scan_kernel(const PrefillArgs p, int slices)
                 gam = gf[(size_t)(CH) * (2 * kC) + kC - 1];                                    \
             }                                                                                  \
         }
-        // State tile mt into S^T (buffer par) at its d_k-permuted position.
-        auto put_state = [&](int par, int mt, const f32x4 &v) {
+        // State tile (mt, column tile nt) into S^T (buffer par) at its
+        // d_k-permuted position.
+        auto put_state = [&](int par, int mt, int nt, const f32x4 &v) {
             __bf16 h[4], l[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) split1(v[e], h[e], l[e]);
-            const int pos = col * RK + 32 * (mt >> 1) + 8 * kq + 4 * (mt & 1);
+            const int pos = (16 * nt + col) * RK + 32 * (mt >> 1) + 8 * kq + 4 * (mt & 1);
             *reinterpret_cast<uint2 *>(&sS[par][0][pos]) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
             *reinterpret_cast<uint2 *>(&sS[par][1][pos]) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
         };
@@ -1215,16 +1223,21 @@ scan_kernel(const PrefillArgs p, int slices)
             for (int u = 0; u < MTW; ++u) {
                 const int mt = w + 4 * u;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * mt + 4 * kq + e;
-                    S[u][e] = (mt < MTS && Sin) ? Sin[(size_t)i * p.d_v + slice * kBV + col] : 0.0f;
+                for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * mt + 4 * kq + e;
+                        S[u][nt][e] = (mt < MTS && Sin) ? Sin[(size_t)i * p.d_v + c0 + 16 * nt + col] : 0.0f;
+                    }
+                    if (mt < MTS) put_state(0, mt, nt, S[u][nt]);
                 }
-                if (mt < MTS) put_state(0, mt, S[u]);
             }
         }
-        GDN_CHAIN_LOAD1(0)
-        GDN_CHAIN_LOAD1B(0)
-        GDN_CHAIN_LOAD2(0)
+        if (nchunks > 0) {
+            GDN_CHAIN_LOAD1(0)
+            GDN_CHAIN_LOAD1B(0)
+            GDN_CHAIN_LOAD2(0)
+        }
         // Drain the prologue's loads (issued in whatever order the compiler
         // chose) so that only the loop's own issue order decides its waits.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -1233,22 +1246,28 @@ scan_kernel(const PrefillArgs p, int slices)
             const int par = c & 1;
             const int cn = c + 1 < nchunks ? c + 1 : c; // chunk whose operands are prefetched
             // ---- phase 1: D = U - W S -> sD, e^{G_C-G} D -> sE
-            f32x4 Dv = cU;
+            f32x4 Dv[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) Dv[nt] = cU[nt];
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const int o = col * RK + 32 * s + 8 * kq;
-                Dv = mma3(cW[s], frag_at(&sS[par][0][o], &sS[par][1][o]), Dv);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int o = (16 * nt + col) * RK + 32 * s + 8 * kq;
+                    Dv[nt] = mma3(cW[s], frag_at(&sS[par][0][o], &sS[par][1][o]), Dv[nt]);
+                }
             }
             GDN_CHAIN_LOAD1(cn)
-            {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
                 // this lane's 4 consecutive tokens: 8-byte writes
                 __bf16 dh[4], dl[4], eh[4], el[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    split1(Dv[e], dh[e], dl[e]);
-                    split1(KDA ? Dv[e] : Dv[e] * cEGC[e], eh[e], el[e]);
+                    split1(Dv[nt][e], dh[e], dl[e]);
+                    split1(KDA ? Dv[nt][e] : Dv[nt][e] * cEGC[e], eh[e], el[e]);
                 }
-                const int o = col * RT + 16 * w + 4 * kq;
+                const int o = (16 * nt + col) * RT + 16 * w + 4 * kq;
                 *reinterpret_cast<uint2 *>(&sD[par][0][o]) = make_uint2(pack2(dh[0], dh[1]), pack2(dh[2], dh[3]));
                 *reinterpret_cast<uint2 *>(&sD[par][1][o]) = make_uint2(pack2(dl[0], dl[1]), pack2(dl[2], dl[3]));
                 *reinterpret_cast<uint2 *>(&sE[0][o]) = make_uint2(pack2(eh[0], eh[1]), pack2(eh[2], eh[3]));
@@ -1260,22 +1279,27 @@ scan_kernel(const PrefillArgs p, int slices)
             // (the state is pinned here so that e^{G_C} S, which waits for the
             // phase-2 loads, is not hoisted into phase 1)
 #pragma unroll
-            for (int u = 0; u < MTW; ++u) asm volatile("" : "+v"(S[u]));
-            Frag Be[2];
+            for (int u = 0; u < MTW; ++u)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int o = col * RT + 32 * s + 8 * kq;
-                Be[s] = frag_at(&sE[0][o], &sE[1][o]);
-            }
+                for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(S[u][nt]));
 #pragma unroll
-            for (int u = 0; u < MTW; ++u) {
-                const int mt = w + 4 * u;
-                if (mt < MTS) {
-                    f32x4 acc = KDA ? gam4[u] * S[u] : gam * S[u];
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag Be[2];
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) acc = mma3(cK[u][s], Be[s], acc);
-                    S[u] = acc;
-                    put_state(par ^ 1, mt, acc);
+                for (int s = 0; s < 2; ++s) {
+                    const int o = (16 * nt + col) * RT + 32 * s + 8 * kq;
+                    Be[s] = frag_at(&sE[0][o], &sE[1][o]);
+                }
+#pragma unroll
+                for (int u = 0; u < MTW; ++u) {
+                    const int mt = w + 4 * u;
+                    if (mt < MTS) {
+                        f32x4 acc = KDA ? gam4[u] * S[u][nt] : gam * S[u][nt];
+#pragma unroll
+                        for (int s = 0; s < 2; ++s) acc = mma3(cK[u][s], Be[s], acc);
+                        S[u][nt] = acc;
+                        put_state(par ^ 1, mt, nt, acc);
+                    }
                 }
             }
             GDN_CHAIN_LOAD2(cn)
@@ -1290,23 +1314,25 @@ scan_kernel(const PrefillArgs p, int slices)
             const int mt = w + 4 * u;
             if (mt < MTS)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + slice * kBV + col] = S[u][e];
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        Sout[(size_t)(16 * mt + 4 * kq + e) * p.d_v + c0 + 16 * nt + col] = S[u][nt][e];
         }
     } else {
         // ================= output waves (one chunk behind) ==============
         // Issue priority: the output waves' products gate the barriers both
         // roles meet at, so they run at priority 3 over the chain waves
         // sharing their SIMD, and drop to 0 while issuing their loads so
-        // that the chain's loads are not queued behind them (scan at
-        // T=4096: 148 us with equal priorities, 145 us with the output
-        // waves at 3 throughout, 143 us with this split).
+        // that the chain's loads are not queued behind them.
         const __bf16 *qf = p.ws_qf + ((size_t)(KDA ? hv : hk) * p.ns + slot0) * (2 * kC * DK) + lane * 8;
         const __bf16 *pf = p.ws_pf + ((size_t)hv * p.ns + slot0) * (2 * kC * kC) + lane * 8;
         const float *gf = p.ws_gf + ((size_t)hv * p.ns + slot0) * (2 * kC);
-        float *o_head = p.ws_o + (size_t)hv * p.t_total * p.d_v + slice * kBV + col;
+        float *o_head = p.ws_o + (size_t)hv * p.t_total * p.d_v + c0 + col;
         Frag cQ[KS], cP[2];
-        f32x4 cEG, Y = {0.f, 0.f, 0.f, 0.f};
+        f32x4 cEG, Y[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) Y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #define GDN_OUT_LOAD1(CH)                                                                      \
         {                                                                                      \
             const size_t off = (size_t)(CH) * (2 * kC * DK);                                   \
@@ -1328,45 +1354,54 @@ scan_kernel(const PrefillArgs p, int slices)
         // Y = e^G (Q S) of chunk cc from the state buffer of its parity.
         auto readout = [&](int cc) {
             const int par = cc & 1;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int o = col * RK + 32 * s + 8 * kq;
-                acc = mma3(cQ[s], frag_at(&sS[par][0][o], &sS[par][1][o]), acc);
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int o = (16 * nt + col) * RK + 32 * s + 8 * kq;
+                    acc = mma3(cQ[s], frag_at(&sS[par][0][o], &sS[par][1][o]), acc);
+                }
+                Y[nt] = KDA ? acc : acc * cEG; // (q already carries e^G per channel)
             }
-            return KDA ? acc : acc * cEG; // (q already carries e^G per channel)
         };
         // O = Y + P D of chunk cc, stored for its rows inside the sequence.
-        auto finish = [&](int cc, f32x4 y) {
+        auto finish = [&](int cc) {
             const int par = cc & 1;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s == 0 || w >= 2) { // P is lower triangular
-                    const int o = col * RT + 32 * s + 8 * kq;
-                    y = mma3(cP[s], frag_at(&sD[par][0][o], &sD[par][1][o]), y);
-                }
-            }
             const int Lc = min(kC, L - cc * kC);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * w + 4 * kq + e;
-                if (t < Lc) o_head[(size_t)(s0 + cc * kC + t) * p.d_v] = y[e];
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4 y = Y[nt];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s == 0 || w >= 2) { // P is lower triangular
+                        const int o = (16 * nt + col) * RT + 32 * s + 8 * kq;
+                        y = mma3(cP[s], frag_at(&sD[par][0][o], &sD[par][1][o]), y);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * w + 4 * kq + e;
+                    if (t < Lc) o_head[(size_t)(s0 + cc * kC + t) * p.d_v + 16 * nt] = y[e];
+                }
             }
         };
-        GDN_OUT_LOAD1(0)
-        GDN_OUT_LOAD2(0)
+        if (nchunks > 0) {
+            GDN_OUT_LOAD1(0)
+            GDN_OUT_LOAD2(0)
+        }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         lds_barrier();
         for (int c = 0; c < nchunks; ++c) {
             // phase 1: readout of chunk c-1 (its state is still in LDS)
             __builtin_amdgcn_s_setprio(3);
-            if (c > 0) Y = readout(c - 1);
+            if (c > 0) readout(c - 1);
             __builtin_amdgcn_s_setprio(0);
             GDN_OUT_LOAD1(c)
             lds_barrier();
             // phase 2: finish chunk c-1 (its D is still in LDS)
             __builtin_amdgcn_s_setprio(3);
-            if (c > 0) finish(c - 1, Y);
+            if (c > 0) finish(c - 1);
             __builtin_amdgcn_s_setprio(0);
             GDN_OUT_LOAD2(c)
             lds_barrier();
@@ -1374,7 +1409,10 @@ scan_kernel(const PrefillArgs p, int slices)
 #undef GDN_OUT_LOAD1
 #undef GDN_OUT_LOAD2
         // the last chunk: the chain has left its state and D in LDS
-        if (nchunks > 0) finish(nchunks - 1, readout(nchunks - 1));
+        if (nchunks > 0) {
+            readout(nchunks - 1);
+            finish(nchunks - 1);
+        }
     }
 }
 
@@ -1471,6 +1509,22 @@ static hipError_t launch_norm(const PrefillArgs &a, int rows, int n_seq, hipStre
     return hipGetLastError();
 }
 
+// 16-column tiles of d_v per scan workgroup.  Every slice of a head loads
+// the same chunk operands, so wider slices cut the operand stream per
+// column, but they lengthen each workgroup's per-chunk critical path.
+// Widen (up to 4 tiles, the LDS limit) only while at least one workgroup per
+// compute unit remains.  Measured at H_v=32, d=128: one sequence of 4096
+// tokens (32 heads) is fastest at one tile (prefill 284 us against 294 at
+// two and 362 at four); 8 packed sequences (256 heads) at four (1282 us
+// against 1323 at two and 1560 at one).
+static int scan_tiles(int heads, int tiles_per_head, int ncu)
+{
+    int nt = 1;
+    while (nt < 4 && nt * 2 <= tiles_per_head && heads * (tiles_per_head / (nt * 2)) >= ncu)
+        nt *= 2;
+    return nt;
+}
+
 // Every sequence of the call is empty: each final state is its initial
 // state (zeros when none is given).  One thread per float (the state
 // pointers carry no alignment promise beyond 4 bytes); nothing to do when the
@@ -1517,9 +1571,17 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (n_seq > 0) {
-        const int slices = DV / kBV;
-        hipLaunchKernelGGL((scan_kernel<DK, KDA>), dim3(n_seq * a.h_v * slices), dim3(512), 0, s,
-                           a, slices);
+        int ncu = 0;
+        if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
+        const int nt = scan_tiles(n_seq * a.h_v, DV / kBV, ncu);
+        const int slices = DV / kBV / nt;
+        const dim3 grid(n_seq * a.h_v * slices);
+        if (nt == 4)
+            hipLaunchKernelGGL((scan_kernel<DK, KDA, 4>), grid, dim3(512), 0, s, a, slices);
+        else if (nt == 2)
+            hipLaunchKernelGGL((scan_kernel<DK, KDA, 2>), grid, dim3(512), 0, s, a, slices);
+        else
+            hipLaunchKernelGGL((scan_kernel<DK, KDA, 1>), grid, dim3(512), 0, s, a, slices);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return launch_norm<TIn, DV>(a, t_total * a.h_v, n_seq, s);

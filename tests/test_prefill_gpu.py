@@ -68,6 +68,35 @@ def test_prefill_small(gdn, v, act):
     np.testing.assert_array_equal(conv.numpy(), r["conv"])
 
 
+# Enough sequences that the scan widens its column slices: with 256 compute
+# units and 4 value heads per sequence, d_v = 64 takes two 16-column tiles
+# per workgroup from 32 sequences and four (the whole head) from 64; d_v =
+# 128 takes two from 16 sequences and four from 32.
+MANY = [
+    # h_k, h_v, d_k, d_v, decay mode, n_seq
+    (2, 4, 64, 64, "head", 32),
+    (2, 4, 64, 64, "head", 64),
+    (1, 4, 128, 128, "head", 16),
+    (1, 4, 128, 128, "head", 32),
+    (2, 4, 32, 64, "channel", 64),
+]
+
+
+@pytest.mark.parametrize("v", MANY, ids=lambda v: "hk%d_hv%d_dk%d_dv%d_%s_n%d" % v)
+def test_prefill_many_sequences_wide_slices(gdn, v):
+    hk, hv, dk, dv, mode, n = v
+    d = Dims(hk, hv, dk, dv, 4, "silu" if mode == "head" else "sigmoid", decay=mode)
+    lens = [(37 * i + 11) % 150 for i in range(n)]
+    lens[3], lens[5] = 0, 1
+    case = make_case(d, lens, act_dtype="bf16", seed=500 + n + dk + dv, decay="weak",
+                     s0_std=0.3, conv0_std=1.0)
+    y, S, conv = run_prefill(gdn, case)
+    r = P.run_oracle(case)
+    P.assert_y_close(y, r["y"])
+    P.assert_state_close(S, r["S"])
+    np.testing.assert_array_equal(conv.numpy(), r["conv"])
+
+
 LAYOUTS = [
     # h_k, h_v, d, head_map, decay form
     (2, 6, 64, "tiled", "decay_coef"),
