@@ -51,6 +51,7 @@ struct MultiArgs {
     int gate, out_bf16, tiled;
     int out_split;   // out: bf16 hi parts, then the lo parts at out + split_off
     size_t split_off;
+    int preconv;     // qkv already holds silu(conv) and the history is current
     float norm_eps, l2_eps;
 };
 // (with one decay per key channel, a is [batch][t_new][H_v*d_k] and dt_bias
@@ -177,7 +178,7 @@ decode_multi_kernel(const MultiArgs p)
     TIn x00 = TIn(0);
     if (kPre && tid < nch) {
         const int ch = channel_of(tid);
-        load_conv(ch, win0, tap0);
+        if (!p.preconv) load_conv(ch, win0, tap0);
         if (n > 0) x00 = qkv[(size_t)bs * T * CD + ch];
     }
     if (kPre) load_state();
@@ -192,12 +193,20 @@ decode_multi_kernel(const MultiArgs p)
             for (int pos = 0; pos < 4; ++pos) tap[pos] = tap0[pos];
             xs[0] = act_to_f32(x00);
         } else {
-            load_conv(ch, win, tap);
+            if (!p.preconv) load_conv(ch, win, tap);
             xs[0] = n > 0 ? load_act(qkv, (size_t)bs * T * CD + ch) : 0.0f;
         }
 #pragma unroll
         for (int t = 1; t < kDecodeMultiMaxTokens; ++t)
             xs[t] = t < n ? load_act(qkv, ((size_t)bs * T + t) * CD + ch) : 0.0f;
+        if (p.preconv) {
+            // the projection has applied the conv and SiLU and moved the
+            // history on already
+#pragma unroll
+            for (int t = 0; t < kDecodeMultiMaxTokens; ++t)
+                if (t < n) cb[(size_t)t * nch + l] = xs[t];
+            continue;
+        }
 #pragma unroll
         for (int t = 0; t < kDecodeMultiMaxTokens; ++t) {
             if (t < n) {
@@ -481,6 +490,7 @@ hipError_t launch_decode_multi(const Dims &d, const Params &p, int batch, int t_
     args.tiled = d.tiled;
     args.out_split = d.out_split;
     args.split_off = (size_t)batch * t_new * d.value_dim;
+    args.preconv = d.preconv;
     args.norm_eps = d.norm_eps;
     args.l2_eps = d.l2_eps;
     if (d.act_bf16) return launch_multi_dims<bf16_t>(args, d.chan_decay, d.d_k, d.d_v, batch, s);

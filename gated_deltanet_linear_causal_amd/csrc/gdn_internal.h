@@ -8,6 +8,8 @@
 
 namespace gdn {
 
+typedef uint16_t bf16_t; // (also in gdn_device.h) bf16 as its raw bits
+
 struct Dims {
     int h_k, h_v, d_k, d_v, conv_k;
     int group;      // h_v / h_k
@@ -19,6 +21,7 @@ struct Dims {
     int tiled;      // 0: key head hv / group, 1: key head hv % h_k
     int chan_decay; // 0: one decay per value head, 1: one per key channel
     int out_split;  // 1: out receives bf16 hi parts, then (after all of them) bf16 lo parts
+    int preconv;    // 1 (decode only): qkv holds silu(conv) already and the history is current
     float norm_eps, l2_eps;
 };
 
@@ -70,6 +73,46 @@ hipError_t launch_prefill(const Dims &d, const Params &p, int n_seq, int t_total
                           const void *z, const void *a, const void *b,
                           const float *state_in, float *state_out, const float *conv_in,
                           float *conv_out, void *out, void *ws, hipStream_t s);
+
+// Skinny matrix products of a mixer decode step (skinny.hip): D[M][N] =
+// sum over parts of A_part[M][K] . W[N][K]^T, bf16 operands, fp32 partial
+// products per contraction slice.  W is the concatenation of up to four
+// row blocks: output column n < N lives in w[b] at row n - wstart[b] for the
+// last b with wstart[b] <= n.
+constexpr int kSkinnyRows = 64;     // rows of A per call, at most
+constexpr int kSkinnyCols = 64;     // output columns per workgroup
+constexpr int kSkinnyMaxSplit = 16; // contraction slices, at most (K <= 16 slices)
+constexpr int kSkinnyDirectRows = 8; // up to this many rows in_proj runs as one slice
+struct SkinnyGemm {
+    const bf16_t *a[2];
+    int M, K, N;
+    const bf16_t *w[4];
+    int wstart[4];
+    float *part; // [skinny_ksplit(K, parts)][M][N]
+    int kslice;  // (set by launch_skinny_gemm)
+};
+// Adds the slices' partials of in_proj and stores them per block (qkv, z,
+// b, a), the qkv block through the causal conv + SiLU with its history
+// conv_state [M][conv_k-1][qkv columns] moved on in place.
+struct ProjEpilogue {
+    const float *part;
+    int ksplit, M, N;
+    int start[5]; // block column starts, start[4] = N
+    float *dst[4];
+    const float *conv_w;
+    float *conv_state;
+    int conv_k;
+};
+// Contraction slices of a skinny product, 0 if K cannot be split for it.
+int skinny_ksplit(int K, int nparts);
+// With epi (one A part, the whole contraction in one slice: K of 256, 512,
+// 1024 or 2048, skinny_direct_ok) the product kernel applies the in_proj
+// epilogue itself instead of storing partial products.
+bool skinny_direct_ok(int K);
+hipError_t launch_skinny_gemm(SkinnyGemm g, int nparts, const ProjEpilogue *epi, hipStream_t s);
+hipError_t launch_proj_epilogue(const ProjEpilogue &e, hipStream_t s);
+hipError_t launch_out_epilogue(const float *part, int ksplit, size_t n, void *out, int out_bf16,
+                               hipStream_t s);
 
 // Workspace of the allocation-free prefill: a static device array of this
 // many bytes per device, its address resolved once per device.

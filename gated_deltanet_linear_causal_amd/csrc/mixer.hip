@@ -225,7 +225,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t kBlasWorkspace = size_t(32) << 20;
 
 struct MixerWs {
-    size_t qkv, z, b, a, core, hl, acc, blas, prefill, total;
+    size_t qkv, z, b, a, core, hl, acc, blas, prefill, part_in, part_out, total;
 };
 
 // The core runs on fp32 activations and writes its output as bf16 hi and
@@ -262,6 +262,13 @@ MixerWs mixer_ws(const Dims &d, int hidden, int n_seq, int t_total, bool prefill
     off = align256(off + kBlasWorkspace);
     w.prefill = off;
     off = align256(off + (prefill ? prefill_workspace_bytes(core_dims(d, true), n_seq, t_total) : 0));
+    // the decode step's matrix-core projections: partial products of the
+    // contraction slices of in_proj and out_proj
+    const size_t n_in = (size_t)d.conv_dim + d.value_dim + d.h_v + (size_t)d.h_v * gw;
+    w.part_in = off;
+    off = align256(off + (prefill ? 0 : (size_t)skinny_ksplit(hidden, 1) * T * n_in * 4));
+    w.part_out = off;
+    off = align256(off + (prefill ? 0 : (size_t)skinny_ksplit(d.value_dim, 2) * T * hidden * 4));
     w.total = off;
     return w;
 }
@@ -345,7 +352,11 @@ hipError_t out_proj(const Dims &d, const Proj &pj, const MixerGemms &g, int T, c
 
 size_t mixer_workspace_bytes(const Dims &d, int hidden, int n_seq, int t_total, bool prefill)
 {
-    return mixer_ws(d, hidden, n_seq, t_total, prefill).total;
+    const size_t dec = mixer_ws(d, hidden, t_total, t_total, false).total;
+    if (!prefill) return dec;
+    // (the prefill size also covers a decode step of up to t_total sequences)
+    const size_t pre = mixer_ws(d, hidden, n_seq, t_total, true).total;
+    return pre > dec ? pre : dec;
 }
 
 hipError_t launch_mixer_prefill(const Dims &d, const Params &p, const Proj &pj, int n_seq,
@@ -366,12 +377,95 @@ hipError_t launch_mixer_prefill(const Dims &d, const Params &p, const Proj &pj, 
     return out_proj(d, pj, g, t_total, base, w, y, false, s);
 }
 
+// The decode step with its projections on the matrix cores (skinny.hip):
+// possible for up to 64 sequences, a hidden size and value_dim that split
+// into contraction slices (multiples of 256), 16-byte aligned x and
+// weights, and a core that takes the one-token path.
+static bool fused_decode_ok(const Dims &d, const Proj &pj, int batch, const void *x)
+{
+    const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(pj.w_qkv) |
+                         reinterpret_cast<uintptr_t>(pj.w_z) | reinterpret_cast<uintptr_t>(pj.w_b) |
+                         reinterpret_cast<uintptr_t>(pj.w_a) | reinterpret_cast<uintptr_t>(pj.w_out);
+    return batch <= kSkinnyRows && (al & 15) == 0 && skinny_ksplit(pj.hidden, 1) > 0 &&
+           skinny_ksplit(d.value_dim, 2) > 0 && d.h_v % 4 == 0 && // (epilogue: column quads)
+           decode_multi_lds_bytes(core_dims(d, true), 1) <= kDecodeMultiMaxLds;
+}
+
+// in_proj (one skinny product over the four weights, then the conv epilogue
+// into fp32 activations), the core on convolved activations writing bf16 hi
+// and lo parts, and out_proj over both parts with its epilogue.
+static hipError_t mixer_decode_fused(const Dims &d, const Params &p, const Proj &pj, int batch,
+                                     const void *x, float *conv_state, float *state, void *y,
+                                     char *base, const MixerWs &w, hipStream_t s)
+{
+    const int gw = d.chan_decay ? d.d_k : 1;
+    const int s1 = d.conv_dim, s2 = s1 + d.value_dim, s3 = s2 + d.h_v, n_in = s3 + d.h_v * gw;
+    SkinnyGemm g{};
+    g.a[0] = static_cast<const bf16_t *>(x);
+    g.a[1] = nullptr;
+    g.M = batch;
+    g.K = pj.hidden;
+    g.N = n_in;
+    g.w[0] = static_cast<const bf16_t *>(pj.w_qkv);
+    g.w[1] = static_cast<const bf16_t *>(pj.w_z);
+    g.w[2] = static_cast<const bf16_t *>(pj.w_b);
+    g.w[3] = static_cast<const bf16_t *>(pj.w_a);
+    g.wstart[0] = 0, g.wstart[1] = s1, g.wstart[2] = s2, g.wstart[3] = s3;
+    g.part = reinterpret_cast<float *>(base + w.part_in);
+    hipError_t e;
+    ProjEpilogue pe{};
+    pe.part = g.part;
+    pe.ksplit = skinny_ksplit(g.K, 1);
+    pe.M = batch;
+    pe.N = n_in;
+    pe.start[0] = 0, pe.start[1] = s1, pe.start[2] = s2, pe.start[3] = s3, pe.start[4] = n_in;
+    pe.dst[0] = reinterpret_cast<float *>(base + w.qkv);
+    pe.dst[1] = reinterpret_cast<float *>(base + w.z);
+    pe.dst[2] = reinterpret_cast<float *>(base + w.b);
+    pe.dst[3] = reinterpret_cast<float *>(base + w.a);
+    pe.conv_w = p.conv_w;
+    pe.conv_state = conv_state;
+    pe.conv_k = d.conv_k;
+    // A few rows: one contraction slice, the product kernel applies the
+    // epilogue (B=1: 30.6 against 34.1 us per mixer step at hidden 2048).
+    // More rows: split slices and a separate, vectorised epilogue (B=64: the
+    // product with its epilogue took 37 us, the split product and the
+    // epilogue 13.6 + 6.8 us).
+    if (batch <= kSkinnyDirectRows && skinny_direct_ok(g.K)) {
+        if ((e = launch_skinny_gemm(g, 1, &pe, s)) != hipSuccess) return e;
+    } else {
+        if ((e = launch_skinny_gemm(g, 1, nullptr, s)) != hipSuccess) return e;
+        if ((e = launch_proj_epilogue(pe, s)) != hipSuccess) return e;
+    }
+    Dims c = core_dims(d, true);
+    c.preconv = 1;
+    bf16_t *hi = reinterpret_cast<bf16_t *>(base + w.hl);
+    if ((e = launch_decode_multi(c, p, batch, 1, nullptr, base + w.qkv, base + w.z, base + w.a,
+                                 base + w.b, conv_state, conv_state, state, state, nullptr, hi, s)) !=
+        hipSuccess)
+        return e;
+    SkinnyGemm o{};
+    o.a[0] = hi;
+    o.a[1] = hi + (size_t)batch * d.value_dim;
+    o.M = batch;
+    o.K = d.value_dim;
+    o.N = pj.hidden;
+    o.w[0] = o.w[1] = o.w[2] = o.w[3] = static_cast<const bf16_t *>(pj.w_out);
+    o.wstart[0] = 0, o.wstart[1] = o.wstart[2] = o.wstart[3] = pj.hidden;
+    o.part = reinterpret_cast<float *>(base + w.part_out);
+    if ((e = launch_skinny_gemm(o, 2, nullptr, s)) != hipSuccess) return e;
+    return launch_out_epilogue(o.part, skinny_ksplit(o.K, 2), (size_t)batch * pj.hidden, y,
+                               d.out_bf16, s);
+}
+
 hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, int batch,
                                const void *x, float *conv_state, float *state, void *y, void *ws,
                                hipStream_t s)
 {
     const MixerWs w = mixer_ws(d, pj.hidden, batch, batch, false);
     char *base = static_cast<char *>(ws);
+    if (fused_decode_ok(d, pj, batch, x))
+        return mixer_decode_fused(d, p, pj, batch, x, conv_state, state, y, base, w, s);
     MixerGemms g;
     hipError_t e;
     if ((e = prepare_gemms(d, pj, batch, x, g)) != hipSuccess) return e;

@@ -87,6 +87,49 @@ def test_mixer_decode_steps(gdn):
     conv_close(C.cpu(), r["conv"])
 
 
+DECODE_LAYERS = [
+    # h_k, h_v, d, hidden, decay mode, K, batch.  The decode step projects on
+    # the matrix cores (conv in the in_proj epilogue) when hidden and
+    # value_dim are multiples of 256, H_v of 4 and batch <= 64 (hidden 4096:
+    # two contraction slices and a separate epilogue); the last three cases
+    # take the library GEMMs (hidden, batch, H_v).
+    (2, 4, 64, 256, "head", 4, 5),
+    (2, 4, 64, 256, "channel", 3, 7),
+    (1, 4, 128, 512, "head", 1, 33),
+    (4, 8, 32, 1024, "head", 2, 64),
+    (2, 4, 64, 4096, "head", 4, 3),
+    (2, 4, 32, 200, "head", 4, 3),
+    (2, 4, 64, 256, "head", 4, 70),
+    (1, 2, 128, 256, "head", 4, 4),
+]
+
+
+@pytest.mark.parametrize("v", DECODE_LAYERS, ids=lambda v: "hk%d_hv%d_d%d_H%d_%s_K%d_B%d" % v)
+def test_mixer_decode_layers(gdn, v):
+    """Four consecutive mixer decode steps against the oracle's layer run
+    over the same tokens ("oxinfer 0.0.5 src/qwen.rs", gdn_forward)."""
+    hk, hv, dd, H, mode, K, B = v
+    d = Dims(hk, hv, dd, dd, K, "sigmoid" if mode == "channel" else "silu", decay=mode)
+    steps = 4
+    case = make_case(d, [0] * B, act_dtype="bf16", seed=850 + H + B + K, decay="weak",
+                     s0_std=0.3, conv0_std=1.0)
+    proj = make_projections(d, H, seed=851 + H)
+    xs = make_hidden(steps * B, H, seed=852 + B).view(steps, B, H)
+    cfg = P.gpu_config(d, "bf16", torch.float32)
+    prm, pj = P.dev_params(case), dev_proj(proj)
+    S, C = case.S0.clone().cuda(), case.conv0.clone().cuda()
+    outs = [gdn.mixer_decode(cfg, prm, pj, xs[t].to(torch.bfloat16).cuda(), C, S)
+            for t in range(steps)]
+    torch.cuda.synchronize()
+    y = torch.stack(outs).float().cpu()
+    x_seq = xs.transpose(0, 1).reshape(B * steps, H)
+    r = oracle.mixer_layer(P.oracle_shape(d), [i * steps for i in range(B + 1)], case.params,
+                           proj, x_seq, case.S0, case.conv0, nthreads=P.n_threads())
+    P.assert_y_close(y.transpose(0, 1).reshape(B * steps, H), r["out"], "mixer decode out")
+    P.assert_state_close(S.cpu(), r["S"])
+    conv_close(C.cpu(), r["conv"])
+
+
 def test_mixer_decode_full_layer_b64(gdn):
     """The full layer (hidden 2048, H_k=16, H_v=32, d=128) for B=64, one step,
     bf16 output = RNE of the fp32 output."""
