@@ -227,3 +227,43 @@ def test_decode_batch_zero_is_noop(gdn):
                           torch.empty((0, 3, d.conv_dim), device="cuda"),
                           torch.empty((0, d.h_v, 64, 64), device="cuda"))
     assert out.shape == (0, d.value_dim)
+
+
+def test_decode_steps_replayed_as_a_graph_match_eager(gdn):
+    """The decode steps captured in a HIP graph (as the bench times the
+    launch-bound workloads) give, replay after replay with eager work in
+    between, the states and outputs of the same steps run eagerly."""
+    case = tiny_recurrent()
+    steps = 8
+    cfg = P.gpu_config(case.dims, case.act_dtype)
+    params = P.dev_params(case)
+    x = [P.to_dev(case.dec[k][:steps], case.act_dtype) for k in ("qkv", "z", "a", "b")]
+    S, C = case.S0.clone().cuda(), case.conv0.clone().cuda()
+    outs = torch.zeros((steps, 1, case.dims.value_dim), device="cuda")
+
+    def run():
+        for j in range(steps):
+            gdn.decode_step(cfg, params, x[0][j], x[1][j], x[2][j], x[3][j], C, S, out=outs[j])
+
+    S0, C0 = S.clone(), C.clone()
+    run()
+    torch.cuda.synchronize()
+    ref = (outs.clone(), S.clone(), C.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        S.copy_(S0)
+        C.copy_(C0)
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(3):
+        S.copy_(S0)
+        C.copy_(C0)
+        outs.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, ref[0]) and torch.equal(S, ref[1]) and torch.equal(C, ref[2])
