@@ -22,7 +22,7 @@
  *   - sigmoid / SiLU use the exact exponential ([exp.rs]); the pages' fast
  *     exponential is an approximation of it.
  *   - The gated-norm weight is a plain multiplier of shape [d_v], shared by
- *     all value heads ([qwen.rs] Gdn struct, "plain weight (gated norm)").
+ *     all value heads ([qwen.rs] Gdn struct, its norm weight field).
  *   - Value head hv reads key head hv / (H_v / H_k) (contiguous groups,
  *     [cpu.rs] deltanet), or hv mod H_k when the layer uses the tiled order
  *     ([qwen.rs] DeltaRule::run, `tiled`).
