@@ -29,6 +29,8 @@
 // columns 32w .. 32w+31; lane l holds column quad 8w + (l mod 8) of rows
 // l/8, l/8 + 8, ... (d_k/8 rows of 4 columns).
 
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -52,6 +54,11 @@ struct MultiArgs {
     int out_split;   // out: bf16 hi parts, then the lo parts at out + split_off
     size_t split_off;
     int preconv;     // qkv already holds silu(conv) and the history is current
+    // Row strides (elements) of the qkv, z, b and a rows of one (sequence,
+    // token); with NSPLIT = 2 each input is the sum of two partial products,
+    // the second split_stride elements after the first.
+    int ld_qkv, ld_z, ld_b, ld_a;
+    size_t split_stride;
     float norm_eps, l2_eps;
 };
 // (with one decay per key channel, a is [batch][t_new][H_v*d_k] and dt_bias
@@ -69,10 +76,11 @@ __device__ __forceinline__ float pick3(const float (&w)[3], int i)
     return i == 0 ? w[0] : (i == 1 ? w[1] : w[2]);
 }
 
-template <typename TIn, int DK, int DV, int NSLOT, bool CH>
+template <typename TIn, int DK, int DV, int NSLOT, bool CH, int NSPLIT>
 __global__ void __launch_bounds__(2 * DV * NSLOT) __attribute__((amdgpu_waves_per_eu(4)))
 decode_multi_kernel(const MultiArgs p)
 {
+    static_assert(NSPLIT == 1 || (NSPLIT == 2 && !CH), "split inputs: scalar decay only");
     constexpr int TPH = 2 * DV;     // threads per value head
     constexpr int NT = TPH * NSLOT; // threads per workgroup
     constexpr int NW = NT / 64;     // waves
@@ -126,22 +134,46 @@ decode_multi_kernel(const MultiArgs p)
     const int ngate = n * group;                   // (token, value head) pairs
     const int nzq = p.out ? ngate * C4 : 0;        // z quads
     const int nalpha = CH ? ngate * DK : 0;        // per-channel decays
-    auto gate_index = [&](int i) {
+    // (token, value head) pair i of this sequence's rows of a ([.][H_v], or
+    // [.][H_v*d_k] with one decay per key channel) and b ([.][H_v])
+    auto gate_index = [&](int i, int ld) { // b, and a with one decay per value head
         const int hv = value_head_of(hk, i % group, p.h_k, group, p.tiled);
-        return ((size_t)bs * T + i / group) * p.h_v + hv;
+        return ((size_t)bs * T + i / group) * ld + hv;
     };
-    auto out_index = [&](int q) { // quad q of the [n][group][DV] rows
+    auto out_index = [&](int q, int ld) { // quad q of the [n][group][DV] rows
         const int pair = q / C4, t = pair / group;
         const int hv = value_head_of(hk, pair % group, p.h_k, group, p.tiled);
-        return ((size_t)bs * T + t) * p.value_dim + (size_t)hv * DV + 4 * (q % C4);
+        return ((size_t)bs * T + t) * ld + (size_t)hv * DV + 4 * (q % C4);
     };
-    TIn ga0 = TIn(0), gb0 = TIn(0);
+    // an input element: one load, or the sum of the two partial products
+    const size_t ss = NSPLIT == 2 ? p.split_stride : 0;
+    auto in1 = [&](const TIn *x, size_t i) {
+        if constexpr (NSPLIT == 2)
+            return load_act(x, i) + load_act(x, i + ss);
+        else
+            return load_act(x, i);
+    };
+    auto sum2 = [&](TIn u, TIn v) {
+        if constexpr (NSPLIT == 2)
+            return act_to_f32(u) + act_to_f32(v);
+        else
+            return act_to_f32(u);
+    };
+    TIn ga0 = TIn(0), gb0 = TIn(0), ga1 = TIn(0), gb1 = TIn(0);
     if (tid < ngate) {
-        if (!CH) ga0 = pa[gate_index(tid)];
-        gb0 = pb[gate_index(tid)];
+        if (!CH) ga0 = pa[gate_index(tid, p.ld_a)];
+        gb0 = pb[gate_index(tid, p.ld_b)];
+        if constexpr (NSPLIT == 2) {
+            ga1 = pa[gate_index(tid, p.ld_a) + ss];
+            gb1 = pb[gate_index(tid, p.ld_b) + ss];
+        }
     }
     // per-channel decay inputs: element e = (pair, channel) of a [.][H_v*d_k]
-    auto alpha_index = [&](int e) { return gate_index(e / DK) * DK + e % DK; };
+    auto alpha_index = [&](int e) {
+        const int i = e / DK;
+        const int hv = value_head_of(hk, i % group, p.h_k, group, p.tiled);
+        return ((size_t)bs * T + i / group) * p.ld_a + (size_t)hv * DK + e % DK;
+    };
     constexpr int kAlphaPre = 2; // elements per thread loaded up front
     TIn gac[kAlphaPre];
 #pragma unroll
@@ -149,8 +181,11 @@ decode_multi_kernel(const MultiArgs p)
         const int e = tid + k * NT;
         gac[k] = (CH && e < nalpha) ? pa[alpha_index(e)] : TIn(0);
     }
-    RawQuad<TIn> zq0;
-    if (tid < nzq) zq0.load(pz + out_index(tid));
+    RawQuad<TIn> zq0, zq1;
+    if (tid < nzq) {
+        zq0.load(pz + out_index(tid, p.ld_z));
+        if constexpr (NSPLIT == 2) zq1.load(pz + out_index(tid, p.ld_z) + ss);
+    }
 
     // Causal conv + SiLU of the owned channels.  The window holds the last
     // three raw inputs, oldest first, and the taps are right-aligned to four
@@ -175,24 +210,31 @@ decode_multi_kernel(const MultiArgs p)
             tap[pos] = j >= 0 ? p.conv_w[(size_t)ch * K + j] : 0.0f;
         }
     };
+    const int LQ = p.ld_qkv;
     float win0[3] = {0.f, 0.f, 0.f}, tap0[4] = {0.f, 0.f, 0.f, 0.f};
-    TIn x00 = TIn(0);
+    TIn x00 = TIn(0), x01 = TIn(0);
     if (kPre && tid < nch) {
         const int ch = channel_of(tid);
         if (!p.preconv) load_conv(ch, win0, tap0);
-        if (n > 0) x00 = qkv[(size_t)bs * T * CD + ch];
+        if (n > 0) {
+            x00 = qkv[(size_t)bs * T * LQ + ch];
+            if constexpr (NSPLIT == 2) x01 = qkv[(size_t)bs * T * LQ + ch + ss];
+        }
     }
     // (the second owned channel too, when a thread has one: a channel
     // loaded after the state would make its conv, and so the gates and the
     // L2 scales, wait for all of the state; kept in separate registers, as
     // an indexed pair the step measured 5 us slower)
     float win1[3] = {0.f, 0.f, 0.f}, tap1[4] = {0.f, 0.f, 0.f, 0.f};
-    TIn x10 = TIn(0);
+    TIn x10 = TIn(0), x11 = TIn(0);
     const int l1 = tid + NT;
     if (kPre && l1 < nch) {
         const int ch = channel_of(l1);
         if (!p.preconv) load_conv(ch, win1, tap1);
-        if (n > 0) x10 = qkv[(size_t)bs * T * CD + ch];
+        if (n > 0) {
+            x10 = qkv[(size_t)bs * T * LQ + ch];
+            if constexpr (NSPLIT == 2) x11 = qkv[(size_t)bs * T * LQ + ch + ss];
+        }
     }
     if (kPre) load_state();
 
@@ -204,20 +246,20 @@ decode_multi_kernel(const MultiArgs p)
             for (int pos = 0; pos < 3; ++pos) win[pos] = win0[pos];
 #pragma unroll
             for (int pos = 0; pos < 4; ++pos) tap[pos] = tap0[pos];
-            xs[0] = act_to_f32(x00);
+            xs[0] = sum2(x00, x01);
         } else if (kPre && l == l1) {
 #pragma unroll
             for (int pos = 0; pos < 3; ++pos) win[pos] = win1[pos];
 #pragma unroll
             for (int pos = 0; pos < 4; ++pos) tap[pos] = tap1[pos];
-            xs[0] = act_to_f32(x10);
+            xs[0] = sum2(x10, x11);
         } else {
             if (!p.preconv) load_conv(ch, win, tap);
-            xs[0] = n > 0 ? load_act(qkv, (size_t)bs * T * CD + ch) : 0.0f;
+            xs[0] = n > 0 ? in1(qkv, (size_t)bs * T * LQ + ch) : 0.0f;
         }
 #pragma unroll
         for (int t = 1; t < kDecodeMultiMaxTokens; ++t)
-            xs[t] = t < n ? load_act(qkv, ((size_t)bs * T + t) * CD + ch) : 0.0f;
+            xs[t] = t < n ? in1(qkv, ((size_t)bs * T + t) * LQ + ch) : 0.0f;
         if (p.preconv) {
             // the projection has applied the conv and SiLU and moved the
             // history on already
@@ -247,10 +289,10 @@ decode_multi_kernel(const MultiArgs p)
     // fn deltanet) and z, into LDS.
     for (int i = tid; i < ngate; i += NT) {
         const int hv = value_head_of(hk, i % group, p.h_k, group, p.tiled);
-        const float br = i == tid ? act_to_f32(gb0) : load_act(pb, gate_index(i));
+        const float br = i == tid ? sum2(gb0, gb1) : in1(pb, gate_index(i, p.ld_b));
         sgate[2 * i + 0] = sigmoidf_(br);
         if (!CH) {
-            const float ar = i == tid ? act_to_f32(ga0) : load_act(pa, gate_index(i));
+            const float ar = i == tid ? sum2(ga0, ga1) : in1(pa, gate_index(i, p.ld_a));
             const float g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplusf_(ar + p.dt_bias[hv]);
             sgate[2 * i + 1] = expf(g);
         }
@@ -272,7 +314,12 @@ decode_multi_kernel(const MultiArgs p)
         }
     }
     for (int q = tid; q < nzq; q += NT) {
-        const float4 z4 = q == tid ? zq0.to_f32() : load_act4(pz, out_index(q));
+        float4 z4;
+        if constexpr (NSPLIT == 2)
+            z4 = q == tid ? zq0.to_f32() + zq1.to_f32()
+                          : load_act4(pz, out_index(q, p.ld_z)) + load_act4(pz, out_index(q, p.ld_z) + ss);
+        else
+            z4 = q == tid ? zq0.to_f32() : load_act4(pz, out_index(q, p.ld_z));
         *reinterpret_cast<float4 *>(sz + 4 * (size_t)q) = z4;
     }
     lds_sync_m();
@@ -402,9 +449,9 @@ decode_multi_kernel(const MultiArgs p)
             y.z = o[2] * rn * w4.z * gatef_(z4.z, p.gate);
             y.w = o[3] * rn * w4.w * gatef_(z4.w, p.gate);
             if (p.out_split)
-                store_split4(p.out, out_index(q), p.split_off, y);
+                store_split4(p.out, out_index(q, p.value_dim), p.split_off, y);
             else
-                store_out4(p.out, out_index(q), y, p.out_bf16);
+                store_out4(p.out, out_index(q, p.value_dim), y, p.out_bf16);
         }
     }
 }
@@ -422,7 +469,7 @@ size_t decode_multi_lds_bytes(const Dims &d, int t_new)
 }
 
 template <typename TIn, int DK, int DV, int NSLOT>
-static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int batch, hipStream_t s)
+static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int nsplit, int batch, hipStream_t s)
 {
     constexpr int NT = 2 * DV * NSLOT;
     Dims d;
@@ -431,11 +478,22 @@ static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int batch, hipStre
     d.group = a.group;
     d.chan_decay = ch;
     const size_t shmem = decode_multi_lds_bytes(d, a.t_new); // <= 64 KiB, checked by the caller
+    if (nsplit == 2) {
+        // (inputs summed from two partial products: the mixer's fp32 in_proj
+        // slices at d_k = d_v = 128)
+        if constexpr (std::is_same<TIn, float>::value && DK == 128 && DV == 128) {
+            if (ch) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 2>), dim3(batch * a.h_k),
+                               dim3(NT), shmem, s, a);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     if (ch)
-        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true>), dim3(batch * a.h_k),
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true, 1>), dim3(batch * a.h_k),
                            dim3(NT), shmem, s, a);
     else
-        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false>), dim3(batch * a.h_k),
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1>), dim3(batch * a.h_k),
                            dim3(NT), shmem, s, a);
     return hipGetLastError();
 }
@@ -449,22 +507,22 @@ static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int batch, hipStre
 // better); B=64 with the state out of cache 62.1 against 65.4 us and with
 // 8 tokens 76 against 82 us (one at a time better).
 template <typename TIn, int DK, int DV>
-static hipError_t launch_multi_slots(const MultiArgs &a, bool ch, int batch, hipStream_t s)
+static hipError_t launch_multi_slots(const MultiArgs &a, bool ch, int nsplit, int batch, hipStream_t s)
 {
     int ncu = 0;
     const hipError_t e = device_cu_count(&ncu);
     if (e != hipSuccess) return e;
     if (a.group % 2 == 0 && (long long)batch * a.h_k <= 2LL * ncu)
-        return launch_multi_t<TIn, DK, DV, 2>(a, ch, batch, s);
-    return launch_multi_t<TIn, DK, DV, 1>(a, ch, batch, s);
+        return launch_multi_t<TIn, DK, DV, 2>(a, ch, nsplit, batch, s);
+    return launch_multi_t<TIn, DK, DV, 1>(a, ch, nsplit, batch, s);
 }
 
 template <typename TIn>
-static hipError_t launch_multi_dims(const MultiArgs &a, bool ch, int dk, int dv, int batch,
+static hipError_t launch_multi_dims(const MultiArgs &a, bool ch, int nsplit, int dk, int dv, int batch,
                                     hipStream_t s)
 {
 #define GDN_MULTI_CASE(K_, V_)                                                                \
-    if (dk == K_ && dv == V_) return launch_multi_slots<TIn, K_, V_>(a, ch, batch, s);
+    if (dk == K_ && dv == V_) return launch_multi_slots<TIn, K_, V_>(a, ch, nsplit, batch, s);
     GDN_MULTI_CASE(32, 32) GDN_MULTI_CASE(32, 64) GDN_MULTI_CASE(32, 128)
     GDN_MULTI_CASE(64, 32) GDN_MULTI_CASE(64, 64) GDN_MULTI_CASE(64, 128)
     GDN_MULTI_CASE(128, 32) GDN_MULTI_CASE(128, 64) GDN_MULTI_CASE(128, 128)
@@ -510,10 +568,17 @@ hipError_t launch_decode_multi(const Dims &d, const Params &p, int batch, int t_
     args.out_split = d.out_split;
     args.split_off = (size_t)batch * t_new * d.value_dim;
     args.preconv = d.preconv;
+    const bool split = d.in_split == 2;
+    args.ld_qkv = split ? d.in_ld : d.conv_dim;
+    args.ld_z = split ? d.in_ld : d.value_dim;
+    args.ld_b = split ? d.in_ld : d.h_v;
+    args.ld_a = split ? d.in_ld : d.h_v * (d.chan_decay ? d.d_k : 1);
+    args.split_stride = split ? d.in_split_stride : 0;
     args.norm_eps = d.norm_eps;
     args.l2_eps = d.l2_eps;
-    if (d.act_bf16) return launch_multi_dims<bf16_t>(args, d.chan_decay, d.d_k, d.d_v, batch, s);
-    return launch_multi_dims<float>(args, d.chan_decay, d.d_k, d.d_v, batch, s);
+    const int nsplit = split ? 2 : 1;
+    if (d.act_bf16) return launch_multi_dims<bf16_t>(args, d.chan_decay, nsplit, d.d_k, d.d_v, batch, s);
+    return launch_multi_dims<float>(args, d.chan_decay, nsplit, d.d_k, d.d_v, batch, s);
 }
 
 } // namespace gdn

@@ -76,6 +76,9 @@ gdn_status check_config(const gdn_config *cfg, gdn::Dims &d)
     d.out_bf16 = cfg->out_dtype == GDN_BF16;
     d.out_split = 0;
     d.preconv = 0;
+    d.in_split = 1;
+    d.in_ld = 0;
+    d.in_split_stride = 0;
     d.gate = cfg->gate;
     d.tiled = cfg->head_map == GDN_HEADS_TILED;
     d.chan_decay = cfg->decay_mode == GDN_DECAY_CHANNEL;

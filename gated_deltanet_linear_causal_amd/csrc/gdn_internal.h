@@ -22,6 +22,11 @@ struct Dims {
     int chan_decay; // 0: one decay per value head, 1: one per key channel
     int out_split;  // 1: out receives bf16 hi parts, then (after all of them) bf16 lo parts
     int preconv;    // 1 (decode only): qkv holds silu(conv) already and the history is current
+    // Decode inputs as the mixer's split in_proj products (decode_multi only):
+    // in_split 2 = every input is the sum of two fp32 partial products
+    // in_split_stride elements apart, all four with row stride in_ld; else 1.
+    int in_split, in_ld;
+    size_t in_split_stride;
     float norm_eps, l2_eps;
 };
 

@@ -428,22 +428,34 @@ static hipError_t mixer_decode_fused(const Dims &d, const Params &p, const Proj 
     pe.conv_k = d.conv_k;
     // A few rows: one contraction slice, the product kernel applies the
     // epilogue (B=1: 30.6 against 34.1 us per mixer step at hidden 2048).
-    // More rows: split slices and a separate, vectorised epilogue (B=64: the
-    // product with its epilogue took 37 us, the split product and the
-    // epilogue 13.6 + 6.8 us).
-    if (batch <= kSkinnyDirectRows && skinny_direct_ok(g.K)) {
+    // More rows: split slices (B=64: the product with its epilogue took
+    // 37 us, the split product 13.6 us).  With two slices at d_k = d_v = 128
+    // the core sums them as it loads its inputs and runs the conv itself
+    // (B=64: saves the separate epilogue launch, 6.8 us); otherwise a
+    // separate, vectorised epilogue writes the convolved activations.
+    Dims c = core_dims(d, true);
+    bf16_t *hi = reinterpret_cast<bf16_t *>(base + w.hl);
+    const bool direct = batch <= kSkinnyDirectRows && skinny_direct_ok(g.K);
+    const bool core_sums = !direct && pe.ksplit == 2 && !d.chan_decay && d.d_k == 128 && d.d_v == 128;
+    if (direct) {
         if ((e = launch_skinny_gemm(g, 1, &pe, s)) != hipSuccess) return e;
     } else {
         if ((e = launch_skinny_gemm(g, 1, nullptr, s)) != hipSuccess) return e;
-        if ((e = launch_proj_epilogue(pe, s)) != hipSuccess) return e;
+        if (!core_sums && (e = launch_proj_epilogue(pe, s)) != hipSuccess) return e;
     }
-    Dims c = core_dims(d, true);
-    c.preconv = 1;
-    bf16_t *hi = reinterpret_cast<bf16_t *>(base + w.hl);
-    if ((e = launch_decode_multi(c, p, batch, 1, nullptr, base + w.qkv, base + w.z, base + w.a,
-                                 base + w.b, conv_state, conv_state, state, state, nullptr, hi, s)) !=
-        hipSuccess)
-        return e;
+    if (core_sums) {
+        c.in_split = 2;
+        c.in_ld = n_in;
+        c.in_split_stride = (size_t)batch * n_in;
+        const float *part = g.part;
+        e = launch_decode_multi(c, p, batch, 1, nullptr, part, part + s1, part + s3, part + s2,
+                                conv_state, conv_state, state, state, nullptr, hi, s);
+    } else {
+        c.preconv = 1;
+        e = launch_decode_multi(c, p, batch, 1, nullptr, base + w.qkv, base + w.z, base + w.a,
+                                base + w.b, conv_state, conv_state, state, state, nullptr, hi, s);
+    }
+    if (e != hipSuccess) return e;
     SkinnyGemm o{};
     o.a[0] = hi;
     o.a[1] = hi + (size_t)batch * d.value_dim;
