@@ -29,6 +29,7 @@ one-GPU build (the sharding design is written up, not launched).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -351,23 +352,32 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     # Decode with the Infinity Cache cold for the states: four state sets
-    # (4 x 134 MiB, more than the 256 MB cache) used in rotation.
+    # (4 x 134 MiB, more than the 256 MB cache) used in rotation, as in a
+    # model whose other layers evict a layer's state between its steps.  Timed
+    # with the state cache hint for that case (streamed: non-temporal state
+    # loads and stores) and, for comparison, with the default (cached).
     rot = 4
     S_rot = [S_dc.clone() for _ in range(rot)]
     c_rot = [c_dc.clone() for _ in range(rot)]
     cold_steps = 2 * n_sets
-    for j in range(rot):
-        gdn.decode_step(cfg, dparams, x_dc[0][j], x_dc[1][j], x_dc[2][j], x_dc[3][j], c_rot[j],
-                        S_rot[j], out=out_dc, stream=stream)
-    ev_c = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev_c[0].record(stream)
-    for j in range(cold_steps):
-        k = j % n_sets
-        gdn.decode_step(cfg, dparams, x_dc[0][k], x_dc[1][k], x_dc[2][k], x_dc[3][k],
-                        c_rot[j % rot], S_rot[j % rot], out=out_dc, stream=stream)
-    ev_c[1].record(stream)
-    torch.cuda.synchronize()
-    dc_cold_ms = ev_c[0].elapsed_time(ev_c[1]) / cold_steps
+
+    def cold_leg(c):
+        for j in range(rot):
+            gdn.decode_step(c, dparams, x_dc[0][j], x_dc[1][j], x_dc[2][j], x_dc[3][j], c_rot[j],
+                            S_rot[j], out=out_dc, stream=stream)
+        ev_c = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev_c[0].record(stream)
+        for j in range(cold_steps):
+            k = j % n_sets
+            gdn.decode_step(c, dparams, x_dc[0][k], x_dc[1][k], x_dc[2][k], x_dc[3][k],
+                            c_rot[j % rot], S_rot[j % rot], out=out_dc, stream=stream)
+        ev_c[1].record(stream)
+        torch.cuda.synchronize()
+        return ev_c[0].elapsed_time(ev_c[1]) / cold_steps
+
+    cfg_stream = dataclasses.replace(cfg, state_cache="streamed")
+    dc_cold_ms = cold_leg(cfg_stream)
+    dc_cold_cached_ms = cold_leg(cfg)
     del S_rot, c_rot
 
     def time_calls(fn, calls, warm=2):
@@ -586,7 +596,11 @@ def main():
     roof_dec_cold = dict(roof_dec, achieved=round(dec_cold_gbs, 1),
                          frac=round(dec_cold_gbs / PEAK_HBM_GBS, 4),
                          duration_us=round(dc_cold_ms * 1e3, 2), launches_timed=cold_steps,
-                         note="4 state sets in rotation (Infinity Cache cold for the state)")
+                         traffic=None,
+                         note="4 state sets in rotation (Infinity Cache cold for the state), "
+                              "state_cache=streamed (non-temporal state loads and stores); "
+                              "with the default cached hint: %.2f us"
+                              % (dc_cold_cached_ms * 1e3))
     roof_pf = {"kernel": "gdn_prefill_chunked (qknorm, tri, scan, norm launches)",
                "bound": "mfma", "achieved": round(pf_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                "unit": "TFLOP/s", "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
@@ -713,6 +727,8 @@ def main():
         "prefill_ms": round(pf_ms, 4),
         "decode_us_per_step": round(dc_ms * 1e3, 2),
         "decode_cold_us_per_step": round(dc_cold_ms * 1e3, 2),
+        "decode_cold_note": "four state sets in rotation, state_cache=streamed",
+        "decode_cold_cached_hint_us_per_step": round(dc_cold_cached_ms * 1e3, 2),
         "decode_tokens_per_s": round(B / (dc_ms * 1e-3), 1),
         "roofline": dominant,
         "roofline_note": "roofline is the kernel that takes most of the step's time (the 100 "

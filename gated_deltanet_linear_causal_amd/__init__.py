@@ -23,6 +23,7 @@ GDN_BF16, GDN_F32 = 0, 1
 GDN_GATE_SILU, GDN_GATE_SIGMOID = 0, 1
 GDN_HEADS_GROUPED, GDN_HEADS_TILED = 0, 1
 GDN_DECAY_HEAD, GDN_DECAY_CHANNEL = 0, 1
+GDN_STATE_CACHED, GDN_STATE_STREAMED = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_EINVAL", 2: "GDN_EUNSUPPORTED",
           3: "GDN_EWORKSPACE", 4: "GDN_EHIP"}
 CHUNK = 64
@@ -40,7 +41,8 @@ class _Config(ctypes.Structure):
                 ("conv_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("norm_eps", ctypes.c_float), ("l2_eps", ctypes.c_float),
-                ("head_map", ctypes.c_int32), ("decay_mode", ctypes.c_int32)]
+                ("head_map", ctypes.c_int32), ("decay_mode", ctypes.c_int32),
+                ("state_cache", ctypes.c_int32)]
 
 
 class _Params(ctypes.Structure):
@@ -124,6 +126,9 @@ class Config:
     l2_eps: float = 1e-6
     head_map: str = "grouped"   # "grouped" (hv // group) or "tiled" (hv % h_k)
     decay: str = "head"         # "head" (one decay per value head) or "channel" (per key channel)
+    # "cached" (the decode state is reread soon, from cache) or "streamed"
+    # (evicted in between, e.g. many layers: loaded and stored non-temporally)
+    state_cache: str = "cached"
 
     @property
     def gate_width(self):
@@ -151,12 +156,15 @@ class Config:
             raise ValueError(f"unknown head_map {self.head_map!r}")
         if self.decay not in ("head", "channel"):
             raise ValueError(f"unknown decay {self.decay!r}")
+        if self.state_cache not in ("cached", "streamed"):
+            raise ValueError(f"unknown state_cache {self.state_cache!r}")
         return _Config(self.h_k, self.h_v, self.d_k, self.d_v, self.conv_k,
                        code(self.act_dtype), code(self.out_dtype),
                        GDN_GATE_SIGMOID if self.gate == "sigmoid" else GDN_GATE_SILU,
                        self.norm_eps, self.l2_eps,
                        GDN_HEADS_TILED if self.head_map == "tiled" else GDN_HEADS_GROUPED,
-                       GDN_DECAY_CHANNEL if self.decay == "channel" else GDN_DECAY_HEAD)
+                       GDN_DECAY_CHANNEL if self.decay == "channel" else GDN_DECAY_HEAD,
+                       GDN_STATE_STREAMED if self.state_cache == "streamed" else GDN_STATE_CACHED)
 
 
 def _ptr(t):

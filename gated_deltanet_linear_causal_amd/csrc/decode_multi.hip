@@ -76,7 +76,7 @@ __device__ __forceinline__ float pick3(const float (&w)[3], int i)
     return i == 0 ? w[0] : (i == 1 ? w[1] : w[2]);
 }
 
-template <typename TIn, int DK, int DV, int NSLOT, bool CH, int NSPLIT>
+template <typename TIn, int DK, int DV, int NSLOT, bool CH, int NSPLIT, bool NTS>
 __global__ void __launch_bounds__(2 * DV * NSLOT) __attribute__((amdgpu_waves_per_eu(4)))
 decode_multi_kernel(const MultiArgs p)
 {
@@ -122,11 +122,22 @@ decode_multi_kernel(const MultiArgs p)
     // then spill: there the state is loaded first.)
     constexpr bool kPre = !CH;
     f32x4 s[RPT];
-    auto load_state = [&]() {
-        const float *Sin = p.state_in + head_base(value_head_of(hk, slot, p.h_k, group, p.tiled));
+    // (NTS: the state is loaded and stored non-temporally; a compile-time
+    // choice, since the compiler would merge two otherwise identical load
+    // sequences and drop the cache hint)
+    auto load_state_at = [&](const float *Sin) {
+        if constexpr (NTS) {
 #pragma unroll
-        for (int r = 0; r < RPT; ++r)
-            s[r] = *reinterpret_cast<const f32x4 *>(Sin + toff + r * 8 * DV);
+            for (int r = 0; r < RPT; ++r)
+                s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sin + toff + r * 8 * DV));
+        } else {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                s[r] = *reinterpret_cast<const f32x4 *>(Sin + toff + r * 8 * DV);
+        }
+    };
+    auto load_state = [&]() {
+        load_state_at(p.state_in + head_base(value_head_of(hk, slot, p.h_k, group, p.tiled)));
     };
     if (!kPre) load_state();
     const TIn *pa = static_cast<const TIn *>(p.a), *pb = static_cast<const TIn *>(p.b);
@@ -354,12 +365,7 @@ decode_multi_kernel(const MultiArgs p)
         const int hl = pass * NSLOT + slot;
         const int hv = value_head_of(hk, hl, p.h_k, group, p.tiled);
         const size_t head = head_base(hv);
-        if (pass > 0) {
-            const float *Sin = p.state_in + head;
-#pragma unroll
-            for (int r = 0; r < RPT; ++r)
-                s[r] = *reinterpret_cast<const f32x4 *>(Sin + toff + r * 8 * DV);
-        }
+        if (pass > 0) load_state_at(p.state_in + head);
 #pragma unroll 1
         for (int t = 0; t < n; ++t) {
             const float *ct = cb + (size_t)t * nch;
@@ -421,9 +427,15 @@ decode_multi_kernel(const MultiArgs p)
                 *reinterpret_cast<f32x4 *>(so + ((size_t)t * group + hl) * DV + 4 * c4) = o;
         }
         float *Sout = p.state_out + head;
+        if constexpr (NTS) {
 #pragma unroll
-        for (int r = 0; r < RPT; ++r)
-            *reinterpret_cast<f32x4 *>(Sout + toff + r * 8 * DV) = s[r];
+            for (int r = 0; r < RPT; ++r)
+                __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4 *>(Sout + toff + r * 8 * DV));
+        } else {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                *reinterpret_cast<f32x4 *>(Sout + toff + r * 8 * DV) = s[r];
+        }
     }
 
     // ---- 3. gated RMSNorm of every (token, value head) row ----------------
@@ -468,7 +480,7 @@ size_t decode_multi_lds_bytes(const Dims &d, int t_new)
     return sizeof(float) * ((size_t)t_new * nch + 4 * (size_t)t_new + gates + 2 * rows + alphas);
 }
 
-template <typename TIn, int DK, int DV, int NSLOT>
+template <typename TIn, int DK, int DV, int NSLOT, bool NTS>
 static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int nsplit, int batch, hipStream_t s)
 {
     constexpr int NT = 2 * DV * NSLOT;
@@ -483,17 +495,17 @@ static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int nsplit, int ba
         // slices at d_k = d_v = 128)
         if constexpr (std::is_same<TIn, float>::value && DK == 128 && DV == 128) {
             if (ch) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 2>), dim3(batch * a.h_k),
+            hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 2, NTS>), dim3(batch * a.h_k),
                                dim3(NT), shmem, s, a);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
     }
     if (ch)
-        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true, 1>), dim3(batch * a.h_k),
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true, 1, NTS>), dim3(batch * a.h_k),
                            dim3(NT), shmem, s, a);
     else
-        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1>), dim3(batch * a.h_k),
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1, NTS>), dim3(batch * a.h_k),
                            dim3(NT), shmem, s, a);
     return hipGetLastError();
 }
@@ -507,22 +519,25 @@ static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int nsplit, int ba
 // better); B=64 with the state out of cache 62.1 against 65.4 us and with
 // 8 tokens 76 against 82 us (one at a time better).
 template <typename TIn, int DK, int DV>
-static hipError_t launch_multi_slots(const MultiArgs &a, bool ch, int nsplit, int batch, hipStream_t s)
+static hipError_t launch_multi_slots(const MultiArgs &a, bool ch, int nsplit, bool nts, int batch,
+                                     hipStream_t s)
 {
     int ncu = 0;
     const hipError_t e = device_cu_count(&ncu);
     if (e != hipSuccess) return e;
     if (a.group % 2 == 0 && (long long)batch * a.h_k <= 2LL * ncu)
-        return launch_multi_t<TIn, DK, DV, 2>(a, ch, nsplit, batch, s);
-    return launch_multi_t<TIn, DK, DV, 1>(a, ch, nsplit, batch, s);
+        return nts ? launch_multi_t<TIn, DK, DV, 2, true>(a, ch, nsplit, batch, s)
+                   : launch_multi_t<TIn, DK, DV, 2, false>(a, ch, nsplit, batch, s);
+    return nts ? launch_multi_t<TIn, DK, DV, 1, true>(a, ch, nsplit, batch, s)
+               : launch_multi_t<TIn, DK, DV, 1, false>(a, ch, nsplit, batch, s);
 }
 
 template <typename TIn>
-static hipError_t launch_multi_dims(const MultiArgs &a, bool ch, int nsplit, int dk, int dv, int batch,
-                                    hipStream_t s)
+static hipError_t launch_multi_dims(const MultiArgs &a, bool ch, int nsplit, bool nts, int dk, int dv,
+                                    int batch, hipStream_t s)
 {
 #define GDN_MULTI_CASE(K_, V_)                                                                \
-    if (dk == K_ && dv == V_) return launch_multi_slots<TIn, K_, V_>(a, ch, nsplit, batch, s);
+    if (dk == K_ && dv == V_) return launch_multi_slots<TIn, K_, V_>(a, ch, nsplit, nts, batch, s);
     GDN_MULTI_CASE(32, 32) GDN_MULTI_CASE(32, 64) GDN_MULTI_CASE(32, 128)
     GDN_MULTI_CASE(64, 32) GDN_MULTI_CASE(64, 64) GDN_MULTI_CASE(64, 128)
     GDN_MULTI_CASE(128, 32) GDN_MULTI_CASE(128, 64) GDN_MULTI_CASE(128, 128)
@@ -577,8 +592,10 @@ hipError_t launch_decode_multi(const Dims &d, const Params &p, int batch, int t_
     args.norm_eps = d.norm_eps;
     args.l2_eps = d.l2_eps;
     const int nsplit = split ? 2 : 1;
-    if (d.act_bf16) return launch_multi_dims<bf16_t>(args, d.chan_decay, nsplit, d.d_k, d.d_v, batch, s);
-    return launch_multi_dims<float>(args, d.chan_decay, nsplit, d.d_k, d.d_v, batch, s);
+    const bool nts = d.nt_state;
+    if (d.act_bf16)
+        return launch_multi_dims<bf16_t>(args, d.chan_decay, nsplit, nts, d.d_k, d.d_v, batch, s);
+    return launch_multi_dims<float>(args, d.chan_decay, nsplit, nts, d.d_k, d.d_v, batch, s);
 }
 
 } // namespace gdn

@@ -53,6 +53,8 @@ gdn_status check_config(const gdn_config *cfg, gdn::Dims &d)
         return fail(GDN_EINVAL, "head_map %d is not a gdn_head_map", cfg->head_map);
     if (cfg->decay_mode != GDN_DECAY_HEAD && cfg->decay_mode != GDN_DECAY_CHANNEL)
         return fail(GDN_EINVAL, "decay_mode %d is not a gdn_decay_mode", cfg->decay_mode);
+    if (cfg->state_cache != GDN_STATE_CACHED && cfg->state_cache != GDN_STATE_STREAMED)
+        return fail(GDN_EINVAL, "state_cache %d is not a gdn_state_cache", cfg->state_cache);
     if (!(cfg->norm_eps >= 0.0f) || !std::isfinite(cfg->norm_eps) || !(cfg->l2_eps >= 0.0f) ||
         !std::isfinite(cfg->l2_eps))
         return fail(GDN_EINVAL, "norm_eps and l2_eps must be finite and >= 0");
@@ -82,6 +84,7 @@ gdn_status check_config(const gdn_config *cfg, gdn::Dims &d)
     d.gate = cfg->gate;
     d.tiled = cfg->head_map == GDN_HEADS_TILED;
     d.chan_decay = cfg->decay_mode == GDN_DECAY_CHANNEL;
+    d.nt_state = cfg->state_cache == GDN_STATE_STREAMED;
     d.norm_eps = cfg->norm_eps;
     d.l2_eps = cfg->l2_eps;
     return GDN_OK;

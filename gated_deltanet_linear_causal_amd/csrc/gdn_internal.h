@@ -27,6 +27,7 @@ struct Dims {
     // in_split_stride elements apart, all four with row stride in_ld; else 1.
     int in_split, in_ld;
     size_t in_split_stride;
+    int nt_state;   // 1: decode loads and stores the state non-temporally
     float norm_eps, l2_eps;
 };
 

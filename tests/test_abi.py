@@ -8,6 +8,7 @@ skipped whenever a GPU is visible so that a validation bug can never turn
 into a launch on bogus pointers.
 """
 import ctypes
+import os
 import subprocess
 import threading
 
@@ -96,7 +97,7 @@ def _decode(lib, cfg=None, params=None, batch=2, ptrs=None):
     (dict(d_v=256), EUNSUP), (dict(conv_k=5), EUNSUP), (dict(conv_k=0), EINVAL),
     (dict(act_dtype=7), EINVAL), (dict(gate=2), EINVAL), (dict(norm_eps=-1.0), EINVAL),
     (dict(l2_eps=float("nan")), EINVAL), (dict(head_map=2), EINVAL),
-    (dict(decay_mode=2), EINVAL)])
+    (dict(decay_mode=2), EINVAL), (dict(state_cache=2), EINVAL), (dict(state_cache=-1), EINVAL)])
 def test_decode_rejects_bad_config(lib, kw, code):
     assert _decode(lib, _cfg(**kw)) == code
     assert lib.gdn_last_error().decode() != ""
@@ -289,3 +290,20 @@ def test_last_error_is_thread_local(lib):
     th.start()
     th.join()
     assert seen["msg"] == ""
+
+
+def test_config_struct_layout_matches_header():
+    """The binding's gdn_config mirrors include/gdn.h field for field (13
+    four-byte fields, the cache hint last, zero meaning CACHED)."""
+    names = [f[0] for f in gdn._Config._fields_]
+    assert names[-1] == "state_cache" and len(names) == 13
+    assert ctypes.sizeof(gdn._Config) == 13 * 4
+    assert gdn.Config(2, 4, 64, 64).c_struct().state_cache == gdn.GDN_STATE_CACHED
+    assert gdn.Config(2, 4, 64, 64, state_cache="streamed").c_struct().state_cache == \
+        gdn.GDN_STATE_STREAMED
+    with pytest.raises(ValueError):
+        gdn.Config(2, 4, 64, 64, state_cache="warm").c_struct()
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "include", "gdn.h")).read()
+    body = hdr[hdr.index("typedef struct {\n    int32_t h_k, h_v;"):hdr.index("} gdn_config;")]
+    assert "int32_t state_cache;" in body and body.rstrip().endswith("*/")

@@ -267,3 +267,31 @@ def test_decode_steps_replayed_as_a_graph_match_eager(gdn):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(outs, ref[0]) and torch.equal(S, ref[1]) and torch.equal(C, ref[2])
+
+
+@pytest.mark.parametrize("batch,t_new", [(64, 1), (64, 4), (8, 1), (2, 3)])
+def test_state_cache_hint_changes_nothing_but_speed(gdn, batch, t_new):
+    """The streamed state hint (non-temporal state loads and stores) gives
+    the cached path's outputs, states and conv histories bit for bit, for
+    single steps and multi-token calls, one head per pass and two side by
+    side."""
+    import dataclasses
+    case = decode_batch(steps=2 * t_new, batch=batch)
+    cfg = P.gpu_config(case.dims, case.act_dtype)
+    params = P.dev_params(case)
+    x = [P.to_dev(case.dec[k], case.act_dtype) for k in ("qkv", "z", "a", "b")]
+    res = []
+    for c in (cfg, dataclasses.replace(cfg, state_cache="streamed")):
+        S, C = case.S0.clone().cuda(), case.conv0.clone().cuda()
+        ys = []
+        for call in range(2):
+            xs = [v[call * t_new:(call + 1) * t_new] for v in x]
+            if t_new == 1:
+                ys.append(gdn.decode_step(c, params, *(v[0] for v in xs), C, S))
+            else:
+                xm = [v.transpose(0, 1).contiguous() for v in xs]
+                ys.append(gdn.decode_multi(c, params, *xm, C, S))
+        torch.cuda.synchronize()
+        res.append((torch.stack(ys).cpu(), S.cpu(), C.cpu()))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
