@@ -95,7 +95,7 @@ typedef enum { GDN_DECAY_HEAD = 0, GDN_DECAY_CHANNEL = 1 } gdn_decay_mode;
  * non-temporally.  Only the speed differs (the results are bit-identical);
  * the persistent kernel for very wide head groups and the prefill ignore it.
  * Measured at B=64, H_k=16, H_v=32, d=128: CACHED 45.2 us per step with the
- * state cached, 60.8 us without; STREAMED 53.0 us and 54.2 us. */
+ * state cached, 60.8 us without; STREAMED 50.7 us and 52.0 us. */
 typedef enum { GDN_STATE_CACHED = 0, GDN_STATE_STREAMED = 1 } gdn_state_cache;
 
 typedef struct {
