@@ -410,11 +410,15 @@ decode_multi_kernel(const MultiArgs p)
                 }
             }
             // (one row at a time: the scheduler would otherwise form all
-            // the k delta^T products first and double the live registers)
+            // the k delta^T products first and double the live registers;
+            // the decayed state is the accumulator, so each new value stays
+            // in its own register: with the product as the accumulator the
+            // values moved one register per token and the loop began with
+            // 64 moves)
 #pragma unroll
             for (int r = 0; r < RPT; ++r) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s[r][e] = fmaf(alpha, s[r][e], kk[r] * delta[e]);
+                for (int e = 0; e < 4; ++e) s[r][e] = fmaf(kk[r], delta[e], alpha * s[r][e]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (p.ckpt) {
