@@ -334,9 +334,11 @@ decode_multi_kernel(const MultiArgs p)
         *reinterpret_cast<float4 *>(sz + 4 * (size_t)q) = z4;
     }
     lds_sync_m();
-    // L2 scales of q and k and q^.k^ per token (a wave per token).
+    // L2 scales of q and k and q^.k^ per token (a wave per token); the
+    // token's q and k rows in LDS are then scaled in place to q^ and k^, so
+    // the token loop reads them ready to use.
     for (int t = wave; t < n; t += NW) {
-        const float *ct = cb + (size_t)t * nch;
+        float *ct = cb + (size_t)t * nch;
         float ssq = 0.f, ssk = 0.f, dqk = 0.f;
         for (int i = lane; i < DK; i += 64) {
             const float qv = ct[i], kv = ct[DK + i];
@@ -347,12 +349,16 @@ decode_multi_kernel(const MultiArgs p)
         ssq = group_sum<64>(ssq);
         ssk = group_sum<64>(ssk);
         dqk = group_sum<64>(dqk);
+        const float qs = rsqrtf(ssq + p.l2_eps) * rsqrtf((float)DK);
+        const float ks = rsqrtf(ssk + p.l2_eps);
         if (lane == 0) {
-            const float qs = rsqrtf(ssq + p.l2_eps) * rsqrtf((float)DK);
-            const float ks = rsqrtf(ssk + p.l2_eps);
             scal[4 * t + 0] = qs;
             scal[4 * t + 1] = ks;
             scal[4 * t + 2] = dqk * qs * ks; // q^ . k^
+        }
+        for (int i = lane; i < DK; i += 64) {
+            ct[i] *= qs;
+            ct[DK + i] *= ks;
         }
     }
     lds_sync_m();
@@ -368,8 +374,8 @@ decode_multi_kernel(const MultiArgs p)
         if (pass > 0) load_state_at(p.state_in + head);
 #pragma unroll 1
         for (int t = 0; t < n; ++t) {
-            const float *ct = cb + (size_t)t * nch;
-            const float qs = scal[4 * t + 0], ks = scal[4 * t + 1], qk = scal[4 * t + 2];
+            const float *ct = cb + (size_t)t * nch; // q^, k^ (scaled), v
+            const float qk = scal[4 * t + 2];
             const float beta = sgate[2 * (t * group + hl) + 0];
             // scalar decay: folded into the sums below; per-channel decay:
             // applied to the state rows first
@@ -384,9 +390,9 @@ decode_multi_kernel(const MultiArgs p)
 #pragma unroll
             for (int r = 0; r < RPT; ++r) {
                 const int i = rg + 8 * r;
-                kk[r] = ct[DK + i] * ks;
+                kk[r] = ct[DK + i];
                 mk += kk[r] * s[r];
-                mq += (ct[i] * qs) * s[r];
+                mq += ct[i] * s[r];
             }
             // sum over the 8 row groups of the wave (lanes l, l^8, l^16, ...)
 #pragma unroll
