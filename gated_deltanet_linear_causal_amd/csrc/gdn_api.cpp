@@ -380,6 +380,8 @@ gdn_status prefill_common(const gdn_config *cfg, const gdn_params *params, int32
     if (t_total > 0 && ((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(z) |
                          reinterpret_cast<uintptr_t>(out)) & 15))
         return fail(GDN_EINVAL, "qkv, z and out must be 16-byte aligned");
+    if (t_total > 0 && d.chan_decay && (reinterpret_cast<uintptr_t>(a) & 15))
+        return fail(GDN_EINVAL, "a must be 16-byte aligned with per-channel decay");
     if (n_seq > 0 && (!state_out || (d.conv_k > 1 && !conv_out)))
         return fail(GDN_EINVAL, "state_out (and conv_out when K > 1) are required");
     const size_t need = gdn::prefill_workspace_bytes(d, n_seq, t_total);

@@ -41,6 +41,7 @@
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
+#include <algorithm>
 #include <mutex>
 
 namespace gdn {
@@ -287,25 +288,26 @@ struct PrefillArgs {
 
 // Conv taps of 4 channels starting at ch, right-aligned to 4 taps (zero
 // taps in front when K < 4): w[e][j] multiplies the input 3-j tokens back.
+// Every tap is loaded unconditionally (K = 4: one 16-byte row per channel;
+// K < 4: clamped single loads, the missing front taps selected to zero), so
+// the loads stay in flight until the conv uses them.
 __device__ __forceinline__ void load_taps4(const PrefillArgs &p, int ch, float (&w)[4][4])
 {
     const int K = p.conv_k;
-    if (K == 4) { // four 16-byte rows (ch is a multiple of 4): one load per channel
+    f32x4 t[4];
+    if (K == 4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const f32x4 t = ld4(p.conv_w + (size_t)(ch + e) * 4);
+        for (int e = 0; e < 4; ++e) t[e] = ld4(p.conv_w + (size_t)(ch + e) * 4);
+    } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[e][j] = t[j];
-        }
-        return;
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t[e][j] = p.conv_w[(size_t)(ch + e) * K + max(j - (4 - K), 0)];
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int jj = j - (4 - K);
-            w[e][j] = jj >= 0 ? p.conv_w[(size_t)(ch + e) * K + jj] : 0.0f;
-        }
+        for (int j = 0; j < 4; ++j) w[e][j] = j >= 4 - K ? t[e][j] : 0.0f;
 }
 
 // Raw inputs of 4 channels at sequence position tau (< 0 reaches into the
@@ -525,152 +527,260 @@ qknorm_kernel(const PrefillArgs p)
 //   P'[i][j] = sum_d q[i][d] k[j][d] e^{G[i][d] - G[j][d]}     (j <= i),
 // with G[t][d] the prefix over the chunk of g[t][d] = c softplus(a + dt_bias)
 // (G <= 0, non-increasing in t), so no Gram matrix can be shared by the
-// value heads of a group.  One workgroup per (chunk, value head, sequence),
-// 512 threads (the fp32 rows fill 100 KB of LDS, so one workgroup per CU;
-// eight waves keep two per SIMD):
+// value heads of a group.  A workgroup (16 waves at d_k = 128, 8 below; its
+// fp32 rows fill ~110 KB of LDS, so one per CU) walks up to 8 consecutive
+// chunks of one (value head, sequence), issuing each chunk's input loads
+// while the previous chunk is processed.  Per chunk:
 //   1. conv + SiLU + L2 norm of the chunk's q and k rows (fp32 in LDS) and
 //      the per-channel prefix G;
 //   2. A' and P': 16x16 blocks below the diagonal on the matrix cores with
 //      both factors taken relative to the last row r of the column block
 //      (e^{G[i]-G[r]} <= 1 for i > r, e^{G[r]-G[j]} <= 1 for j <= r, so
-//      nothing overflows), diagonal blocks with one exponential per
+//      nothing overflows); the diagonal blocks the same way at the level of
+//      4-row sub-blocks, and inside the sub-blocks one exponential per
 //      (i, j, d);
 //   3. the fragments the later kernels read: (k^ (.) e^G)^T for W, q^ (.) e^G
 //      for the read-out, (k^ (.) e^{G_C-G})^T for the state update, and the
 //      chunk decay e^{G_C} of each channel.
 // ---------------------------------------------------------------------------
-template <int DK> constexpr size_t kda_smem_bytes() { return 3 * (size_t)kC * (DK + 4) * 4; }
+// LDS: the q, k and G rows (fp32, stride d_k + 4), the head's conv taps
+// (q then k channels, four taps each), its dt_bias row and the three
+// incoming history rows of its q and k channels (first chunk only)
+template <int DK> constexpr size_t kda_smem_bytes()
+{
+    return 3 * (size_t)kC * (DK + 4) * 4 + 2 * DK * 16 + DK * 4 + 3 * 2 * DK * 4;
+}
 // Waves of kda_intra: its LDS rows allow one workgroup per CU, so at d_k = 128
 // it runs 16 waves (twice the latency hiding of 8 for the same LDS).
 template <int DK> constexpr int kda_waves() { return DK == 128 ? 16 : 8; }
 
+// Lane roles of kda_intra (from the thread index): the conv rows and
+// channels it loads, its gate channel and part, its fragment row and quad.
+template <int DK> struct KdaLane {
+    static constexpr int NW = kda_waves<DK>(), LPT = DK / 4, TPI = 64 / LPT;
+    static constexpr int TPL = kC / (NW * TPI), NPART = 64 * NW / DK, TPP = kC / NPART;
+    static constexpr int GL = DK / 8;            // lanes per gate row (8 channels each)
+    int tid, lane, col, kq, c8, ch, r0, gd, gpart, gt, g8;
+    bool isk;
+    __device__ __forceinline__ KdaLane(int t, int wave, int hk, int h_k)
+    {
+        tid = t;
+        lane = t & 63;
+        col = lane & 15;
+        kq = lane >> 4;
+        const int sub = lane / LPT, ll = lane % LPT;
+        isk = ll >= DK / 8;
+        c8 = (isk ? ll - DK / 8 : ll) * 8;
+        ch = (isk ? h_k * DK : 0) + hk * DK + c8;
+        r0 = kC / NW * wave + TPL * sub;
+        gd = t % DK;
+        gpart = t / DK;
+        gt = t / GL;
+        g8 = 8 * (t % GL);
+    }
+};
+
 template <typename TIn, int DK>
 __global__ void __launch_bounds__(64 * kda_waves<DK>())
-kda_intra_kernel(const PrefillArgs p)
+kda_intra_kernel(const PrefillArgs p, int per)
 {
-    constexpr int NW = kda_waves<DK>();      // waves
+    typedef KdaLane<DK> Lane;
+    constexpr int NW = Lane::NW;             // waves
     constexpr int RQ = DK + 4;               // fp32 LDS row stride
-    constexpr int LPT = DK / 4;              // lanes per token row (8 channels each)
-    constexpr int TPI = 64 / LPT;            // token rows per wave pass
-    constexpr int TPL = kC / (NW * TPI);     // consecutive tokens per lane
+    constexpr int TPL = Lane::TPL;           // consecutive tokens per lane
     constexpr int WIN = TPL + 3;             // raw rows a lane reads
     constexpr int KS = DK / 32, MTS = DK / 16;
-    constexpr int NPART = 64 * NW / DK, TPP = kC / NPART; // gate prefix: parts of the chunk
-    const int c = blockIdx.x, hv = blockIdx.y, n = blockIdx.z;
+    constexpr int TPP = Lane::TPP;           // gate prefix: tokens per part of the chunk
+    const int hv = blockIdx.y, n = blockIdx.z;
     const int s0 = p.cu[n], L = p.cu[n + 1] - s0;
-    if (c * kC >= L) return;
-    const int t0 = s0 + c * kC;
-    const int Lc = min(kC, L - c * kC);
+    const int cbeg = blockIdx.x * per, cend = min(cbeg + per, (L + kC - 1) / kC);
+    if (cbeg >= cend) return;
     const int hk = key_head_of(hv, p.h_k, p.group, p.tiled);
-    const int slot = s0 / kC + n + c;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, kq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float *sQ = reinterpret_cast<float *>(smem);
     float *sK = sQ + kC * RQ;
     float *sG = sK + kC * RQ;
-
-    // ---- loads: raw q/k rows (as the scalar-decay path) and gate inputs
-    const int sub = lane / LPT, ll = lane % LPT;
-    const bool isk = ll >= DK / 8;
-    const int c8 = (isk ? ll - DK / 8 : ll) * 8;
-    const int ch = (isk ? p.h_k * DK : 0) + hk * DK + c8;
+    float *sW = sG + kC * RQ;
+    float *sDt = sW + 8 * DK;
+    float *sH = sDt + DK;
     const TIn *x = static_cast<const TIn *>(p.qkv);
-    const int r0 = kC / NW * wave + TPL * sub;
-    const int tl0 = c * kC + r0;
-    typedef typename RawAct<TIn>::type RawT;
-    RawT raw[WIN][2];
-#pragma unroll
-    for (int j = 0; j < WIN; ++j) {
-        const int tau = min(max(tl0 - 3 + j, 0), L - 1);
-        const size_t base = (size_t)(s0 + tau) * p.conv_dim + ch;
-        RawAct<TIn>::load8(x, base, raw[j][0], raw[j][1]);
-    }
     const TIn *pa = static_cast<const TIn *>(p.a);
-    const int gd = tid % DK, gpart = tid / DK;
-    float araw[TPP];
-#pragma unroll
-    for (int tt = 0; tt < TPP; ++tt) {
-        const int t = gpart * TPP + tt;
-        araw[tt] = t < Lc ? load_act(pa, (size_t)(t0 + t) * p.h_v * DK + (size_t)hv * DK + gd) : 0.0f;
-    }
-    float w0[4][4], w1[4][4];
-    load_taps4(p, ch, w0);
-    load_taps4(p, ch + 4, w1);
-    const float extra = isk ? 1.0f : rsqrtf((float)DK);
 
-    // ---- 1. conv + SiLU + L2 norm, fp32 rows (zero past the sequence end)
-    {
-        f32x4 xv[WIN][2];
+    // ---- per-head constants: conv taps (in LDS), gate parameters
+    const int tid = threadIdx.x;
+    if (tid < 2 * DK) {
+        const int ct = (tid >= DK ? p.h_k * DK : 0) + hk * DK + (tid % DK);
+        f32x4 t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int jj = j - (4 - p.conv_k);
+            t[j] = jj >= 0 ? p.conv_w[(size_t)ct * p.conv_k + jj] : 0.0f;
+        }
+        *reinterpret_cast<f32x4 *>(sW + 4 * tid) = t;
+    }
+    if (tid < DK) sDt[tid] = p.dt_bias[(size_t)hv * DK + tid];
+    if (cbeg == 0) // the raw inputs 3, 2, 1 tokens before the sequence
+        for (int i = tid; i < 3 * 2 * DK / 4; i += 64 * NW) {
+            const int j = i / (2 * DK / 4), c4 = 4 * (i % (2 * DK / 4));
+            const int chh = (c4 >= DK ? p.h_k * DK : 0) + hk * DK + c4 % DK;
+            *reinterpret_cast<f32x4 *>(sH + j * 2 * DK + c4) = raw4(p, x, n, s0, j - 3, chh);
+        }
+    const float coef = decay_coef_of(p.a_log, p.decay_coef, hv);
+
+    // Raw q/k rows (as the scalar-decay path) and gate inputs of chunk cc.
+    // A workgroup walks the chunks [cbeg, cend) of its head; each chunk's
+    // loads are issued while the previous chunk is still being processed,
+    // so their latency and the previous chunk's stores overlap its work.
+    // (fp32 inputs take twice the registers: in flight across the Gram phase
+    // they would spill, so they are loaded when the chunk starts)
+    constexpr bool kPrefetch = sizeof(TIn) == 2;
+    typedef typename RawAct<TIn>::type RawT;
+    RawT raw[WIN][2], araw[2];
+    auto load_chunk = [&](int cc, const Lane &q) {
+        const int tl = cc * kC + q.r0, lc = min(kC, L - cc * kC);
 #pragma unroll
         for (int j = 0; j < WIN; ++j) {
-            xv[j][0] = RawAct<TIn>::to_f32(raw[j][0]);
-            xv[j][1] = RawAct<TIn>::to_f32(raw[j][1]);
+            const int tau = min(max(tl - 3 + j, 0), L - 1);
+            const size_t base = (size_t)(s0 + tau) * p.conv_dim + q.ch;
+            RawAct<TIn>::load8(x, base, raw[j][0], raw[j][1]);
         }
-        if (tl0 < 3) {
+        // gate inputs: 8 channels of token gt (rows past the end, and the
+        // spare threads when d_k < 64, re-read the last row: unused)
+        const int t = min(q.gt, lc - 1);
+        RawAct<TIn>::load8(pa, (size_t)(s0 + cc * kC + t) * p.h_v * DK + (size_t)hv * DK + q.g8, araw[0],
+                           araw[1]);
+    };
+    if (kPrefetch) load_chunk(cbeg, Lane(tid, wave, hk, p.h_k));
+    lds_barrier(); // taps, dt_bias and history stored
+
+    for (int c = cbeg;;) {
+        // The lane roles are recomputed per chunk from an opaque zero, which
+        // keeps the compiler from hoisting their address arithmetic out of
+        // the chunk loop (held there, it spills, and every spill reload
+        // waits for the loads in flight).
+        int lz;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(lz));
+        const Lane q(tid + lz, wave, hk, p.h_k);
+        const int lane = q.lane, col = q.col, kq = q.kq, c8 = q.c8, ch = q.ch, r0 = q.r0;
+        const int gd = q.gd, gpart = q.gpart;
+        const bool isk = q.isk;
+        const float extra = isk ? 1.0f : rsqrtf((float)DK);
+        const int Lc = min(kC, L - c * kC);
+        const int slot = s0 / kC + n + c;
+        const int tl0 = c * kC + r0;
+        if (!kPrefetch) load_chunk(c, q);
+
+        // ---- 1. conv + SiLU + L2 norm, fp32 rows (zero past the sequence end)
+        {
+            f32x4 xv[WIN][2];
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
-                if (tl0 - 3 + j < 0) {
-                    xv[j][0] = raw4(p, x, n, s0, tl0 - 3 + j, ch);
-                    xv[j][1] = raw4(p, x, n, s0, tl0 - 3 + j, ch + 4);
+            for (int j = 0; j < WIN; ++j) {
+                xv[j][0] = RawAct<TIn>::to_f32(raw[j][0]);
+                xv[j][1] = RawAct<TIn>::to_f32(raw[j][1]);
+            }
+            if (tl0 < 3) { // (from LDS: a global load here would wait for every store in flight)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    if (tl0 - 3 + j < 0) {
+                        const float *h = sH + (tl0 + j) * 2 * DK + (isk ? DK : 0) + c8;
+                        xv[j][0] = ld4(h);
+                        xv[j][1] = ld4(h + 4);
+                    }
+            }
+            float w0[4][4], w1[4][4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f32x4 ta = ld4(sW + 4 * ((isk ? DK : 0) + c8 + e));
+                const f32x4 tb = ld4(sW + 4 * ((isk ? DK : 0) + c8 + 4 + e));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    w0[e][j] = ta[j];
+                    w1[e][j] = tb[j];
                 }
+            }
+#pragma unroll
+            for (int k = 0; k < TPL; ++k) {
+                const int r = r0 + k, tl = tl0 + k;
+                const f32x4 xa[4] = {xv[k][0], xv[k + 1][0], xv[k + 2][0], xv[k + 3][0]};
+                const f32x4 xb[4] = {xv[k][1], xv[k + 1][1], xv[k + 2][1], xv[k + 3][1]};
+                const f32x4 ca = conv4(w0, xa), cb = conv4(w1, xb);
+                float ss = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ss += ca[e] * ca[e] + cb[e] * cb[e];
+                ss = row_sum<DK / 8>(ss);
+                const float sc = tl < L ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
+                float *dst = (isk ? sK : sQ) + r * RQ + c8;
+                *reinterpret_cast<f32x4 *>(dst) = ca * sc;
+                *reinterpret_cast<f32x4 *>(dst + 4) = cb * sc;
+            }
         }
+        // per-channel log-decays g (zero past the end), then their prefix
+        // within each part of the chunk, then the parts' offsets
+        if (q.gt < kC) {
+            const f32x4 ga = RawAct<TIn>::to_f32(araw[0]), gb = RawAct<TIn>::to_f32(araw[1]);
+            const f32x4 da = ld4(sDt + q.g8), db = ld4(sDt + q.g8 + 4);
+            f32x4 oa, ob;
 #pragma unroll
-        for (int k = 0; k < TPL; ++k) {
-            const int r = r0 + k, tl = tl0 + k;
-            const f32x4 xa[4] = {xv[k][0], xv[k + 1][0], xv[k + 2][0], xv[k + 3][0]};
-            const f32x4 xb[4] = {xv[k][1], xv[k + 1][1], xv[k + 2][1], xv[k + 3][1]};
-            const f32x4 ca = conv4(w0, xa), cb = conv4(w1, xb);
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ss += ca[e] * ca[e] + cb[e] * cb[e];
-            ss = row_sum<DK / 8>(ss);
-            const float sc = tl < L ? rsqrtf(ss + p.l2_eps) * extra : 0.0f;
-            float *dst = (isk ? sK : sQ) + r * RQ + c8;
-            *reinterpret_cast<f32x4 *>(dst) = ca * sc;
-            *reinterpret_cast<f32x4 *>(dst + 4) = cb * sc;
-        }
-    }
-    // per-channel log-decays and their prefix within each part of the chunk
-    {
-        const float coef = decay_coef_of(p.a_log, p.decay_coef, hv);
-        const float dtb = p.dt_bias[(size_t)hv * DK + gd];
-        float G = 0.0f;
-#pragma unroll
-        for (int tt = 0; tt < TPP; ++tt) {
-            const int t = gpart * TPP + tt;
-            if (t < Lc) { // g = 0 past the end
+            for (int e = 0; e < 8; ++e) {
                 // softplus as everywhere else: x above 20, below it
                 // max(x, 0) + log(1 + e^{-|x|}) with the hardware exp/log
-                // (absolute error ~1e-7; 8192 of them per workgroup)
-                const float x = araw[tt] + dtb;
-                G += coef * (x > 20.0f ? x : fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))));
+                // (absolute error ~1e-7; 8192 of them per chunk)
+                const float xg = (e < 4 ? ga[e] : gb[e - 4]) + (e < 4 ? da[e] : db[e - 4]);
+                const float g = q.gt < Lc ? coef * (xg > 20.0f ? xg : fmaxf(xg, 0.0f) +
+                                                    __logf(1.0f + __expf(-fabsf(xg))))
+                                          : 0.0f;
+                if (e < 4) oa[e] = g; else ob[e - 4] = g;
             }
-            sG[t * RQ + gd] = G;
+            *reinterpret_cast<f32x4 *>(sG + q.gt * RQ + q.g8) = oa;
+            *reinterpret_cast<f32x4 *>(sG + q.gt * RQ + q.g8 + 4) = ob;
         }
-    }
-    __syncthreads();
-    {
-        float off = 0.0f;
-        for (int pp = 0; pp < gpart; ++pp) off += sG[((pp + 1) * TPP - 1) * RQ + gd];
-        __syncthreads();
-        if (gpart > 0)
+        // the next chunk's loads go out now (its raw rows and gates are
+        // free); no barrier below waits for them
+        const bool more = c + 1 < cend;
+        if (kPrefetch && more) load_chunk(c + 1, q);
+        lds_barrier();
+        {
+            float G = 0.0f;
 #pragma unroll
-            for (int tt = 0; tt < TPP; ++tt) sG[(gpart * TPP + tt) * RQ + gd] += off;
-    }
-    __syncthreads();
+            for (int tt = 0; tt < TPP; ++tt) {
+                const int t = gpart * TPP + tt;
+                G += sG[t * RQ + gd];
+                sG[t * RQ + gd] = G;
+            }
+        }
+        lds_barrier();
+        {
+            float off = 0.0f;
+            for (int pp = 0; pp < gpart; ++pp) off += sG[((pp + 1) * TPP - 1) * RQ + gd];
+            lds_barrier();
+            if (gpart > 0)
+#pragma unroll
+                for (int tt = 0; tt < TPP; ++tt) sG[(gpart * TPP + tt) * RQ + gd] += off;
+        }
+        lds_barrier();
 
-    // ---- 2. decayed Gram tiles
-    // (waves 0-5 also take the off-diagonal blocks, so they set the end of
-    // this phase: issue priority 3 for them took kda_intra 211 -> 205 us at
-    // T=4096)
-    if (wave < 6) __builtin_amdgcn_s_setprio(3);
-    float *gram = p.ws_gram + ((size_t)hv * p.ns + slot) * (2 * kC * kC);
-    {
-        // blocks (I, J), I > J, on the matrix cores: wave w < 6 takes pair
-        // w of (1,0) (2,0) (3,0) (2,1) (3,1) (3,2)
-        if (wave < 6) {
-            const int pr = wave;
+        // ---- 2. decayed Gram tiles, in 22 jobs of three kinds:
+        //  off(pr), pr < 6: the 16x16 blocks (I, J), I > J, pair pr of
+        //   (1,0) (2,0) (3,0) (2,1) (3,1) (3,2), on the matrix cores with both
+        //   factors relative to the last row r of column block J
+        //   (e^{G_i-G_r} <= 1, e^{G_r-G_j} <= 1: nothing overflows however
+        //   strong the decay);
+        //  diag(m), m < 12: diagonal block b = m / 3 split into 4-row
+        //   sub-blocks, the pairs (i, j) with j in sub-block J = m % 3 and i
+        //   in a later one, on the matrix cores relative to J's last row r
+        //   (rows scaled by e^{G_i-G_r}, the 4 columns by e^{G_r-G_j}; one
+        //   exponential per (lane, d), its sign set by the lane's role); the
+        //   mirrored entries above the diagonal are written as zeros;
+        //  within(b), b < 4: the 10 pairs j <= i inside each sub-block of
+        //   diagonal block b, one per lane with one exponential per (i, j, d)
+        //   (e^{G_i-G_j} <= 1); lanes 40-63 write the 24 zeros above the
+        //   diagonal inside the sub-blocks.
+        // An off or within job costs about two diag jobs; with 16 waves:
+        // waves 0-5 off, 6-9 within, 10-15 two diag jobs each; with 8: waves
+        // 0-5 off + two diag, 6-7 two within.
+        float *gram = p.ws_gram + ((size_t)hv * p.ns + slot) * (2 * kC * kC);
+        auto job_off = [&](int pr) {
             const int bI = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
             const int bJ = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
             const int r = 16 * bJ + 15, i = 16 * bI + col, j = 16 * bJ + col;
@@ -703,90 +813,141 @@ kda_intra_kernel(const PrefillArgs p)
                 gram[ri * kC + cj] = aa[e];
                 gram[kC * kC + ri * kC + cj] = ap[e];
             }
-        }
-        // diagonal blocks: wave w takes block w % 4 and columns 2 (w / 4),
-        // 2 (w / 4) + 1 of each column quad; lane (row col, quad kq); one
-        // exponential per (i, j, d), computed for every lane and masked (a
-        // term with j > i may overflow, so it is selected away, never
-        // multiplied); zero above the diagonal
-        // (with 16 waves, one column of each quad per wave)
-        constexpr int JJ = 16 / NW;
-        const int b = wave & 3, jh = wave >> 2, i = 16 * b + col;
-        float acc_a[JJ], acc_p[JJ];
-        bool live[JJ];
+        };
+        auto job_diag = [&](int m) {
+            const int b = m / 3, J = m % 3;
+            const int r = 16 * b + 4 * J + 3, i = 16 * b + col;
+            const bool arow = col > 4 * J + 3, bcol = (col >> 2) == J;
+            f32x4 aa = {0.f, 0.f, 0.f, 0.f}, ap = aa;
 #pragma unroll
-        for (int jj = 0; jj < JJ; ++jj) {
-            acc_a[jj] = acc_p[jj] = 0.0f;
-            live[jj] = 4 * kq + JJ * jh + jj <= col;
-        }
-        for (int d4 = 0; d4 < DK / 4; ++d4) {
-            const f32x4 ki = ld4(sK + i * RQ + 4 * d4), qi = ld4(sQ + i * RQ + 4 * d4);
-            const f32x4 gi = ld4(sG + i * RQ + 4 * d4);
+            for (int st = 0; st < KS; ++st) {
+                const int d0 = 32 * st + 8 * kq;
+                float va[8], vq[8], vb[8];
 #pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) {
-                const int j = 16 * b + 4 * kq + JJ * jh + jj;
-                const f32x4 kj = ld4(sK + j * RQ + 4 * d4), gj = ld4(sG + j * RQ + 4 * d4);
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4 gr = ld4(sG + r * RQ + d0 + 4 * h), gi = ld4(sG + i * RQ + d0 + 4 * h);
+                    const f32x4 ki = ld4(sK + i * RQ + d0 + 4 * h), qi = ld4(sQ + i * RQ + d0 + 4 * h);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float ex = __expf(gi[e] - gj[e]);
-                    const float w = live[jj] ? kj[e] * ex : 0.0f;
-                    acc_a[jj] = fmaf(ki[e], w, acc_a[jj]);
-                    acc_p[jj] = fmaf(qi[e], w, acc_p[jj]);
+                    for (int e = 0; e < 4; ++e) {
+                        const float ex = __expf(arow ? gi[e] - gr[e] : gr[e] - gi[e]);
+                        va[4 * h + e] = arow ? ki[e] * ex : 0.0f;
+                        vq[4 * h + e] = arow ? qi[e] * ex : 0.0f;
+                        vb[4 * h + e] = bcol ? ki[e] * ex : 0.0f;
+                    }
                 }
+                const Frag fb = split8(vb);
+                aa = mma3(split8(va), fb, aa);
+                ap = mma3(split8(vq), fb, ap);
             }
-        }
-#pragma unroll
-        for (int jj = 0; jj < JJ; ++jj) {
-            const int j = 16 * b + 4 * kq + JJ * jh + jj;
-            gram[i * kC + j] = live[jj] ? acc_a[jj] : 0.0f;
-            gram[kC * kC + i * kC + j] = live[jj] ? acc_p[jj] : 0.0f;
-        }
-    }
-
-    // ---- 3. decayed operand fragments and the chunk decay
-    __builtin_amdgcn_s_setprio(0);
-    {
-        const size_t fbase = ((size_t)hv * p.ns + slot) * (2 * kC * DK) + lane * 8;
-        // (k^ (.) e^G)^T for W, and (k^ (.) e^{G_C - G})^T for the state
-        // update: lane (i, q) of fragment (rb, s) holds tokens 32 s + 8 q + e
-        // of channel 16 rb + i
-        for (int f = wave; f < MTS * 2; f += NW) {
-            const int st = f & 1, rb = f >> 1;
-            const int d = 16 * rb + col, t = 32 * st + 8 * kq;
-            const float gC = sG[(kC - 1) * RQ + d];
-            float vw[8], vs[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float kv = sK[(t + e) * RQ + d], g = sG[(t + e) * RQ + d];
-                vw[e] = kv * __expf(g);
-                vs[e] = kv * __expf(gC - g);
-            }
-            const Frag a = split8(vw), bq = split8(vs);
-            const int fi = (rb * 2 + st) * 2;
-            *reinterpret_cast<bf16x8 *>(p.ws_kw + fbase + (size_t)fi * 512) = a.hi;
-            *reinterpret_cast<bf16x8 *>(p.ws_kw + fbase + (size_t)(fi + 1) * 512) = a.lo;
-            *reinterpret_cast<bf16x8 *>(p.ws_ktf + fbase + (size_t)fi * 512) = bq.hi;
-            *reinterpret_cast<bf16x8 *>(p.ws_ktf + fbase + (size_t)(fi + 1) * 512) = bq.lo;
-        }
-        // q^ (.) e^G, d_k-permuted: lane (row col, q) of fragment (rb, s) holds
-        // channels 32 s + 4 q + e and 32 s + 16 + 4 q + e of row 16 rb + col
-        for (int f = wave; f < 4 * KS; f += NW) {
-            const int st = f % KS, rb = f / KS;
-            const int t = 16 * rb + col, d0 = 32 * st + 4 * kq;
-            const f32x4 q0 = ld4(sQ + t * RQ + d0), q1 = ld4(sQ + t * RQ + d0 + 16);
-            const f32x4 g0 = ld4(sG + t * RQ + d0), g1 = ld4(sG + t * RQ + d0 + 16);
-            float v[8];
+            // accumulator lane: rows 4 kq + e, column col of the block
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[e] = q0[e] * __expf(g0[e]);
-                v[4 + e] = q1[e] * __expf(g1[e]);
+                const int ri = 4 * kq + e, at = (16 * b + ri) * kC + 16 * b + col;
+                if (ri > 4 * J + 3 && (col >> 2) == J) {
+                    gram[at] = aa[e];
+                    gram[kC * kC + at] = ap[e];
+                }
+                if ((ri >> 2) == J && col > 4 * J + 3) {
+                    gram[at] = 0.0f;
+                    gram[kC * kC + at] = 0.0f;
+                }
             }
-            const Frag fq = split8(v);
-            *reinterpret_cast<bf16x8 *>(p.ws_qf + fbase + (size_t)(2 * f) * 512) = fq.hi;
-            *reinterpret_cast<bf16x8 *>(p.ws_qf + fbase + (size_t)(2 * f + 1) * 512) = fq.lo;
+        };
+        auto job_within = [&](int b) {
+            if (lane < 40) {
+                const int sb = lane / 10, pp = lane % 10;
+                const int il = pp >= 6 ? 3 : (pp >= 3 ? 2 : (pp >= 1 ? 1 : 0));
+                const int jl = pp - il * (il + 1) / 2;
+                const int i = 16 * b + 4 * sb + il, j = 16 * b + 4 * sb + jl;
+                float acc_a = 0.0f, acc_p = 0.0f;
+                for (int d4 = 0; d4 < DK / 4; ++d4) {
+                    const f32x4 ki = ld4(sK + i * RQ + 4 * d4), qi = ld4(sQ + i * RQ + 4 * d4);
+                    const f32x4 gi = ld4(sG + i * RQ + 4 * d4);
+                    const f32x4 kj = ld4(sK + j * RQ + 4 * d4), gj = ld4(sG + j * RQ + 4 * d4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float w = kj[e] * __expf(gi[e] - gj[e]);
+                        acc_a = fmaf(ki[e], w, acc_a);
+                        acc_p = fmaf(qi[e], w, acc_p);
+                    }
+                }
+                gram[i * kC + j] = acc_a;
+                gram[kC * kC + i * kC + j] = acc_p;
+            } else {
+                const int u = lane - 40, sb = u / 6, pu = u % 6;
+                const int il = pu < 3 ? 0 : (pu < 5 ? 1 : 2);
+                const int jl = pu < 3 ? pu + 1 : (pu < 5 ? pu - 1 : 3);
+                const int i = 16 * b + 4 * sb + il, j = 16 * b + 4 * sb + jl;
+                gram[i * kC + j] = 0.0f;
+                gram[kC * kC + i * kC + j] = 0.0f;
+            }
+        };
+        if (NW == 16) {
+            if (wave < 6) {
+                job_off(wave);
+            } else if (wave < 10) {
+                job_within(wave - 6);
+            } else {
+                job_diag(2 * (wave - 10));
+                job_diag(2 * (wave - 10) + 1);
+            }
+        } else {
+            if (wave < 6) {
+                job_off(wave);
+                job_diag(2 * wave);
+                job_diag(2 * wave + 1);
+            } else {
+                job_within(2 * (wave - 6));
+                job_within(2 * (wave - 6) + 1);
+            }
         }
-        if (tid < DK)
-            p.ws_gf[((size_t)hv * p.ns + slot) * (2 * kC) + tid] = __expf(sG[(kC - 1) * RQ + tid]);
+        // ---- 3. decayed operand fragments and the chunk decay
+        {
+            const size_t fbase = ((size_t)hv * p.ns + slot) * (2 * kC * DK) + lane * 8;
+            // (k^ (.) e^G)^T for W, and (k^ (.) e^{G_C - G})^T for the state
+            // update: lane (i, q) of fragment (rb, s) holds tokens 32 s + 8 q + e
+            // of channel 16 rb + i
+            for (int f = wave; f < MTS * 2; f += NW) {
+                const int st = f & 1, rb = f >> 1;
+                const int d = 16 * rb + col, t = 32 * st + 8 * kq;
+                const float gC = sG[(kC - 1) * RQ + d];
+                float vw[8], vs[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float kv = sK[(t + e) * RQ + d], g = sG[(t + e) * RQ + d];
+                    vw[e] = kv * __expf(g);
+                    vs[e] = kv * __expf(gC - g);
+                }
+                const Frag a = split8(vw), bq = split8(vs);
+                const int fi = (rb * 2 + st) * 2;
+                *reinterpret_cast<bf16x8 *>(p.ws_kw + fbase + (size_t)fi * 512) = a.hi;
+                *reinterpret_cast<bf16x8 *>(p.ws_kw + fbase + (size_t)(fi + 1) * 512) = a.lo;
+                *reinterpret_cast<bf16x8 *>(p.ws_ktf + fbase + (size_t)fi * 512) = bq.hi;
+                *reinterpret_cast<bf16x8 *>(p.ws_ktf + fbase + (size_t)(fi + 1) * 512) = bq.lo;
+            }
+            // q^ (.) e^G, d_k-permuted: lane (row col, q) of fragment (rb, s) holds
+            // channels 32 s + 4 q + e and 32 s + 16 + 4 q + e of row 16 rb + col
+            for (int f = wave; f < 4 * KS; f += NW) {
+                const int st = f % KS, rb = f / KS;
+                const int t = 16 * rb + col, d0 = 32 * st + 4 * kq;
+                const f32x4 q0 = ld4(sQ + t * RQ + d0), q1 = ld4(sQ + t * RQ + d0 + 16);
+                const f32x4 g0 = ld4(sG + t * RQ + d0), g1 = ld4(sG + t * RQ + d0 + 16);
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = q0[e] * __expf(g0[e]);
+                    v[4 + e] = q1[e] * __expf(g1[e]);
+                }
+                const Frag fq = split8(v);
+                *reinterpret_cast<bf16x8 *>(p.ws_qf + fbase + (size_t)(2 * f) * 512) = fq.hi;
+                *reinterpret_cast<bf16x8 *>(p.ws_qf + fbase + (size_t)(2 * f + 1) * 512) = fq.lo;
+            }
+            if (q.tid < DK)
+                p.ws_gf[((size_t)hv * p.ns + slot) * (2 * kC) + q.tid] = __expf(sG[(kC - 1) * RQ + q.tid]);
+        }
+        if (!more) break;
+        ++c;
+        lds_barrier(); // this chunk's LDS reads are done before the next one's writes
     }
 }
 
@@ -832,24 +993,25 @@ tri_kernel(const PrefillArgs p)
     // ---- loads of the first phases: gates (wave 0) and Gram rows --------
     const TIn *pa = static_cast<const TIn *>(p.a);
     const TIn *pb = static_cast<const TIn *>(p.b);
-    float a_raw = 0.0f, b_raw = 0.0f;
-    if (wave == 0 && lane < Lc) {
-        const size_t gi = (size_t)(t0 + lane) * p.h_v + hv;
-        if (!KDA) a_raw = load_act(pa, gi);
-        b_raw = load_act(pb, gi);
-    }
+    // (every wave loads them, rows past the end clamped to the last one and
+    // masked where used: a load under a branch would be waited for at once)
+    const size_t gi = (size_t)(t0 + min(lane, Lc - 1)) * p.h_v + hv;
+    const float a_raw = KDA ? 0.0f : load_act(pa, gi), b_raw = load_act(pb, gi);
+    const float dt_b = KDA ? 0.0f : p.dt_bias[hv];
     // Gram rows: thread (i, jq) holds row i, columns 16 jq .. 16 jq + 15 of
-    // tiles on or below the diagonal.
+    // tiles on or below the diagonal.  A thread whose tile lies above the
+    // diagonal reads the diagonal tile of its row instead (finite values,
+    // all multiplied by the zero mask below; unconditional loads are not
+    // waited for where they are issued).
     const int gi_ = tid >> 2, gq = tid & 3;
-    const bool glive = gq <= (gi_ >> 4);
     f32x4 gkk[4], gqk[4];
     {
         const float *g = p.ws_gram + ((size_t)(KDA ? hv : hk) * p.ns + slot) * (2 * kC * kC) +
-                         gi_ * kC + 16 * gq;
+                         gi_ * kC + 16 * min(gq, gi_ >> 4);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            gkk[m] = glive ? ld4(g + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
-            gqk[m] = glive ? ld4(g + kC * kC + 4 * m) : f32x4{0.f, 0.f, 0.f, 0.f};
+            gkk[m] = ld4(g + 4 * m);
+            gqk[m] = ld4(g + kC * kC + 4 * m);
         }
     }
     // ---- loads needed only after the solve, issued right after the Gram
@@ -900,7 +1062,7 @@ tri_kernel(const PrefillArgs p)
         float beta = 0.0f, g = 0.0f;
         if (lane < Lc) {
             beta = sigmoidf_(b_raw);
-            g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplusf_(a_raw + p.dt_bias[hv]);
+            g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplusf_(a_raw + dt_b);
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -1537,6 +1699,14 @@ __global__ void __launch_bounds__(256) state_pass_kernel(const float *__restrict
     sout[i] = sin ? sin[i] : 0.0f;
 }
 
+// Chunks one kda_intra workgroup walks through: as many as keeps about one
+// workgroup per CU (its LDS rows allow no second one), at most 8 so that
+// the last round of a packed batch stays short.
+static int kda_chunks_per_block(int nch_max, int heads, int ncu)
+{
+    return std::max(1, std::min(8, (int)((long long)nch_max * heads / std::max(ncu, 1))));
+}
+
 template <typename TIn, int DK, int DV, bool KDA>
 static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total, int max_len,
                                    hipStream_t s)
@@ -1557,9 +1727,12 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, int n_seq, int t_total,
         const int nch_max = (max_len + kC - 1) / kC;
         const dim3 grid_v((max_len + kC - 1) / kC, a.h_v, n_seq);
         if (KDA) {
-            hipLaunchKernelGGL((kda_intra_kernel<TIn, DK>), grid_v, dim3(64 * kda_waves<DK>()),
-                               kda_smem_bytes<DK>(),
-                               s, a);
+            int ncu = 0;
+            if ((e = device_cu_count(&ncu)) != hipSuccess) return e;
+            const int per = kda_chunks_per_block(nch_max, a.h_v * n_seq, ncu);
+            const dim3 grid_c((nch_max + per - 1) / per, a.h_v, n_seq);
+            hipLaunchKernelGGL((kda_intra_kernel<TIn, DK>), grid_c, dim3(64 * kda_waves<DK>()),
+                               kda_smem_bytes<DK>(), s, a, per);
         } else {
             const dim3 grid_k((nch_max + kQkChunks - 1) / kQkChunks, a.h_k, n_seq);
             hipLaunchKernelGGL((qknorm_kernel<TIn, DK>), grid_k, dim3(256), qknorm_smem_bytes<DK>(),

@@ -240,7 +240,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_config *cfg, int32_t n_seq,
  *   cu_seqlens_host / _dev: as in gdn_conv_update.
  *   qkv [t_total][conv_dim], z [t_total][H_v*d_v], a, b [t_total][H_v];
  *     qkv, z and out are read and written in 16-byte pieces and must be
- *     16-byte aligned (GDN_EINVAL otherwise).
+ *     16-byte aligned (GDN_EINVAL otherwise); with GDN_DECAY_CHANNEL so
+ *     must a ([t_total][H_v*d_k], read in 16-byte rows too).
  *   state_in [n_seq][H_v][d_k][d_v] fp32, or NULL for zeros;
  *   state_out, same shape: each sequence's final state.  May equal
  *     state_in (in place) but must not partially overlap it.

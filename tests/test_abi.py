@@ -203,14 +203,15 @@ def test_mixer_rejects_bad_arguments(lib):
     assert st == EINVAL and "overlap" in lib.gdn_last_error().decode()
 
 
-def _prefill(lib, cu, t_total, cfg=None, chunk=64, ws=(_P[9], 1 << 40), outs=None, qkv=_P[0]):
+def _prefill(lib, cu, t_total, cfg=None, chunk=64, ws=(_P[9], 1 << 40), outs=None, qkv=_P[0],
+             a=_P[2]):
     c = cfg or _cfg()
     cu_h = np.asarray(cu, dtype=np.int32)
     n = len(cu) - 1
     o = outs or dict(state_in=_P[4], state_out=_P[5], conv_in=_P[6], conv_out=_P[7], out=_P[8])
     return lib.gdn_prefill_chunked(
         ctypes.byref(c), ctypes.byref(_params()), chunk, n, t_total,
-        cu_h.ctypes.data_as(ctypes.c_void_p), _P[14], qkv, _P[1], _P[2], _P[3],
+        cu_h.ctypes.data_as(ctypes.c_void_p), _P[14], qkv, _P[1], a, _P[3],
         o["state_in"], o["state_out"], o["conv_in"], o["conv_out"], o["out"], ws[0],
         ws[1], None)
 
@@ -236,6 +237,9 @@ def test_prefill_rejects_chunk_workspace_and_aliases(lib):
     assert _prefill(lib, [0, 10], 10, outs=o) == EINVAL   # partial state overlap
     # activations are read in 16-byte pieces
     assert _prefill(lib, [0, 10], 10, qkv=ctypes.c_void_p(_P[0].value + 8)) == EINVAL
+    assert "16-byte" in lib.gdn_last_error().decode()
+    # with one decay per key channel a ([T][H_v*d_k]) is read in 16-byte rows too
+    assert _prefill(lib, [0, 10], 10, cfg=_cfg(decay_mode=1), a=ctypes.c_void_p(_P[2].value + 2)) == EINVAL
     assert "16-byte" in lib.gdn_last_error().decode()
 
 

@@ -91,13 +91,17 @@ DECODE_LAYERS = [
     # h_k, h_v, d, hidden, decay mode, K, batch.  The decode step projects on
     # the matrix cores (conv in the in_proj epilogue) when hidden and
     # value_dim are multiples of 256, H_v of 4 and batch <= 64 (hidden 4096:
-    # two contraction slices and a separate epilogue); the last three cases
-    # take the library GEMMs (hidden, batch, H_v).
+    # four contraction slices and a separate epilogue; hidden 2048 with
+    # d = 128 above 8 sequences: two slices that the recurrence kernel sums
+    # while it loads them); the last three cases take the library GEMMs
+    # (hidden, batch, H_v).
     (2, 4, 64, 256, "head", 4, 5),
     (2, 4, 64, 256, "channel", 3, 7),
     (1, 4, 128, 512, "head", 1, 33),
     (4, 8, 32, 1024, "head", 2, 64),
     (2, 4, 64, 4096, "head", 4, 3),
+    (1, 4, 128, 2048, "head", 4, 20),
+    (2, 4, 128, 2048, "head", 2, 9),
     (2, 4, 32, 200, "head", 4, 3),
     (2, 4, 64, 256, "head", 4, 70),
     (1, 2, 128, 256, "head", 4, 4),

@@ -165,6 +165,31 @@ def test_prefill_per_channel_decay_t1024_all_heads(gdn):
     np.testing.assert_array_equal(conv.numpy(), r["conv"])
 
 
+KDA_WALK = [
+    # h_k, h_v, d, act, lengths: enough (chunk, value head) pairs that each
+    # kda_intra workgroup walks two or three chunks of its head (on 256 CUs),
+    # with partial last chunks and several sequences
+    (4, 8, 128, "bf16", [1500, 1409, 700]),
+    (4, 8, 64, "f32", [2000, 1000, 33]),
+]
+
+
+@pytest.mark.parametrize("v", KDA_WALK, ids=lambda v: "hk%d_hv%d_d%d_%s_%s" % (*v[:4], "-".join(map(str, v[4]))))
+def test_prefill_per_channel_decay_chunk_walk(gdn, v):
+    """Per-channel decay with workgroups that process several consecutive
+    chunks of a head (the next chunk's inputs loaded during the current
+    one), weak decay so that every chunk's operands reach the output."""
+    hk, hv, dd, act, lengths = v
+    d = Dims(hk, hv, dd, dd, 4, "sigmoid", decay="channel")
+    case = make_case(d, lengths, act_dtype=act, seed=702 + dd, decay="weak", s0_std=0.1,
+                     conv0_std=1.0)
+    y, S, conv = run_prefill(gdn, case)
+    r = P.run_oracle(case)
+    P.assert_y_close(y, r["y"])
+    P.assert_state_close(S, r["S"])
+    np.testing.assert_array_equal(conv.numpy(), r["conv"])
+
+
 def test_prefill_zero_state_pointers_and_empty_sequences(gdn):
     """NULL state_in / conv_in mean zeros; empty sequences pass their state
     through unchanged."""
