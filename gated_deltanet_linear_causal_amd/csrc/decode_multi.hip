@@ -91,11 +91,12 @@ __device__ __forceinline__ float pick3(const float (&w)[3], int i)
     return i == 0 ? w[0] : (i == 1 ? w[1] : w[2]);
 }
 
-template <typename TIn, int DK, int DV, int NSLOT, bool CH, int NSPLIT, bool NTS>
+template <typename TIn, int DK, int DV, int NSLOT, bool CH, int NSPLIT, bool NTS, bool UT>
 __global__ void __launch_bounds__(2 * DV * NSLOT) __attribute__((amdgpu_waves_per_eu(4)))
 decode_multi_kernel(const MultiArgs p)
 {
     static_assert(NSPLIT == 1 || (NSPLIT == 2 && !CH), "split inputs: scalar decay only");
+    static_assert(!UT || !CH, "the in-call UT form: scalar decay only");
     constexpr int TPH = 2 * DV;     // threads per value head
     constexpr int NT = TPH * NSLOT; // threads per workgroup
     constexpr int NW = NT / 64;     // waves
@@ -123,6 +124,13 @@ decode_multi_kernel(const MultiArgs p)
     float *sz = sgate + 2 * ((T * group + 1) & ~1);        // [T][group][DV] z
     float *so = sz + (size_t)T * group * DV;               // [T][group][DV] pre-norm readout
     float *salpha = so + (size_t)T * group * DV;           // [T][group][DK] decays (per channel)
+    // in-call UT form: token Grams, per-head factors, per-wave M/R tiles
+    float *sgk = salpha + (CH ? (size_t)T * group * DK : 0); // [8][8] k^_t . k^_j
+    float *sgq = sgk + 64;                                   // [8][8] q^_t . k^_j
+    float *sfr = sgq + 64;                                   // [group][8][8] r_tj = gamma_t / gamma_j
+    float *sfg = sfr + 64 * group;                           // [group][8] gamma_t
+    float *sfk = sfg + 8 * group;                            // [group][8] gamma_{n-1} / gamma_t
+    float *smr = sfk + 8 * group;                            // [NW][16][17]
 
     // ---- 1. loads, conv, gates, L2 scales ---------------------------------
     // State rows are addressed as a uniform head base plus a 32-bit lane
@@ -140,8 +148,29 @@ decode_multi_kernel(const MultiArgs p)
     // (NTS: the state is loaded and stored non-temporally; a compile-time
     // choice, since the compiler would merge two otherwise identical load
     // sequences and drop the cache hint)
+    // UT layout: s[2 rt + c2] is the 16x16 tile (row block rt, the wave's
+    // column block c2) as the accumulator of a 16x16x16 product holds it:
+    // lane (j, kq) has rows 16 rt + 4 kq + e of column 32 wv + 16 c2 + j.
+    // (addressed as a uniform row-block base plus one lane offset plus
+    // immediate offsets, so that no per-element addresses stay live)
+    const int ucol = lane & 15, ukq = lane >> 4;
+    const int ulane = 4 * ukq * DV + 32 * wv + ucol;
+    auto ut_at = [&](auto *S, int i, int e) {
+        auto *Sr = S + (size_t)16 * (i >> 1) * DV; // uniform
+        return Sr + ulane + e * DV + 16 * (i & 1);
+    };
     auto load_state_at = [&](const float *Sin) {
-        if constexpr (NTS) {
+        if constexpr (UT) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (NTS)
+                        s[i][e] = __builtin_nontemporal_load(ut_at(Sin, i, e));
+                    else
+                        s[i][e] = *ut_at(Sin, i, e);
+                }
+        } else if constexpr (NTS) {
 #pragma unroll
             for (int r = 0; r < RPT; ++r)
                 s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sin + toff + r * 8 * DV));
@@ -377,87 +406,237 @@ decode_multi_kernel(const MultiArgs p)
         }
     }
     lds_sync_m();
+    if constexpr (UT) {
+        if (n > 0) {
+            // the tokens' Grams on the matrix cores (wave 0): D[i][j] =
+            // x_i . k^_j with x_i = k^_i (i < 8) or q^_{i-8}; entries of
+            // tokens past n are not used
+            if (wave == 0) {
+                const int ti = min(ucol & 7, n - 1);
+                const float *xa = cb + (size_t)ti * nch + (ucol < 8 ? DK : 0) + 4 * ukq;
+                const float *xb = cb + (size_t)ti * nch + DK + 4 * ukq;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < DK; c += 16)
+                    acc = mma3k16(split4(*reinterpret_cast<const f32x4 *>(xa + c)),
+                                  split4(*reinterpret_cast<const f32x4 *>(xb + c)), acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (ucol < 8) sgk[(4 * ukq + e) * 8 + ucol] = acc[e]; // (sgq = sgk + 64)
+            }
+            // every head's decay products: thread (h, t) forms gamma_t, the
+            // row r_t. and gamma_{n-1} / gamma_t from the head's alphas
+            if (tid < 8 * group) {
+                const int h = tid >> 3, t = tid & 7;
+                float al[kDecodeMultiMaxTokens];
+#pragma unroll
+                for (int i = 0; i < kDecodeMultiMaxTokens; ++i)
+                    al[i] = sgate[2 * (min(i, n - 1) * group + h) + 1];
+                float g = 1.0f, ks = 1.0f, r = 1.0f;
+#pragma unroll
+                for (int i = 0; i < kDecodeMultiMaxTokens; ++i) {
+                    if (i <= t && i < n) g *= al[i];
+                    if (i > t && i < n) ks *= al[i];
+                }
+                float *row = sfr + (h * 8 + t) * 8;
+#pragma unroll
+                for (int j = kDecodeMultiMaxTokens - 1; j >= 0; --j) {
+                    row[j] = j <= t ? r : 0.0f;
+                    if (j <= t && j > 0) r *= al[j]; // r_{t,j-1} = r_tj alpha_j
+                }
+                sfg[h * 8 + t] = g;
+                sfk[h * 8 + t] = t < n ? ks : 0.0f;
+            }
+        }
+        lds_sync_m();
+    }
 
-    // ---- 2. the delta rule over the tokens, per value head ----------------
-    //   m = S_old^T k^,  r = S_old^T q^,  delta = beta (v - alpha m),
-    //   o = alpha r + (q^.k^) delta  (= S_new^T q^),  S_new = alpha S_old + k^ delta^T
+    if constexpr (UT) {
+    // ---- 2. the call's tokens in the in-chunk (UT) form, per value head ---
+    // ("oxinfer 0.0.5 src/qwen.rs", DeltaRule::run over t tokens, unrolled):
+    // with gamma_t = alpha_0 ... alpha_t and r_tj = gamma_t / gamma_j,
+    //   M = S_0^T [k^_t],  R = S_0^T [q^_t]                     (matrix cores)
+    //   delta_t = beta_t (v_t - gamma_t M_t - sum_{j<t} r_tj (k^_t.k^_j) delta_j)
+    //   o_t = gamma_t R_t + sum_{j<=t} r_tj (q^_t.k^_j) delta_j
+    //   S_n = gamma_{n-1} S_0 + sum_j r_{n-1,j} k^_j delta_j^T    (matrix cores)
+    // which is the token-by-token rule of the other branch, reassociated.
+    // Each wave owns 32 whole columns (two 16-column blocks), so M and R
+    // need no sum across waves; a column's delta and o are solved by one
+    // lane through LDS.
     const int npass = group / NSLOT;
+    float *mr = smr + (size_t)wave * (16 * 17);
     for (int pass = 0; pass < npass; ++pass) {
         const int hl = pass * NSLOT + slot;
         const int hv = value_head_of(hk, hl, p.h_k, group, p.tiled);
         const size_t head = head_base(hv);
         if (pass > 0) load_state_at(p.state_in + head);
-#pragma unroll 1
-        for (int t = 0; t < n; ++t) {
-            const float *ct = cb + (size_t)t * nch; // q^, k^ (scaled), v
-            const float qk = scal[4 * t + 2];
-            const float beta = sgate[2 * (t * group + hl) + 0];
-            // scalar decay: folded into the sums below; per-channel decay:
-            // applied to the state rows first
-            const float alpha = CH ? 1.0f : sgate[2 * (t * group + hl) + 1];
-            if (CH) {
-                const float *al = salpha + ((size_t)t * group + hl) * DK;
+        const float *fr = sfr + 64 * hl, *fg = sfg + 8 * hl, *fk = sfk + 8 * hl;
+        if (n > 0) {
+            const float gN = fg[n - 1];
+            const int ucol0 = ucol, ukq0 = ukq;
 #pragma unroll
-                for (int r = 0; r < RPT; ++r) s[r] = al[rg + 8 * r] * s[r];
-            }
-            float kk[RPT]; // k^ of this thread's rows, for S^T k^ and the update
-            f32x4 mk = {0.f, 0.f, 0.f, 0.f}, mq = mk;
+            for (int c2 = 0; c2 < 2; ++c2) {
+                // (lane indices from an opaque zero: their address arithmetic
+                // is recomputed here instead of being hoisted out of the
+                // loops and spilled)
+                int lz;
+                asm volatile("s_mov_b32 %0, 0" : "=s"(lz));
+                const int ucol = ucol0 + lz, ukq = ukq0 + lz;
+                const int v0 = 32 * wv + 16 * c2; // first column of the block in the head
+                const int tok = ucol & 7, tokc = min(tok, n - 1);
+                const bool tlive = tok < n, isq = ucol >= 8;
+                // M and R: D[v][j] = sum_rows S_0[row][v] x_j[row], x_j = k^_j
+                // (j < 8) or q^_{j-8}, zero for tokens past n
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                const int i = rg + 8 * r;
-                kk[r] = ct[DK + i];
-                mk += kk[r] * s[r];
-                mq += ct[i] * s[r];
-            }
-            // sum over the 8 row groups of the wave (lanes l, l^8, l^16, ...)
+                for (int rt = 0; rt < DK / 16; ++rt) {
+                    const f32x4 xv = *reinterpret_cast<const f32x4 *>(cb + (size_t)tokc * nch + (isq ? 0 : DK) +
+                                                                      16 * rt + 4 * ukq);
+                    const f32x4 bz = {0.f, 0.f, 0.f, 0.f};
+                    acc = mma3k16(split4(s[2 * rt + c2]), split4(tlive ? xv : bz), acc);
+                }
+                // lane (j, kq): columns v0 + 4 kq + e of M (j < 8) or R (j >= 8)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                mk[e] = rowgroup_sum(mk[e]);
-                mq[e] = rowgroup_sum(mq[e]);
-            }
-            const f32x4 v4 = *reinterpret_cast<const f32x4 *>(ct + 2 * DK + hl * DV + 4 * c4);
-            f32x4 delta, o;
+                for (int e = 0; e < 4; ++e) mr[(4 * ukq + e) * 17 + ucol] = acc[e];
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                // delta and o of column v0 + lane, token after token (lanes 0-15)
+                if (lane < 16) {
+                    const int v = v0 + lane;
+                    const float *row = mr + lane * 17;
+                    float d[kDecodeMultiMaxTokens];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (CH) {
-                    delta[e] = beta * (v4[e] - mk[e]);
-                    o[e] = mq[e] + qk * delta[e];
-                } else {
-                    delta[e] = beta * (v4[e] - alpha * mk[e]);
-                    o[e] = fmaf(alpha, mq[e], qk * delta[e]);
+                    for (int t = 0; t < kDecodeMultiMaxTokens; ++t) {
+                        d[t] = 0.0f;
+                        if (t < n) {
+                            float x = cb[(size_t)t * nch + 2 * DK + hl * DV + v] - fg[t] * row[t];
+#pragma unroll
+                            for (int j = 0; j < t; ++j) x = fmaf(-fr[8 * t + j] * sgk[8 * t + j], d[j], x);
+                            d[t] = sgate[2 * (t * group + hl)] * x;
+                            float o = fg[t] * row[8 + t];
+#pragma unroll
+                            for (int j = 0; j <= t; ++j) o = fmaf(fr[8 * t + j] * sgq[8 * t + j], d[j], o);
+                            so[((size_t)t * group + hl) * DV + v] = o;
+                        }
+                        // (token by token: hoisting every token's factor
+                        // reads ahead would hold ~60 more registers)
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+#pragma unroll
+                    for (int t = 0; t < kDecodeMultiMaxTokens; ++t) mr[lane * 17 + t] = d[t];
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                // S <- gamma_{n-1} S + K~ Delta^T: A[row][t] = r_{n-1,t} k^_t[row],
+                // B[t][v] = delta_t of column v0 + v (tokens 8-15 zero)
+                f32x4 dv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dv[e] = ukq < 2 ? mr[ucol * 17 + 4 * ukq + e] : 0.0f;
+                const Frag4 fb = split4(dv);
+#pragma unroll
+                for (int rt = 0; rt < DK / 16; ++rt) {
+                    f32x4 av;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 4 * ukq + e;
+                        av[e] = fk[min(t, 7)] * cb[(size_t)min(t, n - 1) * nch + DK + 16 * rt + ucol];
+                    }
+                    s[2 * rt + c2] = mma3k16(split4(av), fb, gN * s[2 * rt + c2]);
                 }
             }
-            // (one row at a time: the scheduler would otherwise form all
-            // the k delta^T products first and double the live registers;
-            // the decayed state is the accumulator, so each new value stays
-            // in its own register: with the product as the accumulator the
-            // values moved one register per token and the loop began with
-            // 64 moves)
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s[r][e] = fmaf(kk[r], delta[e], alpha * s[r][e]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (p.ckpt) {
-                float *cp = p.ckpt + (((size_t)bs * T + t) * p.h_v + hv) * DK * DV;
-#pragma unroll
-                for (int r = 0; r < RPT; ++r)
-                    *reinterpret_cast<f32x4 *>(cp + toff + r * 8 * DV) = s[r];
-            }
-            if (rg == 0)
-                *reinterpret_cast<f32x4 *>(so + ((size_t)t * group + hl) * DV + 4 * c4) = o;
         }
         float *Sout = p.state_out + head;
-        if constexpr (NTS) {
 #pragma unroll
-            for (int r = 0; r < RPT; ++r)
-                __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4 *>(Sout + toff + r * 8 * DV));
-        } else {
+        for (int i = 0; i < RPT; ++i)
 #pragma unroll
-            for (int r = 0; r < RPT; ++r)
-                *reinterpret_cast<f32x4 *>(Sout + toff + r * 8 * DV) = s[r];
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (NTS)
+                    __builtin_nontemporal_store(s[i][e], ut_at(Sout, i, e));
+                else
+                    *ut_at(Sout, i, e) = s[i][e];
+            }
+    }
+    } else {
+        // ---- 2. the delta rule over the tokens, per value head ----------------
+        //   m = S_old^T k^,  r = S_old^T q^,  delta = beta (v - alpha m),
+        //   o = alpha r + (q^.k^) delta  (= S_new^T q^),  S_new = alpha S_old + k^ delta^T
+        const int npass = group / NSLOT;
+        for (int pass = 0; pass < npass; ++pass) {
+            const int hl = pass * NSLOT + slot;
+            const int hv = value_head_of(hk, hl, p.h_k, group, p.tiled);
+            const size_t head = head_base(hv);
+            if (pass > 0) load_state_at(p.state_in + head);
+#pragma unroll 1
+            for (int t = 0; t < n; ++t) {
+                const float *ct = cb + (size_t)t * nch; // q^, k^ (scaled), v
+                const float qk = scal[4 * t + 2];
+                const float beta = sgate[2 * (t * group + hl) + 0];
+                // scalar decay: folded into the sums below; per-channel decay:
+                // applied to the state rows first
+                const float alpha = CH ? 1.0f : sgate[2 * (t * group + hl) + 1];
+                if (CH) {
+                    const float *al = salpha + ((size_t)t * group + hl) * DK;
+#pragma unroll
+                    for (int r = 0; r < RPT; ++r) s[r] = al[rg + 8 * r] * s[r];
+                }
+                float kk[RPT]; // k^ of this thread's rows, for S^T k^ and the update
+                f32x4 mk = {0.f, 0.f, 0.f, 0.f}, mq = mk;
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    const int i = rg + 8 * r;
+                    kk[r] = ct[DK + i];
+                    mk += kk[r] * s[r];
+                    mq += ct[i] * s[r];
+                }
+                // sum over the 8 row groups of the wave (lanes l, l^8, l^16, ...)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mk[e] = rowgroup_sum(mk[e]);
+                    mq[e] = rowgroup_sum(mq[e]);
+                }
+                const f32x4 v4 = *reinterpret_cast<const f32x4 *>(ct + 2 * DK + hl * DV + 4 * c4);
+                f32x4 delta, o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (CH) {
+                        delta[e] = beta * (v4[e] - mk[e]);
+                        o[e] = mq[e] + qk * delta[e];
+                    } else {
+                        delta[e] = beta * (v4[e] - alpha * mk[e]);
+                        o[e] = fmaf(alpha, mq[e], qk * delta[e]);
+                    }
+                }
+                // (one row at a time: the scheduler would otherwise form all
+                // the k delta^T products first and double the live registers;
+                // the decayed state is the accumulator, so each new value stays
+                // in its own register: with the product as the accumulator the
+                // values moved one register per token and the loop began with
+                // 64 moves)
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[r][e] = fmaf(kk[r], delta[e], alpha * s[r][e]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (p.ckpt) {
+                    float *cp = p.ckpt + (((size_t)bs * T + t) * p.h_v + hv) * DK * DV;
+#pragma unroll
+                    for (int r = 0; r < RPT; ++r)
+                        *reinterpret_cast<f32x4 *>(cp + toff + r * 8 * DV) = s[r];
+                }
+                if (rg == 0)
+                    *reinterpret_cast<f32x4 *>(so + ((size_t)t * group + hl) * DV + 4 * c4) = o;
+            }
+            float *Sout = p.state_out + head;
+            if constexpr (NTS) {
+#pragma unroll
+                for (int r = 0; r < RPT; ++r)
+                    __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4 *>(Sout + toff + r * 8 * DV));
+            } else {
+#pragma unroll
+                for (int r = 0; r < RPT; ++r)
+                    *reinterpret_cast<f32x4 *>(Sout + toff + r * 8 * DV) = s[r];
+            }
         }
+
     }
 
     // ---- 3. gated RMSNorm of every (token, value head) row ----------------
@@ -502,6 +681,13 @@ size_t decode_multi_lds_bytes(const Dims &d, int t_new)
     return sizeof(float) * ((size_t)t_new * nch + 4 * (size_t)t_new + gates + 2 * rows + alphas);
 }
 
+// LDS the in-call UT form adds: the token Grams, the per-head factors of
+// each head slot and one 16 x 17 tile per wave.
+static size_t ut_lds_bytes(int dv, int nslot, int group)
+{
+    return sizeof(float) * (128 + (size_t)group * (64 + 8 + 8) + (size_t)(dv * nslot / 32) * 16 * 17);
+}
+
 template <typename TIn, int DK, int DV, int NSLOT, bool NTS>
 static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int nsplit, int batch, hipStream_t s)
 {
@@ -517,18 +703,29 @@ static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int nsplit, int ba
         // slices at d_k = d_v = 128)
         if constexpr (std::is_same<TIn, float>::value && DK == 128 && DV == 128) {
             if (ch) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 2, NTS>), dim3(batch * a.h_k),
-                               dim3(NT), shmem, s, a);
+            hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 2, NTS, false>),
+                               dim3(batch * a.h_k), dim3(NT), shmem, s, a);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
     }
-    if (ch)
-        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true, 1, NTS>), dim3(batch * a.h_k),
+    if (ch) {
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true, 1, NTS, false>), dim3(batch * a.h_k),
                            dim3(NT), shmem, s, a);
-    else
-        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1, NTS>), dim3(batch * a.h_k),
-                           dim3(NT), shmem, s, a);
+        return hipGetLastError();
+    }
+    // Calls of kUtMinTokens or more tokens per sequence without per-token
+    // states run in the in-call UT form (matrix-core products in place of
+    // the token loop's vector sums); the choice depends only on the call's
+    // shape, so a rewind replays a verification with the same arithmetic.
+    const size_t shmem_ut = shmem + ut_lds_bytes(DV, NSLOT, a.group);
+    if (a.t_new >= kUtMinTokens && !a.ckpt && shmem_ut <= kDecodeMultiMaxLds) {
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1, NTS, true>), dim3(batch * a.h_k),
+                           dim3(NT), shmem_ut, s, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1, NTS, false>), dim3(batch * a.h_k),
+                       dim3(NT), shmem, s, a);
     return hipGetLastError();
 }
 

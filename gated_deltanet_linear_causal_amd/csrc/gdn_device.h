@@ -157,4 +157,42 @@ __device__ __forceinline__ float4 fma4(float s, float4 a, float4 c)
                        fmaf(s, a.w, c.w));
 }
 
+// ---- split-bf16 matrix-core products --------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> (hi, lo) bf16 pair with hi + lo = v to ~16 significant bits.
+__device__ __forceinline__ void split1(float v, __bf16 &h, __bf16 &l)
+{
+    h = static_cast<__bf16>(v);
+    l = static_cast<__bf16>(v - static_cast<float>(h));
+}
+
+// D += A B on one 16x16x16 tile, split-bf16 with three MFMAs (the lo.lo
+// product dropped).  Lane l holds A[l%16][4*(l/16) + e], B[4*(l/16) + e][l%16]
+// and D[4*(l/16) + e][l%16] (e < 4), so an accumulator tile is directly the
+// B operand of the next product.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct Frag4 {
+    s16x4 hi, lo;
+};
+__device__ __forceinline__ Frag4 split4(const f32x4 &v)
+{
+    Frag4 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        __bf16 h, l;
+        split1(v[e], h, l);
+        f.hi[e] = __builtin_bit_cast(short, h);
+        f.lo[e] = __builtin_bit_cast(short, l);
+    }
+    return f;
+}
+__device__ __forceinline__ f32x4 mma3k16(const Frag4 &A, const Frag4 &B, f32x4 c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A.lo, B.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A.hi, B.lo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A.hi, B.hi, c, 0, 0, 0);
+    return c;
+}
+
 } // namespace gdn

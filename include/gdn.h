@@ -185,7 +185,10 @@ gdn_status gdn_decode_step(const gdn_config *cfg, const gdn_params *params,
  *     buffer (in place) but must not partially overlap.
  *   state_ckpt: NULL or [batch][t_new][H_v][d_k][d_v] fp32, the state after
  *     each token (for callers that keep per-token states instead of
- *     replaying; 2 MiB per token and sequence at H_v = 32, d = 128).
+ *     replaying; 2 MiB per token and sequence at H_v = 32, d = 128).  With
+ *     state_ckpt NULL and t_new >= 7 (scalar decay) the call's tokens are
+ *     combined in the in-chunk (UT) form, split-bf16 products on the matrix
+ *     cores, instead of being stepped one at a time.
  *   out: NULL (no outputs) or [batch][t_new][H_v*d_v] (out_dtype).
  *   batch == 0 is a no-op.
  */
@@ -203,8 +206,12 @@ gdn_status gdn_decode_multi(const gdn_config *cfg, const gdn_params *params,
  * before the verified span by replaying the delta rule over the first
  * keep_dev[i] recorded tokens ("oxinfer 0.0.5 src/qwen.rs",
  * QwenSession::rewind and GdnRecord).  The replay is gdn_decode_multi with
- * no outputs, so keeping every recorded token reproduces the state the
- * verification reached bit for bit.
+ * no outputs, so keeping every recorded token reproduces bit for bit the
+ * state that a verification without per-token states (state_ckpt NULL)
+ * reached.  (From 7 tokens per call without per-token states the tokens are
+ * combined in the in-chunk form on the matrix cores; a verification that
+ * asks for per-token states steps token by token, which agrees with it to
+ * rounding, not to the bit.)
  *   t_rec: recorded tokens per sequence (1 <= t_rec <= 8, as t_new above).
  *   keep_dev: NULL (keep all t_rec) or device [batch] int32, clamped to
  *     [0, t_rec].

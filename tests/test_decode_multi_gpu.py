@@ -124,6 +124,52 @@ def test_decode_multi_ragged_counts_and_checkpoints(gdn, v):
                 assert torch.isnan(ck[i, t]).all(), "checkpoint written past the count"
 
 
+UT_VARIANTS = [
+    # calls of 7 or 8 tokens without per-token states (the in-call UT form)
+    (2, 4, 128, 128, 4, "bf16", 8, "grouped", False),
+    (1, 3, 64, 64, 3, "f32", 8, "grouped", False),
+    (2, 4, 32, 128, 1, "f32", 7, "tiled", True),
+    (1, 2, 128, 64, 4, "bf16", 7, "grouped", False),
+    (2, 2, 32, 32, 2, "bf16", 8, "grouped", True),
+]
+
+
+@pytest.mark.parametrize("v", UT_VARIANTS, ids=lambda v: "hk%d_hv%d_dk%d_dv%d_K%d_%s_T%d_%s_%s" % v)
+def test_decode_multi_ragged_counts_in_call_form(gdn, v):
+    """Calls of 7 or more tokens without per-token states run the tokens in
+    the in-call (UT) form on the matrix cores: per-sequence counts, outputs,
+    final states and histories against the oracle, nothing written past a
+    count."""
+    hk, hv, dk, dv, K, act, T, head_map, coef = v
+    d = Dims(hk, hv, dk, dv, K, "silu", head_map)
+    B = 5
+    case = spec_case(d, B, T, act, seed=540 + hk * 10 + hv + dk + T, coef=coef is True)
+    counts = [T, 0, 1, T - 1, max(T // 2, 1)]
+    y, S, conv, _ = run_multi(gdn, case, counts)
+    y_ref, S_ref, conv_ref = oracle_prefix(case, counts)
+    live = np.zeros(y.shape[:2], bool)
+    for i, c in enumerate(counts):
+        live[i, :c] = True
+    assert torch.isnan(y[~torch.from_numpy(live)]).all(), "output written past the count"
+    P.assert_y_close(y.numpy()[live], y_ref[live])
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
+@pytest.mark.parametrize("T", [4, 8])
+def test_decode_multi_b64_full_size_weak_decay(gdn, T):
+    """B=64 sequences of the full layer with a weak decay and random states
+    (so that the state and every token's update reach the outputs), 4
+    drafted tokens (token loop) and 8 (in-call form) at the benched shape."""
+    case = spec_case(BIG, 64, T, "bf16", seed=12 + T, decay="weak")
+    case.S0 = case.S0 * (0.1 / 0.3)
+    y, S, conv, _ = run_multi(gdn, case)
+    y_ref, S_ref, conv_ref = oracle_prefix(case, [T] * 64)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
 def test_decode_multi_b64_t4_full_size(gdn):
     """B=64 sequences of the full layer (H_k=16, H_v=32, d=128, K=4, bf16),
     4 drafted tokens each: every output, state and history."""
@@ -169,6 +215,35 @@ def test_verify_then_rewind(gdn):
     gdn.rewind(cfg, prm, qkv, a, b, S0, C0, keep=keep, state=S0, conv_state=C0)
     torch.cuda.synchronize()
     assert torch.equal(S0, S_k) and torch.equal(C0, C_k)
+
+
+def test_verify_then_rewind_in_call_form(gdn):
+    """The rewind contract for 8 recorded tokens, where verification and
+    replay both run in the in-call form: keeping all tokens reproduces the
+    verified state bit for bit, keeping fewer equals a forward over the
+    prefix bit for bit and the oracle within the bar."""
+    d = Dims(2, 4, 128, 128, 4)
+    B, T = 4, 8
+    case = spec_case(d, B, T, "bf16", seed=23)
+    cfg = P.gpu_config(d, "bf16")
+    prm = P.dev_params(case)
+    qkv, a, b = (P.to_dev(bt(case, k), "bf16") for k in ("qkv", "a", "b"))
+    z = P.to_dev(bt(case, "z"), "bf16")
+    S0, C0 = case.S0.clone().cuda(), case.conv0.clone().cuda()
+    S, C = S0.clone(), C0.clone()
+    gdn.decode_multi(cfg, prm, qkv, z, a, b, C, S)
+    S_all, C_all = gdn.rewind(cfg, prm, qkv, a, b, S0, C0)
+    torch.cuda.synchronize()
+    assert torch.equal(S_all, S) and torch.equal(C_all, C)
+    keep = [0, 3, 7, 8]
+    S_k, C_k = gdn.rewind(cfg, prm, qkv, a, b, S0, C0, keep=keep)
+    S_f, C_f = S0.clone(), C0.clone()
+    gdn.decode_multi(cfg, prm, qkv, z, a, b, C_f, S_f, n_tok=keep, want_out=False)
+    torch.cuda.synchronize()
+    assert torch.equal(S_k, S_f) and torch.equal(C_k, C_f)
+    _, S_ref, C_ref = oracle_prefix(case, keep)
+    P.assert_state_close(S_k.cpu(), S_ref)
+    np.testing.assert_array_equal(C_k.cpu().numpy(), C_ref)
 
 
 def test_verify_then_rewind_per_channel_decay(gdn):
