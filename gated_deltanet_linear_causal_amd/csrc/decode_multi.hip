@@ -23,7 +23,10 @@
 //      token goes to LDS;
 //   3. applies the gated RMSNorm to all (token, head) rows in parallel.
 // The state, the dominant traffic, therefore crosses HBM once per call
-// however many tokens the call carries.
+// however many tokens the call carries.  With 7 or 8 tokens, scalar decay
+// and no per-token states, step 2 combines the call's tokens in the
+// in-chunk (UT) form on split-bf16 matrix-core products instead (UT template
+// flag; the state is then held in the 16x16 accumulator layout).
 //
 // Thread layout per value head: 2*d_v threads = d_v/32 waves; wave w owns
 // columns 32w .. 32w+31; lane l holds column quad 8w + (l mod 8) of rows
