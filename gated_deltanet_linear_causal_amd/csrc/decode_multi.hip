@@ -94,10 +94,11 @@ __device__ __forceinline__ float pick3(const float (&w)[3], int i)
     return i == 0 ? w[0] : (i == 1 ? w[1] : w[2]);
 }
 
-template <typename TIn, int DK, int DV, int NSLOT, bool CH, int NSPLIT, bool NTS, bool UT>
+template <typename TIn, int DK, int DV, int NSLOT, bool CH, int NSPLIT, bool NTS, bool UT, bool T1>
 __global__ void __launch_bounds__(2 * DV * NSLOT) __attribute__((amdgpu_waves_per_eu(4)))
 decode_multi_kernel(const MultiArgs p)
 {
+    static_assert(!(UT && T1), "the in-call UT form needs several tokens");
     static_assert(NSPLIT == 1 || (NSPLIT == 2 && !CH), "split inputs: scalar decay only");
     static_assert(!UT || !CH, "the in-call UT form: scalar decay only");
     constexpr int TPH = 2 * DV;     // threads per value head
@@ -217,13 +218,29 @@ decode_multi_kernel(const MultiArgs p)
         else
             return act_to_f32(u);
     };
+    // With several tokens per call (!T1) the loads ahead of the state are
+    // unconditional (indices clamped into the buffers, values masked where
+    // they are used): a load under a branch is waited for where it is
+    // issued, which would serialise the later tokens' loads (t = 8 64 -> 61
+    // us, t = 4 56 -> 54 us).  The single-token kernel keeps the branches:
+    // there the same change measured 0.5-2 us slower.
     TIn ga0 = TIn(0), gb0 = TIn(0), ga1 = TIn(0), gb1 = TIn(0);
-    if (tid < ngate) {
-        if (!CH) ga0 = pa[gate_index(tid, p.ld_a)];
-        gb0 = pb[gate_index(tid, p.ld_b)];
+    if constexpr (T1) {
+        if (tid < ngate) {
+            if (!CH) ga0 = pa[gate_index(tid, p.ld_a)];
+            gb0 = pb[gate_index(tid, p.ld_b)];
+            if constexpr (NSPLIT == 2) {
+                ga1 = pa[gate_index(tid, p.ld_a) + ss];
+                gb1 = pb[gate_index(tid, p.ld_b) + ss];
+            }
+        }
+    } else {
+        const int i0 = min(tid, max(ngate - 1, 0));
+        if constexpr (!CH) ga0 = pa[gate_index(i0, p.ld_a)];
+        gb0 = pb[gate_index(i0, p.ld_b)];
         if constexpr (NSPLIT == 2) {
-            ga1 = pa[gate_index(tid, p.ld_a) + ss];
-            gb1 = pb[gate_index(tid, p.ld_b) + ss];
+            ga1 = pa[gate_index(i0, p.ld_a) + ss];
+            gb1 = pb[gate_index(i0, p.ld_b) + ss];
         }
     }
     // per-channel decay inputs: element e = (pair, channel) of a [.][H_v*d_k]
@@ -236,8 +253,16 @@ decode_multi_kernel(const MultiArgs p)
     TIn gac[kAlphaPre];
 #pragma unroll
     for (int k = 0; k < kAlphaPre; ++k) {
-        const int e = tid + k * NT;
-        gac[k] = (CH && e < nalpha) ? pa[alpha_index(e)] : TIn(0);
+        if constexpr (T1) {
+            const int e = tid + k * NT;
+            gac[k] = (CH && e < nalpha) ? pa[alpha_index(e)] : TIn(0);
+        } else {
+            const int e = min(tid + k * NT, max(nalpha - 1, 0));
+            if constexpr (CH)
+                gac[k] = pa[alpha_index(e)];
+            else
+                gac[k] = TIn(0);
+        }
     }
     RawQuad<TIn> zq0, zq1;
     if (tid < nzq) {
@@ -256,28 +281,55 @@ decode_multi_kernel(const MultiArgs p)
         return 2 * p.h_k * DK + value_head_of(hk, lv / DV, p.h_k, group, p.tiled) * DV + lv % DV;
     };
     auto load_conv = [&](int ch, float (&win)[3], float (&tap)[4]) {
-        const float *hin = p.conv_in + (size_t)bs * (K - 1) * CD + ch;
+        if constexpr (T1) {
+            const float *hin = p.conv_in + (size_t)bs * (K - 1) * CD + ch;
 #pragma unroll
-        for (int pos = 0; pos < 3; ++pos) {
-            const int j = pos - 4 + K; // history slot feeding window position pos
-            win[pos] = j >= 0 ? hin[(size_t)j * CD] : 0.0f;
-        }
+            for (int pos = 0; pos < 3; ++pos) {
+                const int j = pos - 4 + K; // history slot feeding window position pos
+                win[pos] = j >= 0 ? hin[(size_t)j * CD] : 0.0f;
+            }
 #pragma unroll
-        for (int pos = 0; pos < 4; ++pos) {
-            const int j = pos - 4 + K;
-            tap[pos] = j >= 0 ? p.conv_w[(size_t)ch * K + j] : 0.0f;
+            for (int pos = 0; pos < 4; ++pos) {
+                const int j = pos - 4 + K;
+                tap[pos] = j >= 0 ? p.conv_w[(size_t)ch * K + j] : 0.0f;
+            }
+        } else {
+            // (unconditional loads, masked: with K = 1 there is no history
+            // and conv_in may be NULL, so the window loads then read the taps)
+            const float *hin = K > 1 ? p.conv_in + (size_t)bs * (K - 1) * CD + ch : p.conv_w + (size_t)ch * K;
+#pragma unroll
+            for (int pos = 0; pos < 3; ++pos) {
+                const int j = pos - 4 + K; // history slot feeding window position pos
+                const float v = hin[(size_t)max(j, 0) * CD];
+                win[pos] = j >= 0 ? v : 0.0f;
+            }
+#pragma unroll
+            for (int pos = 0; pos < 4; ++pos) {
+                const int j = pos - 4 + K;
+                const float v = p.conv_w[(size_t)ch * K + max(j, 0)];
+                tap[pos] = j >= 0 ? v : 0.0f;
+            }
         }
     };
     const int LQ = p.ld_qkv;
+    // (the first token's row exists whatever n is; with the conv already
+    // applied (preconv) the window and taps are loaded but unused)
     float win0[3] = {0.f, 0.f, 0.f}, tap0[4] = {0.f, 0.f, 0.f, 0.f};
     TIn x00 = TIn(0), x01 = TIn(0);
-    if (kPre && tid < nch) {
-        const int ch = channel_of(tid);
-        if (!p.preconv) load_conv(ch, win0, tap0);
-        if (n > 0) {
-            x00 = qkv[(size_t)bs * T * LQ + ch];
-            if constexpr (NSPLIT == 2) x01 = qkv[(size_t)bs * T * LQ + ch + ss];
+    if constexpr (T1) {
+        if (kPre && tid < nch) {
+            const int ch = channel_of(tid);
+            if (!p.preconv) load_conv(ch, win0, tap0);
+            if (n > 0) {
+                x00 = qkv[(size_t)bs * T * LQ + ch];
+                if constexpr (NSPLIT == 2) x01 = qkv[(size_t)bs * T * LQ + ch + ss];
+            }
         }
+    } else if (kPre) {
+        const int ch = channel_of(min(tid, nch - 1));
+        load_conv(ch, win0, tap0);
+        x00 = qkv[(size_t)bs * T * LQ + ch];
+        if constexpr (NSPLIT == 2) x01 = qkv[(size_t)bs * T * LQ + ch + ss];
     }
     // (the second owned channel too, when a thread has one: a channel
     // loaded after the state would make its conv, and so the gates and the
@@ -286,13 +338,20 @@ decode_multi_kernel(const MultiArgs p)
     float win1[3] = {0.f, 0.f, 0.f}, tap1[4] = {0.f, 0.f, 0.f, 0.f};
     TIn x10 = TIn(0), x11 = TIn(0);
     const int l1 = tid + NT;
-    if (kPre && l1 < nch) {
-        const int ch = channel_of(l1);
-        if (!p.preconv) load_conv(ch, win1, tap1);
-        if (n > 0) {
-            x10 = qkv[(size_t)bs * T * LQ + ch];
-            if constexpr (NSPLIT == 2) x11 = qkv[(size_t)bs * T * LQ + ch + ss];
+    if constexpr (T1) {
+        if (kPre && l1 < nch) {
+            const int ch = channel_of(l1);
+            if (!p.preconv) load_conv(ch, win1, tap1);
+            if (n > 0) {
+                x10 = qkv[(size_t)bs * T * LQ + ch];
+                if constexpr (NSPLIT == 2) x11 = qkv[(size_t)bs * T * LQ + ch + ss];
+            }
         }
+    } else if (kPre && l1 < nch) { // (uniform: whether the threads own a second channel)
+        const int ch = channel_of(min(l1, nch - 1));
+        load_conv(ch, win1, tap1);
+        x10 = qkv[(size_t)bs * T * LQ + ch];
+        if constexpr (NSPLIT == 2) x11 = qkv[(size_t)bs * T * LQ + ch + ss];
     }
     if (kPre) load_state();
 
@@ -304,20 +363,40 @@ decode_multi_kernel(const MultiArgs p)
             for (int pos = 0; pos < 3; ++pos) win[pos] = win0[pos];
 #pragma unroll
             for (int pos = 0; pos < 4; ++pos) tap[pos] = tap0[pos];
-            xs[0] = sum2(x00, x01);
+            xs[0] = (T1 || n > 0) ? sum2(x00, x01) : 0.0f; // (T1: zero when n == 0)
         } else if (kPre && l == l1) {
 #pragma unroll
             for (int pos = 0; pos < 3; ++pos) win[pos] = win1[pos];
 #pragma unroll
             for (int pos = 0; pos < 4; ++pos) tap[pos] = tap1[pos];
-            xs[0] = sum2(x10, x11);
+            xs[0] = (T1 || n > 0) ? sum2(x10, x11) : 0.0f; // (T1: zero when n == 0)
         } else {
             if (!p.preconv) load_conv(ch, win, tap);
             xs[0] = n > 0 ? in1(qkv, (size_t)bs * T * LQ + ch) : 0.0f;
         }
+        // the later tokens' raw inputs (rows clamped into the call, values
+        // masked below); loaded only when the call has several tokens, left
+        // undefined (and unused) otherwise, so that no value merges at the
+        // end of the branch and no load is waited for where it is issued
+        if constexpr (T1) {
 #pragma unroll
-        for (int t = 1; t < kDecodeMultiMaxTokens; ++t)
-            xs[t] = t < n ? in1(qkv, ((size_t)bs * T + t) * LQ + ch) : 0.0f;
+            for (int t = 1; t < kDecodeMultiMaxTokens; ++t) xs[t] = 0.0f;
+        } else {
+            TIn xr[kDecodeMultiMaxTokens][NSPLIT];
+            if (T > 1) {
+#pragma unroll
+                for (int t = 1; t < kDecodeMultiMaxTokens; ++t)
+#pragma unroll
+                    for (int h = 0; h < NSPLIT; ++h)
+                        xr[t][h] = qkv[((size_t)bs * T + min(t, T - 1)) * LQ + ch + h * ss];
+            }
+#pragma unroll
+            for (int t = 1; t < kDecodeMultiMaxTokens; ++t) {
+                float v = act_to_f32(xr[t][0]);
+                if constexpr (NSPLIT == 2) v += act_to_f32(xr[t][NSPLIT - 1]);
+                xs[t] = t < n ? v : 0.0f;
+            }
+        }
         if (p.preconv) {
             // the projection has applied the conv and SiLU and moved the
             // history on already
@@ -705,16 +784,20 @@ static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int nsplit, int ba
         // (inputs summed from two partial products: the mixer's fp32 in_proj
         // slices at d_k = d_v = 128)
         if constexpr (std::is_same<TIn, float>::value && DK == 128 && DV == 128) {
-            if (ch) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 2, NTS, false>),
+            if (ch || a.t_new != 1) return hipErrorInvalidValue; // (the mixer's single step)
+            hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 2, NTS, false, true>),
                                dim3(batch * a.h_k), dim3(NT), shmem, s, a);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
     }
     if (ch) {
-        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true, 1, NTS, false>), dim3(batch * a.h_k),
-                           dim3(NT), shmem, s, a);
+        if (a.t_new == 1)
+            hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true, 1, NTS, false, true>),
+                               dim3(batch * a.h_k), dim3(NT), shmem, s, a);
+        else
+            hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, true, 1, NTS, false, false>),
+                               dim3(batch * a.h_k), dim3(NT), shmem, s, a);
         return hipGetLastError();
     }
     // Calls of kUtMinTokens or more tokens per sequence without per-token
@@ -723,12 +806,16 @@ static hipError_t launch_multi_t(const MultiArgs &a, bool ch, int nsplit, int ba
     // shape, so a rewind replays a verification with the same arithmetic.
     const size_t shmem_ut = shmem + ut_lds_bytes(DV, NSLOT, a.group);
     if (a.t_new >= kUtMinTokens && !a.ckpt && shmem_ut <= kDecodeMultiMaxLds) {
-        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1, NTS, true>), dim3(batch * a.h_k),
-                           dim3(NT), shmem_ut, s, a);
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1, NTS, true, false>),
+                           dim3(batch * a.h_k), dim3(NT), shmem_ut, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1, NTS, false>), dim3(batch * a.h_k),
-                       dim3(NT), shmem, s, a);
+    if (a.t_new == 1)
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1, NTS, false, true>),
+                           dim3(batch * a.h_k), dim3(NT), shmem, s, a);
+    else
+        hipLaunchKernelGGL((decode_multi_kernel<TIn, DK, DV, NSLOT, false, 1, NTS, false, false>),
+                           dim3(batch * a.h_k), dim3(NT), shmem, s, a);
     return hipGetLastError();
 }
 
