@@ -23,8 +23,8 @@
 //      token goes to LDS;
 //   3. applies the gated RMSNorm to all (token, head) rows in parallel.
 // The state, the dominant traffic, therefore crosses HBM once per call
-// however many tokens the call carries.  With 7 or 8 tokens, scalar decay
-// and no per-token states, step 2 combines the call's tokens in the
+// however many tokens the call carries.  With 8 tokens, scalar decay and
+// no per-token states, step 2 combines the call's tokens in the
 // in-chunk (UT) form on split-bf16 matrix-core products instead (UT template
 // flag; the state is then held in the 16x16 accumulator layout).
 //

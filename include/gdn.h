@@ -186,7 +186,7 @@ gdn_status gdn_decode_step(const gdn_config *cfg, const gdn_params *params,
  *   state_ckpt: NULL or [batch][t_new][H_v][d_k][d_v] fp32, the state after
  *     each token (for callers that keep per-token states instead of
  *     replaying; 2 MiB per token and sequence at H_v = 32, d = 128).  With
- *     state_ckpt NULL and t_new >= 7 (scalar decay) the call's tokens are
+ *     state_ckpt NULL and t_new = 8 (scalar decay) the call's tokens are
  *     combined in the in-chunk (UT) form, split-bf16 products on the matrix
  *     cores, instead of being stepped one at a time.
  *   out: NULL (no outputs) or [batch][t_new][H_v*d_v] (out_dtype).
@@ -208,7 +208,7 @@ gdn_status gdn_decode_multi(const gdn_config *cfg, const gdn_params *params,
  * QwenSession::rewind and GdnRecord).  The replay is gdn_decode_multi with
  * no outputs, so keeping every recorded token reproduces bit for bit the
  * state that a verification without per-token states (state_ckpt NULL)
- * reached.  (From 7 tokens per call without per-token states the tokens are
+ * reached.  (With 8 tokens per call and no per-token states the tokens are
  * combined in the in-chunk form on the matrix cores; a verification that
  * asks for per-token states steps token by token, which agrees with it to
  * rounding, not to the bit.)

@@ -124,8 +124,9 @@ def test_decode_multi_ragged_counts_and_checkpoints(gdn, v):
                 assert torch.isnan(ck[i, t]).all(), "checkpoint written past the count"
 
 
-UT_VARIANTS = [
-    # calls of 7 or 8 tokens without per-token states (the in-call UT form)
+LONG_VARIANTS = [
+    # calls of 7 (stepped) or 8 tokens (in the in-call UT form) without
+    # per-token states
     (2, 4, 128, 128, 4, "bf16", 8, "grouped", False),
     (1, 3, 64, 64, 3, "f32", 8, "grouped", False),
     (2, 4, 32, 128, 1, "f32", 7, "tiled", True),
@@ -134,12 +135,12 @@ UT_VARIANTS = [
 ]
 
 
-@pytest.mark.parametrize("v", UT_VARIANTS, ids=lambda v: "hk%d_hv%d_dk%d_dv%d_K%d_%s_T%d_%s_%s" % v)
-def test_decode_multi_ragged_counts_in_call_form(gdn, v):
-    """Calls of 7 or more tokens without per-token states run the tokens in
-    the in-call (UT) form on the matrix cores: per-sequence counts, outputs,
-    final states and histories against the oracle, nothing written past a
-    count."""
+@pytest.mark.parametrize("v", LONG_VARIANTS, ids=lambda v: "hk%d_hv%d_dk%d_dv%d_K%d_%s_T%d_%s_%s" % v)
+def test_decode_multi_ragged_counts_without_checkpoints(gdn, v):
+    """Calls of 7 or 8 tokens without per-token states (8: the tokens
+    combined in the in-call UT form on the matrix cores): per-sequence
+    counts, outputs, final states and histories against the oracle, nothing
+    written past a count."""
     hk, hv, dk, dv, K, act, T, head_map, coef = v
     d = Dims(hk, hv, dk, dv, K, "silu", head_map)
     B = 5
@@ -160,7 +161,7 @@ def test_decode_multi_ragged_counts_in_call_form(gdn, v):
 def test_decode_multi_b64_full_size_weak_decay(gdn, T):
     """B=64 sequences of the full layer with a weak decay and random states
     (so that the state and every token's update reach the outputs), 4
-    drafted tokens (token loop) and 8 (in-call form) at the benched shape."""
+    drafted tokens (stepped) and 8 (in-call UT form) at the benched shape."""
     case = spec_case(BIG, 64, T, "bf16", seed=12 + T, decay="weak")
     case.S0 = case.S0 * (0.1 / 0.3)
     y, S, conv, _ = run_multi(gdn, case)
@@ -217,9 +218,9 @@ def test_verify_then_rewind(gdn):
     assert torch.equal(S0, S_k) and torch.equal(C0, C_k)
 
 
-def test_verify_then_rewind_in_call_form(gdn):
+def test_verify_then_rewind_eight_tokens(gdn):
     """The rewind contract for 8 recorded tokens, where verification and
-    replay both run in the in-call form: keeping all tokens reproduces the
+    replay run in the in-call UT form: keeping all tokens reproduces the
     verified state bit for bit, keeping fewer equals a forward over the
     prefix bit for bit and the oracle within the bar."""
     d = Dims(2, 4, 128, 128, 4)
