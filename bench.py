@@ -571,6 +571,16 @@ def main():
             ev_m[1].record(stream)
             torch.cuda.synchronize()
             mix[name] = (ev_m[0].elapsed_time(ev_m[1]) / calls, calls, Hd)
+        # A few sequences (launch-latency bound): 10 steps replayed as one
+        # HIP graph, on the first Bs sequences of the decode batch.
+        for Bs in (1, 8):
+            xs, ys = xd[:Bs], yd[:Bs]
+            Ss, cs = S_dc[:Bs], c_dc[:Bs]
+
+            def small_steps(st=None):
+                for _ in range(10):
+                    gdn.mixer_decode(cfg, dparams, pj, xs, cs, Ss, y=ys, workspace=mws, stream=st)
+            mix[f"decode_b{Bs}"] = (time_graph(small_steps, 5) / 10, 50, Hd)
         del mws
 
     if args.calib_copy:
@@ -642,6 +652,22 @@ def main():
             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
             "algorithmic_bytes_per_launch": mb, "duration_us": round(ms * 1e3, 2),
             "launches_timed": calls, "tokens_per_s": round(B / (ms * 1e-3), 1)}
+    for Bs in (1, 8):
+        if f"decode_b{Bs}" not in mix:
+            continue
+        ms, calls, Hd = mix[f"decode_b{Bs}"]
+        nproj = d.conv_dim + d.value_dim + 2 * d.h_v
+        mb = decode_bytes(d, Bs) + (nproj + d.value_dim) * Hd * 2 + 2 * Bs * Hd * 2
+        gbs = mb / (ms * 1e-3) / 1e9
+        roof_multi[f"mixer_decode_b{Bs}"] = {
+            "kernel": "gdn_mixer_decode at B=%d (in_proj product with the conv in its epilogue, "
+                      "decode kernel, out_proj product over hi/lo parts + slice sum), "
+                      "hidden 2048" % Bs,
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": mb, "duration_us": round(ms * 1e3, 2),
+            "duration_note": "device time, 10 steps replayed as one HIP graph",
+            "launches_timed": calls, "tokens_per_s": round(Bs / (ms * 1e-3), 1)}
     if "prefill" in mix:
         ms, calls, Hd = mix["prefill"]
         nproj = d.conv_dim + d.value_dim + 2 * d.h_v

@@ -55,40 +55,6 @@ template <int KSL> constexpr int sk_depth() { return 4; }
 // dropped.  No load is conditional and no arithmetic touches the loaded
 // pieces before they are stored, so the compiler's count of loads in
 // flight stays exact and a wait for one chunk never drains the ones behind.
-// in_proj epilogue of one output (row m, column n of the concatenated
-// blocks) holding the full sum x: the qkv block through the causal conv +
-// SiLU (x is the newest raw input of channel j; history slot 0 is the
-// oldest, the newest input meets the last tap) with the history moved on;
-// z, b and a stored as they are.
-__device__ __forceinline__ void proj_store1(const ProjEpilogue &p, int m, int n, float x)
-{
-    int blk = 0;
-#pragma unroll
-    for (int b = 1; b < 4; ++b)
-        if (n >= p.start[b]) blk = b;
-    const int j = n - p.start[blk];
-    const int cols = p.start[blk + 1] - p.start[blk];
-    if (blk == 0) {
-        const int K = p.conv_k;
-        float *h = p.conv_state + (size_t)m * (K - 1) * cols + j;
-        const float *w = p.conv_w + (size_t)j * K;
-        float hist[3] = {0.f, 0.f, 0.f};
-        float acc = 0.0f;
-#pragma unroll
-        for (int s = 0; s < 3; ++s)
-            if (s < K - 1) {
-                hist[s] = h[(size_t)s * cols];
-                acc = fmaf(w[s], hist[s], acc);
-            }
-        acc = fmaf(w[K - 1], x, acc);
-#pragma unroll
-        for (int s = 0; s < 3; ++s)
-            if (s < K - 1) h[(size_t)s * cols] = s + 1 < K - 1 ? hist[s + 1] : x;
-        x = siluf_(acc);
-    }
-    p.dst[blk][(size_t)m * cols + j] = x;
-}
-
 template <int NPART, int KSL, bool EPI>
 __global__ void __launch_bounds__(256, 2) skinny_gemm_kernel(const SkinnyGemm p, const ProjEpilogue e)
 {
@@ -197,18 +163,75 @@ __global__ void __launch_bounds__(256, 2) skinny_gemm_kernel(const SkinnyGemm p,
 
     // lane (col, kq) holds rows 16 mt + 4 kq + r of column n
     const int n = n0 + 16 * wave + col;
+    if (EPI) {
+        // The in_proj epilogue of rows 4 kq + r of column n (the direct path
+        // carries at most 16 rows: row tile 0).  The column's block comes from
+        // the block starts compared at constant indices (kernel arguments, no
+        // lookup through memory), and every tap and history value is loaded
+        // unconditionally from a clamped address before any is used, so the
+        // lane's loads are in flight together (a load under a per-lane branch
+        // is waited for where it is issued).
+        int blk = 0, st = 0, en = e.start[1];
+        float *dstb = e.dst[0];
+#pragma unroll
+        for (int b = 1; b < 4; ++b)
+            if (n >= e.start[b]) {
+                blk = b;
+                st = e.start[b];
+                en = e.start[b + 1];
+                dstb = e.dst[b];
+            }
+        const int cols = en - st, j = n - st;
+        const int K = e.conv_k, c0 = e.start[1];
+        const int jc = min(max(n, 0), c0 - 1); // a conv channel whatever the block
+        float w[4], hist[4][3];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = e.conv_w[(size_t)jc * K + min(t, K - 1)];
+        if (K > 1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int mc = min(4 * kq + r, e.M - 1);
+                const float *h = e.conv_state + (size_t)mc * (K - 1) * c0 + jc;
+#pragma unroll
+                for (int t = 0; t < 3; ++t) hist[r][t] = h[(size_t)min(t, K - 2) * c0];
+            }
+        }
+        // x is the newest raw input of channel j; history slot 0 is the
+        // oldest, and the newest input meets the last tap.  All results
+        // first, then the stores (stores count against the same load
+        // counter, so a store issued before a wait would be waited for too).
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float a = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+                if (t < K - 1) a = fmaf(w[t], hist[r][t], a);
+            a = fmaf(w[K - 1], acc[0][r], a);
+            y[r] = blk == 0 ? siluf_(a) : acc[0][r];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * kq + r;
+            if (m < e.M && n < e.N) {
+                if (blk == 0) {
+                    float *h = e.conv_state + (size_t)m * (K - 1) * c0 + j;
+#pragma unroll
+                    for (int t = 0; t < 3; ++t)
+                        if (t < K - 1) h[(size_t)t * c0] = t + 1 < K - 1 ? hist[r][t + 1] : acc[0][r];
+                }
+                dstb[(size_t)m * cols + j] = y[r];
+            }
+        }
+        return;
+    }
     float *dst = p.part + (size_t)blockIdx.y * p.M * p.N;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 16 * mt + 4 * kq + r;
-            if (m < p.M && n < p.N) {
-                if (EPI)
-                    proj_store1(e, m, n, acc[mt][r]);
-                else
-                    dst[(size_t)m * p.N + n] = acc[mt][r];
-            }
+            if (m < p.M && n < p.N) dst[(size_t)m * p.N + n] = acc[mt][r];
         }
 }
 
@@ -330,7 +353,8 @@ hipError_t launch_skinny_gemm(SkinnyGemm g, int nparts, const ProjEpilogue *epi,
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     const int ks = epi ? (nparts == 1 && skinny_direct_ok(g.K) ? 1 : 0) : skinny_ksplit(g.K, nparts);
-    if (ks == 0) return hipErrorInvalidValue;
+    // the epilogue inside the product covers row tile 0 only
+    if (ks == 0 || (epi && g.M > kSkinnyDirectRows)) return hipErrorInvalidValue;
     g.kslice = g.K / ks;
     const dim3 grid((g.N + kSkinnyCols - 1) / kSkinnyCols, ks);
     const ProjEpilogue none{};
