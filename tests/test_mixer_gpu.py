@@ -102,6 +102,9 @@ DECODE_LAYERS = [
     (2, 4, 64, 4096, "head", 4, 3),
     (1, 4, 128, 2048, "head", 4, 20),
     (2, 4, 128, 2048, "head", 2, 9),
+    # the one-slice product with the conv in its epilogue at K = 2 and K = 1
+    (2, 4, 64, 256, "head", 2, 6),
+    (2, 4, 64, 512, "head", 1, 8),
     (2, 4, 32, 200, "head", 4, 3),
     (2, 4, 64, 256, "head", 4, 70),
     (1, 2, 128, 256, "head", 4, 4),
