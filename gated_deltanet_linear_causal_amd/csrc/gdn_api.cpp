@@ -425,7 +425,8 @@ gdn_status prefill_common(const gdn_config *cfg, const gdn_params *params, int32
         hipError_t e = gdn::static_scratch(&workspace);
         if (e != hipSuccess) return hip_status(e, "static scratch address");
     }
-    return hip_status(gdn::launch_prefill(d, p, n_seq, t_total, max_len, cu_seqlens_dev, qkv, z, a,
+    return hip_status(gdn::launch_prefill(d, p, n_seq, t_total, max_len, cu_seqlens_host,
+                                          cu_seqlens_dev, qkv, z, a,
                                           b, state_in, state_out, conv_in, conv_out, out, workspace,
                                           static_cast<hipStream_t>(stream)),
                       static_ws ? "gdn_prefill_chunked_noalloc launch" : "gdn_prefill_chunked launch");
@@ -553,7 +554,8 @@ gdn_status gdn_mixer_prefill(const gdn_config *cfg, const gdn_params *params,
         return fail(GDN_EINVAL, "state_out may equal state_in but must not partially overlap it");
     if (overlap(rci, rco) && conv_in != conv_out)
         return fail(GDN_EINVAL, "conv_out may equal conv_in but must not partially overlap it");
-    return hip_status(gdn::launch_mixer_prefill(d, p, pj, n_seq, t_total, max_len, cu_seqlens_dev,
+    return hip_status(gdn::launch_mixer_prefill(d, p, pj, n_seq, t_total, max_len, cu_seqlens_host,
+                                                cu_seqlens_dev,
                                                 x, state_in, state_out, conv_in, conv_out, y,
                                                 workspace, static_cast<hipStream_t>(stream)),
                       "gdn_mixer_prefill launch");

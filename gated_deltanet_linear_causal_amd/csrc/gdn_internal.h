@@ -70,7 +70,8 @@ struct Proj {
 };
 size_t mixer_workspace_bytes(const Dims &d, int hidden, int n_seq, int t_total, bool prefill);
 hipError_t launch_mixer_prefill(const Dims &d, const Params &p, const Proj &pj, int n_seq,
-                                int t_total, int max_len, const int32_t *cu_dev, const void *x,
+                                int t_total, int max_len, const int32_t *cu_host,
+                                const int32_t *cu_dev, const void *x,
                                 const float *state_in, float *state_out, const float *conv_in,
                                 float *conv_out, void *y, void *ws, hipStream_t s);
 hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, int batch,
@@ -79,8 +80,10 @@ hipError_t launch_mixer_decode(const Dims &d, const Params &p, const Proj &pj, i
 
 // Chunked prefill.  Workspace layout and size are owned by prefill.hip.
 size_t prefill_workspace_bytes(const Dims &d, int n_seq, int t_total);
+// cu_host (host copy of cu_dev, may be NULL) orders the scan's work longest
+// sequence first.
 hipError_t launch_prefill(const Dims &d, const Params &p, int n_seq, int t_total,
-                          int max_len, const int32_t *cu_dev, const void *qkv,
+                          int max_len, const int32_t *cu_host, const int32_t *cu_dev, const void *qkv,
                           const void *z, const void *a, const void *b,
                           const float *state_in, float *state_out, const float *conv_in,
                           float *conv_out, void *out, void *ws, hipStream_t s);

@@ -360,7 +360,8 @@ size_t mixer_workspace_bytes(const Dims &d, int hidden, int n_seq, int t_total, 
 }
 
 hipError_t launch_mixer_prefill(const Dims &d, const Params &p, const Proj &pj, int n_seq,
-                                int t_total, int max_len, const int32_t *cu_dev, const void *x,
+                                int t_total, int max_len, const int32_t *cu_host,
+                                const int32_t *cu_dev, const void *x,
                                 const float *state_in, float *state_out, const float *conv_in,
                                 float *conv_out, void *y, void *ws, hipStream_t s)
 {
@@ -370,7 +371,8 @@ hipError_t launch_mixer_prefill(const Dims &d, const Params &p, const Proj &pj, 
     hipError_t e;
     if ((e = prepare_gemms(d, pj, t_total, x, g)) != hipSuccess) return e;
     if ((e = in_proj(d, pj, g, t_total, x, base, w, s)) != hipSuccess) return e;
-    if ((e = launch_prefill(core_dims(d, true), p, n_seq, t_total, max_len, cu_dev, base + w.qkv,
+    if ((e = launch_prefill(core_dims(d, true), p, n_seq, t_total, max_len, cu_host, cu_dev,
+                            base + w.qkv,
                             base + w.z, base + w.a, base + w.b, state_in, state_out, conv_in,
                             conv_out, base + w.hl, base + w.prefill, s)) != hipSuccess)
         return e;

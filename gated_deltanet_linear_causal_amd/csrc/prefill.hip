@@ -48,6 +48,7 @@ namespace gdn {
 
 constexpr int kC = 64;       // tokens per chunk
 constexpr int kBV = 16;      // d_v columns per scan tile
+constexpr int kSeqOrder = 64; // sequences the scan orders by length
 constexpr int kQkChunks = 2; // chunks per qknorm workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -251,6 +252,10 @@ struct PrefillArgs {
     int gate, out_bf16, tiled, kda;
     int out_split;   // out: bf16 hi parts, then the lo parts at out + t_total * value_dim
     float norm_eps, l2_eps;
+    // The scan's sequences in the order its workgroups take them: longest
+    // first (the first kSeqOrder sequences of the call; later ones keep
+    // their own index).
+    uint8_t seq_order[kSeqOrder];
 };
 
 // Conv taps of 4 channels starting at ch, right-aligned to 4 taps (zero
@@ -1269,7 +1274,8 @@ scan_kernel(const PrefillArgs p, int slices)
             hidx = b / slices;
         }
     }
-    const int n = hidx / p.h_v, hv = hidx % p.h_v;
+    const int nq = hidx / p.h_v, hv = hidx % p.h_v;
+    const int n = nq < kSeqOrder ? p.seq_order[nq] : nq;
     const int hk = key_head_of(hv, p.h_k, p.group, p.tiled);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1768,8 +1774,9 @@ static hipError_t dispatch_dv(const PrefillArgs &a, int n_seq, int t_total, int 
 }
 
 hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_total, int max_len,
-                          const int32_t *cu_dev, const void *qkv, const void *z, const void *a,
-                          const void *b, const float *state_in, float *state_out,
+                          const int32_t *cu_host, const int32_t *cu_dev, const void *qkv,
+                          const void *z, const void *a, const void *b,
+                          const float *state_in, float *state_out,
                           const float *conv_in, float *conv_out, void *out, void *ws,
                           hipStream_t s)
 {
@@ -1816,6 +1823,17 @@ hipError_t launch_prefill(const Dims &d, const Params &pr, int n_seq, int t_tota
     A.out_bf16 = d.out_bf16;
     A.norm_eps = d.norm_eps;
     A.l2_eps = d.l2_eps;
+    // Longest sequence first: a scan workgroup walks its sequence's whole
+    // chain, so with more workgroups than CUs (packed sequences) the long
+    // chains should start in the first round (8 packed sequences of 709 to
+    // 4,688 tokens: prefill 1.25 against 1.28 ms, bit-identical).
+    for (int i = 0; i < kSeqOrder; ++i) A.seq_order[i] = (uint8_t)i;
+    if (cu_host && n_seq > 1) {
+        const int m = std::min(n_seq, kSeqOrder);
+        std::stable_sort(A.seq_order, A.seq_order + m, [&](uint8_t x, uint8_t y) {
+            return cu_host[x + 1] - cu_host[x] > cu_host[y + 1] - cu_host[y];
+        });
+    }
 
 #define GDN_PF_CASE(DK_)                                                                      \
     if (d.d_k == DK_)                                                                         \
