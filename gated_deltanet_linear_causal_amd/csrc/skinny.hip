@@ -8,9 +8,10 @@
 // projections: a workgroup takes 64 output columns (16 per wave) and one
 // slice of the contraction, and streams the A rows (the hidden states, or
 // the core output as bf16 hi and lo parts) and its weight rows through LDS
-// in 64-wide chunks of the contraction.  The partial products of the slices go to a workspace and a second, element-wise
-// kernel adds them in slice order (so the result does not depend on timing)
-// and applies the epilogue:
+// in 64-wide chunks of the contraction.  The partial products of the
+// slices go to a workspace and a second, element-wise kernel adds them in
+// slice order (so the result does not depend on timing) and applies the
+// epilogue:
 //   in_proj:  the causal conv + SiLU of the qkv columns over the conv
 //             history, with the history moved on by one token ("cherenkov
 //             qwen4_exp/cpu.rs" fn causal_conv), so the core receives the
@@ -18,6 +19,10 @@
 //   out_proj: the sum of the hi and lo products (the core output split so
 //             that the layer keeps fp32-level accuracy), stored as fp32 or
 //             bf16.
+// Up to 8 rows the in_proj contraction is one slice and the product kernel
+// applies the in_proj epilogue itself (no partial products, no second
+// kernel); above 8 rows at d_k = d_v = 128 the core decode kernel adds the
+// two in_proj slices as it loads them and runs the conv itself.
 // bf16 x bf16 products are exact in fp32 and accumulate in fp32.
 
 #include "gdn_device.h"
