@@ -249,7 +249,10 @@ decode_multi_kernel(const MultiArgs p)
         const int hv = value_head_of(hk, i % group, p.h_k, group, p.tiled);
         return ((size_t)bs * T + i / group) * p.ld_a + (size_t)hv * DK + e % DK;
     };
-    constexpr int kAlphaPre = 2; // elements per thread loaded up front
+    // elements per thread loaded up front: a four-token call of two value
+    // heads at d_k = 128 on 256 threads has four (the rest are loaded in the
+    // decay loop, one round trip each)
+    constexpr int kAlphaPre = T1 ? 2 : 4;
     TIn gac[kAlphaPre];
 #pragma unroll
     for (int k = 0; k < kAlphaPre; ++k) {
@@ -437,17 +440,29 @@ decode_multi_kernel(const MultiArgs p)
     if (CH) {
         // one decay per (token, value head, key channel): Kimi Delta
         // Attention ("cortiq-engine 0.8.76 pipeline.rs", AttnKind::Kda)
+        // Element e = tid + k NT has key channel e % DK and value head
+        // (e / DK) % group: when NT is a multiple of DK * group every k of a
+        // thread has the same head and channel, whose parameters are then
+        // loaded once instead of once per element (each reload a round trip
+        // in this loop).
+        const bool fixed = NT % (DK * group) == 0;
+        const int hv0 = value_head_of(hk, (tid / DK) % group, p.h_k, group, p.tiled);
+        const float coef0 = decay_coef_of(p.a_log, p.decay_coef, hv0);
+        const float dt0 = p.dt_bias[(size_t)hv0 * DK + tid % DK];
         for (int e = tid; e < nalpha; e += NT) {
             const int k = (e - tid) / NT;
-            const int hv = value_head_of(hk, (e / DK) % group, p.h_k, group, p.tiled);
             float ar = 0.0f;
 #pragma unroll
             for (int j = 0; j < kAlphaPre; ++j)
                 if (j == k) ar = act_to_f32(gac[j]);
             if (k >= kAlphaPre) ar = load_act(pa, alpha_index(e));
-            const float g = decay_coef_of(p.a_log, p.decay_coef, hv) *
-                            softplusf_(ar + p.dt_bias[(size_t)hv * DK + e % DK]);
-            salpha[e] = expf(g);
+            float coef = coef0, dtb = dt0;
+            if (!fixed) {
+                const int hv = value_head_of(hk, (e / DK) % group, p.h_k, group, p.tiled);
+                coef = decay_coef_of(p.a_log, p.decay_coef, hv);
+                dtb = p.dt_bias[(size_t)hv * DK + e % DK];
+            }
+            salpha[e] = expf(coef * softplusf_(ar + dtb));
         }
     }
     for (int q = tid; q < nzq; q += NT) {
