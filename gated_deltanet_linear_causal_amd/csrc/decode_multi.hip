@@ -462,7 +462,10 @@ decode_multi_kernel(const MultiArgs p)
                 coef = decay_coef_of(p.a_log, p.decay_coef, hv);
                 dtb = p.dt_bias[(size_t)hv * DK + e % DK];
             }
-            salpha[e] = expf(coef * softplusf_(ar + dtb));
+            // (d_k decays per token and value head: the hardware exp/log
+            // form, as the chunked prefill computes them; t = 4 56.3 against
+            // 60.7 us with the full-precision functions)
+            salpha[e] = __expf(coef * softplus_hw(ar + dtb));
         }
     }
     for (int q = tid; q < nzq; q += NT) {

@@ -108,6 +108,13 @@ __device__ __forceinline__ void store_out1(void *out, size_t i, float v, bool bf
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 __device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
 __device__ __forceinline__ float softplusf_(float x) { return x > 20.0f ? x : log1pf(expf(x)); }
+// The same softplus with the hardware exponential and logarithm, for the
+// per-channel decays (d_k of them per token and value head): x above 20,
+// below it max(x, 0) + log(1 + e^{-|x|}), absolute error about 1e-7.
+__device__ __forceinline__ float softplus_hw(float x)
+{
+    return x > 20.0f ? x : fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x)));
+}
 __device__ __forceinline__ float gatef_(float z, int sigmoid_gate)
 {
     return sigmoid_gate ? sigmoidf_(z) : siluf_(z);
