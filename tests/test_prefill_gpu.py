@@ -71,11 +71,14 @@ def test_prefill_small(gdn, v, act):
 # Enough sequences that the scan widens its column slices: with 256 compute
 # units and 4 value heads per sequence, d_v = 64 takes two 16-column tiles
 # per workgroup from 32 sequences and four (the whole head) from 64; d_v =
-# 128 takes two from 16 sequences and four from 32.
+# 128 takes two from 16 sequences and four from 32.  The scan takes the
+# first 64 sequences longest first and any later ones in their own order
+# (80 sequences: both).
 MANY = [
     # h_k, h_v, d_k, d_v, decay mode, n_seq
     (2, 4, 64, 64, "head", 32),
     (2, 4, 64, 64, "head", 64),
+    (2, 4, 64, 64, "head", 80),
     (1, 4, 128, 128, "head", 16),
     (1, 4, 128, 128, "head", 32),
     (2, 4, 32, 64, "channel", 64),
