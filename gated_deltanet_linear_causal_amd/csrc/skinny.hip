@@ -70,11 +70,18 @@ __global__ void __launch_bounds__(256, 2) skinny_gemm_kernel(const SkinnyGemm p,
     constexpr int nch = KSL / kSkKC;
     constexpr int D = sk_depth<KSL>();
     static_assert(nch % D == 0, "ring depth");
+    // Row tiles of 16 A rows: the direct path (the epilogue in the product)
+    // carries at most 8 rows, so it stages and multiplies one tile, a
+    // quarter of the A loads and products of the four-tile form.
+    constexpr int MT = EPI ? 1 : 4;
     const int k0 = blockIdx.y * KSL;
     const int n0 = blockIdx.x * kSkinnyCols;
 
-    // the two pieces of this thread: tile row tid/8 (+32), 16-byte column tid%8
+    // the two pieces of this thread: tile row tid/8 (+32), 16-byte column
+    // tid%8 (one row tile of A: one 8-byte piece, row tid/16, 8-byte column
+    // tid%16)
     const int prow = tid >> 3, pc = tid & 7;
+    const int arow1 = tid >> 4, ac1 = tid & 15;
     const bf16_t *ap[2][NPART];
     const bf16_t *wp[2];
 #pragma unroll
@@ -82,7 +89,8 @@ __global__ void __launch_bounds__(256, 2) skinny_gemm_kernel(const SkinnyGemm p,
         const int r = prow + 32 * q;
 #pragma unroll
         for (int part = 0; part < NPART; ++part)
-            ap[q][part] = p.a[part] + (size_t)min(r, p.M - 1) * p.K + k0 + 8 * pc;
+            ap[q][part] = MT == 4 ? p.a[part] + (size_t)min(r, p.M - 1) * p.K + k0 + 8 * pc
+                                  : p.a[part] + (size_t)min(arow1, p.M - 1) * p.K + k0 + 4 * ac1;
         const int n = min(n0 + r, p.N - 1);
         int blk = 0;
 #pragma unroll
@@ -105,8 +113,14 @@ __global__ void __launch_bounds__(256, 2) skinny_gemm_kernel(const SkinnyGemm p,
     {                                                                                          \
         const int off_ = ((min((CH), nch - 1) + rot) % nch) * kSkKC;                           \
         _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                        \
-            _Pragma("unroll") for (int part = 0; part < NPART; ++part)                         \
-                R[q][part] = *reinterpret_cast<const u32x4 *>(ap[q][part] + off_);             \
+            _Pragma("unroll") for (int part = 0; part < NPART; ++part) {                       \
+                if (MT == 4) {                                                                 \
+                    R[q][part] = *reinterpret_cast<const u32x4 *>(ap[q][part] + off_);         \
+                } else if (q == 0) {                                                           \
+                    const uint2 v_ = *reinterpret_cast<const uint2 *>(ap[0][part] + off_);     \
+                    R[0][part] = u32x4{v_.x, v_.y, 0u, 0u};                                    \
+                }                                                                              \
+            }                                                                                  \
             R[q][NPART] = *reinterpret_cast<const u32x4 *>(wp[q] + off_);                      \
         }                                                                                      \
     }
@@ -121,17 +135,22 @@ __global__ void __launch_bounds__(256, 2) skinny_gemm_kernel(const SkinnyGemm p,
         GDN_SK_ISSUE(r7, 7)
     }
 
-    f32x4 acc[4];
+    f32x4 acc[MT];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     // one chunk: store the ring slot to LDS buffer BUF, refill the slot D
     // chunks ahead, meet, and run the chunk's products
 #define GDN_SK_STEP(R, BUF, CH)                                                                \
     {                                                                                          \
         _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                        \
             const int o = (prow + 32 * q) * kSkRS + 8 * pc;                                    \
-            _Pragma("unroll") for (int part = 0; part < NPART; ++part)                         \
-                *reinterpret_cast<u32x4 *>(&sa[BUF][part][o]) = R[q][part];                    \
+            _Pragma("unroll") for (int part = 0; part < NPART; ++part) {                       \
+                if (MT == 4)                                                                   \
+                    *reinterpret_cast<u32x4 *>(&sa[BUF][part][o]) = R[q][part];                \
+                else if (q == 0)                                                               \
+                    *reinterpret_cast<uint2 *>(&sa[BUF][part][arow1 * kSkRS + 4 * ac1]) =      \
+                        make_uint2(R[0][part].x, R[0][part].y);                                \
+            }                                                                                  \
             *reinterpret_cast<u32x4 *>(&sw[BUF][o]) = R[q][NPART];                             \
         }                                                                                      \
         GDN_SK_ISSUE(R, (CH) + D)                                                              \
@@ -139,7 +158,7 @@ __global__ void __launch_bounds__(256, 2) skinny_gemm_kernel(const SkinnyGemm p,
         _Pragma("unroll") for (int s = 0; s < kSkKC / 32; ++s) {                               \
             const bf16x8 bw = *reinterpret_cast<const bf16x8 *>(                               \
                 &sw[BUF][(16 * wave + col) * kSkRS + 32 * s + 8 * kq]);                        \
-            _Pragma("unroll") for (int mt = 0; mt < 4; ++mt) {                                 \
+            _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                \
                 _Pragma("unroll") for (int part = 0; part < NPART; ++part) {                   \
                     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(                        \
                         &sa[BUF][part][(16 * mt + col) * kSkRS + 32 * s + 8 * kq]);            \
@@ -232,7 +251,7 @@ __global__ void __launch_bounds__(256, 2) skinny_gemm_kernel(const SkinnyGemm p,
     }
     float *dst = p.part + (size_t)blockIdx.y * p.M * p.N;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 16 * mt + 4 * kq + r;
