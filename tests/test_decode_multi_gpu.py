@@ -171,6 +171,22 @@ def test_decode_multi_b64_full_size_weak_decay(gdn, T):
     np.testing.assert_array_equal(conv.numpy(), conv_ref)
 
 
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_decode_multi_b64_full_size_per_channel_decay(gdn, T):
+    """B=64 sequences of the full layer with one decay per key channel
+    ("cortiq-engine 0.8.76 pipeline.rs", AttnKind::Kda; sigmoid output gate),
+    weak decay and random states, 1, 4 and 8 tokens: the benched shapes of the
+    per-channel-decay decode."""
+    d = Dims(BIG.h_k, BIG.h_v, BIG.d_k, BIG.d_v, BIG.conv_k, "sigmoid", decay="channel")
+    case = spec_case(d, 64, T, "bf16", seed=31 + T, decay="weak")
+    case.S0 = case.S0 * (0.1 / 0.3)
+    y, S, conv, _ = run_multi(gdn, case)
+    y_ref, S_ref, conv_ref = oracle_prefix(case, [T] * 64)
+    P.assert_y_close(y, y_ref)
+    P.assert_state_close(S, S_ref)
+    np.testing.assert_array_equal(conv.numpy(), conv_ref)
+
+
 def test_decode_multi_b64_t4_full_size(gdn):
     """B=64 sequences of the full layer (H_k=16, H_v=32, d=128, K=4, bf16),
     4 drafted tokens each: every output, state and history."""
