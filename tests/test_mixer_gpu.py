@@ -137,11 +137,14 @@ def test_mixer_decode_layers(gdn, v):
     conv_close(C.cpu(), r["conv"])
 
 
-def test_mixer_decode_full_layer_b64(gdn):
-    """The full layer (hidden 2048, H_k=16, H_v=32, d=128) for B=64, one step,
-    bf16 output = RNE of the fp32 output."""
-    H, B = 2048, 64
-    case = make_case(BIG, [0] * B, act_dtype="bf16", seed=820, s0_std=0.02, conv0_std=1.0)
+@pytest.mark.parametrize("B", [1, 8, 64])
+def test_mixer_decode_full_layer(gdn, B):
+    """The full layer (hidden 2048, H_k=16, H_v=32, d=128), one step at the
+    benched batch sizes (B = 1 and 8: the one-slice product with the conv in
+    its epilogue; B = 64: two slices summed by the core), bf16 output = RNE
+    of the fp32 output."""
+    H = 2048
+    case = make_case(BIG, [0] * B, act_dtype="bf16", seed=820 + B, s0_std=0.02, conv0_std=1.0)
     proj = make_projections(BIG, H, seed=821)
     x = make_hidden(B, H, seed=822)
     prm, pj = P.dev_params(case), dev_proj(proj)
