@@ -497,11 +497,11 @@ def main():
         multi[t_new] = (ev_m[0].elapsed_time(ev_m[1]) / calls, calls)
 
     # The per-channel-decay variant (Kimi Delta Attention) on the same batch:
-    # one token per sequence and four.
+    # one, four and eight tokens per sequence.
     from gdn_inputs import make_case
     kd = BIG.__class__(d.h_k, d.h_v, d.d_k, d.d_v, d.conv_k, "sigmoid", decay="channel")
     kcase = None if args.no_multi else make_case(kd, [0] * B, act_dtype="bf16", seed=5,
-                                                  s0_std=0.02, conv0_std=1.0, decode_steps=4)
+                                                  s0_std=0.02, conv0_std=1.0, decode_steps=8)
     kda = {}
     kda_pf = None
     if kcase is not None:
@@ -509,7 +509,7 @@ def main():
                           decay="channel")
         kparams = {k: v.to(dev) for k, v in kcase.params.items()}
         S_k, c_k = kcase.S0.to(dev), kcase.conv0.to(dev)
-        for t_new in (1, 4):
+        for t_new in (1, 4, 8):
             xm = [kcase.dec[k][:t_new].transpose(0, 1).to(bf).to(dev).contiguous()
                   for k in ("qkv", "z", "a", "b")]
             out_m = torch.empty((B, t_new, d.value_dim), dtype=bf, device=dev)
