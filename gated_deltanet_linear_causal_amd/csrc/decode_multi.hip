@@ -416,7 +416,7 @@ decode_multi_kernel(const MultiArgs p)
                 acc = fmaf(tap[1], win[1], acc);
                 acc = fmaf(tap[2], win[2], acc);
                 acc = fmaf(tap[3], xs[t], acc);
-                cb[(size_t)t * nch + l] = siluf_(acc);
+                cb[(size_t)t * nch + l] = acc * sigmoid_hw(acc);
                 win[0] = win[1];
                 win[1] = win[2];
                 win[2] = xs[t];
@@ -433,7 +433,7 @@ decode_multi_kernel(const MultiArgs p)
     for (int i = tid; i < ngate; i += NT) {
         const int hv = value_head_of(hk, i % group, p.h_k, group, p.tiled);
         const float br = i == tid ? sum2(gb0, gb1) : in1(pb, gate_index(i, p.ld_b));
-        sgate[2 * i + 0] = __builtin_amdgcn_rcpf(1.0f + __expf(-br));
+        sgate[2 * i + 0] = sigmoid_hw(br);
         if (!CH) {
             const float ar = i == tid ? sum2(ga0, ga1) : in1(pa, gate_index(i, p.ld_a));
             const float g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplus_hw(ar + p.dt_bias[hv]);
@@ -760,10 +760,10 @@ decode_multi_kernel(const MultiArgs p)
             const float4 z4 = *reinterpret_cast<const float4 *>(sz + 4 * (size_t)q);
             const float rn = rsqrtf(ss / DV + p.norm_eps);
             float4 y;
-            y.x = o[0] * rn * w4.x * gatef_(z4.x, p.gate);
-            y.y = o[1] * rn * w4.y * gatef_(z4.y, p.gate);
-            y.z = o[2] * rn * w4.z * gatef_(z4.z, p.gate);
-            y.w = o[3] * rn * w4.w * gatef_(z4.w, p.gate);
+            y.x = o[0] * rn * w4.x * gate_hw(z4.x, p.gate);
+            y.y = o[1] * rn * w4.y * gate_hw(z4.y, p.gate);
+            y.z = o[2] * rn * w4.z * gate_hw(z4.z, p.gate);
+            y.w = o[3] * rn * w4.w * gate_hw(z4.w, p.gate);
             if (p.out_split)
                 store_split4(p.out, out_index(q, p.value_dim), p.split_off, y);
             else

@@ -115,6 +115,14 @@ __device__ __forceinline__ float softplus_hw(float x)
 {
     return x > 20.0f ? x : fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x)));
 }
+// σ and the output gate with the hardware exponential and reciprocal (a few
+// ulp), for the decode kernel's conv, gates and output, where a handful of
+// threads per value head compute them while the rest of the workgroup waits.
+__device__ __forceinline__ float sigmoid_hw(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float gate_hw(float z, int sigmoid_gate)
+{
+    return sigmoid_gate ? sigmoid_hw(z) : z * sigmoid_hw(z);
+}
 __device__ __forceinline__ float gatef_(float z, int sigmoid_gate)
 {
     return sigmoid_gate ? sigmoidf_(z) : siluf_(z);

@@ -317,7 +317,7 @@ template <int W> __device__ __forceinline__ float row_sum(float v)
 // parity tolerance is orders of magnitude wider).
 __device__ __forceinline__ float silu_fast(float x)
 {
-    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+    return x * sigmoid_hw(x);
 }
 
 // silu(causal conv) of 4 channels from the 4 taps' raw inputs.
