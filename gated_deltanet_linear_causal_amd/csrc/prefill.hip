@@ -1021,7 +1021,7 @@ tri_kernel(const PrefillArgs p)
     // (with one decay per key channel the decay is already inside the Gram
     // tiles and the k operand: only beta is needed here)
     if (KDA && wave == 0) {
-        const float beta = lane < Lc ? sigmoidf_(b_raw) : 0.0f;
+        const float beta = lane < Lc ? sigmoid_hw(b_raw) : 0.0f;
         sG[lane] = 0.0f;
         sB[lane] = beta;
         sBE[lane] = beta;
@@ -1029,8 +1029,8 @@ tri_kernel(const PrefillArgs p)
     if (!KDA && wave == 0) {
         float beta = 0.0f, g = 0.0f;
         if (lane < Lc) {
-            beta = sigmoidf_(b_raw);
-            g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplusf_(a_raw + dt_b);
+            beta = sigmoid_hw(b_raw);
+            g = decay_coef_of(p.a_log, p.decay_coef, hv) * softplus_hw(a_raw + dt_b);
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -1038,13 +1038,13 @@ tri_kernel(const PrefillArgs p)
             if (lane >= off) g += u;
         }
         const float gC = __shfl(g, 63, 64);
-        const float eg = expf(g);
+        const float eg = __expf(g);
         sG[lane] = g;
         sB[lane] = beta;
         sBE[lane] = beta * eg;
         float *gf = p.ws_gf + ((size_t)hv * p.ns + slot) * (2 * kC);
         gf[lane] = eg;
-        gf[kC + lane] = expf(gC - g);
+        gf[kC + lane] = __expf(gC - g);
     }
     __syncthreads();
 
@@ -1612,10 +1612,10 @@ norm_kernel(const PrefillArgs p, int rows, int conv_blocks, int conv_bx)
         ss = group_sum<LPR>(ss);
         const float rn = rsqrtf(ss / DV + p.norm_eps);
         float4 y;
-        y.x = o[k][0] * rn * w[0] * gatef_(z[k][0], p.gate);
-        y.y = o[k][1] * rn * w[1] * gatef_(z[k][1], p.gate);
-        y.z = o[k][2] * rn * w[2] * gatef_(z[k][2], p.gate);
-        y.w = o[k][3] * rn * w[3] * gatef_(z[k][3], p.gate);
+        y.x = o[k][0] * rn * w[0] * gate_hw(z[k][0], p.gate);
+        y.y = o[k][1] * rn * w[1] * gate_hw(z[k][1], p.gate);
+        y.z = o[k][2] * rn * w[2] * gate_hw(z[k][2], p.gate);
+        y.w = o[k][3] * rn * w[3] * gate_hw(z[k][3], p.gate);
         if (rbase + k * RPW < rows) {
             if (p.out_split)
                 store_split4(p.out, base[k], (size_t)p.t_total * p.value_dim, y);
