@@ -232,7 +232,7 @@ __global__ void __launch_bounds__(256, 2) skinny_gemm_kernel(const SkinnyGemm p,
             for (int t = 0; t < 3; ++t)
                 if (t < K - 1) a = fmaf(w[t], hist[r][t], a);
             a = fmaf(w[K - 1], acc[0][r], a);
-            y[r] = blk == 0 ? siluf_(a) : acc[0][r];
+            y[r] = blk == 0 ? a * sigmoid_hw(a) : acc[0][r];
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(256) proj_epilogue_kernel(const ProjEpilogue p
             if (s < K - 1)
                 *reinterpret_cast<f32x4 *>(h + (size_t)s * cols) = s + 1 < K - 1 ? hist[s + 1] : x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = siluf_(acc[e]);
+        for (int e = 0; e < 4; ++e) x[e] = acc[e] * sigmoid_hw(acc[e]);
     }
     *reinterpret_cast<f32x4 *>(p.dst[blk] + (size_t)m * cols + j) = x;
 }
