@@ -145,9 +145,12 @@ __device__ __forceinline__ int value_head_of(int hk, int hl, int h_k, int group,
 // Coefficient of softplus in the log-decay g of value head hv: -exp(A_log),
 // or the coefficient itself when a layer stores it directly (GGUF ssm_a;
 // "oxinfer 0.0.5 src/qwen.rs", weight loading).
+// (one load from whichever array is given, so that the load is not under a
+// branch; the hardware exponential, ~1e-7 relative)
 __device__ __forceinline__ float decay_coef_of(const float *a_log, const float *decay_coef, int hv)
 {
-    return decay_coef ? decay_coef[hv] : -expf(a_log[hv]);
+    const float raw = (decay_coef ? decay_coef : a_log)[hv];
+    return decay_coef ? raw : -__expf(raw);
 }
 
 // Sum over the lanes of an aligned group of W lanes (W a power of two <= 64).
