@@ -44,9 +44,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CALIB_BYTES = 1 << 30          # the calibration copy reads and writes 1 GiB
+# (the kernels of the measured launches and the device helpers they include)
 KERNEL_SOURCES = ["gated_deltanet_linear_causal_amd/csrc/decode.hip",
                   "gated_deltanet_linear_causal_amd/csrc/decode_multi.hip",
-                  "gated_deltanet_linear_causal_amd/csrc/prefill.hip"]
+                  "gated_deltanet_linear_causal_amd/csrc/prefill.hip",
+                  "gated_deltanet_linear_causal_amd/csrc/gdn_device.h"]
 DECODE_KERNELS = ("decode_multi_kernel", "decode_kernel")
 
 
