@@ -985,7 +985,7 @@ tri_kernel(const PrefillArgs p)
     // ---- loads needed only after the solve, issued right after the Gram
     // rows (loads complete in issue order, so they do not delay the Gram
     // rows) and in flight during the gates, A, P and the solve: raw v
-    // inputs, thread (channel group cg, token group tg)
+    // inputs, thread (channel group cg, token group tg), and the v taps
     typedef typename RawAct<TIn>::type RawT;
     const TIn *x = static_cast<const TIn *>(p.qkv);
     const int cg = tid % CG, tg = tid / CG;
@@ -996,22 +996,6 @@ tri_kernel(const PrefillArgs p)
     for (int j = 0; j < VWIN; ++j) {
         const int tau = min(max(vt0 - 3 + j, 0), L - 1);
         vraw[j] = RawAct<TIn>::load(x, (size_t)(s0 + tau) * p.conv_dim + vch);
-    }
-    // k^T fragments for the W^T tiles of this wave: column blocks 2 sp and
-    // 2 sp + 1 of d_k (sp = wave), both token steps
-    const int sp = wave;
-    const bool wact = sp < KS;
-    Frag kA[2][2];
-    if (wact) {
-        const __bf16 *kt = (KDA ? p.ws_kw + ((size_t)hv * p.ns + slot) * (2 * kC * DK)
-                                : p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK)) + lane * 8;
-#pragma unroll
-        for (int n2 = 0; n2 < 2; ++n2)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int f = ((2 * sp + n2) * 2 + s) * 2;
-                kA[n2][s] = frag_at(kt + (size_t)f * 512, kt + (size_t)(f + 1) * 512);
-            }
     }
     float wv[4][4];
     load_taps4(p, vch, wv);
@@ -1115,6 +1099,26 @@ tri_kernel(const PrefillArgs p)
                 for (int e = 0; e < 4; ++e) sT[(16 * b + 4 * kq + e) * LC + 16 * bj + col] = 0.0f;
     }
     __syncthreads();
+    // k^T fragments for the W^T tiles of this wave: column blocks 2 sp and
+    // 2 sp + 1 of d_k (sp = wave), both token steps.  Issued only now, in
+    // flight during the off-diagonal blocks and the v conv: issued with the
+    // Gram rows, every resident workgroup's 32 KB of them queued ahead of
+    // the next workgroups' gates and Gram rows (bench-step prefill 269-272
+    // against 274-280 us).
+    const int sp = wave;
+    const bool wact = sp < KS;
+    Frag kA[2][2];
+    if (wact) {
+        const __bf16 *kt = (KDA ? p.ws_kw + ((size_t)hv * p.ns + slot) * (2 * kC * DK)
+                                : p.ws_ktf + ((size_t)hk * p.ns + slot) * (2 * kC * DK)) + lane * 8;
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int f = ((2 * sp + n2) * 2 + s) * 2;
+                kA[n2][s] = frag_at(kt + (size_t)f * 512, kt + (size_t)(f + 1) * 512);
+            }
+    }
     // Off-diagonal blocks, by distance d from the diagonal, on the matrix
     // cores (split products, fp32 accumulate):
     //   T_ij = -T_ii (sum_{m=j}^{i-1} A_im T_mj);
