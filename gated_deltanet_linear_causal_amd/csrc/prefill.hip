@@ -1312,6 +1312,9 @@ scan_kernel(const PrefillArgs p, int slices)
         // and e^{G_C} (phase 2).  The loads are unconditional (the last chunk
         // reloads itself) so that the compiler's load counters stay exact and
         // each wait covers only its own group, never the prefetch behind it.
+        // U is the one operand only this workgroup reads, once: its loads are
+        // non-temporal, which leaves the cache to the operands the head's
+        // slices share (T=4096: 139.4 against 146.2 us).
 #define GDN_CHAIN_LOAD1(CH)                                                                    \
         {                                                                                      \
             const size_t off = (size_t)(CH) * (2 * kC * DK);                                   \
@@ -1320,7 +1323,8 @@ scan_kernel(const PrefillArgs p, int slices)
                 cW[s] = frag_at(wf + off + f * 512, wf + off + (f + 1) * 512);                 \
             }                                                                                  \
             _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                  \
-                cU[nt] = ld4(uf + (size_t)(CH) * kC * p.d_v + nt * 4 * 256);                   \
+                cU[nt] = __builtin_nontemporal_load(                                           \
+                    reinterpret_cast<const f32x4 *>(uf + (size_t)(CH) * kC * p.d_v + nt * 4 * 256)); \
         }
 #define GDN_CHAIN_LOAD1B(CH) cEGC = ld4(gf + (size_t)(CH) * (2 * kC) + kC + 16 * w + 4 * kq);
 #define GDN_CHAIN_LOAD2(CH)                                                                    \
