@@ -44,11 +44,13 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CALIB_BYTES = 1 << 30          # the calibration copy reads and writes 1 GiB
-# (the kernels of the measured launches and the device helpers they include)
+# (the kernels of the measured launches and the local headers they include:
+# device helpers, and the constants the kernels are compiled with)
 KERNEL_SOURCES = ["gated_deltanet_linear_causal_amd/csrc/decode.hip",
                   "gated_deltanet_linear_causal_amd/csrc/decode_multi.hip",
                   "gated_deltanet_linear_causal_amd/csrc/prefill.hip",
-                  "gated_deltanet_linear_causal_amd/csrc/gdn_device.h"]
+                  "gated_deltanet_linear_causal_amd/csrc/gdn_device.h",
+                  "gated_deltanet_linear_causal_amd/csrc/gdn_internal.h"]
 DECODE_KERNELS = ("decode_multi_kernel", "decode_kernel")
 
 

@@ -311,3 +311,29 @@ def test_config_struct_layout_matches_header():
                             "include", "gdn.h")).read()
     body = hdr[hdr.index("typedef struct {\n    int32_t h_k, h_v;"):hdr.index("} gdn_config;")]
     assert "int32_t state_cache;" in body and body.rstrip().endswith("*/")
+
+
+def test_traffic_counter_hash_covers_every_local_include():
+    """The stored HBM traffic counters are keyed by a hash of the measured
+    kernels' sources; every local header those kernels include must be part
+    of it, or an edit there would leave stale counters in the bench line."""
+    import re
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    hashed = {os.path.normpath(p) for p in bench.KERNEL_SOURCES}
+    todo = [p for p in bench.KERNEL_SOURCES if p.endswith(".hip")]
+    seen = set()
+    while todo:
+        rel = todo.pop()
+        if rel in seen:
+            continue
+        seen.add(rel)
+        with open(os.path.join(root, rel)) as f:
+            for inc in re.findall(r'^#include "([^"]+)"', f.read(), re.M):
+                dep = os.path.normpath(os.path.join(os.path.dirname(rel), inc))
+                if dep.startswith("include" + os.sep):
+                    continue  # the public C header: declarations only
+                assert dep in hashed, f"{rel} includes {dep}, which the traffic hash does not cover"
+                todo.append(dep)
